@@ -1,0 +1,344 @@
+"""Pins for the fp64 oracle against facts fixed by the pages and by mathematics (CPU only).
+
+Every check here is independent of the oracle's own code path: printed values
+from the pages (tests/golden), closed forms, an algebraic identity, scalar
+brute force written with complex-number rotations, special cases with known
+answers, and a library cross-check for the fp8 format.  The last group plants
+plausible mistakes into copies of the oracle and confirms the pins catch them.
+"""
+import cmath
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle.mla_oracle as orc
+from mla_latent_kv_40_amd import workloads as wl
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def rel_err(a, b):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    return float(np.max(np.abs(a - b)) / max(np.max(np.abs(b)), 1e-300))
+
+
+# ---------------------------------------------------------------- page values
+
+def test_katajob_snippet_shapes():
+    g = golden("katajob_code_shapes.json")
+    rng = np.random.default_rng(0)
+    x = rng.standard_normal((g["seq"], g["d_model"]))
+    W_down = rng.standard_normal((g["d_model"], g["d_latent"]))
+    W_up_k = rng.standard_normal((g["d_latent"], g["n_heads"] * g["d_head"]))
+    W_q = rng.standard_normal((g["d_model"], g["n_heads"] * g["d_head"]))
+    W_kr = rng.standard_normal((g["d_model"], 4))
+    W_qr = rng.standard_normal((g["d_model"], g["n_heads"] * 4))
+    C, KR, qC, qR = orc.project_from_hidden(x, W_down, W_kr, W_q, W_qr, g["n_heads"], g["d_head"], 4,
+                                            [g["seq"] - 1])
+    keys = orc.up_project(C, W_up_k, g["n_heads"], g["d_head"])
+    assert list(C.shape) == g["latent_shape"]
+    assert list(keys.shape) == g["keys_shape"]
+    # head-major layout: head i's key is the column block i*d_head .. of latent @ W_up_k
+    i = 5
+    blk = C @ W_up_k[:, i * g["d_head"]:(i + 1) * g["d_head"]]
+    assert np.allclose(keys[:, i, :], blk, rtol=0, atol=1e-9)
+
+
+def test_zenaique_mha_count_and_mla_row():
+    g = golden("zenaique_mha_cache_count.json")
+    mha = orc.mha_cache_elements_per_token(g["heads"], g["d_head"])
+    assert mha == 32768 and mha > g["mha_elements_exclusive_lower_bound"]
+    mla = orc.mla_cache_elements_per_token(g["latent_dim"], 64)
+    assert mla == 576
+    assert round(mha / mla, 1) == 56.9
+    # the tiny case: 2*8*64 = 1024 against 64 + 16 = 80
+    assert orc.mha_cache_elements_per_token(8, 64) == 1024
+    assert orc.mla_cache_elements_per_token(64, 16) == 80
+
+
+def test_podcast_gqa_sizing():
+    g = golden("podcast_gqa_sizing.json")
+    b = orc.gqa_cache_bytes_per_token(g["layers"], g["kv_heads"], g["d_head"], g["bytes_per_value"])
+    assert b == g["bytes_per_token"]
+    assert b // 1024 == g["kib_per_token"]
+    assert round(b * g["tokens"] / 2**30, 2) == g["gib_rounded_2dp"]
+
+
+def test_talentme_footprint_context():
+    g = golden("talentme_footprint.json")
+    assert 1 - g["mla_gb"] / g["gqa_variant_gb"] >= g["stated_min_reduction"]
+    # 2 H d for the DeepSeek-V2-shaped heads dwarfs d_c
+    assert orc.mha_cache_elements_per_token(128, 128) > 50 * g["d_c"]
+
+
+# ------------------------------------------------------------ brute force
+
+def _rot_complex(v, pos, base):
+    """RoPE written as complex multiplication: pair (v[2j], v[2j+1]) is the complex number
+    v[2j] + i v[2j+1], multiplied by exp(i * pos * base^(-2j/d))."""
+    d = len(v)
+    out = []
+    for j in range(d // 2):
+        z = complex(v[2 * j], v[2 * j + 1]) * cmath.exp(1j * pos * base ** (-2.0 * j / d))
+        out += [z.real, z.imag]
+    return out
+
+
+def brute_force(C, KR, qC, qR, W_UK, W_UV, L, scale, base):
+    """Scalar Python loops, no numpy arithmetic: every head's key and value is rebuilt
+    element by element from the latent, scores formed, softmax taken, values summed."""
+    C = np.asarray(C, dtype=np.float64).tolist()
+    KR = np.asarray(KR, dtype=np.float64).tolist()
+    qC = np.asarray(qC, dtype=np.float64).tolist()
+    qR = np.asarray(qR, dtype=np.float64).tolist()
+    W_UK = np.asarray(W_UK, dtype=np.float64).tolist()
+    W_UV = np.asarray(W_UV, dtype=np.float64).tolist()
+    Sq, H, d_h = len(qC), len(qC[0]), len(qC[0][0])
+    d_c = len(C[0])
+    d_v = len(W_UV[0]) // H
+    o = [[[0.0] * d_v for _ in range(H)] for _ in range(Sq)]
+    ol = [[[0.0] * d_c for _ in range(H)] for _ in range(Sq)]
+    lse = [[0.0] * H for _ in range(Sq)]
+    for j in range(Sq):
+        p = L - Sq + j
+        for i in range(H):
+            qr = _rot_complex(qR[j][i], p, base)
+            scores = []
+            for t in range(p + 1):
+                kc = [sum(C[t][c] * W_UK[c][i * d_h + d] for c in range(d_c)) for d in range(d_h)]
+                kr = _rot_complex(KR[t], t, base)
+                s = sum(qC[j][i][d] * kc[d] for d in range(d_h)) + sum(a * b for a, b in zip(qr, kr))
+                scores.append(s * scale)
+            m = max(scores)
+            z = sum(math.exp(s - m) for s in scores)
+            lse[j][i] = m + math.log(z)
+            for t, s in enumerate(scores):
+                w = math.exp(s - lse[j][i])
+                for v in range(d_v):
+                    o[j][i][v] += w * sum(C[t][c] * W_UV[c][i * d_v + v] for c in range(d_c))
+                for c in range(d_c):
+                    ol[j][i][c] += w * C[t][c]
+    return {"o": np.array(o), "o_lat": np.array(ol), "lse": np.array(lse)}
+
+
+def _small_case(seed=3, L=10, Sq=1, H=3, d_h=4, d_c=5, d_r=4, d_v=3, base=10000.0):
+    rng = np.random.default_rng(seed)
+    return dict(C=rng.standard_normal((L, d_c)), KRraw=rng.standard_normal((L, d_r)),
+                qC=rng.standard_normal((Sq, H, d_h)), qR=rng.standard_normal((Sq, H, d_r)),
+                W_UK=rng.standard_normal((d_c, H * d_h)) / np.sqrt(d_c),
+                W_UV=rng.standard_normal((d_c, H * d_v)) / np.sqrt(d_c),
+                kv_len=L, softmax_scale=1 / np.sqrt(d_h + d_r), rope_base=base)
+
+
+def _brute(case):
+    return brute_force(case["C"], case["KRraw"], case["qC"], case["qR"], case["W_UK"], case["W_UV"],
+                       case["kv_len"], case["softmax_scale"], case["rope_base"])
+
+
+@pytest.mark.parametrize("Sq", [1, 3])
+def test_bruteforce_ten_tokens(Sq):
+    case = _small_case(Sq=Sq, base=7.0)   # small base: large angles exercise the rotation
+    ref = _brute(case)
+    got = orc.decode(**case)
+    for k in ("o", "o_lat", "lse"):
+        assert rel_err(got[k], ref[k]) < 1e-12, k
+
+
+def test_lse_is_log_sum_exp_of_scores():
+    case = _small_case(L=7)
+    got = orc.decode(**case)
+    # scores by the absorbed route, exp-summed directly
+    qa = orc.absorbed_query(case["qC"], case["qR"], case["W_UK"], [6], case["rope_base"])
+    rows = np.concatenate([case["C"], orc.rope(case["KRraw"], np.arange(7), case["rope_base"])], 1)
+    s = np.einsum("hr,tr->ht", qa[0], rows) * case["softmax_scale"]
+    assert np.allclose(np.exp(got["lse"][0]), np.exp(s).sum(axis=1), rtol=1e-13, atol=0)
+
+
+# ----------------------------------------------------------- algebraic identity
+
+def test_absorbed_equals_unabsorbed_tiny_from_x():
+    w = wl.get("tiny_f32")
+    bt = wl.draw_batch(w)
+    W = bt.weights
+    L = int(bt.kv_lens[0])
+    C, KR, qC, qR = orc.project_from_hidden(W["x"], W["W_down"], W["W_KR"], W["W_Q"], W["W_QR"],
+                                            w.heads, w.d_h, w.d_r, [L - 1])
+    a = orc.decode(C, KR, qC, qR, W["W_UK"], W["W_UV"], L, w.softmax_scale, w.rope_base)
+    b = orc.decode_absorbed(C, KR, qC, qR, W["W_UK"], W["W_UV"], L, w.softmax_scale, w.rope_base)
+    for k in ("o", "o_lat", "lse"):
+        assert rel_err(a[k], b[k]) < 1e-12, k
+    # softmax scale is 1/sqrt(d_h + d_R) = 1/sqrt(80), not the latent width
+    assert abs(w.softmax_scale - 1 / math.sqrt(80)) < 1e-15
+
+
+def test_absorbed_equals_unabsorbed_dsv2_shapes():
+    w = wl.get("dsv2_b16_l4k")
+    rng = np.random.default_rng(11)
+    L = 10
+    C = rng.standard_normal((L, 512))
+    KR = rng.standard_normal((L, 64))
+    qC = rng.standard_normal((2, 128, 128))
+    qR = rng.standard_normal((2, 128, 64))
+    W_UK = rng.standard_normal((512, 128 * 128)) / np.sqrt(512)
+    W_UV = rng.standard_normal((512, 128 * 128)) / np.sqrt(512)
+    a = orc.decode(C, KR, qC, qR, W_UK, W_UV, L, w.softmax_scale)
+    b = orc.decode_absorbed(C, KR, qC, qR, W_UK, W_UV, L, w.softmax_scale)
+    for k in ("o", "o_lat", "lse"):
+        assert rel_err(a[k], b[k]) < 1e-12, k
+    assert abs(w.softmax_scale - 1 / math.sqrt(192)) < 1e-15
+    # out_project of the latent-space output gives the layer output
+    assert rel_err(orc.out_project(a["o_lat"], W_UV), a["o"]) < 1e-12
+
+
+# ------------------------------------------------------------ special cases
+
+def test_single_token_output_is_its_value():
+    case = _small_case(L=1)
+    got = orc.decode(**case)
+    H = case["qC"].shape[1]
+    V0 = (case["C"][0] @ case["W_UV"]).reshape(H, -1)
+    assert np.allclose(got["o"][0], V0, rtol=0, atol=1e-14)
+    assert np.allclose(got["o_lat"][0], np.broadcast_to(case["C"][0], (H, 5)), rtol=0, atol=1e-14)
+
+
+def test_equal_scores_give_mean_of_values():
+    case = _small_case(L=9)
+    case["qC"][:] = 0.0
+    case["qR"][:] = 0.0
+    got = orc.decode(**case)
+    H = case["qC"].shape[1]
+    mean_v = (case["C"].mean(axis=0) @ case["W_UV"]).reshape(H, -1)
+    assert np.allclose(got["o"][0], mean_v, rtol=0, atol=1e-14)
+    assert np.allclose(got["lse"], math.log(9), rtol=0, atol=1e-14)
+
+
+def test_score_shift_leaves_output_unchanged():
+    # appending a constant 1 to every latent and a matching column to the folded query
+    # adds the same constant to every score: weights and outputs must not move.
+    case = _small_case(L=8)
+    base = orc.decode(**case)
+    c2 = dict(case)
+    c2["C"] = np.concatenate([case["C"], np.ones((8, 1))], axis=1)
+    H, d_h = case["qC"].shape[1:]
+    extra = np.zeros((1, H * d_h))
+    extra[0, 0::d_h] = 1.0        # row that maps the constant onto each head's first key dim
+    c2["W_UK"] = np.concatenate([case["W_UK"], extra], axis=0)
+    c2["W_UV"] = np.concatenate([case["W_UV"], np.zeros((1, case["W_UV"].shape[1]))], axis=0)
+    shifted = orc.decode(**c2)
+    assert rel_err(shifted["o"], base["o"]) < 1e-12
+    # the shift changes lse by exactly the added score q^C[:,0]*scale
+    delta = case["qC"][0, :, 0] * case["softmax_scale"]
+    assert np.allclose(shifted["lse"][0] - base["lse"][0], delta, rtol=0, atol=1e-12)
+
+
+def test_rope_invariants():
+    rng = np.random.default_rng(5)
+    v = rng.standard_normal((6, 64))
+    pos = rng.integers(0, 40000, 6)
+    r = orc.rope(v, pos)
+    assert np.allclose(np.linalg.norm(r, axis=1), np.linalg.norm(v, axis=1), rtol=1e-13)
+    assert np.array_equal(orc.rope(v, np.zeros(6)), v)
+    q, k = v[0], v[1]
+    for p, t, dlt in [(9, 3, 17), (32767, 100, 5), (4, 4, 1000)]:
+        s0 = orc.rope(q, p) @ orc.rope(k, t)
+        s1 = orc.rope(q, p + dlt) @ orc.rope(k, t + dlt)
+        assert abs(s0 - s1) < 1e-9 * np.linalg.norm(q) * np.linalg.norm(k)
+    # one pair, base irrelevant for j = 0: (1, 0) at position 1 rotates by one radian
+    assert np.allclose(orc.rope(np.array([1.0, 0.0]), 1), [math.cos(1), math.sin(1)], atol=1e-15)
+
+
+def test_causal_multi_query_reduces_to_single_query():
+    case = _small_case(L=12, Sq=4)
+    multi = orc.decode(**case)
+    for j in range(4):
+        single = dict(case)
+        single["qC"] = case["qC"][j:j + 1]
+        single["qR"] = case["qR"][j:j + 1]
+        single["kv_len"] = 12 - 4 + j + 1
+        one = orc.decode(**single)
+        for k in ("o", "o_lat", "lse"):
+            assert rel_err(multi[k][j], one[k][0]) < 1e-13, (j, k)
+
+
+def test_chunking_and_head_subset_do_not_change_results():
+    case = _small_case(L=23, Sq=2, H=5)
+    full = orc.decode(**case)
+    chunked = orc.decode(**case, chunk=4)
+    sub = orc.decode(**case, heads=[4, 1])
+    for k in ("o", "o_lat", "lse"):
+        assert rel_err(chunked[k], full[k]) < 1e-13
+        assert rel_err(sub[k], full[k][:, [4, 1]]) < 1e-13
+
+
+# --------------------------------------------------------------------- fp8
+
+def test_e4m3_matches_torch_cast():
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(7)
+    x = np.concatenate([
+        rng.standard_normal(400_000) * 50,
+        rng.standard_normal(300_000) * 0.02,             # subnormal range
+        rng.uniform(-448, 448, 300_000),
+        np.array([0.0, 448.0, -448.0, 2.0**-9, 2.0**-10, 3 * 2.0**-11, 0.5 * (416 + 448)]),
+    ]).astype(np.float32)
+    x = np.clip(x, -448, 448)
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = orc.e4m3_round(x.astype(np.float64))
+    assert np.array_equal(got, ref)
+
+
+def test_fp8_row_quantiser():
+    rng = np.random.default_rng(8)
+    rows = rng.standard_normal((200, 576))
+    rows[3] = 0.0
+    codes, scale = orc.quantize_rows_fp8(rows)
+    assert scale.dtype == np.float32 and scale[3] == 1.0
+    amax = np.abs(codes).max(axis=1)
+    assert np.all(amax[np.arange(200) != 3] == 448.0)
+    assert np.all(amax <= 448.0)
+    rec = codes * scale[:, None].astype(np.float64)
+    # 3 mantissa bits: error at most half a step, i.e. 2^-4 of the value (plus the subnormal floor)
+    err = np.abs(rec - rows)
+    assert np.all(err <= np.abs(rows) * 2.0**-4 + scale[:, None] * 2.0**-10 + 1e-30)
+
+
+# ------------------------------------------------------ planted mistakes are caught
+
+def _planted_decode(kind):
+    """A copy of the oracle's decode with one plausible mistake."""
+    def bad(C, KRraw, qC, qR, W_UK, W_UV, kv_len, softmax_scale, rope_base=10000.0, **kw):
+        C = np.asarray(C, float)
+        Sq, H, d_h = np.shape(qC)
+        if kind == "drop_positional":
+            qR = np.zeros_like(qR)
+        elif kind == "dim_major_reshape":        # reshape (L, d_h, H) instead of (L, H, d_h)
+            W_UK = np.asarray(W_UK).reshape(-1, d_h, H).transpose(0, 2, 1).reshape(-1, H * d_h)
+        elif kind == "rope_sign":
+            KRraw = np.asarray(KRraw, float).copy()
+            KRraw[:, 1::2] *= -1
+        elif kind == "scale_latent_width":
+            softmax_scale = 1 / np.sqrt(C.shape[1] + np.shape(qR)[-1])
+        elif kind == "off_by_one_mask":
+            kv_len = kv_len - 1
+            C = C[:]
+        return orc.decode(C, KRraw, qC, qR, W_UK, W_UV, kv_len, softmax_scale, rope_base, **kw)
+    return bad
+
+
+@pytest.mark.parametrize("kind", ["drop_positional", "dim_major_reshape", "rope_sign",
+                                  "scale_latent_width", "off_by_one_mask"])
+def test_planted_mistake_fails_bruteforce_pin(kind):
+    case = _small_case(L=10, H=3, d_h=4, d_c=5, d_r=4, base=7.0)
+    ref = _brute(case)
+    got = _planted_decode(kind)(**case)
+    errs = [rel_err(got[k], ref[k]) if got[k].shape == ref[k].shape else 1.0 for k in ("o", "lse")]
+    assert max(errs) > 1e-6, kind
