@@ -1,0 +1,203 @@
+/*
+ * libmla -- Multi-head Latent Attention (MLA) decode over a paged latent cache, for AMD
+ * Instinct MI355X (gfx950).  Plain C ABI: pointers and sizes only.
+ *
+ * The method (katajob interview page "What does Multi-head Latent Attention compress ...",
+ * sections "The mechanism" and "Why it is not just extra work at decode time"; zenaique
+ * "How does DeepSeek's Multi-Latent Attention (MLA) compress the KV cache below GQA?",
+ * "What MLA caches versus what MHA and GQA cache"):
+ *   - each token is cached only as a latent c_t (d_c values) plus a small positional key
+ *     k_R,t (d_R values, RoPE applied) that is shared by all heads;
+ *   - the per-head key up-projection W_UK is folded into the query, and the value
+ *     up-projection W_UV is applied to the output once per query, so attention runs
+ *     directly against the cached rows [c_t ; k_R,t] and per-head K and V never exist.
+ *
+ * One decode step is four calls on one stream:
+ *   mla_cache_append  write the step's new tokens into the paged cache (RoPE on k_R here)
+ *   mla_absorb_q      q_abs[t,i] = [ q^C_{t,i} W_UK,i^T ; RoPE(q^R_{t,i}, p_t) ]
+ *   mla_decode_attn   o_lat[t,i] = sum_s softmax_s(scale * q_abs[t,i] . row_s) c_s,  lse[t,i]
+ *   mla_out_proj      out[t,i]   = o_lat[t,i] W_UV,i
+ *
+ * Conventions shared by every call
+ *   Vectors are rows and weights are stored [in, out] with head-major output columns, as
+ *   in the katajob numpy snippet (keys = (latent @ W_up_k).reshape(seq, n_heads, d_head)):
+ *   head i of W_UK owns columns i*d_h .. i*d_h+d_h-1.  All arrays are row-major, contiguous,
+ *   device memory owned by the caller, 16-byte aligned.  Nothing is allocated or freed by
+ *   the library.  Every call validates its arguments before touching the device: on error
+ *   it returns a status and launches nothing.  Launches are asynchronous on `stream`
+ *   (a hipStream_t; NULL is the default stream); a launch failure returns MLA_ERR_HIP.
+ *   Calls on the same device may run from several host threads; calls that write the
+ *   same buffers must be ordered by the caller (same stream or events).
+ *
+ * Positions and the causal mask
+ *   Sequence b holds kv_len[b] tokens at positions 0 .. kv_len[b]-1; token t lives at
+ *   page block_table[b*max_blocks + t/64], slot t%64.  A step has Sq new query tokens per
+ *   sequence (rows t = b*Sq + j of the query arrays, j = 0..Sq-1); query j sits at
+ *   position p = kv_len[b] - Sq + j and attends to tokens 0..p.
+ *
+ * Number formats (mla_config_t.cache_dtype / act_dtype)
+ *   F32 cache with F32 activations   any head shape within the generic limits below
+ *   BF16 cache with BF16 activations DeepSeek-V2 shape (H=128, d_h=128, d_R=64, d_c=512,
+ *                                    d_v=128) on matrix cores; other shapes on the generic path
+ *   FP8_E4M3 cache with BF16 activ.  DeepSeek-V2 shape only.  Each cached row (all d_c+d_R
+ *                                    values of a token) is stored as OCP e4m3fn codes with
+ *                                    one fp32 scale = amax(row)/448 (1.0 for a zero row);
+ *                                    value = code * scale.  The folded query is likewise fp8
+ *                                    with one fp32 scale per (query row, head).
+ *   Generic limits: num_heads <= 128, d_c + d_R <= 1024, d_h <= 256, d_v <= 256.
+ *   All shapes: d_c, d_R, d_h, d_v multiples of 16, d_R even, block_size == 64.
+ */
+#ifndef LIBMLA_MLA_H
+#define LIBMLA_MLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MLA_OK = 0,
+  MLA_ERR_INVALID_ARG = 1,   /* null/misaligned pointer, bad size or shape */
+  MLA_ERR_UNSUPPORTED = 2,   /* valid but not implemented (format/shape combination) */
+  MLA_ERR_WORKSPACE = 3,     /* workspace missing or smaller than mla_decode_workspace_size */
+  MLA_ERR_HIP = 4            /* the HIP runtime reported an error (device query or launch) */
+} mla_status_t;
+
+typedef enum { MLA_F32 = 0, MLA_BF16 = 1, MLA_FP8_E4M3 = 2 } mla_dtype_t;
+
+typedef struct {
+  int32_t num_heads;     /* H */
+  int32_t d_c;           /* latent width (512 in DeepSeek-V2, talentme card "Core Definition") */
+  int32_t d_r;           /* decoupled RoPE key width */
+  int32_t d_h;           /* per-head content query/key width */
+  int32_t d_v;           /* per-head value width */
+  int32_t block_size;    /* tokens per cache page; must be 64 */
+  float softmax_scale;   /* multiplies q.k; 1/sqrt(d_h + d_r) for concatenated keys */
+  float rope_base;       /* RoPE frequency base (10000) */
+  int32_t cache_dtype;   /* mla_dtype_t of the cache rows */
+  int32_t act_dtype;     /* mla_dtype_t of q_nope, q_rope, c_kv, k_r, weights and out */
+} mla_config_t;
+
+/*
+ * mla_cache_append -- write n new tokens into the paged latent cache.
+ *
+ * Only the latent and the positional key are stored (podcast "What Is Multi-head Latent
+ * Attention ...": the system caches the compact latent and the positional part; zenaique:
+ * the latent is the only thing written to the cache).  RoPE is applied to k_R here, at the
+ * token's own position, because rotation does not commute with the absorbed up-projection
+ * (katajob, end of "Why it is not just extra work at decode time"; bembew "Multi-head
+ * Latent Attention", "Decoupling RoPE from Compression"; bembew "Implementation Logic",
+ * step 4).
+ *
+ *   cache        [num_blocks, 64, d_c + d_R] in cache_dtype; row = [c ; RoPE(k_R, pos)]
+ *   cache_scale  [num_blocks, 64] fp32, written for FP8 caches; must be NULL otherwise
+ *   c_kv         [n, d_c]  act_dtype      k_r [n, d_R] act_dtype, before RoPE
+ *   pos          [n] int32 (device)       position of each token within its sequence
+ *   seq_of       [n] int32 (device)       sequence of each token, 0 .. batch-1
+ *   block_table  [batch, max_blocks] int32 (device) physical page ids
+ * RoPE: the pair (2j, 2j+1) of k_R is rotated by pos * rope_base^(-2j/d_R); the angle
+ * and its cosine/sine are evaluated in fp64.
+ * A token whose sequence, page slot or page id is out of range is skipped (not written).
+ * FP8: scale = amax/448 in fp32, code = e4m3(value / scale), nearest-even, saturating.
+ */
+mla_status_t mla_cache_append(const mla_config_t* cfg, void* cache, float* cache_scale,
+                              int32_t num_blocks, const void* c_kv, const void* k_r,
+                              const int32_t* pos, const int32_t* seq_of,
+                              const int32_t* block_table, int32_t batch, int32_t max_blocks,
+                              int32_t n, void* stream);
+
+/*
+ * mla_absorb_q -- fold W_UK into the query and rotate the positional query.
+ *
+ * q_abs[t,i] = [ q_nope[t,i] W_UK,i^T ; RoPE(q_rope[t,i], q_pos[t]) ], W_UK,i = columns
+ * i*d_h .. i*d_h+d_h-1 of w_uk.  Since k^C = c W_UK,i, the content score q^C . k^C equals
+ * (q^C W_UK,i^T) . c (katajob "solid answer": the up-projections fold into the query and
+ * output projections; "Why it is not just extra work at decode time").
+ *
+ *   q_nope  [T, H, d_h] act_dtype      q_rope [T, H, d_R] act_dtype (before RoPE)
+ *   q_pos   [T] int32 (device)         w_uk [d_c, H*d_h] act_dtype
+ *   q_abs   [T, H, d_c + d_R]: act_dtype for F32/BF16 caches; e4m3 codes for FP8 caches
+ *   q_scale [T, H] fp32: FP8 caches only (amax/448 of the row), NULL otherwise
+ * Matrix-core path: bf16 products, fp32 accumulation, one rounding to the output format.
+ */
+mla_status_t mla_absorb_q(const mla_config_t* cfg, const void* q_nope, const void* q_rope,
+                          const int32_t* q_pos, const void* w_uk, void* q_abs, float* q_scale,
+                          int32_t T, void* stream);
+
+/*
+ * mla_decode_workspace_size -- bytes of scratch mla_decode_attn needs for batch B,
+ * Sq queries per sequence and block tables of width max_blocks on the current device.
+ * Returns 0 for invalid arguments.  The value depends only on these arguments and the
+ * device's compute-unit count (it bounds the split-K partial results).
+ */
+size_t mla_decode_workspace_size(const mla_config_t* cfg, int32_t B, int32_t Sq,
+                                 int32_t max_blocks);
+
+/*
+ * mla_decode_attn -- attention in latent space (katajob: after folding, the model "attends
+ * in the latent space directly"; zenaique: decode streams the whole cache from HBM, so the
+ * bytes per cached token set the ceiling).
+ *
+ * For every query row t = b*Sq + j and head i, over tokens s = 0 .. p (p = kv_len[b]-Sq+j):
+ *   score[s] = softmax_scale * (q_abs[t,i] . cache_row[s])       (content + positional)
+ *   o_lat[t,i] = sum_s softmax(score)[s] * c_s                   ([T, H, d_c] fp32)
+ *   lse[t,i]   = log sum_s exp(score[s])                         ([T, H] fp32, natural log)
+ * FP8: row values are code*cache_scale, query values code*q_scale.
+ * The token range is split across workgroups (split-K); partial results go to `workspace`
+ * and are merged by a log-sum-exp combine.  A sequence with kv_len <= 0 gives o_lat = 0 and
+ * lse = -inf.  Preconditions: Sq <= kv_len[b] <= 64*max_blocks (longer lengths are clamped
+ * to the table), pages in [0, num_blocks) (tokens on other pages are skipped).
+ *
+ *   q_abs       [T, H, d_c + d_R] (mla_absorb_q output)    q_scale [T, H] (FP8) or NULL
+ *   cache       [num_blocks, 64, d_c + d_R]                 cache_scale [num_blocks, 64] or NULL
+ *   block_table [B, max_blocks] int32 (device)              kv_lens [B] int32 (device)
+ *   workspace   >= mla_decode_workspace_size(cfg, B, Sq, max_blocks) bytes, 256-byte aligned;
+ *               contents need no initialisation and are not preserved.
+ */
+mla_status_t mla_decode_attn(const mla_config_t* cfg, const void* q_abs, const float* q_scale,
+                             const void* cache, const float* cache_scale, int32_t num_blocks,
+                             const int32_t* block_table, int32_t max_blocks,
+                             const int32_t* kv_lens, int32_t B, int32_t Sq, void* workspace,
+                             size_t ws_bytes, float* o_lat, float* lse, void* stream);
+
+/*
+ * mla_decode_split / mla_decode_combine -- the two launches of mla_decode_attn, for callers
+ * that time or schedule them separately.  Same arguments as mla_decode_attn; calling split
+ * then combine on one stream is exactly mla_decode_attn.  split writes o_lat/lse of every
+ * sequence that one token range covers whole and workspace partials for the others;
+ * combine merges the partials (and writes the kv_len <= 0 results).  On the generic
+ * (non-matrix-core) path split does all the work and combine launches nothing.
+ */
+mla_status_t mla_decode_split(const mla_config_t* cfg, const void* q_abs, const float* q_scale,
+                              const void* cache, const float* cache_scale, int32_t num_blocks,
+                              const int32_t* block_table, int32_t max_blocks,
+                              const int32_t* kv_lens, int32_t B, int32_t Sq, void* workspace,
+                              size_t ws_bytes, float* o_lat, float* lse, void* stream);
+mla_status_t mla_decode_combine(const mla_config_t* cfg, const void* q_abs, const float* q_scale,
+                                const void* cache, const float* cache_scale, int32_t num_blocks,
+                                const int32_t* block_table, int32_t max_blocks,
+                                const int32_t* kv_lens, int32_t B, int32_t Sq, void* workspace,
+                                size_t ws_bytes, float* o_lat, float* lse, void* stream);
+
+/*
+ * mla_out_proj -- apply W_UV once per query on the output side:
+ * out[t,i] = o_lat[t,i] W_UV,i, W_UV,i = columns i*d_v .. i*d_v+d_v-1 of w_uv
+ * (katajob "solid answer": the value up-projection folds into the output projection).
+ *   o_lat [T, H, d_c] fp32     w_uv [d_c, H*d_v] act_dtype     out [T, H, d_v] act_dtype
+ * Matrix-core path: o_lat rounded to bf16, fp32 accumulation.
+ */
+mla_status_t mla_out_proj(const mla_config_t* cfg, const float* o_lat, const void* w_uv,
+                          void* out, int32_t T, void* stream);
+
+/* Human-readable name of a status code (static storage). */
+const char* mla_status_string(mla_status_t status);
+
+/* ABI version of this header: 1. */
+int32_t mla_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LIBMLA_MLA_H */

@@ -1,0 +1,170 @@
+"""ctypes binding for libmla (include/mla.h): same entry-point names, argument marshalling only.
+
+Torch tensors supply device memory and the stream; every step of the decode path runs in
+the library's HIP kernels.  Loading fails loudly if ``libmla.so`` has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmla.so")
+
+MLA_OK, MLA_ERR_INVALID_ARG, MLA_ERR_UNSUPPORTED, MLA_ERR_WORKSPACE, MLA_ERR_HIP = range(5)
+MLA_F32, MLA_BF16, MLA_FP8_E4M3 = range(3)
+DTYPES = {"f32": MLA_F32, "bf16": MLA_BF16, "fp8": MLA_FP8_E4M3}
+
+EXPORTS = ("mla_cache_append", "mla_absorb_q", "mla_decode_workspace_size", "mla_decode_attn",
+           "mla_decode_split", "mla_decode_combine", "mla_out_proj", "mla_status_string", "mla_abi_version")
+
+
+class MlaConfig(ctypes.Structure):
+    _fields_ = [("num_heads", ctypes.c_int32), ("d_c", ctypes.c_int32), ("d_r", ctypes.c_int32),
+                ("d_h", ctypes.c_int32), ("d_v", ctypes.c_int32), ("block_size", ctypes.c_int32),
+                ("softmax_scale", ctypes.c_float), ("rope_base", ctypes.c_float),
+                ("cache_dtype", ctypes.c_int32), ("act_dtype", ctypes.c_int32)]
+
+
+class MlaError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn}: {msg}")
+        self.status = status
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libmla.so (once).  Raises if it is missing: there is no fallback path."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"libmla.so not built at {LIB_PATH}; run __graft_entry__.build() "
+                               "or python -m mla_latent_kv_40_amd.build")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, f32p = ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p
+        cfgp = ctypes.POINTER(MlaConfig)
+        L.mla_cache_append.argtypes = [cfgp, vp, f32p, i32, vp, vp, vp, vp, vp, i32, i32, i32, vp]
+        L.mla_absorb_q.argtypes = [cfgp, vp, vp, vp, vp, vp, f32p, i32, vp]
+        L.mla_decode_workspace_size.argtypes = [cfgp, i32, i32, i32]
+        L.mla_decode_workspace_size.restype = ctypes.c_size_t
+        for name in ("mla_decode_attn", "mla_decode_split", "mla_decode_combine"):
+            getattr(L, name).argtypes = [cfgp, vp, f32p, vp, f32p, i32, vp, i32, vp, i32, i32, vp, ctypes.c_size_t,
+                                         f32p, f32p, vp]
+        L.mla_out_proj.argtypes = [cfgp, f32p, vp, vp, i32, vp]
+        L.mla_status_string.argtypes = [ctypes.c_int]
+        L.mla_status_string.restype = ctypes.c_char_p
+        L.mla_abi_version.restype = ctypes.c_int32
+        for name in ("mla_cache_append", "mla_absorb_q", "mla_decode_attn", "mla_decode_split", "mla_decode_combine",
+                     "mla_out_proj"):
+            getattr(L, name).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+@dataclass
+class Config:
+    num_heads: int
+    d_c: int
+    d_r: int
+    d_h: int
+    d_v: int
+    softmax_scale: float
+    rope_base: float = 10000.0
+    cache_dtype: str = "bf16"
+    act_dtype: str = "bf16"
+    block_size: int = 64
+
+    def c(self) -> MlaConfig:
+        return MlaConfig(self.num_heads, self.d_c, self.d_r, self.d_h, self.d_v, self.block_size,
+                         self.softmax_scale, self.rope_base, DTYPES[self.cache_dtype], DTYPES[self.act_dtype])
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(fn: str, st: int) -> None:
+    if st != MLA_OK:
+        raise MlaError(fn, st, lib().mla_status_string(st).decode())
+
+
+def mla_cache_append(cfg: Config, cache, cache_scale, num_blocks, c_kv, k_r, pos, seq_of, block_table,
+                     batch, max_blocks, n, stream=None, check=True) -> int:
+    st = lib().mla_cache_append(ctypes.byref(cfg.c()), _ptr(cache), _ptr(cache_scale), num_blocks, _ptr(c_kv),
+                                _ptr(k_r), _ptr(pos), _ptr(seq_of), _ptr(block_table), batch, max_blocks, n,
+                                _stream(stream))
+    if check:
+        _check("mla_cache_append", st)
+    return st
+
+
+def mla_absorb_q(cfg: Config, q_nope, q_rope, q_pos, w_uk, q_abs, q_scale, T, stream=None, check=True) -> int:
+    st = lib().mla_absorb_q(ctypes.byref(cfg.c()), _ptr(q_nope), _ptr(q_rope), _ptr(q_pos), _ptr(w_uk),
+                            _ptr(q_abs), _ptr(q_scale), T, _stream(stream))
+    if check:
+        _check("mla_absorb_q", st)
+    return st
+
+
+def mla_decode_workspace_size(cfg: Config, B: int, Sq: int, max_blocks: int) -> int:
+    return int(lib().mla_decode_workspace_size(ctypes.byref(cfg.c()), B, Sq, max_blocks))
+
+
+def _decode(fn, cfg, q_abs, q_scale, cache, cache_scale, num_blocks, block_table, max_blocks, kv_lens, B, Sq,
+            workspace, ws_bytes, o_lat, lse, stream, check):
+    st = getattr(lib(), fn)(ctypes.byref(cfg.c()), _ptr(q_abs), _ptr(q_scale), _ptr(cache), _ptr(cache_scale),
+                            num_blocks, _ptr(block_table), max_blocks, _ptr(kv_lens), B, Sq, _ptr(workspace),
+                            ws_bytes, _ptr(o_lat), _ptr(lse), _stream(stream))
+    if check:
+        _check(fn, st)
+    return st
+
+
+def mla_decode_attn(cfg: Config, q_abs, q_scale, cache, cache_scale, num_blocks, block_table, max_blocks,
+                    kv_lens, B, Sq, workspace, ws_bytes, o_lat, lse, stream=None, check=True) -> int:
+    return _decode("mla_decode_attn", cfg, q_abs, q_scale, cache, cache_scale, num_blocks, block_table, max_blocks,
+                   kv_lens, B, Sq, workspace, ws_bytes, o_lat, lse, stream, check)
+
+
+def mla_decode_split(cfg: Config, q_abs, q_scale, cache, cache_scale, num_blocks, block_table, max_blocks,
+                     kv_lens, B, Sq, workspace, ws_bytes, o_lat, lse, stream=None, check=True) -> int:
+    return _decode("mla_decode_split", cfg, q_abs, q_scale, cache, cache_scale, num_blocks, block_table, max_blocks,
+                   kv_lens, B, Sq, workspace, ws_bytes, o_lat, lse, stream, check)
+
+
+def mla_decode_combine(cfg: Config, q_abs, q_scale, cache, cache_scale, num_blocks, block_table, max_blocks,
+                       kv_lens, B, Sq, workspace, ws_bytes, o_lat, lse, stream=None, check=True) -> int:
+    return _decode("mla_decode_combine", cfg, q_abs, q_scale, cache, cache_scale, num_blocks, block_table,
+                   max_blocks, kv_lens, B, Sq, workspace, ws_bytes, o_lat, lse, stream, check)
+
+
+def mla_out_proj(cfg: Config, o_lat, w_uv, out, T, stream=None, check=True) -> int:
+    st = lib().mla_out_proj(ctypes.byref(cfg.c()), _ptr(o_lat), _ptr(w_uv), _ptr(out), T, _stream(stream))
+    if check:
+        _check("mla_out_proj", st)
+    return st
+
+
+def mla_status_string(status: int) -> str:
+    return lib().mla_status_string(status).decode()
+
+
+def mla_abi_version() -> int:
+    return int(lib().mla_abi_version())
