@@ -81,7 +81,18 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="dsv2_b64_l1k_32k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a 256 MiB device-to-device copy 3 times (scales HBM counters)")
     a = ap.parse_args()
+    if a.calibrate_copy:
+        import torch
+        x = torch.empty(1 << 28, dtype=torch.uint8, device="cuda:0").fill_(1)
+        y = torch.empty_like(x)
+        for _ in range(3):
+            y.copy_(x)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": 1 << 28, "runs": 3}))
+        return 0
     if a.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {a.gpus}): the decode path is a single-GPU "
               "kernel; a multi-GPU split would shard whole sequences per GPU.", file=sys.stderr)

@@ -9,17 +9,16 @@
 // "Concept explanation"), which makes this kernel the step's bandwidth roofline.
 //
 // Matrix-core kernel (DeepSeek-V2 shape: H=128, d_c=512, d_R=64, bf16 cache)
-//   grid      G*Sq*2 workgroups: G token ranges split the batch's pages evenly ("stream-K":
-//             a range may span sequence boundaries), times Sq queries, times two head halves.
-//             blockIdx is remapped so that the workgroups sharing a range sit on one XCD and
-//             read each page through the same L2.
-//   block     256 threads = 4 waves (1 per SIMD); wave w owns 16 heads of the workgroup's 64
-//             and keeps their folded queries (72 VGPRs) and O^T (128 AGPRs) in registers.
-//   per page  (64 tokens = one tile) staged in LDS by 16-byte global->LDS loads, double
-//             buffered (2 x 72 KiB), rows XOR-swizzled at 16-byte granularity:
-//               S^T[64 tok, 16 heads] = Tile[64, 576] . Qabs^T     v_mfma_f32_16x16x32_bf16
+//   grid      G*Sq workgroups: G token ranges split the batch's pages evenly ("stream-K":
+//             a range may span sequence boundaries), times Sq queries.  blockIdx is remapped
+//             so that the Sq workgroups of one range sit on one XCD and share its L2.
+//   block     512 threads = 8 waves (2 per SIMD); all 128 heads of the query live in the
+//             workgroup, so every cached row is read from HBM once per query.
+//   per step  32 tokens (half a page) staged in LDS by 16-byte global->LDS loads, four
+//             stages in flight, rows XOR-swizzled at 16-byte granularity:
+//               S^T[32 tok, 16 heads] = Stage[32, 576] . Qabs^T   v_mfma_f32_16x16x32_bf16
 //               online softmax in the exp2 domain (rescale only when the max grows by > 8)
-//               O^T[512, 16 heads]   += Tile[:, :512]^T . P^T       (V^T via ds_read_tr16_b64)
+//               O^T[256 cols, 32 heads] += Stage[:, :512]^T . P^T (V^T via ds_read_b64_tr_b16)
 //   output    a range that covers a whole sequence writes o_lat/lse directly; otherwise it
 //             writes a normalised partial (O/l, lse) to the workspace slot g + b.
 #include "common.h"
@@ -43,9 +42,20 @@ struct DecodeArgs {
   float scale_log2;           // softmax_scale * log2(e)
 };
 
+// Read-only kernel inputs are read through the constant address space: with a uniform index
+// that is a scalar load, which the compiler may not prove safe through a plain pointer.
+__device__ __forceinline__ int ld_const(const int32_t* p, size_t i) {
+  return ((const __attribute__((address_space(4))) int32_t*)p)[i];
+}
+
+// Workgroup barrier without a memory fence: the caller has already waited for its own LDS
+// writes (lgkmcnt) and page DMA (vmcnt); the "memory" clobber keeps the compiler from moving
+// memory accesses across it.  (A fenced barrier would also wait for the pages in flight.)
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // tiles (pages) of sequence b that hold tokens, with kv_len clamped to the table width
 __device__ __forceinline__ int seq_tiles(const int32_t* kv_lens, int b, int max_blocks, int* L) {
-  int len = kv_lens[b];
+  int len = ld_const(kv_lens, b);
   len = len < 0 ? 0 : len;
   const int cap = max_blocks * kBlock;
   len = len > cap ? cap : len;
@@ -86,284 +96,365 @@ __device__ void scan_batch(const int32_t* kv_lens, int B, int max_blocks, long l
     }
     run += __shfl(incl, 63, 64);
   }
-  *total = run;
-  *seq = found_b;
-  *seq_first = found_s;
+  // wave-uniform results: hand them back as scalars
+  *total = ((long long)__builtin_amdgcn_readfirstlane((int)(run >> 32)) << 32) |
+           (unsigned)__builtin_amdgcn_readfirstlane((int)run);
+  *seq = __builtin_amdgcn_readfirstlane(found_b);
+  *seq_first = ((long long)__builtin_amdgcn_readfirstlane((int)(found_s >> 32)) << 32) |
+               (unsigned)__builtin_amdgcn_readfirstlane((int)found_s);
 }
 
-// LDS image of one page (73728 B): the 64 latent rows (1024 B each) first, then the 64
-// positional rows (128 B each).  Inside a latent row, 16-byte chunk c is stored at chunk
-// c ^ key(r) with key(r) = 8(r&1) + ((r>>1)&7); inside a positional row, chunk c is stored at
-// c ^ ((r>>1)&7).  With 64 banks (256 B) this makes the two access patterns conflict-free:
-// 16 consecutive rows reading one logical chunk (S operand) land on 16 distinct 16-byte bank
-// groups, and two rows of opposite parity reading the same 128 B (V operand) land in opposite
-// halves of the bank window.  XOR keys below 16 (8 for positional rows) keep chunks in-row.
-__device__ __forceinline__ int lat_key(int r) { return ((r & 1) << 3) | ((r >> 1) & 7); }
+// ---------------------------------------------------------------------------------------
+// LDS layout.  The page stream is cut into 32-token half pages; four stages of 36 KiB hold
+// the half page being computed and the next three in flight (global->LDS DMA).  One stage:
+// 32 latent rows of 1024 B, then 32 positional rows of 128 B.  Inside a latent row, 16-byte
+// chunk c is stored at c ^ key(r), key linear over GF(2) in the low four row bits (columns
+// 9, 11, 6, 7); inside a positional row at c ^ ((r>>1)&7).  The key was chosen by timing
+// the two read patterns on gfx950: 16 rows x one 16-byte chunk per lane group (S operand,
+// ds_read_b128) and 4 rows x 32 bytes per 16-lane group (V operand, ds_read_b64_tr_b16) both
+// run at the bank-conflict-free rate with it (plain row-parity keys leave one of them 2x
+// slower).  XOR keys below 16 (8) keep every chunk inside its row.
+// After the stages: one 16-byte P fragment per lane per wave (8 KiB) and a small per-wave
+// exchange area (rescale factors, flags, 1/l).
+constexpr unsigned long long kLatKeys = 0x3A815CE74DF62B90ull;   // key(r), r = 0..15, one nibble each
+constexpr int lat_key_c(int r) { return (int)((kLatKeys >> (4 * (r & 15))) & 15); }
+static_assert(lat_key_c(1) == 9 && lat_key_c(2) == 11 && lat_key_c(4) == 6 && lat_key_c(8) == 7 &&
+                  lat_key_c(15) == (9 ^ 11 ^ 6 ^ 7),
+              "latent-row XOR key is the linear map with columns 9, 11, 6, 7");
+__device__ __forceinline__ int lat_key(int r) { return lat_key_c(r); }
 __device__ __forceinline__ int pos_key(int r) { return (r >> 1) & 7; }
-constexpr int kLatBytes = kBlock * kDC * 2;       // 65536: offset of the positional rows
-
-// Wave w loads rows 16w .. 16w+15 of a page: sixteen 1 KiB latent rows (one row per
-// instruction, lane l fetches logical chunk l ^ key) and their 128-byte positional rows (two
-// instructions, lane l -> row 16w + 8u + l/8).  Rows at or past `nvalid` are fetched from row
-// 0 instead (finite data; their scores are masked).
-__device__ __forceinline__ void load_tile(uint8_t* lds_buf, const uint8_t* page, int nvalid, int wave, int lane) {
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int r = 16 * wave + i;
-    const int rs = r < nvalid ? r : 0;
-    const uint8_t* src = page + rs * (kRow * 2) + ((lane ^ lat_key(r)) << 4);
-    __builtin_amdgcn_global_load_lds((const void*)src, (MLA_LDS void*)(lds_buf + r * 1024), 16, 0, 0);
-  }
-#pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int r = 16 * wave + 8 * u + (lane >> 3);
-    const int rs = r < nvalid ? r : 0;
-    const uint8_t* src = page + rs * (kRow * 2) + kDC * 2 + (((lane & 7) ^ pos_key(r)) << 4);
-    __builtin_amdgcn_global_load_lds((const void*)src,
-                                     (MLA_LDS void*)(lds_buf + kLatBytes + (16 * wave + 8 * u) * 128), 16, 0, 0);
-  }
-}
+constexpr int kHalf = 32;                            // tokens per pipeline step
+constexpr int kStageLat = kHalf * 1024;              // 32768: offset of the positional rows
+constexpr int kStageBytes = kHalf * (1024 + 128);    // 36864
+constexpr int kStages = 4;
+constexpr int kPBufOff = kStages * kStageBytes;      // 147456
+constexpr int kXchOff = kPBufOff + 8 * 64 * 16;      // 155648
+constexpr int kXchWave = 256;                        // per wave: alpha[16], inv_l[16], flag
+constexpr int kDecodeLds = kXchOff + 8 * kXchWave;   // 157696 bytes (< 160 KiB)
 
 __device__ __forceinline__ u32x4 lds_read_b128(const uint8_t* p) { return *reinterpret_cast<const u32x4*>(p); }
-__device__ __forceinline__ u32x2 lds_read_b64(const uint8_t* p) { return *reinterpret_cast<const u32x2*>(p); }
+
+// s_waitcnt immediate that waits until at most n vector-memory operations are outstanding and
+// leaves the other counters alone (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4,
+// lgkmcnt 11:8).  Vector loads complete in order, so vmcnt(n) with n = number of loads issued
+// after the ones waited for is sufficient even with stores outstanding.
+constexpr int waitcnt_vm(int n) { return (n & 15) | (((n >> 4) & 3) << 14) | (7 << 4) | (15 << 8); }
+
+// Position in the page stream: sequence b (kv_len L, nb pages), page tb, half h.
+struct Cursor {
+  int b, tb, h, L, nb;
+};
+
+// Wave-uniform values are pinned to scalar registers: table and length lookups then become
+// scalar loads, which never wait behind the vector-memory counter of the page DMA.
+__device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+__device__ __forceinline__ void cursor_next(Cursor& c, const int32_t* kv_lens, int B, int max_blocks) {
+  if (c.h == 0) {
+    c.h = 1;
+  } else {
+    c.h = 0;
+    if (++c.tb >= c.nb) {
+      c.tb = 0;
+      do {
+        if (c.b + 1 >= B) { c.nb = 1; break; }          // past the batch: only reached beyond the range
+        ++c.b;
+        c.nb = seq_tiles(kv_lens, c.b, max_blocks, &c.L);
+      } while (c.nb == 0);
+    }
+  }
+  c.b = uni(c.b); c.tb = uni(c.tb); c.h = uni(c.h); c.L = uni(c.L); c.nb = uni(c.nb);
+}
+
+// Valid tokens of the cursor's half page (may be <= 0 for the empty second half of a short
+// last page) and its page base; out-of-range page ids read page 0 with no valid token.
+__device__ __forceinline__ const uint8_t* half_page(const DecodeArgs& a, const Cursor& c, int* nvalid) {
+  int pg = uni(ld_const(a.block_table, (size_t)c.b * a.max_blocks + c.tb));
+  int nv = c.L - c.tb * kBlock - c.h * kHalf;
+  nv = nv > kHalf ? kHalf : nv;
+  if (pg < 0 || pg >= a.num_blocks) { pg = 0; nv = 0; }
+  *nvalid = nv;
+  return a.cache + (size_t)pg * kTileBytes;
+}
+
+// Waves 0..3 each issue nine 1 KiB global->LDS loads per half page: latent rows 8w .. 8w+7
+// (lane l fetches logical chunk l ^ key) and the positional rows 8w .. 8w+7 (lane l -> row
+// 8w + l/8).  Rows at or past `nvalid` are fetched from the page's row 0 instead (finite
+// data, masked scores).
+__device__ __forceinline__ void load_half(uint8_t* stage, const uint8_t* page, int h, int nvalid, int wave,
+                                          int lane) {
+  asm volatile("" : "+v"(lane));   // rebuild the per-lane offsets here rather than keep them live
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int r = 8 * wave + i;
+    const int rs = r < nvalid ? kHalf * h + r : 0;
+    const uint8_t* src = page + rs * (kRow * 2) + ((lane ^ lat_key(r)) << 4);
+    __builtin_amdgcn_global_load_lds((const void*)src, (MLA_LDS void*)(stage + r * 1024), 16, 0, 0);
+  }
+  const int r = 8 * wave + (lane >> 3);
+  const int rs = r < nvalid ? kHalf * h + r : 0;
+  const uint8_t* src = page + rs * (kRow * 2) + kDC * 2 + (((lane & 7) ^ pos_key(r)) << 4);
+  __builtin_amdgcn_global_load_lds((const void*)src, (MLA_LDS void*)(stage + kStageLat + 8 * wave * 128), 16, 0, 0);
+}
 
 // 16x16x32 bf16 MFMA layout (wave64): A lane l holds row l%16 and the 8 K values of K-group
 // l/16; B lane l holds column l%16 and the same K-group; the result lane l holds column
 // l%16, rows 4*(l/16) + i, i = 0..3.  The order of K inside one instruction is irrelevant as
 // long as A and B agree, so P and V may use any common token order.
 //
-// Token order inside a 16-row M-tile of S^T: result row 4q+i is token 4i+q (q = l/16), so the
-// four lane groups of one V read touch rows of alternating parity (opposite bank halves).
-__global__ void __launch_bounds__(256, 1) decode_mfma_bf16_kernel(DecodeArgs a) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];   // 2 pages
+// Work split (waves w = 0..7, head group hg = w&3 owns heads 32hg .. 32hg+31, sh = w>>2):
+//   scores/softmax  wave w: heads 32hg + 16sh + (0..15), all 576 columns, 32 tokens
+//                   S^T[32 tok, 16 heads] = Stage[32, 576] . Qabs^T; result row 4q+i of M-tile
+//                   mt is token 16mt + 4q + i (q = l/16), which is exactly the P^T operand
+//                   order below, so each lane's probabilities are its own B fragment.
+//   values          wave w: O^T[256 columns 256sh.., 32 heads of hg] += V^T . P^T with the two
+//                   P^T fragments of the pair (hg, hg+4); one transposed V fragment feeds both.
+__global__ void __launch_bounds__(512, 1) decode_mfma_bf16_kernel(DecodeArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;            // 0..3
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: keeps row math scalar
   const int m = lane & 15, q = lane >> 4;
+  const int hg = wave & 3, sh = wave >> 2;
+  const int s_head = 32 * hg + 16 * sh + m;       // scores/softmax head of this lane
 
-  // logical (range g, query j, head half hh) of this workgroup.  Consecutive logical ids
-  // share a range, and on an 8-XCD part the remap puts consecutive ids on one XCD (blocks
-  // are dealt to XCDs round-robin), so the two halves and Sq queries of a range read each
-  // page through the same L2.
-  const int NG = a.G * a.Sq * 2;
+  // logical (range g, query j) of this workgroup; consecutive logical ids sit on one XCD
+  // (blocks are dealt to the 8 XCDs round-robin), so the Sq queries of a range share L2.
+  const int NG = a.G * a.Sq;
   int lid = blockIdx.x;
   if ((NG & 7) == 0) lid = (blockIdx.x & 7) * (NG >> 3) + (blockIdx.x >> 3);
-  const int hh = lid & 1;
-  const int g = (lid >> 1) / a.Sq;
-  const int j = (lid >> 1) - g * a.Sq;
+  const int g = lid / a.Sq;
+  const int j = lid - g * a.Sq;
 
   long long T_all, s_first;
-  int b;
+  int b0;
   {
-    int dummy_b;
-    long long dummy_s;
-    scan_batch(a.kv_lens, a.B, a.max_blocks, -1, &T_all, &dummy_b, &dummy_s);
+    int db;
+    long long ds;
+    scan_batch(a.kv_lens, a.B, a.max_blocks, -1, &T_all, &db, &ds);
   }
   const long long x0 = (long long)g * T_all / a.G;
   const long long x1 = (long long)(g + 1) * T_all / a.G;
   if (x0 >= x1) return;
   {
     long long tot;
-    scan_batch(a.kv_lens, a.B, a.max_blocks, x0, &tot, &b, &s_first);
+    scan_batch(a.kv_lens, a.B, a.max_blocks, x0, &tot, &b0, &s_first);
   }
-  if (b < 0) return;                            // unreachable: x0 < T_all lies in some sequence
-  int L;
-  int nb = seq_tiles(a.kv_lens, b, a.max_blocks, &L);
-  int tb = (int)(x0 - s_first);
-  int seg_tb0 = tb;
+  if (b0 < 0) return;                             // unreachable: x0 < T_all lies in some sequence
+  const int n_steps = (int)(2 * (x1 - x0));       // half pages of this range
 
-  const int head = 64 * hh + 16 * wave + m;     // head of this lane (N index of S^T and O^T)
+  Cursor cur;
+  cur.b = uni(b0);
+  cur.nb = uni(seq_tiles(a.kv_lens, cur.b, a.max_blocks, &cur.L));
+  cur.L = uni(cur.L);
+  cur.tb = uni((int)(x0 - s_first));
+  cur.h = 0;
+  Cursor pre = cur;                               // prefetch cursor, three half pages ahead
+  int seg_tb0 = cur.tb;
 
-  // S^T operand A = tile row 16mt + rho(m), rho(m) = 4(m%4) + m/4, latent chunk 4ks + q for
-  // ks < 16, positional chunk 4(ks-16) + q for ks = 16, 17.  key(16mt + rho) == key(rho).
-  const int rho = 4 * (m & 3) + (m >> 2);
-  const int lk = lat_key(rho), pk = pos_key(rho);
-  int s_lat[4];                                 // by ks % 4; ks / 4 adds 256 B, mt adds 16 KiB
-#pragma unroll
-  for (int u = 0; u < 4; ++u) s_lat[u] = rho * 1024 + (((4 * u + q) ^ lk) << 4);
-  const int s_pos0 = kLatBytes + rho * 128 + ((q ^ pk) << 4);
-  const int s_pos1 = kLatBytes + rho * 128 + (((4 + q) ^ pk) << 4);
-  // O^T operand A = V^T, read with the transposing LDS load: inside each 16-lane group q,
-  // output lane i, element jj is element i%4 of the 8 bytes addressed by source lane
-  // 4jj + i/4.  Element e = 4h + jj of lane (m, q) must be token 32kk + 16h + 4jj + q (the P^T
-  // order) at latent column 16t + m, so source lane (q, 4jj + u) addresses that token's row,
-  // columns 16t + 4u .. +3 = logical chunk 2t + u/2, byte 8(u&1).  The row's key is
-  // 8(q&1) + ((2jj + q/2)&7) for every kk, h; the chunk XOR splits into a per-lane part
-  // (t&7 ^ key/2, 8 variants) and immediates (kk, h, t&24).
-  int v_addr[8];
-  {
-    const int jj = m >> 2, u = m & 3;
-    const int key = 8 * (q & 1) + ((2 * jj + (q >> 1)) & 7);
-    const int base = (4 * jj + q) * 1024 + 16 * ((u >> 1) ^ (key & 1)) + 8 * (u & 1);
-#pragma unroll
-    for (int tt = 0; tt < 8; ++tt) v_addr[tt] = base + 32 * (tt ^ (key >> 1));
-  }
+  uint8_t* pbuf = smem + kPBufOff;
+  uint8_t* xch = smem + kXchOff;
+  float* x_alpha = reinterpret_cast<float*>(xch + wave * kXchWave);        // [16]
+  float* x_invl = reinterpret_cast<float*>(xch + wave * kXchWave + 64);    // [16]
+  int* x_flag = reinterpret_cast<int*>(xch + wave * kXchWave + 128);
 
-  bf16x8 qf[18];                                // folded query, K-steps 0..17 (32 columns each)
-  f32x4 oacc[32];
-  float m_run = -INFINITY, l_run = 0.f;
-#pragma unroll
-  for (int i = 0; i < 32; ++i) oacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-
+  bf16x8 qf[18];
   auto load_q = [&](int bb) {
-    const uint16_t* qp = a.q_abs + ((size_t)(bb * a.Sq + j) * kH + head) * kRow + 8 * q;
+    const uint16_t* qp = a.q_abs + ((size_t)(bb * a.Sq + j) * kH + s_head) * kRow + 8 * q;
 #pragma unroll
     for (int ks = 0; ks < 18; ++ks)
       qf[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qp + 32 * ks));
   };
 
-  int nvalid_cur;
-  {
-    int pg = a.block_table[(size_t)b * a.max_blocks + tb];
-    int nv = L - tb * kBlock;
-    nv = nv > kBlock ? kBlock : nv;
-    if (pg < 0 || pg >= a.num_blocks) { pg = 0; nv = 0; }
-    nvalid_cur = nv;
-    load_tile(smem, a.cache + (size_t)pg * kTileBytes, nv > 0 ? nv : 1, wave, lane);
+  f32x4 oacc[2][16];                              // [N-tile (head half of hg)][M-tile of 16 columns]
+  float m_run = -INFINITY, l_run = 0.f;
+#pragma unroll
+  for (int n = 0; n < 2; ++n)
+#pragma unroll
+    for (int t = 0; t < 16; ++t) oacc[n][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // prologue: half pages 0, 1, 2 of the range in flight
+#pragma unroll
+  for (int k = 0; k < 3; ++k) {
+    if (k < n_steps) {
+      int nv;
+      const uint8_t* pg = half_page(a, pre, &nv);
+      if (wave < 4) load_half(smem + k * kStageBytes, pg, pre.h, nv, wave, lane);
+      cursor_next(pre, a.kv_lens, a.B, a.max_blocks);
+    }
   }
-  load_q(b);
+  load_q(cur.b);
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
 
-  for (long long x = x0; x < x1; ++x) {
-    const int buf = (int)((x - x0) & 1);
-    int bn = b, tbn = tb + 1, Ln = L, nbn = nb;
-    if (x + 1 < x1 && tbn >= nb) {
-      bn = b + 1;
-      nbn = seq_tiles(a.kv_lens, bn, a.max_blocks, &Ln);
-      while (nbn == 0 && bn + 1 < a.B) { ++bn; nbn = seq_tiles(a.kv_lens, bn, a.max_blocks, &Ln); }
-      tbn = 0;
+  for (int y = 0; y < n_steps; ++y) {
+    // wait for this wave's loads of half page y (the two younger half pages may stay in flight)
+    if (wave < 4) {
+      const int younger = min(2, n_steps - 1 - y);
+      if (younger >= 2) __builtin_amdgcn_s_waitcnt(waitcnt_vm(18));
+      else if (younger == 1) __builtin_amdgcn_s_waitcnt(waitcnt_vm(9));
+      else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     }
-    __builtin_amdgcn_s_waitcnt(0);   // this wave's loads of the current page (and q) landed
-    __syncthreads();                  // ... and every wave's; the other buffer is free
-    int nvalid_next = 0;
-    if (x + 1 < x1) {
-      int pg = a.block_table[(size_t)bn * a.max_blocks + tbn];
-      int nv = Ln - tbn * kBlock;
-      nv = nv > kBlock ? kBlock : nv;
-      if (pg < 0 || pg >= a.num_blocks) { pg = 0; nv = 0; }
-      nvalid_next = nv;
-      load_tile(smem + (buf ^ 1) * kTileBytes, a.cache + (size_t)pg * kTileBytes, nv > 0 ? nv : 1, wave, lane);
+    lds_barrier();   // every wave's loads landed; stage (y-1)%4 is free
+    if (y + 3 < n_steps) {
+      int nv;
+      const uint8_t* pg = half_page(a, pre, &nv);
+      if (wave < 4) load_half(smem + ((y + 3) & 3) * kStageBytes, pg, pre.h, nv, wave, lane);
+      cursor_next(pre, a.kv_lens, a.B, a.max_blocks);
     }
-    const uint8_t* tile = smem + buf * kTileBytes;
+    const uint8_t* tile = smem + (y & 3) * kStageBytes;
+    // Per-lane LDS addresses, rebuilt each step from an opaque copy of the lane id: cheaper
+    // than keeping them live across the loop (the compiler would hoist and spill them).
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int lm = ln & 15, lq = ln >> 4;
+    // S^T operand A: stage row 16mt + m; latent chunk 4ks + q for ks < 16, positional chunk
+    // 4(ks-16) + q for ks = 16, 17.  key(16mt + m) == key(m).
+    const int rho = lm;
+    const int s_row = rho * 1024, s_key = lat_key(rho), p_key = pos_key(rho);
+    // V^T operand through the transposing LDS read: inside each 16-lane group q, output lane
+    // i, element jj is element i%4 of the 8 bytes addressed by source lane 4jj + i/4.  Element
+    // e = 4h + jj of lane (m, q) is token 16h + 4q + jj (the P^T order) at column
+    // 256sh + 16t + m, so source lane (q, 4jj + u) addresses that token's row at columns
+    // 256sh + 16t + 4u .. +3: logical chunk 32sh + 2t + u/2, byte 8(u&1).  The row key is
+    // key(4q + jj) for both h; h adds 16 KiB and t>>3 adds 256 B.
+    const int vjj = lm >> 2, vu = lm & 3;
+    const int v_key = lat_key(4 * lq + vjj);
+    const int v_base = (4 * lq + vjj) * 1024 + 512 * sh + 8 * (vu & 1);
+    int nvalid;
+    {
+      int nv = cur.L - cur.tb * kBlock - cur.h * kHalf;
+      nvalid = nv > kHalf ? kHalf : nv;
+      const int pg = uni(ld_const(a.block_table, (size_t)cur.b * a.max_blocks + cur.tb));
+      if (pg < 0 || pg >= a.num_blocks) nvalid = 0;
+    }
 
-    // ---------------------------------------------------------------- S^T = Tile . Q^T
-    // K-step ks reads four 16-byte A fragments (one per M-tile); two K-steps stay in flight
-    // ahead of the MFMAs that consume them.
+    // ---------------------------------------------------------------- S^T = Stage . Q^T
     auto s_frag = [&](int ks, int mt) -> u32x4 {
-      const uint8_t* base = ks < 16 ? tile + s_lat[ks & 3] + 256 * (ks >> 2) + mt * 16 * 1024
-                                    : tile + (ks == 16 ? s_pos0 : s_pos1) + mt * 16 * 128;
-      return lds_read_b128(base);
+      return ks < 16 ? lds_read_b128(tile + s_row + (((4 * (ks & 3) + lq) ^ s_key) << 4) + 256 * (ks >> 2) +
+                                     mt * 16 * 1024)
+                     : lds_read_b128(tile + kStageLat + rho * 128 + (((4 * (ks - 16) + lq) ^ p_key) << 4) +
+                                     mt * 16 * 128);
     };
-    f32x4 sacc[4];
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) sacc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    u32x4 ring[3][4];
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) { ring[0][mt] = s_frag(0, mt); ring[1][mt] = s_frag(1, mt); }
+    f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    u32x4 ring[2][2];
+    ring[0][0] = s_frag(0, 0);
+    ring[0][1] = s_frag(0, 1);
 #pragma unroll
     for (int ks = 0; ks < 18; ++ks) {
-      if (ks + 2 < 18) {
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) ring[(ks + 2) % 3][mt] = s_frag(ks + 2, mt);
+      if (ks + 1 < 18) {
+        ring[(ks + 1) & 1][0] = s_frag(ks + 1, 0);
+        ring[(ks + 1) & 1][1] = s_frag(ks + 1, 1);
       }
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-        sacc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ring[ks % 3][mt]), qf[ks],
+      for (int mt = 0; mt < 2; ++mt)
+        sacc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ring[ks & 1][mt]), qf[ks],
                                                            sacc[mt], 0, 0, 0);
     }
 
-    // first V fragments (independent of P) go out before the softmax
-    // step v = 32kk + t: K-step kk (tokens 32kk..32kk+31), M-tile t (latent columns 16t..16t+15)
-    auto v_frag = [&](int v) -> bf16x8 {
-      const int kk = v >> 5, t = v & 31;
-      const uint8_t* p0 = tile + v_addr[t & 7] + 32 * (t & 24) + (32 * kk) * 1024;
-      const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)(p0));
-      const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)(p0 + 16 * 1024));
-      return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-    };
-    constexpr int kVDepth = 4;
-    bf16x8 vring[kVDepth];
-#pragma unroll
-    for (int v = 0; v < kVDepth; ++v) vring[v] = v_frag(v);
-
-    // ---------------------------------------------------------------- online softmax
-    // sacc[mt][i] is token 16mt + 4i + q of this tile, head `head`
-    const int lim = (L - a.Sq + j) - tb * kBlock;   // visible tile rows are r <= lim
-    const bool masked = (nvalid_cur <= 0) || (lim < kBlock - 1);
+    // ---------------------------------------------------------------- online softmax (16 heads)
+    // sacc[mt][i] is token 16mt + 4q + i of this half page, head s_head
+    const int lim = (cur.L - a.Sq + j) - (cur.tb * kBlock + cur.h * kHalf);   // visible rows r <= lim
+    const bool masked = (nvalid <= 0) || (lim < kHalf - 1);
     float tmax = -INFINITY;
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
+    for (int mt = 0; mt < 2; ++mt) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         float sv = sacc[mt][i] * a.scale_log2;
-        if (masked && (nvalid_cur <= 0 || 16 * mt + 4 * i + q > lim)) sv = -INFINITY;
+        if (masked && (nvalid <= 0 || 16 * mt + 4 * q + i > lim)) sv = -INFINITY;
         sacc[mt][i] = sv;
         tmax = fmaxf(tmax, sv);
       }
     }
     tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-    if (__ballot(tmax > m_run + 8.0f)) {
+    const bool rescale = __ballot(tmax > m_run + 8.0f) != 0;   // p stays <= 2^8 otherwise
+    if (rescale) {
       const float m_new = fmaxf(m_run, tmax);
       const float alpha = (m_new == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
       l_run *= alpha;
-#pragma unroll
-      for (int i = 0; i < 32; ++i) oacc[i] *= alpha;
       m_run = m_new;
+      if (q == 0) x_alpha[m] = alpha;
     }
+    if (lane == 0) *x_flag = rescale ? 1 : 0;
     const float m_use = (m_run == -INFINITY) ? 0.0f : m_run;
-    uint32_t pw[8];                              // pw[2mt + u]: tokens of M-tile mt, pair u
+    u32x4 own;
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
+    for (int mt = 0; mt < 2; ++mt) {
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         const uint32_t w = pack_bf16x2(__builtin_amdgcn_exp2f(sacc[mt][2 * u] - m_use),
                                        __builtin_amdgcn_exp2f(sacc[mt][2 * u + 1] - m_use));
-        pw[2 * mt + u] = w;
+        own[2 * mt + u] = w;
         l_run += bf16_bits_to_f32(w & 0xFFFFu) + bf16_bits_to_f32(w >> 16);
       }
     }
+    *reinterpret_cast<u32x4*>(pbuf + wave * 1024 + lane * 16) = own;
+    lds_barrier();   // P fragments, rescale flags and factors of all eight waves visible
 
     // ---------------------------------------------------------------- O^T += V^T . P^T
-    // K-step kk covers tokens 32kk .. 32kk+31 = M-tiles 2kk, 2kk+1: P^T fragment pw[4kk..4kk+3].
-    bf16x8 pfrag[2];
+    // N-tile n holds heads 32hg + 16n + (0..15), whose softmax ran on wave hg + 4n.
+    u32x4 pf[2];
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      const u32x4 pf = {pw[4 * kk], pw[4 * kk + 1], pw[4 * kk + 2], pw[4 * kk + 3]};
-      pfrag[kk] = __builtin_bit_cast(bf16x8, pf);
+    for (int n = 0; n < 2; ++n) {
+      const int src = hg + 4 * n;
+      pf[n] = *reinterpret_cast<const u32x4*>(pbuf + src * 1024 + lane * 16);
+      const int flag = *reinterpret_cast<const int*>(xch + src * kXchWave + 128);
+      if (flag) {
+        const float al = reinterpret_cast<const float*>(xch + src * kXchWave)[m];
+#pragma unroll
+        for (int t = 0; t < 16; ++t) oacc[n][t] *= al;
+      }
     }
 #pragma unroll
-    for (int v = 0; v < 64; ++v) {
-      const bf16x8 af = vring[v % kVDepth];
-      if (v + kVDepth < 64) vring[v % kVDepth] = v_frag(v + kVDepth);
-      oacc[v & 31] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, pfrag[v >> 5], oacc[v & 31], 0, 0, 0);
+    for (int t = 0; t < 16; ++t) {
+      const uint8_t* p0 = tile + v_base + 16 * ((2 * (t & 7) + (vu >> 1)) ^ v_key) + 256 * (t >> 3);
+      const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)(p0));
+      const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)(p0 + 16 * 1024));
+      const bf16x8 af = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      oacc[0][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, __builtin_bit_cast(bf16x8, pf[0]), oacc[0][t], 0, 0, 0);
+      oacc[1][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, __builtin_bit_cast(bf16x8, pf[1]), oacc[1][t], 0, 0, 0);
     }
 
-    // ---------------------------------------------------------------- end of a range?
-    if ((tb == nb - 1) || (x + 1 == x1)) {
+    // ---------------------------------------------------------------- end of a range segment?
+    const bool last_half = cur.h == 1;
+    if (last_half && (cur.tb == cur.nb - 1 || y + 1 == n_steps)) {
       float l_tot = l_run + __shfl_xor(l_run, 16, 64);
       l_tot += __shfl_xor(l_tot, 32, 64);
-      const bool whole = (seg_tb0 == 0) && (tb == nb - 1);
-      const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.0f;
-      const float lse_v = l_tot > 0.f ? (m_run + __log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
-      const size_t row = whole ? (size_t)(b * a.Sq + j) * kH + head : ((size_t)(g + b) * a.Sq + j) * kH + head;
-      float* dst_o = (whole ? a.o_lat : a.part_o) + row * kDC;
-      // oacc[t][i] is latent column 16t + 4q + i
+      const bool whole = (seg_tb0 == 0) && (cur.tb == cur.nb - 1);
+      const size_t row_base = whole ? (size_t)(cur.b * a.Sq + j) * kH : ((size_t)(g + cur.b) * a.Sq + j) * kH;
+      if (q == 0) {
+        const float lse_v = l_tot > 0.f ? (m_run + __log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
+        (whole ? a.lse : a.part_lse)[row_base + s_head] = lse_v;
+        x_invl[m] = l_tot > 0.f ? 1.0f / l_tot : 0.0f;
+      }
+      lds_barrier();   // 1/l of every head visible
+      float* obase = (whole ? a.o_lat : a.part_o) + row_base * kDC;
 #pragma unroll
-      for (int t = 0; t < 32; ++t) *reinterpret_cast<f32x4*>(dst_o + 16 * t + 4 * q) = oacc[t] * inv;
-      if (q == 0) (whole ? a.lse : a.part_lse)[row] = lse_v;
-      if (x + 1 < x1) {
-        load_q(bn);
+      for (int n = 0; n < 2; ++n) {
+        const int src = hg + 4 * n;
+        const float inv = reinterpret_cast<const float*>(xch + src * kXchWave + 64)[m];
+        float* dst = obase + (size_t)(32 * hg + 16 * n + m) * kDC + 256 * sh + 4 * q;
+        // oacc[n][t][i] is column 256sh + 16t + 4q + i of head 32hg + 16n + m
 #pragma unroll
-        for (int i = 0; i < 32; ++i) oacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int t = 0; t < 16; ++t) *reinterpret_cast<f32x4*>(dst + 16 * t) = oacc[n][t] * inv;
+      }
+      if (y + 1 < n_steps) {
+        Cursor nx = cur;
+        cursor_next(nx, a.kv_lens, a.B, a.max_blocks);
+        load_q(nx.b);
+        // wait here (rare path) so the steady-state loop carries no pending query loads;
+        // otherwise every step would wait for the whole page pipeline before its first MFMA
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+#pragma unroll
+        for (int n = 0; n < 2; ++n)
+#pragma unroll
+          for (int t = 0; t < 16; ++t) oacc[n][t] = f32x4{0.f, 0.f, 0.f, 0.f};
         m_run = -INFINITY;
         l_run = 0.f;
         seg_tb0 = 0;
       }
     }
-    b = bn;
-    tb = tbn;
-    L = Ln;
-    nb = nbn;
-    nvalid_cur = nvalid_next;
+    cursor_next(cur, a.kv_lens, a.B, a.max_blocks);
   }
 }
 
@@ -504,11 +595,11 @@ __global__ void __launch_bounds__(256) decode_generic_kernel(
 
 bool is_dsv2_shape(const mla_config_t& c);
 
-// Token ranges of the split: one workgroup per (range, query, head half) and one workgroup
-// per compute unit (each holds 144 KiB of LDS), so G = CUs / (2 Sq), capped by the pages.
+// Token ranges of the split: one workgroup per (range, query) and one workgroup per compute
+// unit (each holds 154 KiB of LDS), so G = CUs / Sq, capped by the number of pages.
 int decode_num_ranges(int num_cus, int B, int Sq, int max_blocks) {
   long long cap = (long long)B * max_blocks;
-  int G = num_cus / (2 * (Sq > 0 ? Sq : 1));
+  int G = num_cus / (Sq > 0 ? Sq : 1);
   if (G < 1) G = 1;
   if (cap < G) G = (int)(cap < 1 ? 1 : cap);
   return G;
@@ -551,12 +642,12 @@ hipError_t launch_decode(const mla_config_t& cfg, int num_cus, const void* q_abs
     static bool attr_set = false;   // idempotent; races only repeat the same call
     if (!attr_set) {
       hipError_t e = hipFuncSetAttribute((const void*)decode_mfma_bf16_kernel,
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, 2 * kTileBytes);
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, kDecodeLds);
       if (e != hipSuccess) return e;
       attr_set = true;
     }
     if (phases & 1) {
-      hipLaunchKernelGGL(decode_mfma_bf16_kernel, dim3(G * Sq * 2), dim3(256), 2 * kTileBytes, stream, a);
+      hipLaunchKernelGGL(decode_mfma_bf16_kernel, dim3(G * Sq), dim3(512), kDecodeLds, stream, a);
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
