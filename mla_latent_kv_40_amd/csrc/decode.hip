@@ -17,10 +17,10 @@
 //   per step  32 tokens (half a page) staged in LDS by 16-byte global->LDS loads, four
 //             stages in flight, rows XOR-swizzled at 16-byte granularity:
 //               S^T[32 tok, 16 heads] = Stage[32, 576] . Qabs^T   v_mfma_f32_16x16x32_bf16
-//               online softmax in the exp2 domain (rescale only when the max grows by > 8)
+//               softmax in the exp2 domain against a fixed per-segment reference
 //               O^T[256 cols, 32 heads] += Stage[:, :512]^T . P^T (V^T via ds_read_b64_tr_b16)
-//   output    a range that covers a whole sequence writes o_lat/lse directly; otherwise it
-//             writes a normalised partial (O/l, lse) to the workspace slot g + b.
+//   output    each segment (one sequence's part of a range) writes its unnormalised O and
+//             (m, l) per head to workspace slot g + b; the combine normalises.
 #include "common.h"
 
 namespace mla {
@@ -36,8 +36,8 @@ struct DecodeArgs {
   const int32_t* kv_lens;     // [B]
   float* o_lat;               // [T, H, 512]
   float* lse;                 // [T, H]
-  float* part_o;              // [slots*Sq, H, 512]
-  float* part_lse;            // [slots*Sq, H]
+  float* part_o;              // [slots*Sq, H, 512] unnormalised segment outputs
+  float* part_ml;             // [slots*Sq, H, 2]   (reference max m in log2 units, l)
   int num_blocks, max_blocks, B, Sq, G;
   float scale_log2;           // softmax_scale * log2(e)
 };
@@ -106,38 +106,32 @@ __device__ void scan_batch(const int32_t* kv_lens, int B, int max_blocks, long l
 
 // ---------------------------------------------------------------------------------------
 // LDS layout.  The page stream is cut into 32-token half pages; four stages of 36 KiB hold
-// the half page being computed and the next three in flight (global->LDS DMA).  One stage:
-// 32 latent rows of 1024 B, then 32 positional rows of 128 B.  Inside a latent row, 16-byte
-// chunk c is stored at c ^ key(r), key linear over GF(2) in the low four row bits (columns
-// 9, 11, 6, 7); inside a positional row at c ^ ((r>>1)&7).  The key was chosen by timing
-// the two read patterns on gfx950: 16 rows x one 16-byte chunk per lane group (S operand,
-// ds_read_b128) and 4 rows x 32 bytes per 16-lane group (V operand, ds_read_b64_tr_b16) both
-// run at the bank-conflict-free rate with it (plain row-parity keys leave one of them 2x
-// slower).  XOR keys below 16 (8) keep every chunk inside its row.
-// After the stages: one 16-byte P fragment per lane per wave (8 KiB) and a small per-wave
-// exchange area (rescale factors, flags, 1/l).
-constexpr unsigned long long kLatKeys = 0x3A815CE74DF62B90ull;   // key(r), r = 0..15, one nibble each
-constexpr int lat_key_c(int r) { return (int)((kLatKeys >> (4 * (r & 15))) & 15); }
-static_assert(lat_key_c(1) == 9 && lat_key_c(2) == 11 && lat_key_c(4) == 6 && lat_key_c(8) == 7 &&
-                  lat_key_c(15) == (9 ^ 11 ^ 6 ^ 7),
-              "latent-row XOR key is the linear map with columns 9, 11, 6, 7");
-__device__ __forceinline__ int lat_key(int r) { return lat_key_c(r); }
+// the half page whose values are being accumulated, the one whose scores are being computed
+// and the next two in flight (global->LDS DMA).  One stage: 32 latent rows of 1024 B, then
+// 32 positional rows of 128 B.  Inside a latent row, 16-byte chunk c is stored at c ^ key(r)
+// with key(r) = 4(r&3) + ((r>>2)&3); inside a positional row at c ^ ((r>>1)&7).
+//
+// On gfx950 the LDS has 64 four-byte banks.  A ds_read_b128 serves, per cycle, the 16 lanes
+// that agree on lane bit 5 and on the parity of lane bits 2..4; a ds_read_b64_tr_b16 serves
+// a half wave per cycle (both fitted to timings of 170 access patterns).  Under that model
+// the key makes both reads below conflict-free:
+//   scores  lane l reads row l&31, chunk 2s + (l>>5): within a cycle's 16 lanes the rows
+//           differ in a way the key maps to 16 distinct bank groups;
+//   values  a half wave reads 4 rows x 4 consecutive chunks: the rows' keys differ in bits
+//           2-3, so the four 64-byte blocks land on different banks.
+// XOR keys below 16 (8) keep every chunk inside its row.
+__device__ __forceinline__ int lat_key(int r) { return 4 * (r & 3) + ((r >> 2) & 3); }
 __device__ __forceinline__ int pos_key(int r) { return (r >> 1) & 7; }
 constexpr int kHalf = 32;                            // tokens per pipeline step
 constexpr int kStageLat = kHalf * 1024;              // 32768: offset of the positional rows
 constexpr int kStageBytes = kHalf * (1024 + 128);    // 36864
 constexpr int kStages = 4;
-constexpr int kPBufOff = kStages * kStageBytes;      // 147456
-constexpr int kXchOff = kPBufOff + 8 * 64 * 16;      // 155648
-constexpr int kXchWave = 256;                        // per wave: alpha[16], inv_l[16], flag
-constexpr int kDecodeLds = kXchOff + 8 * kXchWave;   // 157696 bytes (< 160 KiB)
-
-__device__ __forceinline__ u32x4 lds_read_b128(const uint8_t* p) { return *reinterpret_cast<const u32x4*>(p); }
+constexpr int kDecodeLds = kStages * kStageBytes;    // 147456 bytes
+constexpr int kWaves = 4;                            // one per SIMD, 32 heads each
 
 // s_waitcnt immediate that waits until at most n vector-memory operations are outstanding and
 // leaves the other counters alone (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4,
-// lgkmcnt 11:8).  Vector loads complete in order, so vmcnt(n) with n = number of loads issued
-// after the ones waited for is sufficient even with stores outstanding.
+// lgkmcnt 11:8).  Vector loads complete in order.
 constexpr int waitcnt_vm(int n) { return (n & 15) | (((n >> 4) & 3) << 14) | (7 << 4) | (15 << 8); }
 
 // Position in the page stream: sequence b (kv_len L, nb pages), page tb, half h.
@@ -177,10 +171,10 @@ __device__ __forceinline__ const uint8_t* half_page(const DecodeArgs& a, const C
   return a.cache + (size_t)pg * kTileBytes;
 }
 
-// Waves 0..3 each issue nine 1 KiB global->LDS loads per half page: latent rows 8w .. 8w+7
-// (lane l fetches logical chunk l ^ key) and the positional rows 8w .. 8w+7 (lane l -> row
-// 8w + l/8).  Rows at or past `nvalid` are fetched from the page's row 0 instead (finite
-// data, masked scores).
+// Each of the four waves issues nine 1 KiB global->LDS loads per half page: latent rows
+// 8w .. 8w+7 (lane l fetches logical chunk l ^ key) and the positional rows 8w .. 8w+7
+// (lane l -> row 8w + l/8).  Rows at or past `nvalid` are fetched from the page's row 0
+// instead (finite data, masked scores).
 __device__ __forceinline__ void load_half(uint8_t* stage, const uint8_t* page, int h, int nvalid, int wave,
                                           int lane) {
   asm volatile("" : "+v"(lane));   // rebuild the per-lane offsets here rather than keep them live
@@ -197,25 +191,84 @@ __device__ __forceinline__ void load_half(uint8_t* stage, const uint8_t* page, i
   __builtin_amdgcn_global_load_lds((const void*)src, (MLA_LDS void*)(stage + kStageLat + 8 * wave * 128), 16, 0, 0);
 }
 
-// 16x16x32 bf16 MFMA layout (wave64): A lane l holds row l%16 and the 8 K values of K-group
-// l/16; B lane l holds column l%16 and the same K-group; the result lane l holds column
-// l%16, rows 4*(l/16) + i, i = 0..3.  The order of K inside one instruction is irrelevant as
-// long as A and B agree, so P and V may use any common token order.
+__device__ __forceinline__ u32x4 lds_b128(const uint8_t* base, uint32_t off) {
+  return *reinterpret_cast<const u32x4*>(base + off);
+}
+__device__ __forceinline__ bf16x4 lds_tr16(const uint8_t* base, uint32_t off) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)(base + off));
+}
+
+// Value of lane l and lane l^32 of x, combined: max or sum (v_permlane32_swap).
+__device__ __forceinline__ float pair_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// The output tiles accumulate in the accumulation registers (AGPRs) through inline MFMAs, so
+// that the folded queries and the score accumulator keep the 256 architectural VGPRs.  No
+// vector ALU instruction ever reads or writes them: they are zeroed by an MFMA (0 . 0 + 0) and
+// stored straight from the AGPRs at the end of a segment (the combine normalises).  With all
+// 256 AGPRs in use, any vector access would make the compiler move them through VGPRs and
+// spill.
+// The compiler does not see these MFMAs, so their hazards are resolved here: two wait states
+// before each (a vector write of an operand just before), none between chained accumulations
+// into the same registers, and a fence tying all tiles before any other access of O (results
+// of an 8-pass XDL op need 11 wait states, a WAR on src C 15).
+__device__ __forceinline__ void mfma_acc(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_zero(f32x16& acc, const bf16x8& z) {
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %1, 0" : "=a"(acc) : "v"(z));
+}
+template <int N>
+__device__ __forceinline__ void o_fence(f32x16* o) {
+  static_assert(N > 0 && N <= 32, "wait states");
+  if constexpr (N > 16)
+    asm volatile("s_nop 15\n\ts_nop %16"
+                 : "+a"(o[0]), "+a"(o[1]), "+a"(o[2]), "+a"(o[3]), "+a"(o[4]), "+a"(o[5]), "+a"(o[6]), "+a"(o[7]),
+                   "+a"(o[8]), "+a"(o[9]), "+a"(o[10]), "+a"(o[11]), "+a"(o[12]), "+a"(o[13]), "+a"(o[14]), "+a"(o[15])
+                 : "i"(N - 17));
+  else
+    asm volatile("s_nop %16"
+                 : "+a"(o[0]), "+a"(o[1]), "+a"(o[2]), "+a"(o[3]), "+a"(o[4]), "+a"(o[5]), "+a"(o[6]), "+a"(o[7]),
+                   "+a"(o[8]), "+a"(o[9]), "+a"(o[10]), "+a"(o[11]), "+a"(o[12]), "+a"(o[13]), "+a"(o[14]), "+a"(o[15])
+                 : "i"(N - 1));
+}
+
+// Softmax reference.  Probabilities are taken against a fixed per-segment reference m (the
+// first visible score maximum) instead of the running maximum: bf16 and fp32 keep their
+// relative precision at any magnitude, and scores below m merely underflow, which is exact to
+// fp32 precision relative to the final maximum.  A segment whose scores exceed m by more than
+// 2^64 (p could overflow) is marked (l = -1) and the combine recomputes its heads exactly; O is
+// therefore never rescaled in the page loop.
+constexpr float kRescaleLog2 = 64.0f;
+
+// 32x32x16 bf16 MFMA layout (wave64): A lane l holds row l%32 and the 8 K values of K-group
+// l/32; B lane l holds column l%32 and the same K-group; the result lane l holds column l%32,
+// rows 8(i/4) + 4(l/32) + i%4, i = 0..15.  The order of K inside one instruction is free as
+// long as A and B agree.
 //
-// Work split (waves w = 0..7, head group hg = w&3 owns heads 32hg .. 32hg+31, sh = w>>2):
-//   scores/softmax  wave w: heads 32hg + 16sh + (0..15), all 576 columns, 32 tokens
-//                   S^T[32 tok, 16 heads] = Stage[32, 576] . Qabs^T; result row 4q+i of M-tile
-//                   mt is token 16mt + 4q + i (q = l/16), which is exactly the P^T operand
-//                   order below, so each lane's probabilities are its own B fragment.
-//   values          wave w: O^T[256 columns 256sh.., 32 heads of hg] += V^T . P^T with the two
-//                   P^T fragments of the pair (hg, hg+4); one transposed V fragment feeds both.
-__global__ void __launch_bounds__(512, 1) decode_mfma_bf16_kernel(DecodeArgs a) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+// Wave w owns heads 32w .. 32w+31; lane l works for head 32w + l%32 throughout:
+//   scores  S^T[32 tok, 32 heads] = Stage[32, 576] . Qabs^T, 36 K-steps; step s takes
+//           chunks 2s, 2s+1 (lane halves).  Lane l ends up with its head's scores for tokens
+//           8(i/4) + 4(l/32) + i%4.
+//   values  O^T[512, 32 heads] += V^T . P^T, 16 column tiles x 2 token steps.  The B operand
+//           of token step k is the lane's own probabilities i = 8k .. 8k+7, i.e. tokens
+//           16k + 8(e/4) + 4(l/32) + e%4; the transposing reads deliver V^T in that order.
+// The page loop is software-pipelined by one half page: step y computes the scores of half
+// page y+1 and accumulates the values of half page y, whose probabilities it already holds.
+// Every segment (the part of one sequence inside the range) ends with its unnormalised O and
+// (m, l) per head in workspace slot g + b.
+__global__ void __launch_bounds__(256, 1) decode_mfma_bf16_kernel(DecodeArgs a) {
+  extern __shared__ __attribute__((aligned(256))) uint8_t smem[];
   const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: keeps row math scalar
-  const int m = lane & 15, q = lane >> 4;
-  const int hg = wave & 3, sh = wave >> 2;
-  const int s_head = 32 * hg + 16 * sh + m;       // scores/softmax head of this lane
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int hl = lane >> 5;
+  const int head = 32 * wave + (lane & 31);
 
   // logical (range g, query j) of this workgroup; consecutive logical ids sit on one XCD
   // (blocks are dealt to the 8 XCDs round-robin), so the Sq queries of a range share L2.
@@ -248,219 +301,238 @@ __global__ void __launch_bounds__(512, 1) decode_mfma_bf16_kernel(DecodeArgs a) 
   cur.L = uni(cur.L);
   cur.tb = uni((int)(x0 - s_first));
   cur.h = 0;
-  Cursor pre = cur;                               // prefetch cursor, three half pages ahead
-  int seg_tb0 = cur.tb;
+  Cursor pre = cur;                               // DMA cursor
 
-  uint8_t* pbuf = smem + kPBufOff;
-  uint8_t* xch = smem + kXchOff;
-  float* x_alpha = reinterpret_cast<float*>(xch + wave * kXchWave);        // [16]
-  float* x_invl = reinterpret_cast<float*>(xch + wave * kXchWave + 64);    // [16]
-  int* x_flag = reinterpret_cast<int*>(xch + wave * kXchWave + 128);
-
-  bf16x8 qf[18];
+  bf16x8 qf[36];
   auto load_q = [&](int bb) {
-    const uint16_t* qp = a.q_abs + ((size_t)(bb * a.Sq + j) * kH + s_head) * kRow + 8 * q;
+    const uint16_t* qp = a.q_abs + ((size_t)(bb * a.Sq + j) * kH + head) * kRow + 8 * hl;
 #pragma unroll
-    for (int ks = 0; ks < 18; ++ks)
-      qf[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qp + 32 * ks));
+    for (int s = 0; s < 36; ++s) qf[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qp + 16 * s));
+  };
+  // this lane's part of workspace slot (g + b, j): O row of its head, columns 4hl + 8q4 + 32ct
+  auto slot_o = [&](int bb) -> float* {
+    return a.part_o + (((size_t)(g + bb) * a.Sq + j) * kH + head) * kDC + 4 * hl;
   };
 
-  f32x4 oacc[2][16];                              // [N-tile (head half of hg)][M-tile of 16 columns]
-  float m_run = -INFINITY, l_run = 0.f;
+  f32x16 oacc[16];
+  const bf16x8 zero8 = {};
 #pragma unroll
-  for (int n = 0; n < 2; ++n)
-#pragma unroll
-    for (int t = 0; t < 16; ++t) oacc[n][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int t = 0; t < 16; ++t) mfma_zero(oacc[t], zero8);
+  float m_ref = -INFINITY, l_run = 0.f;
+  bool over = false;                              // a score left the reference's safe range
 
-  // prologue: half pages 0, 1, 2 of the range in flight
+  // ---- S^T of the half page in `tile` (36 chained K-steps)
+  auto scores = [&](const uint8_t* tile) -> f32x16 {
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int rr = ln & 31, hh = ln >> 5;
+    const uint32_t lat = (uint32_t)(rr * 1024) | (uint32_t)(16 * (lat_key(rr) ^ hh));
+    const uint32_t pos = (uint32_t)(kStageLat + rr * 128) | (uint32_t)(16 * (pos_key(rr) ^ hh));
+    auto koff = [&](int st) -> uint32_t {
+      return st < 32 ? (lat ^ (32u * (st & 7))) + 256u * (st >> 3) : pos ^ (32u * (st - 32));
+    };
+    f32x16 acc;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+    // K fragments two steps ahead; the scheduling barriers keep the compiler from hoisting
+    // all 36 reads (144 VGPRs) to the top
+    u32x4 kr[3];
+    kr[0] = lds_b128(tile, koff(0));
+    kr[1] = lds_b128(tile, koff(1));
+#pragma unroll
+    for (int st = 0; st < 36; ++st) {
+      if (st + 2 < 36) kr[(st + 2) % 3] = lds_b128(tile, koff(st + 2));
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kr[st % 3]), qf[st], acc, 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    return acc;
+  };
+
+  // ---- O^T += V^T . P^T for the half page in `tile`
+  auto values = [&](const uint8_t* tile, const bf16x8* pf) {
+    o_fence<3>(oacc);   // MFMA/vector writes of O settled
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int gg = ln >> 4, sl = ln & 15, jj = sl >> 2, uu = sl & 3, hh = ln >> 5;
+    // source lane (gg, 4jj + uu): row 4hh + jj (+8E +16k), chunk 4ct + 2(gg&1) + uu/2, byte 8(uu&1)
+    const uint32_t vb = (uint32_t)((4 * hh + jj) * 1024 + 8 * (uu & 1)) |
+                        (uint32_t)(16 * ((2 * (gg & 1) + (uu >> 1)) ^ (4 * jj) ^ hh));
+    auto vfrag = [&](int it) -> bf16x8 {
+      const int k = it >> 4, ct = it & 15;
+      const uint32_t c0 = (vb ^ (64u * (ct & 3))) + 16384u * k + 256u * (ct >> 2);
+      const uint32_t c1 = (vb ^ (64u * (ct & 3) ^ 32u)) + 16384u * k + 8192u + 256u * (ct >> 2);
+      const bf16x4 lo = lds_tr16(tile, c0);
+      const bf16x4 hi = lds_tr16(tile, c1);
+      return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    };
+    bf16x8 vr[3];
+    vr[0] = vfrag(0);
+    vr[1] = vfrag(1);
+#pragma unroll
+    for (int it = 0; it < 32; ++it) {
+      if (it + 2 < 32) vr[(it + 2) % 3] = vfrag(it + 2);
+      mfma_acc(oacc[it & 15], vr[it % 3], pf[it >> 4]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    o_fence<20>(oacc);  // results settled before any other access of O
+  };
+
+  // ---- softmax of one half page (cursor c): scores -> bf16 probabilities against m_ref
+  auto softmax = [&](f32x16 sv, const Cursor& c, bf16x8* pf) {
+    int nv = c.L - c.tb * kBlock - c.h * kHalf;
+    nv = nv > kHalf ? kHalf : nv;
+    const int pg = uni(ld_const(a.block_table, (size_t)c.b * a.max_blocks + c.tb));
+    if (pg < 0 || pg >= a.num_blocks) nv = 0;
+    const int lim = (c.L - a.Sq + j) - (c.tb * kBlock + c.h * kHalf);   // visible rows r <= lim
+    const int vis = nv - 1 < lim ? nv - 1 : lim;                        // last visible row
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float s = sv[i] * a.scale_log2;
+      if (vis < kHalf - 1 && 8 * (i >> 2) + 4 * hl + (i & 3) > vis) s = -INFINITY;
+      sv[i] = s;
+      tmax = fmaxf(tmax, s);
+    }
+    tmax = pair_max(tmax);
+    if (m_ref == -INFINITY) m_ref = tmax;   // first visible scores of the segment (O is 0)
+    over = over || (tmax > m_ref + kRescaleLog2);
+    const float m_use = (m_ref == -INFINITY) ? 0.0f : m_ref;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      u32x4 w;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const uint32_t p = pack_bf16x2(__builtin_amdgcn_exp2f(sv[8 * k + 2 * u] - m_use),
+                                       __builtin_amdgcn_exp2f(sv[8 * k + 2 * u + 1] - m_use));
+        w[u] = p;
+        l_run += bf16_bits_to_f32(p & 0xFFFFu) + bf16_bits_to_f32(p >> 16);
+      }
+      pf[k] = __builtin_bit_cast(bf16x8, w);
+    }
+  };
+
+  // prologue: queries, half pages 0..2 in flight, scores and probabilities of half page 0
+  load_q(cur.b);
 #pragma unroll
   for (int k = 0; k < 3; ++k) {
     if (k < n_steps) {
       int nv;
       const uint8_t* pg = half_page(a, pre, &nv);
-      if (wave < 4) load_half(smem + k * kStageBytes, pg, pre.h, nv, wave, lane);
+      load_half(smem + k * kStageBytes, pg, pre.h, nv, wave, lane);
       cursor_next(pre, a.kv_lens, a.B, a.max_blocks);
     }
   }
-  load_q(cur.b);
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+  lds_barrier();
+  bf16x8 pf[2];
+  softmax(scores(smem), cur, pf);
 
   for (int y = 0; y < n_steps; ++y) {
-    // wait for this wave's loads of half page y (the two younger half pages may stay in flight)
-    if (wave < 4) {
-      const int younger = min(2, n_steps - 1 - y);
-      if (younger >= 2) __builtin_amdgcn_s_waitcnt(waitcnt_vm(18));
-      else if (younger == 1) __builtin_amdgcn_s_waitcnt(waitcnt_vm(9));
+    const bool has_next = y + 1 < n_steps;
+    // this wave's loads of half page y+1 landed (y+2 may stay in flight), then everyone's
+    if (has_next) {
+      if (y + 2 < n_steps) __builtin_amdgcn_s_waitcnt(waitcnt_vm(9));
       else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     }
-    lds_barrier();   // every wave's loads landed; stage (y-1)%4 is free
+    lds_barrier();   // stage (y+3)%4 == (y-1)%4 is no longer read by anyone
     if (y + 3 < n_steps) {
       int nv;
       const uint8_t* pg = half_page(a, pre, &nv);
-      if (wave < 4) load_half(smem + ((y + 3) & 3) * kStageBytes, pg, pre.h, nv, wave, lane);
+      load_half(smem + ((y + 3) & 3) * kStageBytes, pg, pre.h, nv, wave, lane);
       cursor_next(pre, a.kv_lens, a.B, a.max_blocks);
     }
-    const uint8_t* tile = smem + (y & 3) * kStageBytes;
-    // Per-lane LDS addresses, rebuilt each step from an opaque copy of the lane id: cheaper
-    // than keeping them live across the loop (the compiler would hoist and spill them).
-    int ln = lane;
-    asm volatile("" : "+v"(ln));
-    const int lm = ln & 15, lq = ln >> 4;
-    // S^T operand A: stage row 16mt + m; latent chunk 4ks + q for ks < 16, positional chunk
-    // 4(ks-16) + q for ks = 16, 17.  key(16mt + m) == key(m).
-    const int rho = lm;
-    const int s_row = rho * 1024, s_key = lat_key(rho), p_key = pos_key(rho);
-    // V^T operand through the transposing LDS read: inside each 16-lane group q, output lane
-    // i, element jj is element i%4 of the 8 bytes addressed by source lane 4jj + i/4.  Element
-    // e = 4h + jj of lane (m, q) is token 16h + 4q + jj (the P^T order) at column
-    // 256sh + 16t + m, so source lane (q, 4jj + u) addresses that token's row at columns
-    // 256sh + 16t + 4u .. +3: logical chunk 32sh + 2t + u/2, byte 8(u&1).  The row key is
-    // key(4q + jj) for both h; h adds 16 KiB and t>>3 adds 256 B.
-    const int vjj = lm >> 2, vu = lm & 3;
-    const int v_key = lat_key(4 * lq + vjj);
-    const int v_base = (4 * lq + vjj) * 1024 + 512 * sh + 8 * (vu & 1);
-    int nvalid;
-    {
-      int nv = cur.L - cur.tb * kBlock - cur.h * kHalf;
-      nvalid = nv > kHalf ? kHalf : nv;
-      const int pg = uni(ld_const(a.block_table, (size_t)cur.b * a.max_blocks + cur.tb));
-      if (pg < 0 || pg >= a.num_blocks) nvalid = 0;
+    Cursor nx = cur;
+    cursor_next(nx, a.kv_lens, a.B, a.max_blocks);
+    const bool seg_end = (cur.h == 1 && cur.tb == cur.nb - 1) || !has_next;
+    if (seg_end && has_next) {
+      // the next half page starts another sequence: its queries replace this one's (waiting
+      // here keeps the steady-state loop free of pending query loads)
+      load_q(nx.b);
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     }
+    f32x16 snext;
+    if (has_next) snext = scores(smem + ((y + 1) & 3) * kStageBytes);
+    values(smem + (y & 3) * kStageBytes, pf);
 
-    // ---------------------------------------------------------------- S^T = Stage . Q^T
-    auto s_frag = [&](int ks, int mt) -> u32x4 {
-      return ks < 16 ? lds_read_b128(tile + s_row + (((4 * (ks & 3) + lq) ^ s_key) << 4) + 256 * (ks >> 2) +
-                                     mt * 16 * 1024)
-                     : lds_read_b128(tile + kStageLat + rho * 128 + (((4 * (ks - 16) + lq) ^ p_key) << 4) +
-                                     mt * 16 * 128);
-    };
-    f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-    u32x4 ring[2][2];
-    ring[0][0] = s_frag(0, 0);
-    ring[0][1] = s_frag(0, 1);
+    if (seg_end) {
+      // unnormalised O and (m, l) of this segment into its slot; the combine normalises
+      const float l_tot = pair_sum(l_run);
+      const size_t row = ((size_t)(g + cur.b) * a.Sq + j) * kH + head;
+      if (hl == 0) reinterpret_cast<float2*>(a.part_ml)[row] = float2{m_ref, over ? -1.0f : l_tot};
+      float* so = slot_o(cur.b);
+      // oacc[ct][4q4 + i] is column 32ct + 8q4 + 4hl + i of this lane's head
 #pragma unroll
-    for (int ks = 0; ks < 18; ++ks) {
-      if (ks + 1 < 18) {
-        ring[(ks + 1) & 1][0] = s_frag(ks + 1, 0);
-        ring[(ks + 1) & 1][1] = s_frag(ks + 1, 1);
-      }
+      for (int ct = 0; ct < 16; ++ct)
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-        sacc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ring[ks & 1][mt]), qf[ks],
-                                                           sacc[mt], 0, 0, 0);
-    }
-
-    // ---------------------------------------------------------------- online softmax (16 heads)
-    // sacc[mt][i] is token 16mt + 4q + i of this half page, head s_head
-    const int lim = (cur.L - a.Sq + j) - (cur.tb * kBlock + cur.h * kHalf);   // visible rows r <= lim
-    const bool masked = (nvalid <= 0) || (lim < kHalf - 1);
-    float tmax = -INFINITY;
+        for (int q4 = 0; q4 < 4; ++q4)
+          *reinterpret_cast<f32x4*>(so + 32 * ct + 8 * q4) =
+              f32x4{oacc[ct][4 * q4], oacc[ct][4 * q4 + 1], oacc[ct][4 * q4 + 2], oacc[ct][4 * q4 + 3]};
+      if (has_next) {
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float sv = sacc[mt][i] * a.scale_log2;
-        if (masked && (nvalid <= 0 || 16 * mt + 4 * q + i > lim)) sv = -INFINITY;
-        sacc[mt][i] = sv;
-        tmax = fmaxf(tmax, sv);
-      }
-    }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-    const bool rescale = __ballot(tmax > m_run + 8.0f) != 0;   // p stays <= 2^8 otherwise
-    if (rescale) {
-      const float m_new = fmaxf(m_run, tmax);
-      const float alpha = (m_new == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
-      l_run *= alpha;
-      m_run = m_new;
-      if (q == 0) x_alpha[m] = alpha;
-    }
-    if (lane == 0) *x_flag = rescale ? 1 : 0;
-    const float m_use = (m_run == -INFINITY) ? 0.0f : m_run;
-    u32x4 own;
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const uint32_t w = pack_bf16x2(__builtin_amdgcn_exp2f(sacc[mt][2 * u] - m_use),
-                                       __builtin_amdgcn_exp2f(sacc[mt][2 * u + 1] - m_use));
-        own[2 * mt + u] = w;
-        l_run += bf16_bits_to_f32(w & 0xFFFFu) + bf16_bits_to_f32(w >> 16);
-      }
-    }
-    *reinterpret_cast<u32x4*>(pbuf + wave * 1024 + lane * 16) = own;
-    lds_barrier();   // P fragments, rescale flags and factors of all eight waves visible
-
-    // ---------------------------------------------------------------- O^T += V^T . P^T
-    // N-tile n holds heads 32hg + 16n + (0..15), whose softmax ran on wave hg + 4n.
-    u32x4 pf[2];
-#pragma unroll
-    for (int n = 0; n < 2; ++n) {
-      const int src = hg + 4 * n;
-      pf[n] = *reinterpret_cast<const u32x4*>(pbuf + src * 1024 + lane * 16);
-      const int flag = *reinterpret_cast<const int*>(xch + src * kXchWave + 128);
-      if (flag) {
-        const float al = reinterpret_cast<const float*>(xch + src * kXchWave)[m];
-#pragma unroll
-        for (int t = 0; t < 16; ++t) oacc[n][t] *= al;
-      }
-    }
-#pragma unroll
-    for (int t = 0; t < 16; ++t) {
-      const uint8_t* p0 = tile + v_base + 16 * ((2 * (t & 7) + (vu >> 1)) ^ v_key) + 256 * (t >> 3);
-      const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)(p0));
-      const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)(p0 + 16 * 1024));
-      const bf16x8 af = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      oacc[0][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, __builtin_bit_cast(bf16x8, pf[0]), oacc[0][t], 0, 0, 0);
-      oacc[1][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, __builtin_bit_cast(bf16x8, pf[1]), oacc[1][t], 0, 0, 0);
-    }
-
-    // ---------------------------------------------------------------- end of a range segment?
-    const bool last_half = cur.h == 1;
-    if (last_half && (cur.tb == cur.nb - 1 || y + 1 == n_steps)) {
-      float l_tot = l_run + __shfl_xor(l_run, 16, 64);
-      l_tot += __shfl_xor(l_tot, 32, 64);
-      const bool whole = (seg_tb0 == 0) && (cur.tb == cur.nb - 1);
-      const size_t row_base = whole ? (size_t)(cur.b * a.Sq + j) * kH : ((size_t)(g + cur.b) * a.Sq + j) * kH;
-      if (q == 0) {
-        const float lse_v = l_tot > 0.f ? (m_run + __log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
-        (whole ? a.lse : a.part_lse)[row_base + s_head] = lse_v;
-        x_invl[m] = l_tot > 0.f ? 1.0f / l_tot : 0.0f;
-      }
-      lds_barrier();   // 1/l of every head visible
-      float* obase = (whole ? a.o_lat : a.part_o) + row_base * kDC;
-#pragma unroll
-      for (int n = 0; n < 2; ++n) {
-        const int src = hg + 4 * n;
-        const float inv = reinterpret_cast<const float*>(xch + src * kXchWave + 64)[m];
-        float* dst = obase + (size_t)(32 * hg + 16 * n + m) * kDC + 256 * sh + 4 * q;
-        // oacc[n][t][i] is column 256sh + 16t + 4q + i of head 32hg + 16n + m
-#pragma unroll
-        for (int t = 0; t < 16; ++t) *reinterpret_cast<f32x4*>(dst + 16 * t) = oacc[n][t] * inv;
-      }
-      if (y + 1 < n_steps) {
-        Cursor nx = cur;
-        cursor_next(nx, a.kv_lens, a.B, a.max_blocks);
-        load_q(nx.b);
-        // wait here (rare path) so the steady-state loop carries no pending query loads;
-        // otherwise every step would wait for the whole page pipeline before its first MFMA
-        __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-#pragma unroll
-        for (int n = 0; n < 2; ++n)
-#pragma unroll
-          for (int t = 0; t < 16; ++t) oacc[n][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-        m_run = -INFINITY;
+        for (int t = 0; t < 16; ++t) mfma_zero(oacc[t], zero8);
+        m_ref = -INFINITY;
         l_run = 0.f;
-        seg_tb0 = 0;
+        over = false;
       }
     }
-    cursor_next(cur, a.kv_lens, a.B, a.max_blocks);
+    if (has_next) softmax(snext, nx, pf);
+    cur = nx;
   }
 }
 
 // ------------------------------------------------------------------------ LSE combine
 
-// One workgroup per (query row, 4 heads); 64 threads per head, 8 latent columns each.
+// Exact attention of one (query row, head) by one wave, two passes over the visible tokens in
+// fp32 (scores in the exp2 domain).  Used by the combine for heads whose fast-path segments
+// were marked (a score far above the segment's reference); slow, but right for any input.
+__device__ void exact_head(const DecodeArgs& a, int b, int j, int h, int L, float* out) {
+  const int lane = threadIdx.x & 63;
+  const int row = b * a.Sq + j;
+  const int last = L - a.Sq + j;                     // last visible position
+  const int n = last + 1 < L ? last + 1 : L;
+  const uint16_t* qp = a.q_abs + ((size_t)row * kH + h) * kRow + 9 * lane;   // 9 of 576 columns
+  float qv[9];
+#pragma unroll
+  for (int i = 0; i < 9; ++i) qv[i] = bf16_bits_to_f32(qp[i]);
+  auto rowptr = [&](int t) -> const uint16_t* {
+    const int pg = a.block_table[(size_t)b * a.max_blocks + t / kBlock];
+    if (pg < 0 || pg >= a.num_blocks) return nullptr;
+    return reinterpret_cast<const uint16_t*>(a.cache) + ((size_t)pg * kBlock + t % kBlock) * kRow;
+  };
+  auto score = [&](const uint16_t* r) {
+    float d = 0.f;
+#pragma unroll
+    for (int i = 0; i < 9; ++i) d += qv[i] * bf16_bits_to_f32(r[9 * lane + i]);
+    return wave_sum(d) * a.scale_log2;
+  };
+  float mx = -INFINITY;
+  for (int t = 0; t < n; ++t) {
+    const uint16_t* r = rowptr(t);
+    if (r) mx = fmaxf(mx, score(r));
+  }
+  float l = 0.f;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  if (mx != -INFINITY) {
+    for (int t = 0; t < n; ++t) {
+      const uint16_t* r = rowptr(t);
+      if (!r) continue;
+      const float w = __builtin_amdgcn_exp2f(score(r) - mx);
+      l += w;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] += w * bf16_bits_to_f32(r[8 * lane + i]);
+    }
+  }
+  const float inv = l > 0.f ? 1.0f / l : 0.0f;
+  *reinterpret_cast<f32x4*>(out) = f32x4{acc[0], acc[1], acc[2], acc[3]} * inv;
+  *reinterpret_cast<f32x4*>(out + 4) = f32x4{acc[4], acc[5], acc[6], acc[7]} * inv;
+  if (lane == 0) a.lse[(size_t)row * kH + h] = l > 0.f ? (mx + __log2f(l)) * 0.69314718055994531f : -INFINITY;
+}
+
+
+// One workgroup per (query row, 4 heads); 64 threads per head, 8 latent columns each.  Every
+// segment left its unnormalised O_g and (m_g, l_g) in slot g + b; with M = max m_g over the
+// non-empty ones and w_g = 2^(m_g - M):  o = sum w_g O_g / sum w_g l_g,
+// lse = ln 2 * (M + log2 sum w_g l_g).
 __global__ void __launch_bounds__(256) combine_kernel(DecodeArgs a) {
   const int row = blockIdx.x;          // b*Sq + j
   const int b = row / a.Sq, j = row - b * a.Sq;
@@ -488,32 +560,47 @@ __global__ void __launch_bounds__(256) combine_kernel(DecodeArgs a) {
   }
   const int g_lo = range_of_tile(first, T_all, a.G);
   const int g_hi = range_of_tile(first + nb - 1, T_all, a.G);
-  if (g_lo == g_hi) return;            // one range covered the sequence and wrote the result
   // Ranges between g_lo and g_hi that hold no page at all (possible when the batch has fewer
   // pages than ranges) wrote nothing: skip them.
   auto empty = [&](int g) {
     return (long long)g * T_all / a.G == (long long)(g + 1) * T_all / a.G;
   };
-  float mx = -INFINITY;
-  for (int g = g_lo; g <= g_hi; ++g)
-    if (!empty(g)) mx = fmaxf(mx, a.part_lse[((size_t)(g + b) * a.Sq + j) * kH + h]);
-  float den = 0.f;
-  for (int g = g_lo; g <= g_hi; ++g)
-    if (!empty(g) && mx != -INFINITY) den += __expf(a.part_lse[((size_t)(g + b) * a.Sq + j) * kH + h] - mx);
-  const float lse = (den > 0.f) ? mx + __logf(den) : -INFINITY;
-  f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+  const float2* ml = reinterpret_cast<const float2*>(a.part_ml);
+  auto slot = [&](int g) { return ((size_t)(g + b) * a.Sq + j) * kH + h; };
+  float M = -INFINITY;
+  bool redo = false;
   for (int g = g_lo; g <= g_hi; ++g) {
     if (empty(g)) continue;
-    const size_t prow = ((size_t)(g + b) * a.Sq + j) * kH + h;
-    const float ls = a.part_lse[prow];
-    const float w = (lse == -INFINITY || ls == -INFINITY) ? 0.f : __expf(ls - lse);
-    const float* src = a.part_o + prow * kDC + 8 * lane;
-    acc0 += w * *reinterpret_cast<const f32x4*>(src);
-    acc1 += w * *reinterpret_cast<const f32x4*>(src + 4);
+    const float2 v = ml[slot(g)];
+    if (v.y < 0.f) redo = true;
+    else if (v.y > 0.f) M = fmaxf(M, v.x);
   }
-  *reinterpret_cast<f32x4*>(out) = acc0;
-  *reinterpret_cast<f32x4*>(out + 4) = acc1;
-  if (lane == 0) a.lse[(size_t)row * kH + h] = lse;
+  float L = 0.f;
+  f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+  if (!redo && M != -INFINITY) {
+    for (int g = g_lo; g <= g_hi; ++g) {
+      if (empty(g)) continue;
+      const float2 v = ml[slot(g)];
+      if (!(v.y > 0.f)) continue;
+      const float w = __builtin_amdgcn_exp2f(v.x - M);
+      L += w * v.y;
+      const float* src = a.part_o + slot(g) * kDC + 8 * lane;
+      acc0 += w * *reinterpret_cast<const f32x4*>(src);
+      acc1 += w * *reinterpret_cast<const f32x4*>(src + 4);
+    }
+    bool fin = true;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) fin = fin && __builtin_isfinite(acc0[i]) && __builtin_isfinite(acc1[i]);
+    redo = __ballot(!fin) != 0 || !__builtin_isfinite(L);
+  }
+  if (redo) {
+    exact_head(a, b, j, h, Lb, out);
+    return;
+  }
+  const float inv = L > 0.f ? 1.0f / L : 0.0f;
+  *reinterpret_cast<f32x4*>(out) = acc0 * inv;
+  *reinterpret_cast<f32x4*>(out + 4) = acc1 * inv;
+  if (lane == 0) a.lse[(size_t)row * kH + h] = L > 0.f ? (M + __log2f(L)) * 0.69314718055994531f : -INFINITY;
 }
 
 // ------------------------------------------------------------------------ generic decode (VALU)
@@ -610,7 +697,7 @@ size_t decode_workspace_bytes(const mla_config_t& cfg, int num_cus, int B, int S
   const int G = decode_num_ranges(num_cus, B, Sq, max_blocks);
   const size_t slots = (size_t)(G + B - 1) * Sq;
   const size_t o_bytes = slots * kH * kDC * sizeof(float);
-  const size_t l_bytes = slots * kH * sizeof(float);
+  const size_t l_bytes = slots * kH * 2 * sizeof(float);
   return ((o_bytes + 255) & ~(size_t)255) + ((l_bytes + 255) & ~(size_t)255);
 }
 
@@ -631,7 +718,7 @@ hipError_t launch_decode(const mla_config_t& cfg, int num_cus, const void* q_abs
     const int G = decode_num_ranges(num_cus, B, Sq, max_blocks);
     const size_t slots = (size_t)(G + B - 1) * Sq;
     a.part_o = static_cast<float*>(workspace);
-    a.part_lse = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) +
+    a.part_ml = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) +
                                           ((slots * kH * kDC * sizeof(float) + 255) & ~(size_t)255));
     a.num_blocks = num_blocks;
     a.max_blocks = max_blocks;
@@ -647,7 +734,7 @@ hipError_t launch_decode(const mla_config_t& cfg, int num_cus, const void* q_abs
       attr_set = true;
     }
     if (phases & 1) {
-      hipLaunchKernelGGL(decode_mfma_bf16_kernel, dim3(G * Sq), dim3(512), kDecodeLds, stream, a);
+      hipLaunchKernelGGL(decode_mfma_bf16_kernel, dim3(G * Sq), dim3(64 * kWaves), kDecodeLds, stream, a);
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
     }

@@ -141,6 +141,22 @@ def test_needle_tokens():
         compare_seq(w, bt, seqs, got, b, heads=range(0, 128, 3), tag="needle ")
 
 
+def test_extreme_scores_take_the_exact_path():
+    """Needles scaled x128 after the first tiles: their scores exceed the segment's softmax
+    reference by far more than the fast path accepts, so those heads are recomputed exactly
+    by the combine.  Other heads (negative needle scores) stay on the fast path."""
+    log("case extreme needles x128: lengths [3000, 700], needles at 2500 / 300")
+    w, bt, seqs = dsv2(2, [3000, 700], seed=31)
+    for b, t in [(0, 2500), (1, 300)]:
+        seqs[b]["c"] = seqs[b]["c"].copy()
+        seqs[b]["c"][t] = seqs[b]["c"][t] * 128.0        # exact in bf16
+    st = run_state(w, bt, seqs)
+    got = host(st)
+    assert np.all(np.isfinite(got["o"])) and np.all(np.isfinite(got["lse"]))
+    for b in range(w.batch):
+        compare_seq(w, bt, seqs, got, b, heads=range(0, 128, 2), tag="extreme ")
+
+
 def test_page_permutation_and_rerun_are_bitwise_stable():
     log("case page-table permutation invariance and run-to-run determinism")
     w, bt, seqs = dsv2(3, [900, 1500, 31], seed=19)
