@@ -39,6 +39,7 @@ struct DecodeArgs {
   float* part_o;              // [slots*Sq, H, 512] unnormalised segment outputs
   float* part_ml;             // [slots*Sq, H, 2]   (reference max m in log2 units, l)
   int num_blocks, max_blocks, B, Sq, G;
+  int stream_nt;              // page loads non-temporal (no other workgroup reads the pages)
   float scale_log2;           // softmax_scale * log2(e)
 };
 
@@ -126,7 +127,8 @@ constexpr int kHalf = 32;                            // tokens per pipeline step
 constexpr int kStageLat = kHalf * 1024;              // 32768: offset of the positional rows
 constexpr int kStageBytes = kHalf * (1024 + 128);    // 36864
 constexpr int kStages = 4;
-constexpr int kDecodeLds = kStages * kStageBytes;    // 147456 bytes
+constexpr int kPgSlot = kStages * kStageBytes;       // 147456: per-wave 256 B page-id slot
+constexpr int kDecodeLds = kPgSlot + 4 * 256;        // 148480 bytes
 constexpr int kWaves = 4;                            // one per SIMD, 32 heads each
 
 // s_waitcnt immediate that waits until at most n vector-memory operations are outstanding and
@@ -160,42 +162,62 @@ __device__ __forceinline__ void cursor_next(Cursor& c, const int32_t* kv_lens, i
   c.b = uni(c.b); c.tb = uni(c.tb); c.h = uni(c.h); c.L = uni(c.L); c.nb = uni(c.nb);
 }
 
-// Valid tokens of the cursor's half page (may be <= 0 for the empty second half of a short
-// last page) and its page base; out-of-range page ids read page 0 with no valid token.
-__device__ __forceinline__ const uint8_t* half_page(const DecodeArgs& a, const Cursor& c, int* nvalid) {
-  int pg = uni(ld_const(a.block_table, (size_t)c.b * a.max_blocks + c.tb));
+// Page id of the cursor's page (a scalar load; the caller decides when to wait for it).
+__device__ __forceinline__ int page_of(const DecodeArgs& a, const Cursor& c) {
+  return uni(ld_const(a.block_table, (size_t)c.b * a.max_blocks + c.tb));
+}
+
+// Valid tokens of the cursor's half page (<= 0 for the empty second half of a short last
+// page); 0 for an out-of-range page id, whose half page is then read from page 0.
+__device__ __forceinline__ int half_valid(const Cursor& c, int pg, int num_blocks) {
   int nv = c.L - c.tb * kBlock - c.h * kHalf;
   nv = nv > kHalf ? kHalf : nv;
-  if (pg < 0 || pg >= a.num_blocks) { pg = 0; nv = 0; }
-  *nvalid = nv;
-  return a.cache + (size_t)pg * kTileBytes;
+  return (pg < 0 || pg >= num_blocks) ? 0 : nv;
 }
 
 // Each of the four waves issues nine 1 KiB global->LDS loads per half page: latent rows
 // 8w .. 8w+7 (lane l fetches logical chunk l ^ key) and the positional rows 8w .. 8w+7
 // (lane l -> row 8w + l/8).  Rows at or past `nvalid` are fetched from the page's row 0
-// instead (finite data, masked scores).
-__device__ __forceinline__ void load_half(uint8_t* stage, const uint8_t* page, int h, int nvalid, int wave,
+// instead (finite data, masked scores).  The loads go through a buffer descriptor spanning
+// exactly the page (reads outside it would return zeros): unlike the flat-encoded
+// global->LDS form, buffer loads let the compiler keep counting LDS reads precisely while
+// page loads are in flight (a pending flat access forces every LDS wait to zero).  Aux is the
+// cache policy: non-temporal when no other workgroup reads the page, so that the stream does
+// not evict the block table, queries and partial outputs from L2.
+template <int Aux>
+__device__ __forceinline__ void load_half(uint8_t* stage, const uint8_t* cache, int pg, int h, int nvalid, int wave,
                                           int lane) {
+  const uint8_t* page = cache + (size_t)(pg < 0 ? 0 : pg) * kTileBytes;
+  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)page, 0, kTileBytes, 0x00020000);
   asm volatile("" : "+v"(lane));   // rebuild the per-lane offsets here rather than keep them live
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int r = 8 * wave + i;
     const int rs = r < nvalid ? kHalf * h + r : 0;
-    const uint8_t* src = page + rs * (kRow * 2) + ((lane ^ lat_key(r)) << 4);
-    __builtin_amdgcn_global_load_lds((const void*)src, (MLA_LDS void*)(stage + r * 1024), 16, 0, 0);
+    const unsigned off = rs * (kRow * 2) + ((lane ^ lat_key(r)) << 4);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (MLA_LDS void*)(stage + r * 1024), 16, off, 0, 0, Aux);
   }
   const int r = 8 * wave + (lane >> 3);
   const int rs = r < nvalid ? kHalf * h + r : 0;
-  const uint8_t* src = page + rs * (kRow * 2) + kDC * 2 + (((lane & 7) ^ pos_key(r)) << 4);
-  __builtin_amdgcn_global_load_lds((const void*)src, (MLA_LDS void*)(stage + kStageLat + 8 * wave * 128), 16, 0, 0);
+  const unsigned off = rs * (kRow * 2) + kDC * 2 + (((lane & 7) ^ pos_key(r)) << 4);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (MLA_LDS void*)(stage + kStageLat + 8 * wave * 128), 16, off, 0, 0, Aux);
 }
 
-__device__ __forceinline__ u32x4 lds_b128(const uint8_t* base, uint32_t off) {
-  return *reinterpret_cast<const u32x4*>(base + off);
+// LDS reads at absolute LDS byte addresses (the callers fold the array base in once).  The
+// restrict qualifier tells the compiler that the stage read is not written behind its back,
+// which is true (page loads only ever target another stage, and every read of a stage follows
+// the explicit wait and barrier for its loads); without it the compiler waits for all page
+// loads in flight before the first transposing read of every step.
+__device__ __forceinline__ u32x4 lds_b128(uint32_t addr) {
+  const MLA_LDS u32x4* __restrict__ p = (const MLA_LDS u32x4*)(size_t)addr;
+  return *p;
 }
-__device__ __forceinline__ bf16x4 lds_tr16(const uint8_t* base, uint32_t off) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)(base + off));
+__device__ __forceinline__ bf16x4 lds_tr16(const uint8_t* __restrict__ base, uint32_t off) {
+  const MLA_LDS uint8_t* __restrict__ lb = (const MLA_LDS uint8_t*)base;
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)(lb + off));
+}
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(size_t)(const MLA_LDS uint8_t*)p;
 }
 
 // Value of lane l and lane l^32 of x, combined: max or sum (v_permlane32_swap).
@@ -328,118 +350,192 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_bf16_kernel(DecodeArgs a) 
     const int rr = ln & 31, hh = ln >> 5;
     const uint32_t lat = (uint32_t)(rr * 1024) | (uint32_t)(16 * (lat_key(rr) ^ hh));
     const uint32_t pos = (uint32_t)(kStageLat + rr * 128) | (uint32_t)(16 * (pos_key(rr) ^ hh));
-    auto koff = [&](int st) -> uint32_t {
-      return st < 32 ? (lat ^ (32u * (st & 7))) + 256u * (st >> 3) : pos ^ (32u * (st - 32));
-    };
+    // the eight swizzle variants of this lane's row address, stage offset included once (the
+    // XOR touches bits 5..7 only and stages start at multiples of 256); the rest of each
+    // address is the read's immediate offset
+    const uint32_t T = lds_addr(tile);   // 256-byte aligned
+    uint32_t xs[8], xp[4];
+#pragma unroll
+    for (int d = 0; d < 8; ++d) xs[d] = (lat + T) ^ (32u * d);
+#pragma unroll
+    for (int d = 0; d < 4; ++d) xp[d] = (pos + T) ^ (32u * d);
+    auto koff = [&](int st) -> uint32_t { return st < 32 ? xs[st & 7] + 256u * (st >> 3) : xp[st - 32]; };
     f32x16 acc;
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[i] = 0.f;
-    // K fragments two steps ahead; the scheduling barriers keep the compiler from hoisting
-    // all 36 reads (144 VGPRs) to the top
-    u32x4 kr[3];
-    kr[0] = lds_b128(tile, koff(0));
-    kr[1] = lds_b128(tile, koff(1));
+    // K fragments four steps ahead, each read issued before the MFMA it runs under (the
+    // scheduling barriers keep the compiler from hoisting all 36 reads, 144 VGPRs, to the top)
+    constexpr int D = 4;
+    u32x4 kr[D + 1];
+#pragma unroll
+    for (int d = 0; d < D; ++d) kr[d] = lds_b128(koff(d));
 #pragma unroll
     for (int st = 0; st < 36; ++st) {
-      if (st + 2 < 36) kr[(st + 2) % 3] = lds_b128(tile, koff(st + 2));
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kr[st % 3]), qf[st], acc, 0, 0, 0);
+      if (st + D < 36) kr[(st + D) % (D + 1)] = lds_b128(koff(st + D));
+      __builtin_amdgcn_sched_barrier(0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kr[st % (D + 1)]), qf[st], acc, 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
     return acc;
   };
 
+  // ---- softmax of one half page: raw scores sv -> bf16 probabilities against the segment
+  // reference (log2 units).  `fresh` starts a new segment.  The softmax scale rides in the
+  // FMA that feeds exp2; l sums the bf16-rounded probabilities (dot2 with ones), the same
+  // values that enter P.V.
+  struct Soft {
+    float m_new, l_new;
+    bool over_new;
+    bf16x8 p0, p1;
+  };
+  auto softmax = [&](f32x16& sv, int vis, bool fresh, Soft& st) {
+    if (vis < kHalf - 1) {   // partial half page (sequence end, causal limit): mask the tail
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (8 * (i >> 2) + 4 * hl + (i & 3) > vis) sv[i] = -INFINITY;
+    }
+    float mx = fmaxf(fmaxf(sv[0], sv[1]), sv[2]);
+#pragma unroll
+    for (int i = 3; i < 15; i += 2) mx = fmaxf(fmaxf(mx, sv[i]), sv[i + 1]);
+    mx = fmaxf(mx, sv[15]);
+    const float c = a.scale_log2;
+    const float tmax = pair_max(mx) * c;
+    const float m_in = fresh ? -INFINITY : m_ref;
+    st.m_new = (m_in == -INFINITY) ? tmax : m_in;   // first visible scores fix the reference
+    st.over_new = (fresh ? false : over) || (tmax > st.m_new + kRescaleLog2);
+    const float m_use = (st.m_new == -INFINITY) ? 0.0f : st.m_new;
+    float l = fresh ? 0.0f : l_run;
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+    bf16x2 pk[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      pk[u] = bf16x2{(__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(sv[2 * u], c, -m_use)),
+                     (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(sv[2 * u + 1], c, -m_use))};
+      l = __builtin_amdgcn_fdot2_f32_bf16(pk[u], ones, l, false);
+    }
+    st.l_new = l;
+    st.p0 = bf16x8{pk[0][0], pk[0][1], pk[1][0], pk[1][1], pk[2][0], pk[2][1], pk[3][0], pk[3][1]};
+    st.p1 = bf16x8{pk[4][0], pk[4][1], pk[5][0], pk[5][1], pk[6][0], pk[6][1], pk[7][0], pk[7][1]};
+  };
+  auto soft_vis = [&](const Cursor& c, int nv) {
+    const int lim = (c.L - a.Sq + j) - (c.tb * kBlock + c.h * kHalf);   // visible rows r <= lim
+    return nv - 1 < lim ? nv - 1 : lim;                                  // last visible row
+  };
+
   // ---- O^T += V^T . P^T for the half page in `tile`
   auto values = [&](const uint8_t* tile, const bf16x8* pf) {
-    o_fence<3>(oacc);   // MFMA/vector writes of O settled
+    o_fence<3>(oacc);   // MFMA writes of O settled
     int ln = lane;
     asm volatile("" : "+v"(ln));
     const int gg = ln >> 4, sl = ln & 15, jj = sl >> 2, uu = sl & 3, hh = ln >> 5;
     // source lane (gg, 4jj + uu): row 4hh + jj (+8E +16k), chunk 4ct + 2(gg&1) + uu/2, byte 8(uu&1)
     const uint32_t vb = (uint32_t)((4 * hh + jj) * 1024 + 8 * (uu & 1)) |
                         (uint32_t)(16 * ((2 * (gg & 1) + (uu >> 1)) ^ (4 * jj) ^ hh));
+    // eight swizzle variants (column tile mod 4, token half E), stage offset included once
+    const uint32_t T = (uint32_t)(tile - smem);   // stage offset, a multiple of 256
+    const uint8_t* xv[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) xv[e] = smem + ((vb + T) ^ (64u * (e & 3) ^ 32u * (e >> 2)));
     auto vfrag = [&](int it) -> bf16x8 {
       const int k = it >> 4, ct = it & 15;
-      const uint32_t c0 = (vb ^ (64u * (ct & 3))) + 16384u * k + 256u * (ct >> 2);
-      const uint32_t c1 = (vb ^ (64u * (ct & 3) ^ 32u)) + 16384u * k + 8192u + 256u * (ct >> 2);
-      const bf16x4 lo = lds_tr16(tile, c0);
-      const bf16x4 hi = lds_tr16(tile, c1);
+      const bf16x4 lo = lds_tr16(xv[ct & 3], 16384u * k + 256u * (ct >> 2));
+      const bf16x4 hi = lds_tr16(xv[4 + (ct & 3)], 16384u * k + 8192u + 256u * (ct >> 2));
       return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     };
-    bf16x8 vr[3];
-    vr[0] = vfrag(0);
-    vr[1] = vfrag(1);
+    constexpr int D = 3;
+    bf16x8 vr[D + 1];
+#pragma unroll
+    for (int d = 0; d < D; ++d) vr[d] = vfrag(d);
 #pragma unroll
     for (int it = 0; it < 32; ++it) {
-      if (it + 2 < 32) vr[(it + 2) % 3] = vfrag(it + 2);
-      mfma_acc(oacc[it & 15], vr[it % 3], pf[it >> 4]);
+      if (it + D < 32) vr[(it + D) % (D + 1)] = vfrag(it + D);
+      __builtin_amdgcn_sched_barrier(0);
+      mfma_acc(oacc[it & 15], vr[it % (D + 1)], pf[it >> 4]);
       __builtin_amdgcn_sched_barrier(0);
     }
     o_fence<20>(oacc);  // results settled before any other access of O
   };
 
-  // ---- softmax of one half page (cursor c): scores -> bf16 probabilities against m_ref
-  auto softmax = [&](f32x16 sv, const Cursor& c, bf16x8* pf) {
-    int nv = c.L - c.tb * kBlock - c.h * kHalf;
-    nv = nv > kHalf ? kHalf : nv;
-    const int pg = uni(ld_const(a.block_table, (size_t)c.b * a.max_blocks + c.tb));
-    if (pg < 0 || pg >= a.num_blocks) nv = 0;
-    const int lim = (c.L - a.Sq + j) - (c.tb * kBlock + c.h * kHalf);   // visible rows r <= lim
-    const int vis = nv - 1 < lim ? nv - 1 : lim;                        // last visible row
-    float tmax = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      float s = sv[i] * a.scale_log2;
-      if (vis < kHalf - 1 && 8 * (i >> 2) + 4 * hl + (i & 3) > vis) s = -INFINITY;
-      sv[i] = s;
-      tmax = fmaxf(tmax, s);
-    }
-    tmax = pair_max(tmax);
-    if (m_ref == -INFINITY) m_ref = tmax;   // first visible scores of the segment (O is 0)
-    over = over || (tmax > m_ref + kRescaleLog2);
-    const float m_use = (m_ref == -INFINITY) ? 0.0f : m_ref;
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      u32x4 w;
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const uint32_t p = pack_bf16x2(__builtin_amdgcn_exp2f(sv[8 * k + 2 * u] - m_use),
-                                       __builtin_amdgcn_exp2f(sv[8 * k + 2 * u + 1] - m_use));
-        w[u] = p;
-        l_run += bf16_bits_to_f32(p & 0xFFFFu) + bf16_bits_to_f32(p >> 16);
-      }
-      pf[k] = __builtin_bit_cast(bf16x8, w);
-    }
+  bf16x8 pf[2];
+  Soft sm;
+  auto soft_commit = [&](const Soft& st) {
+    m_ref = st.m_new;
+    l_run = st.l_new;
+    over = st.over_new;
+    pf[0] = st.p0;
+    pf[1] = st.p1;
   };
 
-  // prologue: queries, half pages 0..2 in flight, scores and probabilities of half page 0
+  // Page ids for the page loads come one step ahead, through LDS: each wave fetches the next
+  // id with a 4-byte buffer->LDS load into its own slot, issued just before the step's nine
+  // page loads, so the wait for the previous stage at the top of the next step covers it
+  // (vector loads complete in order); the id is then read back from LDS.  A scalar load
+  // would force every LDS wait to zero while pending, and a vector load into a register is
+  // waited for with the whole page pipeline (the compiler cannot count it across the loop).
+  const size_t bt_bytes = (size_t)a.B * a.max_blocks * sizeof(int32_t);
+  const __amdgpu_buffer_rsrc_t bt_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)a.block_table, 0, (int)(bt_bytes < 0x7FFFFFFF ? bt_bytes : 0x7FFFFFFF), 0x00020000);
+  auto page_fetch = [&](const Cursor& c) {
+    const unsigned off = (unsigned)(((size_t)c.b * a.max_blocks + c.tb) * sizeof(int32_t));
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(bt_rsrc, (MLA_LDS void*)(smem + kPgSlot + wave * 256), 4, off, 0, 0, 0);
+  };
+  auto page_read = [&]() -> int {
+    return uni(*reinterpret_cast<const MLA_LDS int*>((const MLA_LDS uint8_t*)smem + kPgSlot + wave * 256));
+  };
+
+  // One page load per stage is issued every step, also past the end of the range (then it
+  // reads row 0 of page 0 and holds no valid token), so that every step issues the same
+  // vector-memory sequence: the next page id, then the nine page loads.  With that fixed
+  // order the wait at the top of a step is always "all but the nine youngest".
+  auto issue = [&](int stage, int pg, int nv, int h) {
+    if (a.stream_nt) load_half<2>(smem + stage * kStageBytes, a.cache, nv > 0 ? pg : 0, h, nv, wave, lane);
+    else load_half<0>(smem + stage * kStageBytes, a.cache, nv > 0 ? pg : 0, h, nv, wave, lane);
+  };
+
+  // prologue: queries, half pages 0..2 in flight, scores and probabilities of half page 0.
+  // nv1..nv3: valid tokens of half pages y+1 .. y+3 (known when their loads are issued).
   load_q(cur.b);
+  int nv1 = 0, nv2 = 0, nv3 = 0;
+  {
+    int nvk[3] = {0, 0, 0};
 #pragma unroll
-  for (int k = 0; k < 3; ++k) {
-    if (k < n_steps) {
-      int nv;
-      const uint8_t* pg = half_page(a, pre, &nv);
-      load_half(smem + k * kStageBytes, pg, pre.h, nv, wave, lane);
-      cursor_next(pre, a.kv_lens, a.B, a.max_blocks);
+    for (int k = 0; k < 3; ++k) {
+      int pg = 0;
+      if (k < n_steps) {
+        pg = page_of(a, pre);
+        nvk[k] = half_valid(pre, pg, a.num_blocks);
+      }
+      issue(k, pg, nvk[k], pre.h);
+      if (k < n_steps) cursor_next(pre, a.kv_lens, a.B, a.max_blocks);
     }
+    page_fetch(3 < n_steps ? pre : cur);
+    nv1 = nvk[1];
+    nv2 = nvk[2];
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    lds_barrier();
+    f32x16 s0 = scores(smem);
+    softmax(s0, soft_vis(cur, nvk[0]), true, sm);
+    soft_commit(sm);
   }
-  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-  lds_barrier();
-  bf16x8 pf[2];
-  softmax(scores(smem), cur, pf);
 
   for (int y = 0; y < n_steps; ++y) {
     const bool has_next = y + 1 < n_steps;
-    // this wave's loads of half page y+1 landed (y+2 may stay in flight), then everyone's
-    if (has_next) {
-      if (y + 2 < n_steps) __builtin_amdgcn_s_waitcnt(waitcnt_vm(9));
-      else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-    }
+    // this wave's loads of half page y+1 and the page id landed (only the nine loads of half
+    // page y+2 may stay in flight), then everyone's
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(9));
     lds_barrier();   // stage (y+3)%4 == (y-1)%4 is no longer read by anyone
-    if (y + 3 < n_steps) {
-      int nv;
-      const uint8_t* pg = half_page(a, pre, &nv);
-      load_half(smem + ((y + 3) & 3) * kStageBytes, pg, pre.h, nv, wave, lane);
-      cursor_next(pre, a.kv_lens, a.B, a.max_blocks);
+    {
+      const int pg = page_read();
+      __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): read before the slot is refilled
+      Cursor la = pre;
+      nv3 = 0;
+      if (y + 3 < n_steps) {
+        nv3 = half_valid(pre, pg, a.num_blocks);
+        cursor_next(la, a.kv_lens, a.B, a.max_blocks);
+      }
+      page_fetch(y + 4 < n_steps ? la : cur);
+      issue((y + 3) & 3, pg, nv3, pre.h);
+      pre = la;
     }
     Cursor nx = cur;
     cursor_next(nx, a.kv_lens, a.B, a.max_blocks);
@@ -450,15 +546,17 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_bf16_kernel(DecodeArgs a) 
       load_q(nx.b);
       __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     }
-    f32x16 snext;
-    if (has_next) snext = scores(smem + ((y + 1) & 3) * kStageBytes);
+    f32x16 snext = scores(smem + ((y + 1) & 3) * kStageBytes);   // stale data if !has_next
+    const float m_old = m_ref, l_old = l_run;
+    const bool over_old = over;
+    softmax(snext, soft_vis(nx, nv1), seg_end, sm);
     values(smem + (y & 3) * kStageBytes, pf);
 
     if (seg_end) {
       // unnormalised O and (m, l) of this segment into its slot; the combine normalises
-      const float l_tot = pair_sum(l_run);
+      const float l_tot = pair_sum(l_old);
       const size_t row = ((size_t)(g + cur.b) * a.Sq + j) * kH + head;
-      if (hl == 0) reinterpret_cast<float2*>(a.part_ml)[row] = float2{m_ref, over ? -1.0f : l_tot};
+      if (hl == 0) reinterpret_cast<float2*>(a.part_ml)[row] = float2{m_old, over_old ? -1.0f : l_tot};
       float* so = slot_o(cur.b);
       // oacc[ct][4q4 + i] is column 32ct + 8q4 + 4hl + i of this lane's head
 #pragma unroll
@@ -470,14 +568,14 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_bf16_kernel(DecodeArgs a) 
       if (has_next) {
 #pragma unroll
         for (int t = 0; t < 16; ++t) mfma_zero(oacc[t], zero8);
-        m_ref = -INFINITY;
-        l_run = 0.f;
-        over = false;
       }
     }
-    if (has_next) softmax(snext, nx, pf);
+    soft_commit(sm);
+    nv1 = nv2;
+    nv2 = nv3;
     cur = nx;
   }
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));   // no page load may land after the workgroup ends
 }
 
 // ------------------------------------------------------------------------ LSE combine
@@ -726,6 +824,7 @@ hipError_t launch_decode(const mla_config_t& cfg, int num_cus, const void* q_abs
     a.Sq = Sq;
     a.G = G;
     a.scale_log2 = scale * 1.4426950408889634f;
+    a.stream_nt = Sq == 1 ? 1 : 0;
     static bool attr_set = false;   // idempotent; races only repeat the same call
     if (!attr_set) {
       hipError_t e = hipFuncSetAttribute((const void*)decode_mfma_bf16_kernel,
