@@ -36,10 +36,9 @@ struct DecodeArgs {
   const int32_t* kv_lens;     // [B]
   float* o_lat;               // [T, H, 512]
   float* lse;                 // [T, H]
-  float* part_o;              // [slots*Sq, H, 512] unnormalised segment outputs
+  float* part_o;              // [slots*Sq] x 256 KiB unnormalised segment outputs (register order)
   float* part_ml;             // [slots*Sq, H, 2]   (reference max m in log2 units, l)
   int num_blocks, max_blocks, B, Sq, G;
-  int stream_nt;              // page loads non-temporal (no other workgroup reads the pages)
   float scale_log2;           // softmax_scale * log2(e)
 };
 
@@ -127,8 +126,10 @@ constexpr int kHalf = 32;                            // tokens per pipeline step
 constexpr int kStageLat = kHalf * 1024;              // 32768: offset of the positional rows
 constexpr int kStageBytes = kHalf * (1024 + 128);    // 36864
 constexpr int kStages = 4;
-constexpr int kPgSlot = kStages * kStageBytes;       // 147456: per-wave 256 B page-id slot
-constexpr int kDecodeLds = kPgSlot + 4 * 256;        // 148480 bytes
+constexpr int kTabOff = kStages * kStageBytes;       // 147456: the range's page table
+constexpr int kTabCap = 1024;                        // entries of 16 bytes: pages per range
+constexpr int kDecodeLds = kTabOff + 16 * kTabCap;   // 163840 bytes (all of a CU's LDS)
+constexpr int kFirst = 1, kLast = 2;                 // page table flags
 constexpr int kWaves = 4;                            // one per SIMD, 32 heads each
 
 // s_waitcnt immediate that waits until at most n vector-memory operations are outstanding and
@@ -136,44 +137,9 @@ constexpr int kWaves = 4;                            // one per SIMD, 32 heads e
 // lgkmcnt 11:8).  Vector loads complete in order.
 constexpr int waitcnt_vm(int n) { return (n & 15) | (((n >> 4) & 3) << 14) | (7 << 4) | (15 << 8); }
 
-// Position in the page stream: sequence b (kv_len L, nb pages), page tb, half h.
-struct Cursor {
-  int b, tb, h, L, nb;
-};
-
 // Wave-uniform values are pinned to scalar registers: table and length lookups then become
 // scalar loads, which never wait behind the vector-memory counter of the page DMA.
 __device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
-
-__device__ __forceinline__ void cursor_next(Cursor& c, const int32_t* kv_lens, int B, int max_blocks) {
-  if (c.h == 0) {
-    c.h = 1;
-  } else {
-    c.h = 0;
-    if (++c.tb >= c.nb) {
-      c.tb = 0;
-      do {
-        if (c.b + 1 >= B) { c.nb = 1; break; }          // past the batch: only reached beyond the range
-        ++c.b;
-        c.nb = seq_tiles(kv_lens, c.b, max_blocks, &c.L);
-      } while (c.nb == 0);
-    }
-  }
-  c.b = uni(c.b); c.tb = uni(c.tb); c.h = uni(c.h); c.L = uni(c.L); c.nb = uni(c.nb);
-}
-
-// Page id of the cursor's page (a scalar load; the caller decides when to wait for it).
-__device__ __forceinline__ int page_of(const DecodeArgs& a, const Cursor& c) {
-  return uni(ld_const(a.block_table, (size_t)c.b * a.max_blocks + c.tb));
-}
-
-// Valid tokens of the cursor's half page (<= 0 for the empty second half of a short last
-// page); 0 for an out-of-range page id, whose half page is then read from page 0.
-__device__ __forceinline__ int half_valid(const Cursor& c, int pg, int num_blocks) {
-  int nv = c.L - c.tb * kBlock - c.h * kHalf;
-  nv = nv > kHalf ? kHalf : nv;
-  return (pg < 0 || pg >= num_blocks) ? 0 : nv;
-}
 
 // Each of the four waves issues nine 1 KiB global->LDS loads per half page: latent rows
 // 8w .. 8w+7 (lane l fetches logical chunk l ^ key) and the positional rows 8w .. 8w+7
@@ -183,24 +149,32 @@ __device__ __forceinline__ int half_valid(const Cursor& c, int pg, int num_block
 // global->LDS form, buffer loads let the compiler keep counting LDS reads precisely while
 // page loads are in flight (a pending flat access forces every LDS wait to zero).  Aux is the
 // cache policy: non-temporal when no other workgroup reads the page, so that the stream does
-// not evict the block table, queries and partial outputs from L2.
-template <int Aux>
-__device__ __forceinline__ void load_half(uint8_t* stage, const uint8_t* cache, int pg, int h, int nvalid, int wave,
-                                          int lane) {
+// not evict the queries and partial outputs from L2.
+struct PageLoad {
+  __amdgpu_buffer_rsrc_t rsrc;   // the page (num_records = one page)
+  uint8_t* stage;
+  int h, nvalid;
+};
+__device__ __forceinline__ PageLoad page_load(uint8_t* stage, const uint8_t* cache, int pg, int h, int nvalid) {
   const uint8_t* page = cache + (size_t)(pg < 0 ? 0 : pg) * kTileBytes;
-  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)page, 0, kTileBytes, 0x00020000);
-  asm volatile("" : "+v"(lane));   // rebuild the per-lane offsets here rather than keep them live
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  return PageLoad{__builtin_amdgcn_make_buffer_rsrc((void*)page, 0, kTileBytes, 0x00020000), stage, h, nvalid};
+}
+// Row load i of this wave (i < 8: latent row 8w + i; i == 8: positional rows 8w .. 8w+7).
+template <int Aux>
+__device__ __forceinline__ void load_row(const PageLoad& p, int i, int wave, int lane) {
+  asm volatile("" : "+v"(lane));   // rebuild the per-lane offset here rather than keep it live
+  if (i < 8) {
     const int r = 8 * wave + i;
-    const int rs = r < nvalid ? kHalf * h + r : 0;
+    const int rs = r < p.nvalid ? kHalf * p.h + r : 0;
     const unsigned off = rs * (kRow * 2) + ((lane ^ lat_key(r)) << 4);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (MLA_LDS void*)(stage + r * 1024), 16, off, 0, 0, Aux);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(p.rsrc, (MLA_LDS void*)(p.stage + r * 1024), 16, off, 0, 0, Aux);
+  } else {
+    const int r = 8 * wave + (lane >> 3);
+    const int rs = r < p.nvalid ? kHalf * p.h + r : 0;
+    const unsigned off = rs * (kRow * 2) + kDC * 2 + (((lane & 7) ^ pos_key(r)) << 4);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(p.rsrc, (MLA_LDS void*)(p.stage + kStageLat + 8 * wave * 128), 16, off,
+                                             0, 0, Aux);
   }
-  const int r = 8 * wave + (lane >> 3);
-  const int rs = r < nvalid ? kHalf * h + r : 0;
-  const unsigned off = rs * (kRow * 2) + kDC * 2 + (((lane & 7) ^ pos_key(r)) << 4);
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (MLA_LDS void*)(stage + kStageLat + 8 * wave * 128), 16, off, 0, 0, Aux);
 }
 
 // LDS reads at absolute LDS byte addresses (the callers fold the array base in once).  The
@@ -285,6 +259,7 @@ constexpr float kRescaleLog2 = 64.0f;
 // page y+1 and accumulates the values of half page y, whose probabilities it already holds.
 // Every segment (the part of one sequence inside the range) ends with its unnormalised O and
 // (m, l) per head in workspace slot g + b.
+template <int Aux>
 __global__ void __launch_bounds__(256, 1) decode_mfma_bf16_kernel(DecodeArgs a) {
   extern __shared__ __attribute__((aligned(256))) uint8_t smem[];
   const int lane = threadIdx.x & 63;
@@ -315,15 +290,114 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_bf16_kernel(DecodeArgs a) 
     scan_batch(a.kv_lens, a.B, a.max_blocks, x0, &tot, &b0, &s_first);
   }
   if (b0 < 0) return;                             // unreachable: x0 < T_all lies in some sequence
-  const int n_steps = (int)(2 * (x1 - x0));       // half pages of this range
 
-  Cursor cur;
-  cur.b = uni(b0);
-  cur.nb = uni(seq_tiles(a.kv_lens, cur.b, a.max_blocks, &cur.L));
-  cur.L = uni(cur.L);
-  cur.tb = uni((int)(x0 - s_first));
-  cur.h = 0;
-  Cursor pre = cur;                               // DMA cursor
+  // ---- page table of the range, built once in LDS: entry k describes range page k
+  //   pg     page id in the cache (out-of-range ids are treated as holding no valid token)
+  //   r      tokens from the page's first row to the end of its sequence (kv_len - 64 tb)
+  //   b      sequence
+  //   flags  kFirst: first page of its segment in this range, kLast: last page of it
+  // One thread per sequence (256 at a time) finds where its pages start in the range; each
+  // sequence marks its first page, a prefix maximum over the marks gives every page its
+  // sequence, and one gather per page fetches the ids.  The step loop then needs no cursor
+  // walking and no scalar loads.
+  // the host sizes the ranges to fit the table; the clamp only keeps LDS accesses in bounds
+  const int n_pages = (int)(x1 - x0 < kTabCap ? x1 - x0 : kTabCap);
+  const int n_steps = 2 * n_pages;               // half pages of this range
+  {
+    int* s_start = reinterpret_cast<int*>(smem);          // [256] stage 0 as scratch
+    int* s_len = s_start + 256;                           // [256]
+    int* s_nb = s_start + 512;                            // [256]
+    int* s_wsum = s_start + 768;                          // [4]
+    int* s_mark = s_start + 1024;                         // [kTabCap]
+    const int t = threadIdx.x;
+    long long chunk_b = b0;
+    long long rel_base = -(x0 - s_first);                 // start of sequence chunk_b in range pages
+    int k_done = 0;
+    while (true) {
+      const long long bl = chunk_b + t;
+      int L = 0;
+      const int nb = bl < a.B ? seq_tiles(a.kv_lens, (int)bl, a.max_blocks, &L) : 0;
+      // block-wide exclusive scan of nb
+      int incl = nb;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int v = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += v;
+      }
+      if (lane == 63) s_wsum[wave] = incl;
+      __syncthreads();
+      int before = 0, total = 0;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const int ws = s_wsum[w];
+        before += w < wave ? ws : 0;
+        total += ws;
+      }
+      const long long start = rel_base + before + incl - nb;
+      s_start[t] = (int)(start < -(1ll << 30) ? -(1 << 30) : start);
+      s_len[t] = L;
+      s_nb[t] = nb;
+      const long long k_end_ll = rel_base + total;       // range pages covered by this chunk
+      const int k_end = (int)(k_end_ll < n_pages ? k_end_ll : n_pages);
+      for (int k = k_done + t; k < k_end; k += 256) s_mark[k] = -1;
+      __syncthreads();
+      if (nb > 0 && start >= k_done && start < k_end) s_mark[start] = t;   // sequence t starts at page start
+      __syncthreads();
+      // pages k_done .. k_end-1: sequence = last mark at or before k (page k_done may continue
+      // the sequence of the previous chunk's last page, or of chunk_b itself at the range start)
+      {
+        // parallel prefix maximum: thread t owns pages k_done + 4t .. +3 (k_end - k_done <= 1024)
+        int m4[4];
+        int run = -1;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int k = k_done + 4 * t + i;
+          const int v = k < k_end ? s_mark[k] : -1;
+          run = v > run ? v : run;
+          m4[i] = run;
+        }
+        int inc = run;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+          const int v = __shfl_up(inc, o, 64);
+          if (lane >= o) inc = v > inc ? v : inc;
+        }
+        __syncthreads();                                   // everyone has read its marks
+        if (lane == 63) s_wsum[wave] = inc;
+        __syncthreads();
+        int prev = __shfl_up(inc, 1, 64);
+        if (lane == 0) prev = -1;
+#pragma unroll
+        for (int w = 0; w < 4; ++w)
+          if (w < wave) prev = s_wsum[w] > prev ? s_wsum[w] : prev;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int k = k_done + 4 * t + i;
+          const int r = m4[i] > prev ? m4[i] : prev;
+          if (k < k_end) s_mark[k] = r < 0 ? 0 : r;        // no mark yet: sequence chunk_b
+        }
+      }
+      __syncthreads();
+      int4* tab = reinterpret_cast<int4*>(smem + kTabOff);
+#pragma unroll
+      for (int i = 0; i < kTabCap / 256; ++i) {
+        const int k = k_done + t + 256 * i;
+        if (k < k_end) {
+          const int st = s_mark[k];
+          const int tb = k - s_start[st];
+          const int bk = (int)(chunk_b + st);
+          const int pg = a.block_table[(size_t)bk * a.max_blocks + tb];
+          const int flags = ((k == 0 || tb == 0) ? kFirst : 0) | ((k == n_pages - 1 || tb == s_nb[st] - 1) ? kLast : 0);
+          tab[k] = int4{pg, s_len[st] - kBlock * tb, bk, flags};
+        }
+      }
+      k_done = k_end;
+      __syncthreads();
+      if (k_done >= n_pages || chunk_b + 256 >= a.B) break;
+      chunk_b += 256;
+      rel_base += total;
+    }
+  }
 
   bf16x8 qf[36];
   auto load_q = [&](int bb) {
@@ -332,8 +406,11 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_bf16_kernel(DecodeArgs a) 
     for (int s = 0; s < 36; ++s) qf[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qp + 16 * s));
   };
   // this lane's part of workspace slot (g + b, j): O row of its head, columns 4hl + 8q4 + 32ct
+  // this lane's part of workspace slot (g + b, j), stored in register order: wave block of
+  // 64 KiB, then (column tile ct, quad q4) blocks of 1 KiB, then 16 bytes per lane, so that
+  // every store instruction writes 1 KiB contiguously
   auto slot_o = [&](int bb) -> float* {
-    return a.part_o + (((size_t)(g + bb) * a.Sq + j) * kH + head) * kDC + 4 * hl;
+    return a.part_o + ((size_t)(g + bb) * a.Sq + j) * (kH * kDC) + (size_t)wave * (32 * kDC) + 4 * lane;
   };
 
   f32x16 oacc[16];
@@ -344,7 +421,7 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_bf16_kernel(DecodeArgs a) 
   bool over = false;                              // a score left the reference's safe range
 
   // ---- S^T of the half page in `tile` (36 chained K-steps)
-  auto scores = [&](const uint8_t* tile) -> f32x16 {
+  auto scores = [&](const uint8_t* tile, auto hook) -> f32x16 {
     int ln = lane;
     asm volatile("" : "+v"(ln));
     const int rr = ln & 31, hh = ln >> 5;
@@ -374,6 +451,7 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_bf16_kernel(DecodeArgs a) 
       if (st + D < 36) kr[(st + D) % (D + 1)] = lds_b128(koff(st + D));
       __builtin_amdgcn_sched_barrier(0);
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kr[st % (D + 1)]), qf[st], acc, 0, 0, 0);
+      hook(st);
       __builtin_amdgcn_sched_barrier(0);
     }
     return acc;
@@ -416,10 +494,6 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_bf16_kernel(DecodeArgs a) 
     st.l_new = l;
     st.p0 = bf16x8{pk[0][0], pk[0][1], pk[1][0], pk[1][1], pk[2][0], pk[2][1], pk[3][0], pk[3][1]};
     st.p1 = bf16x8{pk[4][0], pk[4][1], pk[5][0], pk[5][1], pk[6][0], pk[6][1], pk[7][0], pk[7][1]};
-  };
-  auto soft_vis = [&](const Cursor& c, int nv) {
-    const int lim = (c.L - a.Sq + j) - (c.tb * kBlock + c.h * kHalf);   // visible rows r <= lim
-    return nv - 1 < lim ? nv - 1 : lim;                                  // last visible row
   };
 
   // ---- O^T += V^T . P^T for the half page in `tile`
@@ -466,104 +540,90 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_bf16_kernel(DecodeArgs a) 
     pf[1] = st.p1;
   };
 
-  // Page ids for the page loads come one step ahead, through LDS: each wave fetches the next
-  // id with a 4-byte buffer->LDS load into its own slot, issued just before the step's nine
-  // page loads, so the wait for the previous stage at the top of the next step covers it
-  // (vector loads complete in order); the id is then read back from LDS.  A scalar load
-  // would force every LDS wait to zero while pending, and a vector load into a register is
-  // waited for with the whole page pipeline (the compiler cannot count it across the loop).
-  const size_t bt_bytes = (size_t)a.B * a.max_blocks * sizeof(int32_t);
-  const __amdgpu_buffer_rsrc_t bt_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)a.block_table, 0, (int)(bt_bytes < 0x7FFFFFFF ? bt_bytes : 0x7FFFFFFF), 0x00020000);
-  auto page_fetch = [&](const Cursor& c) {
-    const unsigned off = (unsigned)(((size_t)c.b * a.max_blocks + c.tb) * sizeof(int32_t));
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(bt_rsrc, (MLA_LDS void*)(smem + kPgSlot + wave * 256), 4, off, 0, 0, 0);
-  };
-  auto page_read = [&]() -> int {
-    return uni(*reinterpret_cast<const MLA_LDS int*>((const MLA_LDS uint8_t*)smem + kPgSlot + wave * 256));
-  };
-
   // One page load per stage is issued every step, also past the end of the range (then it
-  // reads row 0 of page 0 and holds no valid token), so that every step issues the same
-  // vector-memory sequence: the next page id, then the nine page loads.  With that fixed
-  // order the wait at the top of a step is always "all but the nine youngest".
-  auto issue = [&](int stage, int pg, int nv, int h) {
-    if (a.stream_nt) load_half<2>(smem + stage * kStageBytes, a.cache, nv > 0 ? pg : 0, h, nv, wave, lane);
-    else load_half<0>(smem + stage * kStageBytes, a.cache, nv > 0 ? pg : 0, h, nv, wave, lane);
+  // reads row 0 of page 0 and holds no valid token), so that every step issues the same nine
+  // vector-memory operations and the wait at the top of a step is always "all but the nine
+  // youngest".
+  auto load_for = [&](int stage, int pg, int nv, int h) {
+    return page_load(smem + stage * kStageBytes, a.cache, nv > 0 ? pg : 0, h, nv);
+  };
+  auto issue = [&](const PageLoad& pl) {
+#pragma unroll
+    for (int i = 0; i < 9; ++i) load_row<Aux>(pl, i, wave, lane);
+  };
+  // table entry of half page z (wave-uniform); past the range: no valid token
+  // (read through an absolute LDS address: through a pointer into the shared array the
+  // compiler would wait for the page loads in flight, which may alias it)
+  const uint32_t tab_addr = lds_addr(smem + kTabOff);
+  auto entry = [&](int z) -> int4 {
+    if (z >= n_steps) return int4{-1, 0, 0, 0};
+    const u32x4 e = lds_b128(tab_addr + 16u * (uint32_t)(z >> 1));
+    return int4{uni((int)e[0]), uni((int)e[1]), uni((int)e[2]), uni((int)e[3])};
+  };
+  auto valid_page = [&](const int4& e) { return e.x >= 0 && e.x < a.num_blocks; };
+  // valid tokens of half page z (<= 0 for an empty second half); 0 for an invalid page
+  auto nvalid = [&](const int4& e, int z) {
+    const int nv = e.y - kHalf * (z & 1);
+    return valid_page(e) ? (nv < kHalf ? nv : kHalf) : 0;
+  };
+  // last visible row of half page z for query j (causal: position kv_len - Sq + j)
+  auto last_visible = [&](const int4& e, int z) {
+    const int v = e.y - kHalf * (z & 1) - a.Sq + j;
+    return valid_page(e) ? (v < kHalf - 1 ? v : kHalf - 1) : -1;
   };
 
   // prologue: queries, half pages 0..2 in flight, scores and probabilities of half page 0.
-  // nv1..nv3: valid tokens of half pages y+1 .. y+3 (known when their loads are issued).
-  load_q(cur.b);
-  int nv1 = 0, nv2 = 0, nv3 = 0;
+  // e0..e3: table entries of half pages y .. y+3.
+  int4 e0 = entry(0), e1 = entry(1), e2 = entry(2), e3;
+  load_q(e0.z);
+  issue(load_for(0, e0.x, nvalid(e0, 0), 0));
+  issue(load_for(1, e1.x, nvalid(e1, 1), 1));
+  issue(load_for(2, e2.x, nvalid(e2, 2), 0));
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+  lds_barrier();
   {
-    int nvk[3] = {0, 0, 0};
-#pragma unroll
-    for (int k = 0; k < 3; ++k) {
-      int pg = 0;
-      if (k < n_steps) {
-        pg = page_of(a, pre);
-        nvk[k] = half_valid(pre, pg, a.num_blocks);
-      }
-      issue(k, pg, nvk[k], pre.h);
-      if (k < n_steps) cursor_next(pre, a.kv_lens, a.B, a.max_blocks);
-    }
-    page_fetch(3 < n_steps ? pre : cur);
-    nv1 = nvk[1];
-    nv2 = nvk[2];
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-    lds_barrier();
-    f32x16 s0 = scores(smem);
-    softmax(s0, soft_vis(cur, nvk[0]), true, sm);
+    f32x16 s0 = scores(smem, [](int) {});
+    softmax(s0, last_visible(e0, 0), true, sm);
     soft_commit(sm);
   }
 
   for (int y = 0; y < n_steps; ++y) {
     const bool has_next = y + 1 < n_steps;
-    // this wave's loads of half page y+1 and the page id landed (only the nine loads of half
-    // page y+2 may stay in flight), then everyone's
+    // this wave's loads of half page y+1 landed (only the nine loads of half page y+2 may
+    // stay in flight), then everyone's
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(9));
     lds_barrier();   // stage (y+3)%4 == (y-1)%4 is no longer read by anyone
-    {
-      const int pg = page_read();
-      __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): read before the slot is refilled
-      Cursor la = pre;
-      nv3 = 0;
-      if (y + 3 < n_steps) {
-        nv3 = half_valid(pre, pg, a.num_blocks);
-        cursor_next(la, a.kv_lens, a.B, a.max_blocks);
-      }
-      page_fetch(y + 4 < n_steps ? la : cur);
-      issue((y + 3) & 3, pg, nv3, pre.h);
-      pre = la;
-    }
-    Cursor nx = cur;
-    cursor_next(nx, a.kv_lens, a.B, a.max_blocks);
-    const bool seg_end = (cur.h == 1 && cur.tb == cur.nb - 1) || !has_next;
+    e3 = entry(y + 3);
+    // the nine page loads of half page y+3 go out one after every fourth score MFMA, so that
+    // their issue (which may wait for queue space) overlaps matrix work
+    const PageLoad pl = load_for((y + 3) & 3, e3.x, nvalid(e3, y + 3), (y + 3) & 1);
+    const bool seg_end = ((y & 1) && (e0.w & kLast)) || !has_next;
     if (seg_end && has_next) {
       // the next half page starts another sequence: its queries replace this one's (waiting
       // here keeps the steady-state loop free of pending query loads)
-      load_q(nx.b);
+      load_q(e1.z);
       __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     }
-    f32x16 snext = scores(smem + ((y + 1) & 3) * kStageBytes);   // stale data if !has_next
+    f32x16 snext = scores(smem + ((y + 1) & 3) * kStageBytes, [&](int st) {   // stale data if !has_next
+      if ((st & 3) == 0) load_row<Aux>(pl, st >> 2, wave, lane);
+    });
     const float m_old = m_ref, l_old = l_run;
     const bool over_old = over;
-    softmax(snext, soft_vis(nx, nv1), seg_end, sm);
+    softmax(snext, last_visible(e1, y + 1), seg_end, sm);
     values(smem + (y & 3) * kStageBytes, pf);
 
     if (seg_end) {
       // unnormalised O and (m, l) of this segment into its slot; the combine normalises
       const float l_tot = pair_sum(l_old);
-      const size_t row = ((size_t)(g + cur.b) * a.Sq + j) * kH + head;
+      const size_t row = ((size_t)(g + e0.z) * a.Sq + j) * kH + head;
       if (hl == 0) reinterpret_cast<float2*>(a.part_ml)[row] = float2{m_old, over_old ? -1.0f : l_tot};
-      float* so = slot_o(cur.b);
+      float* so = slot_o(e0.z);
       // oacc[ct][4q4 + i] is column 32ct + 8q4 + 4hl + i of this lane's head
 #pragma unroll
       for (int ct = 0; ct < 16; ++ct)
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4)
-          *reinterpret_cast<f32x4*>(so + 32 * ct + 8 * q4) =
+          *reinterpret_cast<f32x4*>(so + 256 * (4 * ct + q4)) =
               f32x4{oacc[ct][4 * q4], oacc[ct][4 * q4 + 1], oacc[ct][4 * q4 + 2], oacc[ct][4 * q4 + 3]};
       if (has_next) {
 #pragma unroll
@@ -571,9 +631,9 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_bf16_kernel(DecodeArgs a) 
       }
     }
     soft_commit(sm);
-    nv1 = nv2;
-    nv2 = nv3;
-    cur = nx;
+    e0 = e1;
+    e1 = e2;
+    e2 = e3;
   }
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));   // no page load may land after the workgroup ends
 }
@@ -627,20 +687,28 @@ __device__ void exact_head(const DecodeArgs& a, int b, int j, int h, int L, floa
 }
 
 
-// One workgroup per (query row, 4 heads); 64 threads per head, 8 latent columns each.  Every
-// segment left its unnormalised O_g and (m_g, l_g) in slot g + b; with M = max m_g over the
+// One workgroup per (query row, group of 32 heads).  Every segment left its unnormalised
+// O_g (in register order) and (m_g, l_g) per head in slot g + b; with M = max m_g over the
 // non-empty ones and w_g = 2^(m_g - M):  o = sum w_g O_g / sum w_g l_g,
-// lse = ln 2 * (M + log2 sum w_g l_g).
+// lse = ln 2 * (M + log2 sum w_g l_g).  Thread t reads 16-byte pieces t + 256i of the
+// group's 64 KiB block (coalesced); all of them belong to head 32w + t%32, so each thread
+// needs one head's weights.  The result goes through LDS so that the rows of o_lat are
+// written contiguously.  Heads marked by the fast path are then recomputed exactly.
+constexpr int kCombineLds = 32 * kDC * 4 + 64;
+
 __global__ void __launch_bounds__(256) combine_kernel(DecodeArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t cl[];
+  float* tile = reinterpret_cast<float*>(cl);                 // [32 heads][512]
+  int* redo_mask = reinterpret_cast<int*>(cl + 32 * kDC * 4);  // heads to recompute
   const int row = blockIdx.x;          // b*Sq + j
   const int b = row / a.Sq, j = row - b * a.Sq;
-  const int h = blockIdx.y * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
+  const int w = blockIdx.y;            // heads 32w .. 32w+31
+  const int t = threadIdx.x, lane = t & 63;
+  const int hh = t & 31, h = 32 * w + hh, hl = (t >> 5) & 1;
   long long T_all, S_b;
   int bb;
   scan_batch(a.kv_lens, a.B, a.max_blocks, -1, &T_all, &bb, &S_b);
-  // first tile of sequence b: rescan with an exclusive prefix
-  long long first = 0;
+  long long first = 0;                 // first tile of sequence b
   for (int base = 0; base < b; base += 64) {
     const int q = base + lane;
     int L;
@@ -649,56 +717,68 @@ __global__ void __launch_bounds__(256) combine_kernel(DecodeArgs a) {
   }
   int Lb;
   const int nb = seq_tiles(a.kv_lens, b, a.max_blocks, &Lb);
-  float* out = a.o_lat + ((size_t)row * kH + h) * kDC + 8 * lane;
+  if (t == 0) *redo_mask = 0;
+  __syncthreads();
+  float* out_row = a.o_lat + ((size_t)row * kH + 32 * w) * kDC;
   if (nb == 0) {
-    *reinterpret_cast<f32x4*>(out) = f32x4{0.f, 0.f, 0.f, 0.f};
-    *reinterpret_cast<f32x4*>(out + 4) = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (lane == 0) a.lse[(size_t)row * kH + h] = -INFINITY;
+    for (int i = t; i < 32 * kDC / 4; i += 256) reinterpret_cast<f32x4*>(out_row)[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (t < 32) a.lse[(size_t)row * kH + 32 * w + t] = -INFINITY;
     return;
   }
   const int g_lo = range_of_tile(first, T_all, a.G);
   const int g_hi = range_of_tile(first + nb - 1, T_all, a.G);
   // Ranges between g_lo and g_hi that hold no page at all (possible when the batch has fewer
   // pages than ranges) wrote nothing: skip them.
-  auto empty = [&](int g) {
-    return (long long)g * T_all / a.G == (long long)(g + 1) * T_all / a.G;
-  };
+  auto empty = [&](int g) { return (long long)g * T_all / a.G == (long long)(g + 1) * T_all / a.G; };
   const float2* ml = reinterpret_cast<const float2*>(a.part_ml);
-  auto slot = [&](int g) { return ((size_t)(g + b) * a.Sq + j) * kH + h; };
+  auto slot = [&](int g) { return ((size_t)(g + b) * a.Sq + j); };
   float M = -INFINITY;
   bool redo = false;
   for (int g = g_lo; g <= g_hi; ++g) {
     if (empty(g)) continue;
-    const float2 v = ml[slot(g)];
+    const float2 v = ml[slot(g) * kH + h];
     if (v.y < 0.f) redo = true;
     else if (v.y > 0.f) M = fmaxf(M, v.x);
   }
+  f32x4 acc[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   float L = 0.f;
-  f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
   if (!redo && M != -INFINITY) {
     for (int g = g_lo; g <= g_hi; ++g) {
       if (empty(g)) continue;
-      const float2 v = ml[slot(g)];
+      const float2 v = ml[slot(g) * kH + h];
       if (!(v.y > 0.f)) continue;
-      const float w = __builtin_amdgcn_exp2f(v.x - M);
-      L += w * v.y;
-      const float* src = a.part_o + slot(g) * kDC + 8 * lane;
-      acc0 += w * *reinterpret_cast<const f32x4*>(src);
-      acc1 += w * *reinterpret_cast<const f32x4*>(src + 4);
-    }
-    bool fin = true;
+      const float wg = __builtin_amdgcn_exp2f(v.x - M);
+      L += wg * v.y;
+      const f32x4* src = reinterpret_cast<const f32x4*>(a.part_o + slot(g) * (kH * kDC) + (size_t)w * (32 * kDC));
 #pragma unroll
-    for (int i = 0; i < 4; ++i) fin = fin && __builtin_isfinite(acc0[i]) && __builtin_isfinite(acc1[i]);
-    redo = __ballot(!fin) != 0 || !__builtin_isfinite(L);
+      for (int i = 0; i < 16; ++i) acc[i] += wg * src[t + 256 * i];
+    }
   }
-  if (redo) {
-    exact_head(a, b, j, h, Lb, out);
-    return;
-  }
+  bool fin = __builtin_isfinite(L);
+#pragma unroll
+  for (int i = 0; i < 16; ++i)
+    fin = fin && __builtin_isfinite(acc[i][0]) && __builtin_isfinite(acc[i][1]) && __builtin_isfinite(acc[i][2]) &&
+          __builtin_isfinite(acc[i][3]);
+  redo = redo || !fin;
   const float inv = L > 0.f ? 1.0f / L : 0.0f;
-  *reinterpret_cast<f32x4*>(out) = acc0 * inv;
-  *reinterpret_cast<f32x4*>(out + 4) = acc1 * inv;
-  if (lane == 0) a.lse[(size_t)row * kH + h] = L > 0.f ? (M + __log2f(L)) * 0.69314718055994531f : -INFINITY;
+  // piece t + 256i: block (ct, q4) = (t + 256i) / 64, lane t%64 -> columns 32ct + 8q4 + 4hl
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int blk = (t >> 6) + 4 * i, ct = blk >> 2, q4 = blk & 3;
+    *reinterpret_cast<f32x4*>(tile + hh * kDC + 32 * ct + 8 * q4 + 4 * hl) = acc[i] * inv;
+  }
+  if (redo) atomicOr(redo_mask, 1 << hh);
+  __syncthreads();
+  for (int i = t; i < 32 * kDC / 4; i += 256) reinterpret_cast<f32x4*>(out_row)[i] = reinterpret_cast<const f32x4*>(tile)[i];
+  if (t < 32) a.lse[(size_t)row * kH + h] = L > 0.f ? (M + __log2f(L)) * 0.69314718055994531f : -INFINITY;
+  const int mask = *redo_mask;
+  if (mask) {
+    __syncthreads();   // the plain results are written before any exact row replaces them
+    for (int k = t >> 6; k < 32; k += 4)
+      if (mask & (1 << k)) exact_head(a, b, j, 32 * w + k, Lb, a.o_lat + ((size_t)row * kH + 32 * w + k) * kDC + 8 * lane);
+  }
 }
 
 // ------------------------------------------------------------------------ generic decode (VALU)
@@ -781,13 +861,17 @@ __global__ void __launch_bounds__(256) decode_generic_kernel(
 bool is_dsv2_shape(const mla_config_t& c);
 
 // Token ranges of the split: one workgroup per (range, query) and one workgroup per compute
-// unit (each holds 154 KiB of LDS), so G = CUs / Sq, capped by the number of pages.
+// unit (each holds all 160 KiB of LDS), so G = CUs / Sq, capped by the number of pages, and
+// raised where needed so that no range exceeds the LDS page table (kTabCap pages: the pages
+// of the batch are at most B * max_blocks).
 int decode_num_ranges(int num_cus, int B, int Sq, int max_blocks) {
-  long long cap = (long long)B * max_blocks;
-  int G = num_cus / (Sq > 0 ? Sq : 1);
+  const long long cap = (long long)B * max_blocks;
+  long long G = num_cus / (Sq > 0 ? Sq : 1);
   if (G < 1) G = 1;
-  if (cap < G) G = (int)(cap < 1 ? 1 : cap);
-  return G;
+  const long long need = (cap + kTabCap - 1) / kTabCap;
+  if (G < need) G = need;
+  if (cap < G) G = cap < 1 ? 1 : cap;
+  return (int)G;
 }
 
 size_t decode_workspace_bytes(const mla_config_t& cfg, int num_cus, int B, int Sq, int max_blocks) {
@@ -824,20 +908,35 @@ hipError_t launch_decode(const mla_config_t& cfg, int num_cus, const void* q_abs
     a.Sq = Sq;
     a.G = G;
     a.scale_log2 = scale * 1.4426950408889634f;
-    a.stream_nt = Sq == 1 ? 1 : 0;
     static bool attr_set = false;   // idempotent; races only repeat the same call
     if (!attr_set) {
-      hipError_t e = hipFuncSetAttribute((const void*)decode_mfma_bf16_kernel,
+      hipError_t e = hipFuncSetAttribute((const void*)decode_mfma_bf16_kernel<0>,
                                          hipFuncAttributeMaxDynamicSharedMemorySize, kDecodeLds);
+      if (e == hipSuccess)
+        e = hipFuncSetAttribute((const void*)decode_mfma_bf16_kernel<2>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                kDecodeLds);
       if (e != hipSuccess) return e;
       attr_set = true;
     }
     if (phases & 1) {
-      hipLaunchKernelGGL(decode_mfma_bf16_kernel, dim3(G * Sq), dim3(64 * kWaves), kDecodeLds, stream, a);
+      // non-temporal page loads when no other workgroup reads the same pages (one query)
+      if (Sq == 1)
+        hipLaunchKernelGGL(decode_mfma_bf16_kernel<2>, dim3(G * Sq), dim3(64 * kWaves), kDecodeLds, stream, a);
+      else
+        hipLaunchKernelGGL(decode_mfma_bf16_kernel<0>, dim3(G * Sq), dim3(64 * kWaves), kDecodeLds, stream, a);
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
-    if (phases & 2) hipLaunchKernelGGL(combine_kernel, dim3(B * Sq, kH / 4), dim3(256), 0, stream, a);
+    if (phases & 2) {
+      static bool cattr = false;
+      if (!cattr) {
+        hipError_t e = hipFuncSetAttribute((const void*)combine_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                           kCombineLds);
+        if (e != hipSuccess) return e;
+        cattr = true;
+      }
+      hipLaunchKernelGGL(combine_kernel, dim3(B * Sq, kH / 32), dim3(256), kCombineLds, stream, a);
+    }
     return hipGetLastError();
   }
   if (!(phases & 1)) return hipSuccess;   // generic path: one launch does everything
