@@ -12,13 +12,15 @@
 //   grid      G*Sq workgroups: G token ranges split the batch's pages evenly ("stream-K":
 //             a range may span sequence boundaries), times Sq queries.  blockIdx is remapped
 //             so that the Sq workgroups of one range sit on one XCD and share its L2.
-//   block     512 threads = 8 waves (2 per SIMD); all 128 heads of the query live in the
-//             workgroup, so every cached row is read from HBM once per query.
-//   per step  32 tokens (half a page) staged in LDS by 16-byte global->LDS loads, four
+//   block     256 threads = 4 waves, one per SIMD; wave w owns heads 32w .. 32w+31, so all
+//             128 heads of the query live in the workgroup and every cached row is read from
+//             HBM once per query.
+//   per step  32 tokens (half a page) staged in LDS by 16-byte buffer->LDS loads, four
 //             stages in flight, rows XOR-swizzled at 16-byte granularity:
-//               S^T[32 tok, 16 heads] = Stage[32, 576] . Qabs^T   v_mfma_f32_16x16x32_bf16
+//               S^T[32 tok, 32 heads] = Stage[32, 576] . Qabs^T   v_mfma_f32_32x32x16_bf16
 //               softmax in the exp2 domain against a fixed per-segment reference
-//               O^T[256 cols, 32 heads] += Stage[:, :512]^T . P^T (V^T via ds_read_b64_tr_b16)
+//               O^T[512 cols, 32 heads] += Stage[:, :512]^T . P^T (V^T via ds_read_b64_tr_b16),
+//               O held in the accumulation registers for the whole segment
 //   output    each segment (one sequence's part of a range) writes its unnormalised O and
 //             (m, l) per head to workspace slot g + b; the combine normalises.
 #include "common.h"
