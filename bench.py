@@ -149,7 +149,7 @@ def main() -> int:
              "frac": round(gbs / PEAK_HBM_GBS, 4)} if bound_hbm else
             {"bound": "mfma", "achieved": round(tflops, 1), "peak": peak_mfma, "unit": "TFLOP/s",
              "frac": round(tflops / peak_mfma, 4)})
-    roof["kernel"] = "decode_mfma_bf16_kernel"
+    roof["kernel"] = "decode_mfma_fp8_kernel" if w.dtype == "fp8" else "decode_mfma_bf16_kernel"
     roof["traffic"] = None
     value = w.batch * w.sq / (ms_per_step * 1e-3)
     line = {

@@ -42,8 +42,8 @@
  *   FP8_E4M3 cache with BF16 activ.  DeepSeek-V2 shape only.  Each cached row (all d_c+d_R
  *                                    values of a token) is stored as OCP e4m3fn codes with
  *                                    one fp32 scale = amax(row)/448 (1.0 for a zero row);
- *                                    value = code * scale.  The folded query is likewise fp8
- *                                    with one fp32 scale per (query row, head).
+ *                                    value = code * scale.  Queries, weights and outputs
+ *                                    stay bf16.
  *   Generic limits: num_heads <= 128, d_c + d_R <= 1024, d_h <= 256, d_v <= 256.
  *   All shapes: d_c, d_R, d_h, d_v multiples of 16, d_R even, block_size == 64.
  */
@@ -118,13 +118,11 @@ mla_status_t mla_cache_append(const mla_config_t* cfg, void* cache, float* cache
  *
  *   q_nope  [T, H, d_h] act_dtype      q_rope [T, H, d_R] act_dtype (before RoPE)
  *   q_pos   [T] int32 (device)         w_uk [d_c, H*d_h] act_dtype
- *   q_abs   [T, H, d_c + d_R]: act_dtype for F32/BF16 caches; e4m3 codes for FP8 caches
- *   q_scale [T, H] fp32: FP8 caches only (amax/448 of the row), NULL otherwise
+ *   q_abs   [T, H, d_c + d_R] act_dtype (for every cache format)
  * Matrix-core path: bf16 products, fp32 accumulation, one rounding to the output format.
  */
 mla_status_t mla_absorb_q(const mla_config_t* cfg, const void* q_nope, const void* q_rope,
-                          const int32_t* q_pos, const void* w_uk, void* q_abs, float* q_scale,
-                          int32_t T, void* stream);
+                          const int32_t* q_pos, const void* w_uk, void* q_abs, int32_t T, void* stream);
 
 /*
  * mla_decode_workspace_size -- bytes of scratch mla_decode_attn needs for batch B,
@@ -144,19 +142,21 @@ size_t mla_decode_workspace_size(const mla_config_t* cfg, int32_t B, int32_t Sq,
  *   score[s] = softmax_scale * (q_abs[t,i] . cache_row[s])       (content + positional)
  *   o_lat[t,i] = sum_s softmax(score)[s] * c_s                   ([T, H, d_c] fp32)
  *   lse[t,i]   = log sum_s exp(score[s])                         ([T, H] fp32, natural log)
- * FP8: row values are code*cache_scale, query values code*q_scale.
+ * FP8: row values are code*cache_scale.  The matrix instructions take e4m3 operands: each
+ * head's query becomes two e4m3 terms (hi + lo/16 with one fp32 scale, about 8 significant
+ * bits) and the probabilities one e4m3 term per token with a power-of-two block scale.
  * The token range is split across workgroups (split-K); partial results go to `workspace`
  * and are merged by a log-sum-exp combine.  A sequence with kv_len <= 0 gives o_lat = 0 and
  * lse = -inf.  Preconditions: Sq <= kv_len[b] <= 64*max_blocks (longer lengths are clamped
  * to the table), pages in [0, num_blocks) (tokens on other pages are skipped).
  *
- *   q_abs       [T, H, d_c + d_R] (mla_absorb_q output)    q_scale [T, H] (FP8) or NULL
+ *   q_abs       [T, H, d_c + d_R] act_dtype (mla_absorb_q output)
  *   cache       [num_blocks, 64, d_c + d_R]                 cache_scale [num_blocks, 64] or NULL
  *   block_table [B, max_blocks] int32 (device)              kv_lens [B] int32 (device)
  *   workspace   >= mla_decode_workspace_size(cfg, B, Sq, max_blocks) bytes, 256-byte aligned;
  *               contents need no initialisation and are not preserved.
  */
-mla_status_t mla_decode_attn(const mla_config_t* cfg, const void* q_abs, const float* q_scale,
+mla_status_t mla_decode_attn(const mla_config_t* cfg, const void* q_abs,
                              const void* cache, const float* cache_scale, int32_t num_blocks,
                              const int32_t* block_table, int32_t max_blocks,
                              const int32_t* kv_lens, int32_t B, int32_t Sq, void* workspace,
@@ -170,12 +170,12 @@ mla_status_t mla_decode_attn(const mla_config_t* cfg, const void* q_abs, const f
  * combine merges the partials (and writes the kv_len <= 0 results).  On the generic
  * (non-matrix-core) path split does all the work and combine launches nothing.
  */
-mla_status_t mla_decode_split(const mla_config_t* cfg, const void* q_abs, const float* q_scale,
+mla_status_t mla_decode_split(const mla_config_t* cfg, const void* q_abs,
                               const void* cache, const float* cache_scale, int32_t num_blocks,
                               const int32_t* block_table, int32_t max_blocks,
                               const int32_t* kv_lens, int32_t B, int32_t Sq, void* workspace,
                               size_t ws_bytes, float* o_lat, float* lse, void* stream);
-mla_status_t mla_decode_combine(const mla_config_t* cfg, const void* q_abs, const float* q_scale,
+mla_status_t mla_decode_combine(const mla_config_t* cfg, const void* q_abs,
                                 const void* cache, const float* cache_scale, int32_t num_blocks,
                                 const int32_t* block_table, int32_t max_blocks,
                                 const int32_t* kv_lens, int32_t B, int32_t Sq, void* workspace,
@@ -194,7 +194,7 @@ mla_status_t mla_out_proj(const mla_config_t* cfg, const float* o_lat, const voi
 /* Human-readable name of a status code (static storage). */
 const char* mla_status_string(mla_status_t status);
 
-/* ABI version of this header: 1. */
+/* ABI version of this header: 2. */
 int32_t mla_abi_version(void);
 
 #ifdef __cplusplus

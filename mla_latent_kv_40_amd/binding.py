@@ -48,11 +48,11 @@ def lib() -> ctypes.CDLL:
         vp, i32, f32p = ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p
         cfgp = ctypes.POINTER(MlaConfig)
         L.mla_cache_append.argtypes = [cfgp, vp, f32p, i32, vp, vp, vp, vp, vp, i32, i32, i32, vp]
-        L.mla_absorb_q.argtypes = [cfgp, vp, vp, vp, vp, vp, f32p, i32, vp]
+        L.mla_absorb_q.argtypes = [cfgp, vp, vp, vp, vp, vp, i32, vp]
         L.mla_decode_workspace_size.argtypes = [cfgp, i32, i32, i32]
         L.mla_decode_workspace_size.restype = ctypes.c_size_t
         for name in ("mla_decode_attn", "mla_decode_split", "mla_decode_combine"):
-            getattr(L, name).argtypes = [cfgp, vp, f32p, vp, f32p, i32, vp, i32, vp, i32, i32, vp, ctypes.c_size_t,
+            getattr(L, name).argtypes = [cfgp, vp, vp, f32p, i32, vp, i32, vp, i32, i32, vp, ctypes.c_size_t,
                                          f32p, f32p, vp]
         L.mla_out_proj.argtypes = [cfgp, f32p, vp, vp, i32, vp]
         L.mla_status_string.argtypes = [ctypes.c_int]
@@ -115,9 +115,9 @@ def mla_cache_append(cfg: Config, cache, cache_scale, num_blocks, c_kv, k_r, pos
     return st
 
 
-def mla_absorb_q(cfg: Config, q_nope, q_rope, q_pos, w_uk, q_abs, q_scale, T, stream=None, check=True) -> int:
+def mla_absorb_q(cfg: Config, q_nope, q_rope, q_pos, w_uk, q_abs, T, stream=None, check=True) -> int:
     st = lib().mla_absorb_q(ctypes.byref(cfg.c()), _ptr(q_nope), _ptr(q_rope), _ptr(q_pos), _ptr(w_uk),
-                            _ptr(q_abs), _ptr(q_scale), T, _stream(stream))
+                            _ptr(q_abs), T, _stream(stream))
     if check:
         _check("mla_absorb_q", st)
     return st
@@ -127,9 +127,9 @@ def mla_decode_workspace_size(cfg: Config, B: int, Sq: int, max_blocks: int) -> 
     return int(lib().mla_decode_workspace_size(ctypes.byref(cfg.c()), B, Sq, max_blocks))
 
 
-def _decode(fn, cfg, q_abs, q_scale, cache, cache_scale, num_blocks, block_table, max_blocks, kv_lens, B, Sq,
+def _decode(fn, cfg, q_abs, cache, cache_scale, num_blocks, block_table, max_blocks, kv_lens, B, Sq,
             workspace, ws_bytes, o_lat, lse, stream, check):
-    st = getattr(lib(), fn)(ctypes.byref(cfg.c()), _ptr(q_abs), _ptr(q_scale), _ptr(cache), _ptr(cache_scale),
+    st = getattr(lib(), fn)(ctypes.byref(cfg.c()), _ptr(q_abs), _ptr(cache), _ptr(cache_scale),
                             num_blocks, _ptr(block_table), max_blocks, _ptr(kv_lens), B, Sq, _ptr(workspace),
                             ws_bytes, _ptr(o_lat), _ptr(lse), _stream(stream))
     if check:
@@ -137,21 +137,21 @@ def _decode(fn, cfg, q_abs, q_scale, cache, cache_scale, num_blocks, block_table
     return st
 
 
-def mla_decode_attn(cfg: Config, q_abs, q_scale, cache, cache_scale, num_blocks, block_table, max_blocks,
+def mla_decode_attn(cfg: Config, q_abs, cache, cache_scale, num_blocks, block_table, max_blocks,
                     kv_lens, B, Sq, workspace, ws_bytes, o_lat, lse, stream=None, check=True) -> int:
-    return _decode("mla_decode_attn", cfg, q_abs, q_scale, cache, cache_scale, num_blocks, block_table, max_blocks,
+    return _decode("mla_decode_attn", cfg, q_abs, cache, cache_scale, num_blocks, block_table, max_blocks,
                    kv_lens, B, Sq, workspace, ws_bytes, o_lat, lse, stream, check)
 
 
-def mla_decode_split(cfg: Config, q_abs, q_scale, cache, cache_scale, num_blocks, block_table, max_blocks,
+def mla_decode_split(cfg: Config, q_abs, cache, cache_scale, num_blocks, block_table, max_blocks,
                      kv_lens, B, Sq, workspace, ws_bytes, o_lat, lse, stream=None, check=True) -> int:
-    return _decode("mla_decode_split", cfg, q_abs, q_scale, cache, cache_scale, num_blocks, block_table, max_blocks,
+    return _decode("mla_decode_split", cfg, q_abs, cache, cache_scale, num_blocks, block_table, max_blocks,
                    kv_lens, B, Sq, workspace, ws_bytes, o_lat, lse, stream, check)
 
 
-def mla_decode_combine(cfg: Config, q_abs, q_scale, cache, cache_scale, num_blocks, block_table, max_blocks,
+def mla_decode_combine(cfg: Config, q_abs, cache, cache_scale, num_blocks, block_table, max_blocks,
                        kv_lens, B, Sq, workspace, ws_bytes, o_lat, lse, stream=None, check=True) -> int:
-    return _decode("mla_decode_combine", cfg, q_abs, q_scale, cache, cache_scale, num_blocks, block_table,
+    return _decode("mla_decode_combine", cfg, q_abs, cache, cache_scale, num_blocks, block_table,
                    max_blocks, kv_lens, B, Sq, workspace, ws_bytes, o_lat, lse, stream, check)
 
 

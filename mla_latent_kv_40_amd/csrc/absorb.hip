@@ -20,12 +20,10 @@ namespace mla {
 constexpr int kAbsH = 128, kAbsDH = 128, kAbsDC = 512, kAbsDR = 64, kAbsRow = 576;
 constexpr int kAbsLdsStride = kAbsRow + 4;   // fp32 words per staged row
 
-// OutFmt: MLA_BF16 -> bf16 q_abs; MLA_FP8_E4M3 -> e4m3 codes + per-(t,h) scale.
-template <int OutFmt>
 __global__ void __launch_bounds__(256) absorb_q_mfma_kernel(
     const uint16_t* __restrict__ q_nope, const uint16_t* __restrict__ q_rope,
-    const int32_t* __restrict__ q_pos, const uint16_t* __restrict__ w_uk, void* __restrict__ q_abs,
-    float* __restrict__ q_scale, int T, float rope_base) {
+    const int32_t* __restrict__ q_pos, const uint16_t* __restrict__ w_uk, uint16_t* __restrict__ q_abs, int T,
+    float rope_base) {
   __shared__ float stage[32 * kAbsLdsStride];
   const int h = blockIdx.x;
   const int t0 = blockIdx.y * 32;
@@ -84,19 +82,8 @@ __global__ void __launch_bounds__(256) absorb_q_mfma_kernel(
     if (t >= T) break;
     const float* src = stage + r * kAbsLdsStride;
     const size_t obase = ((size_t)t * kAbsH + h) * kAbsRow;
-    if constexpr (OutFmt == MLA_BF16) {
-      uint16_t* dst = static_cast<uint16_t*>(q_abs) + obase;
-      for (int i = lane; i < kAbsRow; i += 64) dst[i] = (uint16_t)f32_to_bf16_bits(src[i]);
-    } else {
-      float amax = 0.f;
-      for (int i = lane; i < kAbsRow; i += 64) amax = fmaxf(amax, fabsf(src[i]));
-      amax = wave_max(amax);
-      float sc = amax / 448.0f;
-      if (!(sc > 0.0f)) sc = 1.0f;
-      uint8_t* dst = static_cast<uint8_t*>(q_abs) + obase;
-      for (int i = lane; i < kAbsRow; i += 64) dst[i] = (uint8_t)f32_to_e4m3(src[i] / sc);
-      if (lane == 0) q_scale[(size_t)t * kAbsH + h] = sc;
-    }
+    uint16_t* dst = q_abs + obase;
+    for (int i = lane; i < kAbsRow; i += 64) dst[i] = (uint16_t)f32_to_bf16_bits(src[i]);
   }
 }
 
@@ -208,20 +195,15 @@ static unsigned generic_grid(size_t total) {
 }
 
 hipError_t launch_absorb_q(const mla_config_t& cfg, const void* q_nope, const void* q_rope,
-                           const int32_t* q_pos, const void* w_uk, void* q_abs, float* q_scale, int T,
-                           hipStream_t stream) {
+                           const int32_t* q_pos, const void* w_uk, void* q_abs, int T, hipStream_t stream) {
   if (T == 0) return hipSuccess;
   if (cfg.act_dtype == MLA_BF16 && is_dsv2_shape(cfg)) {
     dim3 grid(kAbsH, (T + 31) / 32);
     auto* qn = static_cast<const uint16_t*>(q_nope);
     auto* qr = static_cast<const uint16_t*>(q_rope);
     auto* w = static_cast<const uint16_t*>(w_uk);
-    if (cfg.cache_dtype == MLA_FP8_E4M3)
-      hipLaunchKernelGGL(absorb_q_mfma_kernel<MLA_FP8_E4M3>, grid, dim3(256), 0, stream, qn, qr, q_pos, w,
-                         q_abs, q_scale, T, cfg.rope_base);
-    else
-      hipLaunchKernelGGL(absorb_q_mfma_kernel<MLA_BF16>, grid, dim3(256), 0, stream, qn, qr, q_pos, w, q_abs,
-                         q_scale, T, cfg.rope_base);
+    hipLaunchKernelGGL(absorb_q_mfma_kernel, grid, dim3(256), 0, stream, qn, qr, q_pos, w,
+                       static_cast<uint16_t*>(q_abs), T, cfg.rope_base);
     return hipGetLastError();
   }
   const size_t total = (size_t)T * cfg.num_heads * (cfg.d_c + cfg.d_r);

@@ -33,7 +33,8 @@ constexpr int kTileBytes = kBlock * kRow * 2;     // 73728
 
 struct DecodeArgs {
   const uint16_t* q_abs;      // [T, H, 576] bf16
-  const uint8_t* cache;       // [num_blocks, 64, 576] bf16
+  const uint8_t* cache;       // [num_blocks, 64, 576] bf16 (e4m3 codes for an fp8 cache)
+  const float* cache_scale;   // [num_blocks, 64] fp8 only: cached row value = code * scale
   const int32_t* block_table; // [B, max_blocks]
   const int32_t* kv_lens;     // [B]
   float* o_lat;               // [T, H, 512]
@@ -42,6 +43,7 @@ struct DecodeArgs {
   float* part_ml;             // [slots*Sq, H, 2]   (reference max m in log2 units, l)
   int num_blocks, max_blocks, B, Sq, G;
   float scale_log2;           // softmax_scale * log2(e)
+  int fp8;                    // cache and queries are e4m3 codes with scales
 };
 
 // Read-only kernel inputs are read through the constant address space: with a uniform index
@@ -237,6 +239,115 @@ __device__ __forceinline__ void o_fence(f32x16* o) {
                  : "i"(N - 1));
 }
 
+// ---- page table of the range, built once in LDS: entry k describes range page k
+//   pg     page id in the cache (out-of-range ids are treated as holding no valid token)
+//   r      tokens from the page's first row to the end of its sequence (kv_len - 64 tb)
+//   b      sequence
+//   flags  kFirst: first page of its segment in this range, kLast: last page of it
+// One thread per sequence (256 at a time) finds where its pages start in the range; each
+// sequence marks its first page, a prefix maximum over the marks gives every page its
+// sequence, and one gather per page fetches the ids.  The step loop then needs no cursor
+// walking and no scalar loads.
+// Scratch space is the start of stage 0 (not in use yet): 3 KiB of per-sequence arrays, then
+// 4 KiB of page marks.  Every thread of the workgroup calls it; n_pages <= 1024.
+__device__ void build_page_table(const DecodeArgs& a, uint8_t* smem, int4* tab, int n_pages, long long x0, int b0,
+                                 long long s_first) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  int* s_start = reinterpret_cast<int*>(smem);          // [256] stage 0 as scratch
+  int* s_len = s_start + 256;                           // [256]
+  int* s_nb = s_start + 512;                            // [256]
+  int* s_wsum = s_start + 768;                          // [4]
+  int* s_mark = s_start + 1024;                         // [kTabCap]
+  const int t = threadIdx.x;
+  long long chunk_b = b0;
+  long long rel_base = -(x0 - s_first);                 // start of sequence chunk_b in range pages
+  int k_done = 0;
+  while (true) {
+    const long long bl = chunk_b + t;
+    int L = 0;
+    const int nb = bl < a.B ? seq_tiles(a.kv_lens, (int)bl, a.max_blocks, &L) : 0;
+    // block-wide exclusive scan of nb
+    int incl = nb;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int v = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += v;
+    }
+    if (lane == 63) s_wsum[wave] = incl;
+    __syncthreads();
+    int before = 0, total = 0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const int ws = s_wsum[w];
+      before += w < wave ? ws : 0;
+      total += ws;
+    }
+    const long long start = rel_base + before + incl - nb;
+    s_start[t] = (int)(start < -(1ll << 30) ? -(1 << 30) : start);
+    s_len[t] = L;
+    s_nb[t] = nb;
+    const long long k_end_ll = rel_base + total;       // range pages covered by this chunk
+    const int k_end = (int)(k_end_ll < n_pages ? k_end_ll : n_pages);
+    for (int k = k_done + t; k < k_end; k += 256) s_mark[k] = -1;
+    __syncthreads();
+    if (nb > 0 && start >= k_done && start < k_end) s_mark[start] = t;   // sequence t starts at page start
+    __syncthreads();
+    // pages k_done .. k_end-1: sequence = last mark at or before k (page k_done may continue
+    // the sequence of the previous chunk's last page, or of chunk_b itself at the range start)
+    {
+      // parallel prefix maximum: thread t owns pages k_done + 4t .. +3 (k_end - k_done <= 1024)
+      int m4[4];
+      int run = -1;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int k = k_done + 4 * t + i;
+        const int v = k < k_end ? s_mark[k] : -1;
+        run = v > run ? v : run;
+        m4[i] = run;
+      }
+      int inc = run;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int v = __shfl_up(inc, o, 64);
+        if (lane >= o) inc = v > inc ? v : inc;
+      }
+      __syncthreads();                                   // everyone has read its marks
+      if (lane == 63) s_wsum[wave] = inc;
+      __syncthreads();
+      int prev = __shfl_up(inc, 1, 64);
+      if (lane == 0) prev = -1;
+#pragma unroll
+      for (int w = 0; w < 4; ++w)
+        if (w < wave) prev = s_wsum[w] > prev ? s_wsum[w] : prev;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int k = k_done + 4 * t + i;
+        const int r = m4[i] > prev ? m4[i] : prev;
+        if (k < k_end) s_mark[k] = r < 0 ? 0 : r;        // no mark yet: sequence chunk_b
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {                       // k_end - k_done <= 1024
+      const int k = k_done + t + 256 * i;
+      if (k < k_end) {
+        const int st = s_mark[k];
+        const int tb = k - s_start[st];
+        const int bk = (int)(chunk_b + st);
+        const int pg = a.block_table[(size_t)bk * a.max_blocks + tb];
+        const int flags = ((k == 0 || tb == 0) ? kFirst : 0) | ((k == n_pages - 1 || tb == s_nb[st] - 1) ? kLast : 0);
+        tab[k] = int4{pg, s_len[st] - kBlock * tb, bk, flags};
+      }
+    }
+    k_done = k_end;
+    __syncthreads();
+    if (k_done >= n_pages || chunk_b + 256 >= a.B) break;
+    chunk_b += 256;
+    rel_base += total;
+  }
+}
+
 // Softmax reference.  Probabilities are taken against a fixed per-segment reference m (the
 // first visible score maximum) instead of the running maximum: bf16 and fp32 keep their
 // relative precision at any magnitude, and scores below m merely underflow, which is exact to
@@ -293,113 +404,10 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_bf16_kernel(DecodeArgs a) 
   }
   if (b0 < 0) return;                             // unreachable: x0 < T_all lies in some sequence
 
-  // ---- page table of the range, built once in LDS: entry k describes range page k
-  //   pg     page id in the cache (out-of-range ids are treated as holding no valid token)
-  //   r      tokens from the page's first row to the end of its sequence (kv_len - 64 tb)
-  //   b      sequence
-  //   flags  kFirst: first page of its segment in this range, kLast: last page of it
-  // One thread per sequence (256 at a time) finds where its pages start in the range; each
-  // sequence marks its first page, a prefix maximum over the marks gives every page its
-  // sequence, and one gather per page fetches the ids.  The step loop then needs no cursor
-  // walking and no scalar loads.
   // the host sizes the ranges to fit the table; the clamp only keeps LDS accesses in bounds
   const int n_pages = (int)(x1 - x0 < kTabCap ? x1 - x0 : kTabCap);
   const int n_steps = 2 * n_pages;               // half pages of this range
-  {
-    int* s_start = reinterpret_cast<int*>(smem);          // [256] stage 0 as scratch
-    int* s_len = s_start + 256;                           // [256]
-    int* s_nb = s_start + 512;                            // [256]
-    int* s_wsum = s_start + 768;                          // [4]
-    int* s_mark = s_start + 1024;                         // [kTabCap]
-    const int t = threadIdx.x;
-    long long chunk_b = b0;
-    long long rel_base = -(x0 - s_first);                 // start of sequence chunk_b in range pages
-    int k_done = 0;
-    while (true) {
-      const long long bl = chunk_b + t;
-      int L = 0;
-      const int nb = bl < a.B ? seq_tiles(a.kv_lens, (int)bl, a.max_blocks, &L) : 0;
-      // block-wide exclusive scan of nb
-      int incl = nb;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const int v = __shfl_up(incl, o, 64);
-        if (lane >= o) incl += v;
-      }
-      if (lane == 63) s_wsum[wave] = incl;
-      __syncthreads();
-      int before = 0, total = 0;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const int ws = s_wsum[w];
-        before += w < wave ? ws : 0;
-        total += ws;
-      }
-      const long long start = rel_base + before + incl - nb;
-      s_start[t] = (int)(start < -(1ll << 30) ? -(1 << 30) : start);
-      s_len[t] = L;
-      s_nb[t] = nb;
-      const long long k_end_ll = rel_base + total;       // range pages covered by this chunk
-      const int k_end = (int)(k_end_ll < n_pages ? k_end_ll : n_pages);
-      for (int k = k_done + t; k < k_end; k += 256) s_mark[k] = -1;
-      __syncthreads();
-      if (nb > 0 && start >= k_done && start < k_end) s_mark[start] = t;   // sequence t starts at page start
-      __syncthreads();
-      // pages k_done .. k_end-1: sequence = last mark at or before k (page k_done may continue
-      // the sequence of the previous chunk's last page, or of chunk_b itself at the range start)
-      {
-        // parallel prefix maximum: thread t owns pages k_done + 4t .. +3 (k_end - k_done <= 1024)
-        int m4[4];
-        int run = -1;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int k = k_done + 4 * t + i;
-          const int v = k < k_end ? s_mark[k] : -1;
-          run = v > run ? v : run;
-          m4[i] = run;
-        }
-        int inc = run;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-          const int v = __shfl_up(inc, o, 64);
-          if (lane >= o) inc = v > inc ? v : inc;
-        }
-        __syncthreads();                                   // everyone has read its marks
-        if (lane == 63) s_wsum[wave] = inc;
-        __syncthreads();
-        int prev = __shfl_up(inc, 1, 64);
-        if (lane == 0) prev = -1;
-#pragma unroll
-        for (int w = 0; w < 4; ++w)
-          if (w < wave) prev = s_wsum[w] > prev ? s_wsum[w] : prev;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int k = k_done + 4 * t + i;
-          const int r = m4[i] > prev ? m4[i] : prev;
-          if (k < k_end) s_mark[k] = r < 0 ? 0 : r;        // no mark yet: sequence chunk_b
-        }
-      }
-      __syncthreads();
-      int4* tab = reinterpret_cast<int4*>(smem + kTabOff);
-#pragma unroll
-      for (int i = 0; i < kTabCap / 256; ++i) {
-        const int k = k_done + t + 256 * i;
-        if (k < k_end) {
-          const int st = s_mark[k];
-          const int tb = k - s_start[st];
-          const int bk = (int)(chunk_b + st);
-          const int pg = a.block_table[(size_t)bk * a.max_blocks + tb];
-          const int flags = ((k == 0 || tb == 0) ? kFirst : 0) | ((k == n_pages - 1 || tb == s_nb[st] - 1) ? kLast : 0);
-          tab[k] = int4{pg, s_len[st] - kBlock * tb, bk, flags};
-        }
-      }
-      k_done = k_end;
-      __syncthreads();
-      if (k_done >= n_pages || chunk_b + 256 >= a.B) break;
-      chunk_b += 256;
-      rel_base += total;
-    }
-  }
+  build_page_table(a, smem, reinterpret_cast<int4*>(smem + kTabOff), n_pages, x0, b0, s_first);
 
   bf16x8 qf[36];
   auto load_q = [&](int bb) {
@@ -640,46 +648,473 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_bf16_kernel(DecodeArgs a) 
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));   // no page load may land after the workgroup ends
 }
 
+// ------------------------------------------------------------------------ fp8 cache
+
+// An fp8 cache holds OCP e4m3 codes with one fp32 scale per token (value = code * scale), so
+// a page of codes is 36,864 B, the size of a bf16 half page.  The kernel below keeps the bf16
+// kernel's structure (ranges, LDS page table, four stages, one barrier per step, O in the
+// accumulation registers) with one whole page per step and the scaled fp8 matrix instruction
+// v_mfma_scale_f32_32x32x64_f8f6f4:
+//   scores  S^T[64 tok, 32 heads] = Codes[64, 576] . (Qhi + Qlo/16)^T, 2 token blocks x 9
+//           K-steps of 64 x 2 query terms: the bf16 folded query is split into two e4m3 terms
+//           per segment, so the query keeps about 8 bits; the token scale, the query scale and
+//           the softmax scale multiply the fp32 result;
+//   values  O^T[512, 32 heads] += Codes[:, :512]^T . Pt^T, one 64-token K-step per column
+//           tile.  Pt = p * token scale * 2^-e is rounded to e4m3 and the instruction's E8M0
+//           block scale of the B operand multiplies 2^e back in; e (per head and page) keeps
+//           every Pt of the page at or below 256.
+// Scaled 32x32x64 fp8 operands (measured on gfx950): lane l of A (of B) holds row (column)
+// l%32; its bytes 0..15 belong to K-block 0 and bytes 16..31 to K-block 1, and byte j of lane
+// l meets byte j of the other operand's lane with the same l/32.  The block scale of row
+// (column) r and K-block k is byte 0 of lane r + 32k's scale register.  Results use the 32x32
+// layout of the bf16 instruction.
+constexpr int kPage8 = kBlock * kRow;                // 36864: one page of codes
+constexpr int kStage8 = kPage8 + kWaves * 256;       // + one copy of the page's 64 scales per wave
+constexpr int kTabOff8 = kStages * kStage8;          // 151552
+constexpr int kTabCap8 = 512;
+constexpr int kDecodeLds8 = kTabOff8 + 16 * kTabCap8;   // 159744
+constexpr int kE8M0One = 127;                        // E8M0 code of 1.0
+
+// LDS layout of a page of codes: row r (576 B = 36 chunks of 16 B) at 576r, chunk c stored at
+// c ^ key8(r), which flips only the two low chunk bits (every chunk stays in its 64-byte group).
+//   scores  ds_read_b128 of chunks 4s + h and 4s + 2 + h (h = l/32) of row l%32 (+32): in one
+//           cycle's 16 lanes the two low row bits pick the bank quarter (the pitch is 36
+//           chunks) and key8 of the three next row bits the 16-byte slot in it;
+//   values  ds_read_b64_tr_b8: a half wave reads 8 rows x 4 eight-byte columns; key8 moves the
+//           rows that the pitch would put on the same banks to different 16-byte slots.
+__device__ __forceinline__ int key8(int r) { return 2 * (((r >> 3) ^ (r >> 4)) & 1) + (((r >> 2) ^ (r >> 4)) & 1); }
+
+// Transposing 8-bit LDS read (gfx950): output lane l, byte j = byte l%8 of the 8 bytes at the
+// address of source lane 16(l/16) + 2j + (l/8)%2 (measured).
+__device__ __forceinline__ i32x2 lds_tr8(const uint8_t* __restrict__ base, uint32_t off) {
+  const MLA_LDS uint8_t* __restrict__ lb = (const MLA_LDS uint8_t*)base;
+  return __builtin_amdgcn_ds_read_tr8_b64_v2i32((MLA_LDS i32x2*)(lb + off));
+}
+
+// O tile += A . B on fp8 operands in the accumulation registers (hazards as for mfma_acc; the
+// 16-pass instruction needs 19 wait states before its results are read, see o_fence<20>).
+__device__ __forceinline__ void mfma8_acc(f32x16& acc, const i32x8& a, const i32x8& b, int sa, int sb) {
+  asm volatile("s_nop 1\n\tv_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel_hi:[0,0,0]"
+               : "+a"(acc)
+               : "v"(a), "v"(b), "v"(sa), "v"(sb));
+}
+
+// Page loads of the fp8 kernel: each wave moves 9 KiB of codes (LDS bytes 9216w .. +9215 of the
+// stage, lane l of load i writing bytes 1024(9w + i) + 16l) and the page's 64 scales into its
+// own 256-byte copy.  Both descriptors end at the page's last valid token: rows past it are
+// out of range and the load writes zeros for them (codes and scales 0: finite, and masked).
+struct PageLoad8 {
+  __amdgpu_buffer_rsrc_t rows, scales;
+  uint8_t* stage;
+};
+__device__ __forceinline__ PageLoad8 page_load8(uint8_t* stage, const uint8_t* cache, const float* cache_scale,
+                                                int pg, int nvalid) {
+  const size_t p = (size_t)(pg < 0 ? 0 : pg);
+  const int nv = nvalid < 0 ? 0 : nvalid;
+  return PageLoad8{__builtin_amdgcn_make_buffer_rsrc((void*)(cache + p * kPage8), 0, nv * kRow, 0x00020000),
+                   __builtin_amdgcn_make_buffer_rsrc((void*)(cache_scale + p * kBlock), 0, nv * 4, 0x00020000),
+                   stage};
+}
+// source offset in the page of the 16 bytes that lane `lane` of load i (of wave `wave`) writes
+__device__ __forceinline__ int page8_src(int wave, int i, int lane) {
+  const int ch = 64 * (9 * wave + i) + lane;     // LDS chunk of the stage, 0 .. 2303
+  const int r = ch / 36, pos = ch - 36 * r;
+  return r * kRow + 16 * (pos ^ key8(r));
+}
+template <int Aux>
+__device__ __forceinline__ void load_row8(const PageLoad8& p, int i, int wave, int lane) {
+  asm volatile("" : "+v"(lane));   // rebuild the per-lane offset here rather than keep it live
+  if (i < 9) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(p.rows, (MLA_LDS void*)(p.stage + 1024 * (9 * wave + i)), 16,
+                                             page8_src(wave, i, lane), 0, 0, Aux);
+  } else {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(p.scales, (MLA_LDS void*)(p.stage + kPage8 + 256 * wave), 4, 4 * lane,
+                                             0, 0, Aux);
+  }
+}
+
+// Wave w owns heads 32w .. 32w+31 and lane l works for head 32w + l%32, as in the bf16 kernel.
+//   scores  token block tb (rows 32tb ..), K-step s: A = chunks 4s + l/32 and 4s + 2 + l/32 of
+//           row 32tb + l%32, B = the same 32 columns of the head's query terms.  Lane l ends
+//           up with its head's scores for tokens 32tb + 8(i/4) + 4(l/32) + i%4, i = 0..15.
+//   values  B byte j of lane l = Pt of that lane's own score i = j%16 of block tb = j/16, i.e.
+//           token T(l/32, j) = 32(j/16) + 8((j%16)/4) + 4(l/32) + j%4.  The A operand of
+//           column tile ct must hold Codes[T(l/32, j), 32ct + l%32] in byte j: four
+//           transposing reads (bytes 8q .. 8q+7) whose source lane σ points at token
+//           16q + 8((σ>>3)&1) + 4(σ>>5) + ((σ>>1)&3), columns 32ct + 8(2((σ>>4)&1) + (σ&1)).
+template <int Aux>
+__global__ void __launch_bounds__(256, 1) decode_mfma_fp8_kernel(DecodeArgs a) {
+  extern __shared__ __attribute__((aligned(256))) uint8_t smem[];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int hl = lane >> 5;
+  const int head = 32 * wave + (lane & 31);
+
+  const int NG = a.G * a.Sq;
+  int lid = blockIdx.x;
+  if ((NG & 7) == 0) lid = (blockIdx.x & 7) * (NG >> 3) + (blockIdx.x >> 3);
+  const int g = lid / a.Sq;
+  const int j = lid - g * a.Sq;
+
+  long long T_all, s_first;
+  int b0;
+  {
+    int db;
+    long long ds;
+    scan_batch(a.kv_lens, a.B, a.max_blocks, -1, &T_all, &db, &ds);
+  }
+  const long long x0 = (long long)g * T_all / a.G;
+  const long long x1 = (long long)(g + 1) * T_all / a.G;
+  if (x0 >= x1) return;
+  {
+    long long tot;
+    scan_batch(a.kv_lens, a.B, a.max_blocks, x0, &tot, &b0, &s_first);
+  }
+  if (b0 < 0) return;
+  const int n_steps = (int)(x1 - x0 < kTabCap8 ? x1 - x0 : kTabCap8);   // pages of this range
+  build_page_table(a, smem, reinterpret_cast<int4*>(smem + kTabOff8), n_steps, x0, b0, s_first);
+
+  // The folded query (bf16) becomes two e4m3 operands per K-step: with s = amax/448 over the
+  // head's 576 values and x = q/s, hi = e4m3(x) and lo = e4m3(16 (x - hi)), so that
+  // q = s (hi + lo/16) to about 2^-8 relative.  The lo products enter the same accumulator
+  // with the B block scale 2^-4.  Lane l holds, for K-step k, the values 64k + 16(l/32) + 0..15
+  // (bytes 0..15) and 64k + 32 + 16(l/32) + 0..15 (bytes 16..31) of its head.
+  i32x8 qhi[9], qlo[9];
+  float kq = 0.f;   // s * softmax scale * log2(e) of this lane's head
+  auto load_q = [&](int bb) {
+    const size_t row = (size_t)(bb * a.Sq + j) * kH + head;
+    const uint16_t* qp = a.q_abs + row * kRow + 16 * hl;
+    auto qword = [&](int k, int v) {   // values 64k + 32(v/2) + 16hl + 8(v%2) .. +7
+      return *reinterpret_cast<const u32x4*>(qp + 64 * k + 32 * (v >> 1) + 8 * (v & 1));
+    };
+    // two passes over the (cached) query: its maximum first, then the split, one K-step at a
+    // time so that only one step's raw values are live next to the finished terms
+    float amax = 0.f;
+#pragma unroll
+    for (int k = 0; k < 9; ++k)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const u32x4 r = qword(k, v);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          amax = fmaxf(amax, fmaxf(fabsf(bf16_bits_to_f32(r[e] & 0xFFFFu)), fabsf(bf16_bits_to_f32(r[e] >> 16))));
+      }
+    amax = pair_max(amax);
+    const float inv = amax > 0.f ? 448.0f / amax : 1.0f;
+    kq = (amax > 0.f ? amax / 448.0f : 1.0f) * a.scale_log2;
+#pragma unroll
+    for (int k = 0; k < 9; ++k) {
+      __builtin_amdgcn_sched_barrier(0);
+      const u32x4 raw[4] = {qword(k, 0), qword(k, 1), qword(k, 2), qword(k, 3)};
+      int hw[8], lw[8];
+#pragma unroll
+      for (int d = 0; d < 8; ++d) {   // dword d: values 4d .. 4d+3 of the 32
+        const u32x4& r = raw[d >> 1];
+        const uint32_t w0 = r[2 * (d & 1)], w1 = r[2 * (d & 1) + 1];
+        const float x0 = bf16_bits_to_f32(w0 & 0xFFFFu) * inv, x1 = bf16_bits_to_f32(w0 >> 16) * inv;
+        const float x2 = bf16_bits_to_f32(w1 & 0xFFFFu) * inv, x3 = bf16_bits_to_f32(w1 >> 16) * inv;
+        int h = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, 0, false);
+        h = __builtin_amdgcn_cvt_pk_fp8_f32(x2, x3, h, true);
+        const auto h01 = __builtin_amdgcn_cvt_pk_f32_fp8(h, false), h23 = __builtin_amdgcn_cvt_pk_f32_fp8(h, true);
+        int l = __builtin_amdgcn_cvt_pk_fp8_f32((x0 - h01[0]) * 16.0f, (x1 - h01[1]) * 16.0f, 0, false);
+        l = __builtin_amdgcn_cvt_pk_fp8_f32((x2 - h23[0]) * 16.0f, (x3 - h23[1]) * 16.0f, l, true);
+        hw[d] = h;
+        lw[d] = l;
+      }
+      qhi[k] = i32x8{hw[0], hw[1], hw[2], hw[3], hw[4], hw[5], hw[6], hw[7]};
+      qlo[k] = i32x8{lw[0], lw[1], lw[2], lw[3], lw[4], lw[5], lw[6], lw[7]};
+    }
+  };
+  auto slot_o = [&](int bb) -> float* {
+    return a.part_o + ((size_t)(g + bb) * a.Sq + j) * (kH * kDC) + (size_t)wave * (32 * kDC) + 4 * lane;
+  };
+
+  f32x16 oacc[16];
+  const bf16x8 zero8 = {};
+#pragma unroll
+  for (int t = 0; t < 16; ++t) mfma_zero(oacc[t], zero8);
+  float m_ref = -INFINITY, l_run = 0.f;
+  bool over = false;
+  const int one = kE8M0One;
+
+  // ---- raw S^T of the page in `tile`: per K-step, the hi and the lo query terms of both token
+  // blocks (36 MFMAs; the accumulators alternate)
+  const int lo_scale = kE8M0One - 4;   // 2^-4
+  auto scores = [&](const uint8_t* tile, auto hook, f32x16& s0, f32x16& s1) {
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int rr = ln & 31, hh = ln >> 5, key = key8(rr);
+    const uint32_t T = lds_addr(tile);
+    const uint32_t a0 = T + (uint32_t)(rr * kRow + 16 * (hh ^ key));
+    const uint32_t a1 = T + (uint32_t)(rr * kRow + 16 * ((2 + hh) ^ key));
+    auto kfrag = [&](int f) -> i32x8 {   // K-step f/2, token block f%2
+      const uint32_t o = 64u * (f >> 1) + (uint32_t)(32 * kRow) * (f & 1);
+      const u32x4 lo = lds_b128(a0 + o), hi = lds_b128(a1 + o);
+      return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+    };
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      s0[i] = 0.f;
+      s1[i] = 0.f;
+    }
+    // fragment f = (K-step f/2, token block f%2) feeds two consecutive MFMAs (hi, lo); the next
+    // two fragments are read ahead
+    constexpr int D = 2;
+    i32x8 kr[D + 1];
+#pragma unroll
+    for (int d = 0; d < D; ++d) kr[d] = kfrag(d);
+#pragma unroll
+    for (int f = 0; f < 18; ++f) {
+      if (f + D < 18) kr[(f + D) % (D + 1)] = kfrag(f + D);
+      const int k = f >> 1;
+      f32x16& acc = (f & 1) ? s1 : s0;
+      __builtin_amdgcn_sched_barrier(0);
+      acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kr[f % (D + 1)], qhi[k], acc, 0, 0, 0, one, 0, one);
+      hook(2 * f);
+      __builtin_amdgcn_sched_barrier(0);
+      acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kr[f % (D + 1)], qlo[k], acc, 0, 0, 0, one, 0, lo_scale);
+      hook(2 * f + 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // ---- softmax of one page: raw scores -> e4m3 Pt and the B block scale, against the segment
+  // reference (log2 units).  y = raw * token scale; log2-domain score = kq * y.
+  struct Soft {
+    float m_new, l_new;
+    bool over_new;
+    i32x8 p;
+    int sb;
+  };
+  auto softmax = [&](f32x16& s0, f32x16& s1, const uint8_t* tile, int vis, bool fresh, Soft& st) {
+    const uint32_t sbase = lds_addr(tile) + kPage8 + 256 * wave + 16 * hl;
+    // scales of tokens 32tb + 8u + 4hl + 0..3 (block d = 4tb + u); read where they are used
+    auto scales = [&](int d) { return __builtin_bit_cast(f32x4, lds_b128(sbase + 128 * (d >> 2) + 32 * (d & 3))); };
+    float cm = 0.f;
+#pragma unroll
+    for (int d = 0; d < 8; ++d) {
+      const f32x4 c4 = scales(d);
+      f32x16& sv = (d < 4) ? s0 : s1;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        sv[4 * (d & 3) + k] *= c4[k];
+        cm = fmaxf(cm, c4[k]);
+      }
+    }
+    if (vis < kBlock - 1) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int t = 8 * (i >> 2) + 4 * hl + (i & 3);
+        if (t > vis) s0[i] = -INFINITY;
+        if (t + 32 > vis) s1[i] = -INFINITY;
+      }
+    }
+    float mx = fmaxf(s0[0], s1[0]);
+#pragma unroll
+    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, fmaxf(s0[i], s1[i]));
+    const float tmax = pair_max(mx) * kq;
+    cm = pair_max(cm);
+    const float m_in = fresh ? -INFINITY : m_ref;
+    st.m_new = (m_in == -INFINITY) ? tmax : m_in;
+    st.over_new = (fresh ? false : over) || (tmax > st.m_new + kRescaleLog2);
+    const float m_use = (st.m_new == -INFINITY) ? 0.0f : st.m_new;
+    // largest Pt of the page <= 2^(tmax - m) * max scale < 2^frexp_exp(...): shift it to <= 256
+    int e = __builtin_amdgcn_frexp_expf(__builtin_amdgcn_exp2f(tmax - m_use) * cm) - 8;
+    e = e < -120 ? -120 : (e > 120 ? 120 : e);
+    const float neg = -(m_use + (float)e);
+    float lsum = 0.f;
+    int pk[8];
+#pragma unroll
+    for (int d = 0; d < 8; ++d) {
+      const f32x16& sv = (d < 4) ? s0 : s1;
+      const f32x4 c4 = scales(d);
+      float u[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        u[k] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[4 * (d & 3) + k], kq, neg));
+        lsum += u[k];
+      }
+      int w = __builtin_amdgcn_cvt_pk_fp8_f32(u[0] * c4[0], u[1] * c4[1], 0, false);
+      pk[d] = __builtin_amdgcn_cvt_pk_fp8_f32(u[2] * c4[2], u[3] * c4[3], w, true);
+    }
+    st.l_new = (fresh ? 0.0f : l_run) + __builtin_ldexpf(lsum, e);
+    st.p = i32x8{pk[0], pk[1], pk[2], pk[3], pk[4], pk[5], pk[6], pk[7]};
+    st.sb = e + kE8M0One;
+  };
+
+  // ---- O^T += Codes^T . Pt^T for the page in `tile`
+  auto values = [&](const uint8_t* tile, const i32x8& pf, int sb) {
+    o_fence<3>(oacc);
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int rl = 8 * ((ln >> 3) & 1) + 4 * (ln >> 5) + ((ln >> 1) & 3);
+    const int h4 = (ln >> 4) & 1;
+    const uint32_t T = (uint32_t)(tile - smem);
+    const uint8_t* xv[4];   // [2 * (q & 1) + (ct & 1)]
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = 16 * (e >> 1) + rl;
+      xv[e] = smem + T + (uint32_t)(r * kRow + 16 * ((2 * (e & 1) + h4) ^ key8(r)) + 8 * (ln & 1));
+    }
+    auto vfrag = [&](int ct) -> i32x8 {
+      const uint32_t o = 64u * (ct >> 1);
+      const i32x2 t0 = lds_tr8(xv[ct & 1], o);
+      const i32x2 t1 = lds_tr8(xv[2 + (ct & 1)], o);
+      const i32x2 t2 = lds_tr8(xv[ct & 1], o + 32 * kRow);
+      const i32x2 t3 = lds_tr8(xv[2 + (ct & 1)], o + 32 * kRow);
+      return i32x8{t0[0], t0[1], t1[0], t1[1], t2[0], t2[1], t3[0], t3[1]};
+    };
+    constexpr int D = 2;
+    i32x8 vr[D + 1];
+#pragma unroll
+    for (int d = 0; d < D; ++d) vr[d] = vfrag(d);
+#pragma unroll
+    for (int ct = 0; ct < 16; ++ct) {
+      if (ct + D < 16) vr[(ct + D) % (D + 1)] = vfrag(ct + D);
+      __builtin_amdgcn_sched_barrier(0);
+      mfma8_acc(oacc[ct], vr[ct % (D + 1)], pf, one, sb);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    o_fence<20>(oacc);
+  };
+
+  i32x8 pf;
+  int psb = kE8M0One;
+  Soft sm;
+  auto soft_commit = [&](const Soft& st) {
+    m_ref = st.m_new;
+    l_run = st.l_new;
+    over = st.over_new;
+    pf = st.p;
+    psb = st.sb;
+  };
+  auto load_for = [&](int stage, int pg, int nv) {
+    return page_load8(smem + stage * kStage8, a.cache, a.cache_scale, nv > 0 ? pg : 0, nv);
+  };
+  auto issue = [&](const PageLoad8& pl) {
+#pragma unroll
+    for (int i = 0; i < 10; ++i) load_row8<Aux>(pl, i, wave, lane);
+  };
+  const uint32_t tab_addr = lds_addr(smem + kTabOff8);
+  auto entry = [&](int z) -> int4 {
+    if (z >= n_steps) return int4{-1, 0, 0, 0};
+    const u32x4 e = lds_b128(tab_addr + 16u * (uint32_t)z);
+    return int4{uni((int)e[0]), uni((int)e[1]), uni((int)e[2]), uni((int)e[3])};
+  };
+  auto valid_page = [&](const int4& e) { return e.x >= 0 && e.x < a.num_blocks; };
+  auto nvalid = [&](const int4& e) { return valid_page(e) ? (e.y < kBlock ? e.y : kBlock) : 0; };
+  auto last_visible = [&](const int4& e) {
+    const int v = e.y - a.Sq + j;
+    return valid_page(e) ? (v < kBlock - 1 ? v : kBlock - 1) : -1;
+  };
+
+  int4 e0 = entry(0), e1 = entry(1), e2 = entry(2), e3;
+  load_q(e0.z);
+  issue(load_for(0, e0.x, nvalid(e0)));
+  issue(load_for(1, e1.x, nvalid(e1)));
+  issue(load_for(2, e2.x, nvalid(e2)));
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+  lds_barrier();
+  {
+    f32x16 s0, s1;
+    scores(smem, [](int) {}, s0, s1);
+    softmax(s0, s1, smem, last_visible(e0), true, sm);
+    soft_commit(sm);
+  }
+
+  for (int y = 0; y < n_steps; ++y) {
+    const bool has_next = y + 1 < n_steps;
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(10));   // page y+1 landed (page y+2 may be in flight)
+    lds_barrier();                                 // stage (y+3)%4 is no longer read by anyone
+    e3 = entry(y + 3);
+    const PageLoad8 pl = load_for((y + 3) & 3, e3.x, nvalid(e3));
+    const bool seg_end = (e0.w & kLast) || !has_next;
+    if (seg_end && has_next) {
+      load_q(e1.z);
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    }
+    const uint8_t* next = smem + ((y + 1) & 3) * kStage8;
+    f32x16 s0, s1;
+    scores(next, [&](int st) {   // stale data if !has_next
+      if ((st & 3) == 0) load_row8<Aux>(pl, st >> 2, wave, lane);   // st = 0, 4, .., 32
+      if (st == 34) load_row8<Aux>(pl, 9, wave, lane);
+    }, s0, s1);
+    const float m_old = m_ref, l_old = l_run;
+    const bool over_old = over;
+    softmax(s0, s1, next, last_visible(e1), seg_end, sm);
+    values(smem + (y & 3) * kStage8, pf, psb);
+
+    if (seg_end) {
+      const float l_tot = pair_sum(l_old);
+      const size_t row = ((size_t)(g + e0.z) * a.Sq + j) * kH + head;
+      if (hl == 0) reinterpret_cast<float2*>(a.part_ml)[row] = float2{m_old, over_old ? -1.0f : l_tot};
+      float* so = slot_o(e0.z);
+#pragma unroll
+      for (int ct = 0; ct < 16; ++ct)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+          *reinterpret_cast<f32x4*>(so + 256 * (4 * ct + q4)) =
+              f32x4{oacc[ct][4 * q4], oacc[ct][4 * q4 + 1], oacc[ct][4 * q4 + 2], oacc[ct][4 * q4 + 3]};
+      if (has_next) {
+#pragma unroll
+        for (int t = 0; t < 16; ++t) mfma_zero(oacc[t], zero8);
+      }
+    }
+    soft_commit(sm);
+    e0 = e1;
+    e1 = e2;
+    e2 = e3;
+  }
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+}
+
 // ------------------------------------------------------------------------ LSE combine
 
 // Exact attention of one (query row, head) by one wave, two passes over the visible tokens in
 // fp32 (scores in the exp2 domain).  Used by the combine for heads whose fast-path segments
 // were marked (a score far above the segment's reference); slow, but right for any input.
+// Lane l handles columns 9l .. 9l+8 of the score and 8l .. 8l+7 of the output.
 __device__ void exact_head(const DecodeArgs& a, int b, int j, int h, int L, float* out) {
   const int lane = threadIdx.x & 63;
   const int row = b * a.Sq + j;
   const int last = L - a.Sq + j;                     // last visible position
   const int n = last + 1 < L ? last + 1 : L;
-  const uint16_t* qp = a.q_abs + ((size_t)row * kH + h) * kRow + 9 * lane;   // 9 of 576 columns
+  const size_t qrow = (size_t)row * kH + h;
   float qv[9];
 #pragma unroll
-  for (int i = 0; i < 9; ++i) qv[i] = bf16_bits_to_f32(qp[i]);
-  auto rowptr = [&](int t) -> const uint16_t* {
+  for (int i = 0; i < 9; ++i) qv[i] = bf16_bits_to_f32(a.q_abs[qrow * kRow + 9 * lane + i]);
+  // cache slot of token t, or -1 when its page id is out of range
+  auto slot = [&](int t) -> long long {
     const int pg = a.block_table[(size_t)b * a.max_blocks + t / kBlock];
-    if (pg < 0 || pg >= a.num_blocks) return nullptr;
-    return reinterpret_cast<const uint16_t*>(a.cache) + ((size_t)pg * kBlock + t % kBlock) * kRow;
+    if (pg < 0 || pg >= a.num_blocks) return -1;
+    return (long long)pg * kBlock + t % kBlock;
   };
-  auto score = [&](const uint16_t* r) {
+  auto elem = [&](long long sl, int c) -> float {
+    return a.fp8 ? e4m3_to_f32(a.cache[sl * kRow + c]) : bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(a.cache)[sl * kRow + c]);
+  };
+  auto score = [&](long long sl) {
     float d = 0.f;
 #pragma unroll
-    for (int i = 0; i < 9; ++i) d += qv[i] * bf16_bits_to_f32(r[9 * lane + i]);
-    return wave_sum(d) * a.scale_log2;
+    for (int i = 0; i < 9; ++i) d += qv[i] * elem(sl, 9 * lane + i);
+    const float cs = a.fp8 ? a.cache_scale[sl] : 1.0f;
+    return wave_sum(d) * cs * a.scale_log2;
   };
   float mx = -INFINITY;
   for (int t = 0; t < n; ++t) {
-    const uint16_t* r = rowptr(t);
-    if (r) mx = fmaxf(mx, score(r));
+    const long long sl = slot(t);
+    if (sl >= 0) mx = fmaxf(mx, score(sl));
   }
   float l = 0.f;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   if (mx != -INFINITY) {
     for (int t = 0; t < n; ++t) {
-      const uint16_t* r = rowptr(t);
-      if (!r) continue;
-      const float w = __builtin_amdgcn_exp2f(score(r) - mx);
+      const long long sl = slot(t);
+      if (sl < 0) continue;
+      const float w = __builtin_amdgcn_exp2f(score(sl) - mx);
       l += w;
+      const float wc = a.fp8 ? w * a.cache_scale[sl] : w;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] += w * bf16_bits_to_f32(r[8 * lane + i]);
+      for (int i = 0; i < 8; ++i) acc[i] += wc * elem(sl, 8 * lane + i);
     }
   }
   const float inv = l > 0.f ? 1.0f / l : 0.0f;
@@ -864,13 +1299,14 @@ bool is_dsv2_shape(const mla_config_t& c);
 
 // Token ranges of the split: one workgroup per (range, query) and one workgroup per compute
 // unit (each holds all 160 KiB of LDS), so G = CUs / Sq, capped by the number of pages, and
-// raised where needed so that no range exceeds the LDS page table (kTabCap pages: the pages
-// of the batch are at most B * max_blocks).
-int decode_num_ranges(int num_cus, int B, int Sq, int max_blocks) {
+// raised where needed so that no range exceeds the LDS page table (kTabCap pages for bf16,
+// kTabCap8 for fp8: the pages of the batch are at most B * max_blocks).
+int decode_num_ranges(int num_cus, int B, int Sq, int max_blocks, bool fp8) {
   const long long cap = (long long)B * max_blocks;
+  const int tab = fp8 ? kTabCap8 : kTabCap;
   long long G = num_cus / (Sq > 0 ? Sq : 1);
   if (G < 1) G = 1;
-  const long long need = (cap + kTabCap - 1) / kTabCap;
+  const long long need = (cap + tab - 1) / tab;
   if (G < need) G = need;
   if (cap < G) G = cap < 1 ? 1 : cap;
   return (int)G;
@@ -878,28 +1314,29 @@ int decode_num_ranges(int num_cus, int B, int Sq, int max_blocks) {
 
 size_t decode_workspace_bytes(const mla_config_t& cfg, int num_cus, int B, int Sq, int max_blocks) {
   if (!(cfg.cache_dtype != MLA_F32 && is_dsv2_shape(cfg))) return 256;   // generic path: none needed
-  const int G = decode_num_ranges(num_cus, B, Sq, max_blocks);
+  const int G = decode_num_ranges(num_cus, B, Sq, max_blocks, cfg.cache_dtype == MLA_FP8_E4M3);
   const size_t slots = (size_t)(G + B - 1) * Sq;
   const size_t o_bytes = slots * kH * kDC * sizeof(float);
   const size_t l_bytes = slots * kH * 2 * sizeof(float);
   return ((o_bytes + 255) & ~(size_t)255) + ((l_bytes + 255) & ~(size_t)255);
 }
 
-hipError_t launch_decode(const mla_config_t& cfg, int num_cus, const void* q_abs, const float* q_scale,
-                         const void* cache, const float* cache_scale, int num_blocks, const int32_t* block_table,
+hipError_t launch_decode(const mla_config_t& cfg, int num_cus, const void* q_abs, const void* cache, const float* cache_scale, int num_blocks, const int32_t* block_table,
                          int max_blocks, const int32_t* kv_lens, int B, int Sq, void* workspace, float* o_lat,
                          float* lse, hipStream_t stream, int phases) {
   if (B == 0) return hipSuccess;
   const float scale = cfg.softmax_scale;
-  if (cfg.cache_dtype == MLA_BF16 && is_dsv2_shape(cfg)) {
+  const bool fp8 = cfg.cache_dtype == MLA_FP8_E4M3;
+  if ((cfg.cache_dtype == MLA_BF16 || fp8) && is_dsv2_shape(cfg)) {
     DecodeArgs a;
     a.q_abs = static_cast<const uint16_t*>(q_abs);
     a.cache = static_cast<const uint8_t*>(cache);
+    a.cache_scale = cache_scale;
     a.block_table = block_table;
     a.kv_lens = kv_lens;
     a.o_lat = o_lat;
     a.lse = lse;
-    const int G = decode_num_ranges(num_cus, B, Sq, max_blocks);
+    const int G = decode_num_ranges(num_cus, B, Sq, max_blocks, fp8);
     const size_t slots = (size_t)(G + B - 1) * Sq;
     a.part_o = static_cast<float*>(workspace);
     a.part_ml = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) +
@@ -910,22 +1347,32 @@ hipError_t launch_decode(const mla_config_t& cfg, int num_cus, const void* q_abs
     a.Sq = Sq;
     a.G = G;
     a.scale_log2 = scale * 1.4426950408889634f;
+    a.fp8 = fp8 ? 1 : 0;
     static bool attr_set = false;   // idempotent; races only repeat the same call
     if (!attr_set) {
-      hipError_t e = hipFuncSetAttribute((const void*)decode_mfma_bf16_kernel<0>,
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, kDecodeLds);
-      if (e == hipSuccess)
-        e = hipFuncSetAttribute((const void*)decode_mfma_bf16_kernel<2>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                kDecodeLds);
-      if (e != hipSuccess) return e;
+      const void* kernels[4] = {(const void*)decode_mfma_bf16_kernel<0>, (const void*)decode_mfma_bf16_kernel<2>,
+                                (const void*)decode_mfma_fp8_kernel<0>, (const void*)decode_mfma_fp8_kernel<2>};
+      for (int k = 0; k < 4; ++k) {
+        hipError_t e = hipFuncSetAttribute(kernels[k], hipFuncAttributeMaxDynamicSharedMemorySize,
+                                           k < 2 ? kDecodeLds : kDecodeLds8);
+        if (e != hipSuccess) return e;
+      }
       attr_set = true;
     }
     if (phases & 1) {
       // non-temporal page loads when no other workgroup reads the same pages (one query)
-      if (Sq == 1)
-        hipLaunchKernelGGL(decode_mfma_bf16_kernel<2>, dim3(G * Sq), dim3(64 * kWaves), kDecodeLds, stream, a);
-      else
-        hipLaunchKernelGGL(decode_mfma_bf16_kernel<0>, dim3(G * Sq), dim3(64 * kWaves), kDecodeLds, stream, a);
+      const dim3 grid(G * Sq), block(64 * kWaves);
+      if (fp8) {
+        if (Sq == 1)
+          hipLaunchKernelGGL(decode_mfma_fp8_kernel<2>, grid, block, kDecodeLds8, stream, a);
+        else
+          hipLaunchKernelGGL(decode_mfma_fp8_kernel<0>, grid, block, kDecodeLds8, stream, a);
+      } else {
+        if (Sq == 1)
+          hipLaunchKernelGGL(decode_mfma_bf16_kernel<2>, grid, block, kDecodeLds, stream, a);
+        else
+          hipLaunchKernelGGL(decode_mfma_bf16_kernel<0>, grid, block, kDecodeLds, stream, a);
+      }
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
     }

@@ -12,10 +12,10 @@
 namespace mla {
 hipError_t launch_append(const mla_config_t&, void*, float*, int, const void*, const void*, const int32_t*,
                          const int32_t*, const int32_t*, int, int, int, hipStream_t);
-hipError_t launch_absorb_q(const mla_config_t&, const void*, const void*, const int32_t*, const void*, void*,
-                           float*, int, hipStream_t);
+hipError_t launch_absorb_q(const mla_config_t&, const void*, const void*, const int32_t*, const void*, void*, int,
+                           hipStream_t);
 hipError_t launch_out_proj(const mla_config_t&, const float*, const void*, void*, int, hipStream_t);
-hipError_t launch_decode(const mla_config_t&, int, const void*, const float*, const void*, const float*, int,
+hipError_t launch_decode(const mla_config_t&, int, const void*, const void*, const float*, int,
                          const int32_t*, int, const int32_t*, int, int, void*, float*, float*, hipStream_t,
                          int phases);
 size_t decode_workspace_bytes(const mla_config_t&, int, int, int, int);
@@ -68,7 +68,7 @@ mla_status_t from_hip(hipError_t e) { return e == hipSuccess ? MLA_OK : MLA_ERR_
 
 extern "C" {
 
-int32_t mla_abi_version(void) { return 1; }
+int32_t mla_abi_version(void) { return 2; }
 
 const char* mla_status_string(mla_status_t s) {
   switch (s) {
@@ -99,16 +99,14 @@ mla_status_t mla_cache_append(const mla_config_t* cfg, void* cache, float* cache
 }
 
 mla_status_t mla_absorb_q(const mla_config_t* cfg, const void* q_nope, const void* q_rope, const int32_t* q_pos,
-                          const void* w_uk, void* q_abs, float* q_scale, int32_t T, void* stream) {
+                          const void* w_uk, void* q_abs, int32_t T, void* stream) {
   mla_status_t st = check_cfg(cfg);
   if (st != MLA_OK) return st;
   if (T < 0) return MLA_ERR_INVALID_ARG;
   if (T == 0) return MLA_OK;
   if (!q_nope || !q_rope || !q_pos || !w_uk || !q_abs) return MLA_ERR_INVALID_ARG;
   if (!aligned16(q_nope) || !aligned16(q_rope) || !aligned16(w_uk) || !aligned16(q_abs)) return MLA_ERR_INVALID_ARG;
-  const bool fp8 = cfg->cache_dtype == MLA_FP8_E4M3;
-  if (fp8 != (q_scale != nullptr)) return MLA_ERR_INVALID_ARG;
-  return from_hip(mla::launch_absorb_q(*cfg, q_nope, q_rope, q_pos, w_uk, q_abs, q_scale, T,
+  return from_hip(mla::launch_absorb_q(*cfg, q_nope, q_rope, q_pos, w_uk, q_abs, T,
                                        static_cast<hipStream_t>(stream)));
 }
 
@@ -117,8 +115,7 @@ size_t mla_decode_workspace_size(const mla_config_t* cfg, int32_t B, int32_t Sq,
   return mla::decode_workspace_bytes(*cfg, current_cu_count(), B, Sq, max_blocks);
 }
 
-static mla_status_t decode_common(const mla_config_t* cfg, const void* q_abs, const float* q_scale,
-                                  const void* cache, const float* cache_scale, int32_t num_blocks,
+static mla_status_t decode_common(const mla_config_t* cfg, const void* q_abs, const void* cache, const float* cache_scale, int32_t num_blocks,
                                   const int32_t* block_table, int32_t max_blocks, const int32_t* kv_lens, int32_t B,
                                   int32_t Sq, void* workspace, size_t ws_bytes, float* o_lat, float* lse,
                                   void* stream, int phases) {
@@ -130,37 +127,36 @@ static mla_status_t decode_common(const mla_config_t* cfg, const void* q_abs, co
   if (!q_abs || !cache || !block_table || !kv_lens || !o_lat || !lse) return MLA_ERR_INVALID_ARG;
   if (!aligned16(q_abs) || !aligned16(cache) || !aligned16(o_lat)) return MLA_ERR_INVALID_ARG;
   const bool fp8 = cfg->cache_dtype == MLA_FP8_E4M3;
-  if (fp8 != (cache_scale != nullptr) || fp8 != (q_scale != nullptr)) return MLA_ERR_INVALID_ARG;
+  if (fp8 != (cache_scale != nullptr)) return MLA_ERR_INVALID_ARG;
   const int cus = current_cu_count();
   const size_t need = mla::decode_workspace_bytes(*cfg, cus, B, Sq, max_blocks);
   if (!workspace || ws_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 255u)) return MLA_ERR_WORKSPACE;
-  if (fp8) return MLA_ERR_UNSUPPORTED;
-  return from_hip(mla::launch_decode(*cfg, cus, q_abs, q_scale, cache, cache_scale, num_blocks, block_table,
+  return from_hip(mla::launch_decode(*cfg, cus, q_abs, cache, cache_scale, num_blocks, block_table,
                                      max_blocks, kv_lens, B, Sq, workspace, o_lat, lse,
                                      static_cast<hipStream_t>(stream), phases));
 }
 
-mla_status_t mla_decode_attn(const mla_config_t* cfg, const void* q_abs, const float* q_scale, const void* cache,
+mla_status_t mla_decode_attn(const mla_config_t* cfg, const void* q_abs, const void* cache,
                              const float* cache_scale, int32_t num_blocks, const int32_t* block_table,
                              int32_t max_blocks, const int32_t* kv_lens, int32_t B, int32_t Sq, void* workspace,
                              size_t ws_bytes, float* o_lat, float* lse, void* stream) {
-  return decode_common(cfg, q_abs, q_scale, cache, cache_scale, num_blocks, block_table, max_blocks, kv_lens, B, Sq,
+  return decode_common(cfg, q_abs, cache, cache_scale, num_blocks, block_table, max_blocks, kv_lens, B, Sq,
                        workspace, ws_bytes, o_lat, lse, stream, 3);
 }
 
-mla_status_t mla_decode_split(const mla_config_t* cfg, const void* q_abs, const float* q_scale, const void* cache,
+mla_status_t mla_decode_split(const mla_config_t* cfg, const void* q_abs, const void* cache,
                               const float* cache_scale, int32_t num_blocks, const int32_t* block_table,
                               int32_t max_blocks, const int32_t* kv_lens, int32_t B, int32_t Sq, void* workspace,
                               size_t ws_bytes, float* o_lat, float* lse, void* stream) {
-  return decode_common(cfg, q_abs, q_scale, cache, cache_scale, num_blocks, block_table, max_blocks, kv_lens, B, Sq,
+  return decode_common(cfg, q_abs, cache, cache_scale, num_blocks, block_table, max_blocks, kv_lens, B, Sq,
                        workspace, ws_bytes, o_lat, lse, stream, 1);
 }
 
-mla_status_t mla_decode_combine(const mla_config_t* cfg, const void* q_abs, const float* q_scale, const void* cache,
+mla_status_t mla_decode_combine(const mla_config_t* cfg, const void* q_abs, const void* cache,
                                 const float* cache_scale, int32_t num_blocks, const int32_t* block_table,
                                 int32_t max_blocks, const int32_t* kv_lens, int32_t B, int32_t Sq, void* workspace,
                                 size_t ws_bytes, float* o_lat, float* lse, void* stream) {
-  return decode_common(cfg, q_abs, q_scale, cache, cache_scale, num_blocks, block_table, max_blocks, kv_lens, B, Sq,
+  return decode_common(cfg, q_abs, cache, cache_scale, num_blocks, block_table, max_blocks, kv_lens, B, Sq,
                        workspace, ws_bytes, o_lat, lse, stream, 2);
 }
 

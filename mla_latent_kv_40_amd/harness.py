@@ -78,12 +78,7 @@ class DecodeState:
         self.q_rope = dev(np.concatenate(qr).reshape(self.T, H, w.d_r))
 
         # outputs and scratch
-        if w.dtype == "fp8":
-            self.q_abs = torch.empty((self.T, H, w.row), dtype=torch.uint8, device=device)
-            self.q_scale = torch.empty((self.T, H), dtype=torch.float32, device=device)
-        else:
-            self.q_abs = torch.empty((self.T, H, w.row), dtype=act, device=device)
-            self.q_scale = None
+        self.q_abs = torch.empty((self.T, H, w.row), dtype=act, device=device)
         self.o_lat = torch.empty((self.T, H, w.d_c), dtype=torch.float32, device=device)
         self.lse = torch.empty((self.T, H), dtype=torch.float32, device=device)
         self.out = torch.empty((self.T, H, w.d_v), dtype=act, device=device)
@@ -113,16 +108,15 @@ class DecodeState:
                            self.block_table, self.w.batch, self.batch.max_blocks, n, stream)
 
     def absorb(self, stream=None) -> None:
-        B.mla_absorb_q(self.cfg, self.q_nope, self.q_rope, self.new_pos, self.w_uk, self.q_abs, self.q_scale,
-                       self.T, stream)
+        B.mla_absorb_q(self.cfg, self.q_nope, self.q_rope, self.new_pos, self.w_uk, self.q_abs, self.T, stream)
 
     def decode(self, stream=None) -> None:
-        B.mla_decode_attn(self.cfg, self.q_abs, self.q_scale, self.cache, self.cache_scale, self.batch.num_blocks,
+        B.mla_decode_attn(self.cfg, self.q_abs, self.cache, self.cache_scale, self.batch.num_blocks,
                           self.block_table, self.batch.max_blocks, self.kv_lens, self.w.batch, self.w.sq,
                           self.workspace, self.ws_bytes, self.o_lat, self.lse, stream)
 
     def _dargs(self):
-        return (self.cfg, self.q_abs, self.q_scale, self.cache, self.cache_scale, self.batch.num_blocks,
+        return (self.cfg, self.q_abs, self.cache, self.cache_scale, self.batch.num_blocks,
                 self.block_table, self.batch.max_blocks, self.kv_lens, self.w.batch, self.w.sq, self.workspace,
                 self.ws_bytes, self.o_lat, self.lse)
 

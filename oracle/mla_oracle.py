@@ -261,13 +261,17 @@ def quantize_rows_fp8(rows: np.ndarray):
     """Per-token fp8 storage: scale = amax(row)/448 (1.0 for an all-zero row), codes = e4m3(row/scale).
 
     Returns (codes as float64 values, scales float32) so that row ~= codes * scale.
-    The scale is a float32 quantity because it is stored as float32.
+    The stored scale is a float32 quantity, and the code of each value is decided in that
+    precision: the row is taken in fp32 (a bf16 latent exactly, a rotated positional key
+    rounded once), the scale is fp32(amax) / 448 in fp32 and the quotient value / scale is
+    an fp32 division, which e4m3_round then rounds exactly to the nearest code.
     """
-    rows = np.asarray(rows, dtype=np.float64)
+    rows = np.asarray(rows, dtype=np.float64).astype(np.float32)
     amax = np.abs(rows).max(axis=-1)
-    scale = (amax.astype(np.float32) / np.float32(E4M3_MAX)).astype(np.float32)
+    scale = (amax / np.float32(E4M3_MAX)).astype(np.float32)
     scale = np.where(scale > 0, scale, np.float32(1.0)).astype(np.float32)
-    codes = e4m3_round(rows / scale.astype(np.float64)[..., None])
+    quot = (rows / scale[..., None]).astype(np.float32)
+    codes = e4m3_round(quot.astype(np.float64))
     return codes, scale
 
 

@@ -16,6 +16,8 @@ from _common import check, log, oracle_for, tiny_sequences
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
+FP8 = 4.0   # tolerance factor for an fp8 cache
+
 
 @pytest.fixture(scope="module", autouse=True)
 def _gpu():
@@ -43,13 +45,20 @@ def host(st):
 
 
 def compare_seq(w, bt, seqs, got, b, heads=None, factor=1.0, weights=None, tag=""):
+    """The gate on the layer output o; o_lat and lse under the same rule as diagnostics.
+
+    fp8 cache: the gate is 4x the bf16 rule on o.  Storing the latent in e4m3 alone moves
+    o_lat of a short sequence by up to ~3/4 of that bound (three mantissa bits on each of a few
+    dominant tokens; measured by quantising the oracle's own inputs), and the e4m3 query and
+    probabilities add to it, so the diagnostics get 1.25x the gate there."""
     ref = oracle_for(w, bt, seqs, b, heads=heads, weights=weights)
     sl = slice(b * w.sq, (b + 1) * w.sq)
     hs = slice(None) if heads is None else list(heads)
     g = {k: v[sl][:, hs] for k, v in got.items()}
+    diag = factor * (1.25 if factor > 1.0 else 1.0)
     r = check(f"{tag}b{b} o", g["o"], ref["o"], factor)
-    check(f"{tag}b{b} o_lat", g["o_lat"], ref["o_lat"], factor)
-    check(f"{tag}b{b} lse", g["lse"], ref["lse"], factor)
+    check(f"{tag}b{b} o_lat", g["o_lat"], ref["o_lat"], diag)
+    check(f"{tag}b{b} lse", g["lse"], ref["lse"], diag)
     return r
 
 
@@ -77,7 +86,9 @@ def test_tiny_f32_from_hidden_states():
 
 # --------------------------------------------------------------------------- DS-V2 shapes, bf16
 
-def dsv2(batch, lengths, sq=1, seed=7, name="dsv2_b16_l4k"):
+def dsv2(batch, lengths, sq=1, seed=7, name="dsv2_b16_l4k", fp8=False):
+    if fp8:
+        name = "dsv2_b128_l8k_fp8"
     w = wl.get(name, batch=batch, sq=sq, seed=seed, ctx_lo=0, ctx_hi=0)
     bt = wl.draw_batch(w)
     # replace the lengths with the requested ones (context + sq), rebuilding the page table
@@ -210,12 +221,79 @@ def test_zero_length_sequence_gives_empty_result():
         assert np.allclose(lse[b], ref["lse"][b], rtol=0, atol=1e-5), b
 
 
+# --------------------------------------------------------------------------- DS-V2 shapes, fp8 cache
+
+def test_fp8_edge_lengths_all_heads():
+    log("case dsv2 fp8 lengths [1, 63, 64, 65, 200], Sq=1, all heads (gate x4)")
+    w, bt, seqs = dsv2(5, [1, 63, 64, 65, 200], seed=41, fp8=True)
+    st = run_state(w, bt, seqs)
+    got = host(st)
+    for b in range(w.batch):
+        compare_seq(w, bt, seqs, got, b, factor=FP8)
+    # the folded query stays bf16 with an fp8 cache
+    qa = np.concatenate([orc.absorbed_query(s["q_c"], s["q_r"], bt.weights["W_UK"],
+                                            [int(bt.kv_lens[b]) - 1], w.rope_base) for b, s in enumerate(seqs)])
+    check("q_abs", st.q_abs.float().cpu().numpy(), qa)
+
+
+def test_fp8_cache_append_readback():
+    log("case fp8 cache readback: codes and scales = oracle quantiser of [c ; RoPE(k_R, pos)]")
+    w, bt, seqs = dsv2(2, [70, 3], seed=43, fp8=True)
+    st = run_state(w, bt, seqs)
+    codes = st.cache.view(torch.float8_e4m3fn).to(torch.float64).cpu().numpy()
+    scales = st.cache_scale.cpu().numpy()
+    for b in range(w.batch):
+        L = int(bt.kv_lens[b])
+        t = np.arange(L)
+        rows = np.concatenate([seqs[b]["c"][:L].astype(np.float64), orc.rope(seqs[b]["k_r"][:L], t, w.rope_base)],
+                              axis=1)
+        ref_codes, ref_scale = orc.quantize_rows_fp8(rows)
+        pages = bt.block_table[b, t // 64]
+        assert np.array_equal(scales[pages, t % 64], ref_scale), b
+        assert np.array_equal(codes[pages, t % 64], ref_codes), b
+
+
+def test_fp8_split_ranges_and_needles():
+    log("case dsv2 fp8 lengths [5000, 3001, 77]: split sequences, needles at 0 / 2048 / 76 (gate x4)")
+    w, bt, seqs = dsv2(3, [5000, 3001, 77], seed=47, fp8=True)
+    for b, t in [(0, 0), (1, 2048), (2, 76)]:
+        seqs[b]["c"] = seqs[b]["c"].copy()
+        seqs[b]["c"][t] = seqs[b]["c"][t] * 4.0
+    st = run_state(w, bt, seqs)
+    got = host(st)
+    for b in range(w.batch):
+        compare_seq(w, bt, seqs, got, b, heads=range(0, 128, 3), factor=FP8, tag="fp8 ")
+
+
+def test_fp8_causal_multi_query_sq4():
+    log("case dsv2 fp8 Sq=4 causal, lengths [4, 68, 129, 300] (gate x4)")
+    w, bt, seqs = dsv2(4, [4, 68, 129, 300], sq=4, seed=53, fp8=True)
+    st = run_state(w, bt, seqs)
+    got = host(st)
+    for b in range(w.batch):
+        compare_seq(w, bt, seqs, got, b, heads=range(1, 128, 4), factor=FP8)
+
+
+def test_fp8_extreme_scores_take_the_exact_path():
+    log("case fp8 extreme needles x128: lengths [3000, 700], needles at 2500 / 300 (gate x4)")
+    w, bt, seqs = dsv2(2, [3000, 700], seed=59, fp8=True)
+    for b, t in [(0, 2500), (1, 300)]:
+        seqs[b]["c"] = seqs[b]["c"].copy()
+        seqs[b]["c"][t] = seqs[b]["c"][t] * 128.0
+    st = run_state(w, bt, seqs)
+    got = host(st)
+    assert np.all(np.isfinite(got["o"])) and np.all(np.isfinite(got["lse"]))
+    for b in range(w.batch):
+        compare_seq(w, bt, seqs, got, b, heads=range(0, 128, 2), factor=FP8, tag="fp8 extreme ")
+
+
 # --------------------------------------------------------------------------- full-size workloads
 
 @pytest.mark.parametrize("name,sample", [
     ("dsv2_b16_l4k", [(0, None), (15, None)]),
     ("dsv2_b64_l1k_32k", [("shortest", range(0, 128, 16)), ("longest", range(3, 128, 16))]),
     ("dsv2_b32_l8k_sq4", [(0, range(0, 128, 8)), (31, range(5, 128, 16))]),
+    ("dsv2_b128_l8k_fp8", [(0, range(0, 128, 8)), (127, range(5, 128, 16))]),
 ])
 def test_full_size_sampled(name, sample):
     w = wl.get(name)
@@ -231,4 +309,4 @@ def test_full_size_sampled(name, sample):
         elif b == "longest":
             b = int(np.argmax(bt.kv_lens))
         log(f"  oracle on sequence {b} (kv_len {int(bt.kv_lens[b])})")
-        compare_seq(w, bt, seqs, got, b, heads=heads)
+        compare_seq(w, bt, seqs, got, b, heads=heads, factor=FP8 if w.dtype == "fp8" else 1.0)

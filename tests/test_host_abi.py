@@ -28,7 +28,7 @@ def test_exports_every_declared_symbol(L):
     assert set(syms) == set(B.EXPORTS), syms
     for s in syms:
         assert hasattr(L, s), s
-    assert B.mla_abi_version() == 1
+    assert B.mla_abi_version() == 2
 
 
 def cfg(**kw):
@@ -61,16 +61,17 @@ def test_config_validation(L, kw, code):
 def test_pointer_and_size_validation(L):
     c = cfg()
     # null / misaligned pointers
-    assert B.mla_absorb_q(c, 0, FAKE, FAKE, FAKE, FAKE, None, 4, stream=0, check=False) == B.MLA_ERR_INVALID_ARG
-    assert B.mla_absorb_q(c, FAKE + 8, FAKE, FAKE, FAKE, FAKE, None, 4, stream=0, check=False) == B.MLA_ERR_INVALID_ARG
+    assert B.mla_absorb_q(c, 0, FAKE, FAKE, FAKE, FAKE, 4, stream=0, check=False) == B.MLA_ERR_INVALID_ARG
+    assert B.mla_absorb_q(c, FAKE + 8, FAKE, FAKE, FAKE, FAKE, 4, stream=0, check=False) == B.MLA_ERR_INVALID_ARG
     assert B.mla_out_proj(c, FAKE, FAKE, FAKE, -1, stream=0, check=False) == B.MLA_ERR_INVALID_ARG
     # zero-size work is a no-op that touches nothing
     assert B.mla_out_proj(c, 0, 0, 0, 0, stream=0, check=False) == B.MLA_OK
-    assert B.mla_absorb_q(c, 0, 0, 0, 0, 0, None, 0, stream=0, check=False) == B.MLA_OK
-    # fp8 scale pointers must be given exactly for fp8 caches
+    assert B.mla_absorb_q(c, 0, 0, 0, 0, 0, 0, stream=0, check=False) == B.MLA_OK
+    # the scale pointer must be given exactly for fp8 caches
     c8 = cfg(cache_dtype="fp8")
-    assert B.mla_absorb_q(c8, FAKE, FAKE, FAKE, FAKE, FAKE, None, 4, stream=0, check=False) == B.MLA_ERR_INVALID_ARG
-    assert B.mla_absorb_q(c, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, stream=0, check=False) == B.MLA_ERR_INVALID_ARG
+    dec = [100, FAKE, 512, FAKE, 64, 1, FAKE, 1 << 30, FAKE, FAKE]
+    assert B.mla_decode_attn(c8, FAKE, FAKE, None, *dec, stream=0, check=False) == B.MLA_ERR_INVALID_ARG
+    assert B.mla_decode_attn(c, FAKE, FAKE, FAKE, *dec, stream=0, check=False) == B.MLA_ERR_INVALID_ARG
     assert B.mla_cache_append(c, FAKE, FAKE, 8, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 4, 3, stream=0,
                               check=False) == B.MLA_ERR_INVALID_ARG
     assert B.mla_cache_append(c, FAKE, None, 0, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 4, 3, stream=0,
@@ -84,13 +85,13 @@ def test_decode_workspace_checks(L):
     # more queries per sequence or more sequences never need less scratch
     assert B.mla_decode_workspace_size(c, 64, 4, 512) >= ws
     assert B.mla_decode_workspace_size(c, 128, 1, 512) >= ws
-    args = [c, FAKE, None, FAKE, None, 100, FAKE, 512, FAKE, 64, 1]
+    args = [c, FAKE, FAKE, None, 100, FAKE, 512, FAKE, 64, 1]
     assert B.mla_decode_attn(*args, 0, ws, FAKE, FAKE, stream=0, check=False) == B.MLA_ERR_WORKSPACE
     assert B.mla_decode_attn(*args, FAKE, ws - 256, FAKE, FAKE, stream=0, check=False) == B.MLA_ERR_WORKSPACE
     assert B.mla_decode_attn(*args, FAKE + 16, ws, FAKE, FAKE, stream=0, check=False) == B.MLA_ERR_WORKSPACE
-    bad = [c, FAKE, None, FAKE, None, 100, FAKE, 512, FAKE, 64, 0]
+    bad = [c, FAKE, FAKE, None, 100, FAKE, 512, FAKE, 64, 0]
     assert B.mla_decode_attn(*bad, FAKE, ws, FAKE, FAKE, stream=0, check=False) == B.MLA_ERR_INVALID_ARG
-    assert B.mla_decode_attn(c, FAKE, None, FAKE, None, 100, FAKE, 512, FAKE, 0, 1, 0, 0, 0, 0, stream=0,
+    assert B.mla_decode_attn(c, FAKE, FAKE, None, 100, FAKE, 512, FAKE, 0, 1, 0, 0, 0, 0, stream=0,
                              check=False) == B.MLA_OK
 
 

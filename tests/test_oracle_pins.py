@@ -309,6 +309,12 @@ def test_fp8_row_quantiser():
     # 3 mantissa bits: error at most half a step, i.e. 2^-4 of the value (plus the subnormal floor)
     err = np.abs(rec - rows)
     assert np.all(err <= np.abs(rows) * 2.0**-4 + scale[:, None] * 2.0**-10 + 1e-30)
+    # the codes are the e4m3 cast of the fp32 quotient (torch's own fp32 division and cast)
+    torch = pytest.importorskip("torch")
+    r32 = torch.from_numpy(rows.astype(np.float32))
+    q = r32 / torch.from_numpy(scale)[:, None]
+    ref = q.to(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert np.array_equal(codes, ref)
 
 
 # ------------------------------------------------------ planted mistakes are caught
