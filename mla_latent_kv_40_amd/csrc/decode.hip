@@ -1033,6 +1033,8 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_fp8_kernel(DecodeArgs a) {
       load_q(e1.z);
       __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     }
+    // values of page y first, so that its probabilities are dead before the scores of y+1
+    values(smem + (y & 3) * kStage8, pf, psb);
     const uint8_t* next = smem + ((y + 1) & 3) * kStage8;
     f32x16 s0, s1;
     scores(next, [&](int st) {   // stale data if !has_next
@@ -1042,7 +1044,6 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_fp8_kernel(DecodeArgs a) {
     const float m_old = m_ref, l_old = l_run;
     const bool over_old = over;
     softmax(s0, s1, next, last_visible(e1), seg_end, sm);
-    values(smem + (y & 3) * kStage8, pf, psb);
 
     if (seg_end) {
       const float l_tot = pair_sum(l_old);
