@@ -11,7 +11,9 @@ the timed region.
 value       query tokens decoded per second (B*Sq per step / mean step time)
 roofline    the split-K decode kernel: latent-cache bytes it must read per launch (1152 B per
             visible cached token in bf16, 580 B in fp8 incl. the scale) / its mean duration,
-            against 8 TB/s; durations from HIP events on the launch stream
+            against 8 TB/s; durations from HIP events on the launch stream.  traffic = HBM bytes
+            per launch measured by rocprofv3 counters (profiles/decode_hbm_traffic.md), null
+            when the kernel source differs from the one those counters were taken on
 cpu_baseline the fp64 oracle on the host cores, on a bounded sample of the same workload
 """
 from __future__ import annotations
@@ -44,6 +46,23 @@ def algorithmic(w, kv_lens):
         visible += int((kv - w.sq + j + 1).sum())
     flops = visible * 2 * w.heads * (2 * w.d_c + w.d_r)
     return tokens * per_tok, flops, tokens
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch of `kernel` on `workload` from the committed rocprofv3 counter summary
+    (FETCH_SIZE and WRITE_SIZE, scaled by a calibration copy), or None when that summary was
+    taken on a different decode.hip than the one built here."""
+    import hashlib
+    src = os.path.join(ROOT, "mla_latent_kv_40_amd", "csrc", "decode.hip")
+    prof = os.path.join(ROOT, "profiles", "decode_hbm_traffic.md")
+    if not os.path.exists(prof):
+        return None
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    for line in open(prof):
+        f = line.split()
+        if len(f) == 6 and f[0] == "traffic" and f[1] == kernel and f[2] == workload and f[5] == sha:
+            return int(f[3])
+    return None
 
 
 def cpu_baseline(w, bt, budget_s=20.0):
@@ -150,7 +169,7 @@ def main() -> int:
             {"bound": "mfma", "achieved": round(tflops, 1), "peak": peak_mfma, "unit": "TFLOP/s",
              "frac": round(tflops / peak_mfma, 4)})
     roof["kernel"] = "decode_mfma_fp8_kernel" if w.dtype == "fp8" else "decode_mfma_bf16_kernel"
-    roof["traffic"] = None
+    roof["traffic"] = measured_traffic(roof["kernel"], w.name)
     value = w.batch * w.sq / (ms_per_step * 1e-3)
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": a.steps,
