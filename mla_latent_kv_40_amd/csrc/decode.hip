@@ -147,38 +147,41 @@ __device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlan
 
 // Each of the four waves issues nine 1 KiB global->LDS loads per half page: latent rows
 // 8w .. 8w+7 (lane l fetches logical chunk l ^ key) and the positional rows 8w .. 8w+7
-// (lane l -> row 8w + l/8).  Rows at or past `nvalid` are fetched from the page's row 0
-// instead (finite data, masked scores).  The loads go through a buffer descriptor spanning
-// exactly the page (reads outside it would return zeros): unlike the flat-encoded
-// global->LDS form, buffer loads let the compiler keep counting LDS reads precisely while
-// page loads are in flight (a pending flat access forces every LDS wait to zero).  Aux is the
-// cache policy: non-temporal when no other workgroup reads the page, so that the stream does
-// not evict the queries and partial outputs from L2.
+// (lane l -> row 8w + l/8).  The loads go through a buffer descriptor that starts at the half
+// page's first row and ends after its last valid row: rows past it are out of range and the
+// load writes zeros for them (finite data, masked scores), and the per-lane offsets are the
+// same for every half page.  Unlike the flat-encoded global->LDS form, buffer loads let the
+// compiler keep counting LDS reads precisely while page loads are in flight (a pending flat
+// access forces every LDS wait to zero).  Aux is the cache policy: non-temporal when no other
+// workgroup reads the page, so that the stream does not evict the queries and partial outputs
+// from L2.
 struct PageLoad {
-  __amdgpu_buffer_rsrc_t rsrc;   // the page (num_records = one page)
+  __amdgpu_buffer_rsrc_t rsrc;   // rows 0 .. nvalid-1 of the half page
   uint8_t* stage;
-  int h, nvalid;
 };
 __device__ __forceinline__ PageLoad page_load(uint8_t* stage, const uint8_t* cache, int pg, int h, int nvalid) {
-  const uint8_t* page = cache + (size_t)(pg < 0 ? 0 : pg) * kTileBytes;
-  return PageLoad{__builtin_amdgcn_make_buffer_rsrc((void*)page, 0, kTileBytes, 0x00020000), stage, h, nvalid};
+  const uint8_t* half = cache + (size_t)(pg < 0 ? 0 : pg) * kTileBytes + (size_t)h * (kHalf * kRow * 2);
+  const int nv = nvalid < 0 ? 0 : (nvalid > kHalf ? kHalf : nvalid);
+  return PageLoad{__builtin_amdgcn_make_buffer_rsrc((void*)half, 0, nv * kRow * 2, 0x00020000), stage};
+}
+// Source offset (within the half page) of the 16 bytes lane `lane` of row load i fetches.
+__device__ __forceinline__ int half_src(int wave, int i, int lane) {
+  if (i < 8) {
+    const int r = 8 * wave + i;
+    return r * (kRow * 2) + ((lane ^ lat_key(r)) << 4);
+  }
+  const int r = 8 * wave + (lane >> 3);
+  return r * (kRow * 2) + kDC * 2 + (((lane & 7) ^ pos_key(r)) << 4);
 }
 // Row load i of this wave (i < 8: latent row 8w + i; i == 8: positional rows 8w .. 8w+7).
 template <int Aux>
-__device__ __forceinline__ void load_row(const PageLoad& p, int i, int wave, int lane) {
-  asm volatile("" : "+v"(lane));   // rebuild the per-lane offset here rather than keep it live
-  if (i < 8) {
-    const int r = 8 * wave + i;
-    const int rs = r < p.nvalid ? kHalf * p.h + r : 0;
-    const unsigned off = rs * (kRow * 2) + ((lane ^ lat_key(r)) << 4);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(p.rsrc, (MLA_LDS void*)(p.stage + r * 1024), 16, off, 0, 0, Aux);
-  } else {
-    const int r = 8 * wave + (lane >> 3);
-    const int rs = r < p.nvalid ? kHalf * p.h + r : 0;
-    const unsigned off = rs * (kRow * 2) + kDC * 2 + (((lane & 7) ^ pos_key(r)) << 4);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(p.rsrc, (MLA_LDS void*)(p.stage + kStageLat + 8 * wave * 128), 16, off,
+__device__ __forceinline__ void load_row(const PageLoad& p, int i, int wave, int src) {
+  if (i < 8)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(p.rsrc, (MLA_LDS void*)(p.stage + (8 * wave + i) * 1024), 16, src, 0,
+                                             0, Aux);
+  else
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(p.rsrc, (MLA_LDS void*)(p.stage + kStageLat + 8 * wave * 128), 16, src,
                                              0, 0, Aux);
-  }
 }
 
 // LDS reads at absolute LDS byte addresses (the callers fold the array base in once).  The
@@ -352,9 +355,12 @@ __device__ void build_page_table(const DecodeArgs& a, uint8_t* smem, int4* tab, 
 // first visible score maximum) instead of the running maximum: bf16 and fp32 keep their
 // relative precision at any magnitude, and scores below m merely underflow, which is exact to
 // fp32 precision relative to the final maximum.  A segment whose scores exceed m by more than
-// 2^64 (p could overflow) is marked (l = -1) and the combine recomputes its heads exactly; O is
-// therefore never rescaled in the page loop.
+// a safe margin (p could overflow) is marked (l = -1) and the combine recomputes its heads
+// exactly; O is therefore never rescaled in the page loop.  The bf16 kernel tests the running
+// sum of p (kOverflowSum, 2^80: then every p and O stay far below the fp32 range; an infinite
+// or NaN sum fails the test too), the fp8 kernel the page maximum (kRescaleLog2).
 constexpr float kRescaleLog2 = 64.0f;
+constexpr float kOverflowSum = 0x1p80f;
 
 // 32x32x16 bf16 MFMA layout (wave64): A lane l holds row l%32 and the 8 K values of K-group
 // l/32; B lane l holds column l%32 and the same K-group; the result lane l holds column l%32,
@@ -429,14 +435,17 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_bf16_kernel(DecodeArgs a) 
   for (int t = 0; t < 16; ++t) mfma_zero(oacc[t], zero8);
   float m_ref = -INFINITY, l_run = 0.f;
   bool over = false;                              // a score left the reference's safe range
+  bool m_set = false;                             // the segment's reference is set (uniform)
 
   // ---- S^T of the half page in `tile` (36 chained K-steps)
+  // this lane's LDS read bases inside a stage (kept live: one add per stage and step)
+  const uint32_t lat = (uint32_t)((lane & 31) * 1024) | (uint32_t)(16 * (lat_key(lane & 31) ^ hl));
+  const uint32_t pos = (uint32_t)(kStageLat + (lane & 31) * 128) | (uint32_t)(16 * (pos_key(lane & 31) ^ hl));
+  // transposing reads: source lane (gg, 4jj + uu) reads row 4hh + jj (+8E +16k), chunk
+  // 4ct + 2(gg&1) + uu/2, byte 8(uu&1)
+  const uint32_t vb = (uint32_t)((4 * hl + ((lane & 15) >> 2)) * 1024 + 8 * (lane & 1)) |
+                      (uint32_t)(16 * ((2 * ((lane >> 4) & 1) + ((lane >> 1) & 1)) ^ (4 * ((lane & 15) >> 2)) ^ hl));
   auto scores = [&](const uint8_t* tile, auto hook) -> f32x16 {
-    int ln = lane;
-    asm volatile("" : "+v"(ln));
-    const int rr = ln & 31, hh = ln >> 5;
-    const uint32_t lat = (uint32_t)(rr * 1024) | (uint32_t)(16 * (lat_key(rr) ^ hh));
-    const uint32_t pos = (uint32_t)(kStageLat + rr * 128) | (uint32_t)(16 * (pos_key(rr) ^ hh));
     // the eight swizzle variants of this lane's row address, stage offset included once (the
     // XOR touches bits 5..7 only and stages start at multiples of 256); the rest of each
     // address is the read's immediate offset
@@ -473,7 +482,7 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_bf16_kernel(DecodeArgs a) 
   // values that enter P.V.
   struct Soft {
     float m_new, l_new;
-    bool over_new;
+    bool over_new, m_set_new;
     bf16x8 p0, p1;
   };
   auto softmax = [&](f32x16& sv, int vis, bool fresh, Soft& st) {
@@ -482,15 +491,18 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_bf16_kernel(DecodeArgs a) 
       for (int i = 0; i < 16; ++i)
         if (8 * (i >> 2) + 4 * hl + (i & 3) > vis) sv[i] = -INFINITY;
     }
-    float mx = fmaxf(fmaxf(sv[0], sv[1]), sv[2]);
-#pragma unroll
-    for (int i = 3; i < 15; i += 2) mx = fmaxf(fmaxf(mx, sv[i]), sv[i + 1]);
-    mx = fmaxf(mx, sv[15]);
     const float c = a.scale_log2;
-    const float tmax = pair_max(mx) * c;
     const float m_in = fresh ? -INFINITY : m_ref;
-    st.m_new = (m_in == -INFINITY) ? tmax : m_in;   // first visible scores fix the reference
-    st.over_new = (fresh ? false : over) || (tmax > st.m_new + kRescaleLog2);
+    st.m_set_new = (fresh ? false : m_set) || vis >= 0;   // wave-uniform
+    if (fresh || !m_set) {   // the first visible scores of the segment fix the reference
+      float mx = fmaxf(fmaxf(sv[0], sv[1]), sv[2]);
+#pragma unroll
+      for (int i = 3; i < 15; i += 2) mx = fmaxf(fmaxf(mx, sv[i]), sv[i + 1]);
+      mx = fmaxf(mx, sv[15]);
+      st.m_new = pair_max(mx) * c;
+    } else {
+      st.m_new = m_in;
+    }
     const float m_use = (st.m_new == -INFINITY) ? 0.0f : st.m_new;
     float l = fresh ? 0.0f : l_run;
     const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
@@ -502,6 +514,7 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_bf16_kernel(DecodeArgs a) 
       l = __builtin_amdgcn_fdot2_f32_bf16(pk[u], ones, l, false);
     }
     st.l_new = l;
+    st.over_new = (fresh ? false : over) || !(l < kOverflowSum);   // also catches inf and NaN
     st.p0 = bf16x8{pk[0][0], pk[0][1], pk[1][0], pk[1][1], pk[2][0], pk[2][1], pk[3][0], pk[3][1]};
     st.p1 = bf16x8{pk[4][0], pk[4][1], pk[5][0], pk[5][1], pk[6][0], pk[6][1], pk[7][0], pk[7][1]};
   };
@@ -509,12 +522,6 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_bf16_kernel(DecodeArgs a) 
   // ---- O^T += V^T . P^T for the half page in `tile`
   auto values = [&](const uint8_t* tile, const bf16x8* pf) {
     o_fence<3>(oacc);   // MFMA writes of O settled
-    int ln = lane;
-    asm volatile("" : "+v"(ln));
-    const int gg = ln >> 4, sl = ln & 15, jj = sl >> 2, uu = sl & 3, hh = ln >> 5;
-    // source lane (gg, 4jj + uu): row 4hh + jj (+8E +16k), chunk 4ct + 2(gg&1) + uu/2, byte 8(uu&1)
-    const uint32_t vb = (uint32_t)((4 * hh + jj) * 1024 + 8 * (uu & 1)) |
-                        (uint32_t)(16 * ((2 * (gg & 1) + (uu >> 1)) ^ (4 * jj) ^ hh));
     // eight swizzle variants (column tile mod 4, token half E), stage offset included once
     const uint32_t T = (uint32_t)(tile - smem);   // stage offset, a multiple of 256
     const uint8_t* xv[8];
@@ -546,6 +553,7 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_bf16_kernel(DecodeArgs a) 
     m_ref = st.m_new;
     l_run = st.l_new;
     over = st.over_new;
+    m_set = st.m_set_new;
     pf[0] = st.p0;
     pf[1] = st.p1;
   };
@@ -557,19 +565,25 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_bf16_kernel(DecodeArgs a) 
   auto load_for = [&](int stage, int pg, int nv, int h) {
     return page_load(smem + stage * kStageBytes, a.cache, nv > 0 ? pg : 0, h, nv);
   };
+  int src[9];
+#pragma unroll
+  for (int i = 0; i < 9; ++i) src[i] = half_src(wave, i, lane);
   auto issue = [&](const PageLoad& pl) {
 #pragma unroll
-    for (int i = 0; i < 9; ++i) load_row<Aux>(pl, i, wave, lane);
+    for (int i = 0; i < 9; ++i) load_row<Aux>(pl, i, wave, src[i]);
   };
   // table entry of half page z (wave-uniform); past the range: no valid token
   // (read through an absolute LDS address: through a pointer into the shared array the
   // compiler would wait for the page loads in flight, which may alias it)
   const uint32_t tab_addr = lds_addr(smem + kTabOff);
-  auto entry = [&](int z) -> int4 {
+  auto entry_raw = [&](int z) -> u32x4 {   // z clamped to the table
+    return lds_b128(tab_addr + 16u * (uint32_t)((z < n_steps ? z : n_steps - 1) >> 1));
+  };
+  auto entry_of = [&](const u32x4& e, int z) -> int4 {
     if (z >= n_steps) return int4{-1, 0, 0, 0};
-    const u32x4 e = lds_b128(tab_addr + 16u * (uint32_t)(z >> 1));
     return int4{uni((int)e[0]), uni((int)e[1]), uni((int)e[2]), uni((int)e[3])};
   };
+  auto entry = [&](int z) -> int4 { return entry_of(entry_raw(z), z); };
   auto valid_page = [&](const int4& e) { return e.x >= 0 && e.x < a.num_blocks; };
   // valid tokens of half page z (<= 0 for an empty second half); 0 for an invalid page
   auto nvalid = [&](const int4& e, int z) {
@@ -585,6 +599,7 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_bf16_kernel(DecodeArgs a) 
   // prologue: queries, half pages 0..2 in flight, scores and probabilities of half page 0.
   // e0..e3: table entries of half pages y .. y+3.
   int4 e0 = entry(0), e1 = entry(1), e2 = entry(2), e3;
+  u32x4 e3_raw = entry_raw(3);   // read a step ahead: the page-table read never waits
   load_q(e0.z);
   issue(load_for(0, e0.x, nvalid(e0, 0), 0));
   issue(load_for(1, e1.x, nvalid(e1, 1), 1));
@@ -603,7 +618,8 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_bf16_kernel(DecodeArgs a) 
     // stay in flight), then everyone's
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(9));
     lds_barrier();   // stage (y+3)%4 == (y-1)%4 is no longer read by anyone
-    e3 = entry(y + 3);
+    e3 = entry_of(e3_raw, y + 3);
+    e3_raw = entry_raw(y + 4);
     // the nine page loads of half page y+3 go out one after every fourth score MFMA, so that
     // their issue (which may wait for queue space) overlaps matrix work
     const PageLoad pl = load_for((y + 3) & 3, e3.x, nvalid(e3, y + 3), (y + 3) & 1);
@@ -614,19 +630,22 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_bf16_kernel(DecodeArgs a) 
       load_q(e1.z);
       __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     }
-    f32x16 snext = scores(smem + ((y + 1) & 3) * kStageBytes, [&](int st) {   // stale data if !has_next
-      if ((st & 3) == 0) load_row<Aux>(pl, st >> 2, wave, lane);
+    f32x16 sv = scores(smem + ((y + 1) & 3) * kStageBytes, [&](int st) {   // stale data if !has_next
+      if ((st & 3) == 0) load_row<Aux>(pl, st >> 2, wave, src[st >> 2]);
     });
     const float m_old = m_ref, l_old = l_run;
     const bool over_old = over;
-    softmax(snext, last_visible(e1, y + 1), seg_end, sm);
     values(smem + (y & 3) * kStageBytes, pf);
+    // softmax of half page y+1 (a compact block: on one wave per SIMD, vector instructions
+    // cost the same wherever they sit between the matrix instructions)
+    softmax(sv, last_visible(e1, y + 1), seg_end, sm);
 
     if (seg_end) {
       // unnormalised O and (m, l) of this segment into its slot; the combine normalises
       const float l_tot = pair_sum(l_old);
+      const bool over_seg = pair_sum(over_old ? 1.0f : 0.0f) > 0.0f;   // either half of the head
       const size_t row = ((size_t)(g + e0.z) * a.Sq + j) * kH + head;
-      if (hl == 0) reinterpret_cast<float2*>(a.part_ml)[row] = float2{m_old, over_old ? -1.0f : l_tot};
+      if (hl == 0) reinterpret_cast<float2*>(a.part_ml)[row] = float2{m_old, over_seg ? -1.0f : l_tot};
       float* so = slot_o(e0.z);
       // oacc[ct][4q4 + i] is column 32ct + 8q4 + 4hl + i of this lane's head
 #pragma unroll
