@@ -25,6 +25,8 @@
 //             (m, l) per head to workspace slot g + b; the combine normalises.
 #include "common.h"
 
+#include <type_traits>
+
 namespace mla {
 
 constexpr int kH = 128, kDC = 512, kDR = 64, kRow = 576;
@@ -544,7 +546,7 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_bf16_kernel(DecodeArgs a) 
       mfma_acc(oacc[it & 15], vr[it % (D + 1)], pf[it >> 4]);
       __builtin_amdgcn_sched_barrier(0);
     }
-    o_fence<20>(oacc);  // results settled before any other access of O
+    // (the next accumulation into the same tiles needs no wait; the segment-end stores fence)
   };
 
   bf16x8 pf[2];
@@ -612,7 +614,9 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_bf16_kernel(DecodeArgs a) 
     soft_commit(sm);
   }
 
-  for (int y = 0; y < n_steps; ++y) {
+  // one step; P = y & 1 (a compile-time constant: the loop below runs two steps per page)
+  auto step = [&](int y, auto par) {
+    constexpr int P = decltype(par)::value;
     const bool has_next = y + 1 < n_steps;
     // this wave's loads of half page y+1 landed (only the nine loads of half page y+2 may
     // stay in flight), then everyone's
@@ -622,8 +626,8 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_bf16_kernel(DecodeArgs a) 
     e3_raw = entry_raw(y + 4);
     // the nine page loads of half page y+3 go out one after every fourth score MFMA, so that
     // their issue (which may wait for queue space) overlaps matrix work
-    const PageLoad pl = load_for((y + 3) & 3, e3.x, nvalid(e3, y + 3), (y + 3) & 1);
-    const bool seg_end = ((y & 1) && (e0.w & kLast)) || !has_next;
+    const PageLoad pl = load_for((y + 3) & 3, e3.x, nvalid(e3, y + 3), 1 - P);
+    const bool seg_end = (P == 1 && (e0.w & kLast)) || !has_next;
     if (seg_end && has_next) {
       // the next half page starts another sequence: its queries replace this one's (waiting
       // here keeps the steady-state loop free of pending query loads)
@@ -647,6 +651,7 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_bf16_kernel(DecodeArgs a) 
       const size_t row = ((size_t)(g + e0.z) * a.Sq + j) * kH + head;
       if (hl == 0) reinterpret_cast<float2*>(a.part_ml)[row] = float2{m_old, over_seg ? -1.0f : l_tot};
       float* so = slot_o(e0.z);
+      o_fence<20>(oacc);   // results of the last accumulation settled before the stores
       // oacc[ct][4q4 + i] is column 32ct + 8q4 + 4hl + i of this lane's head
 #pragma unroll
       for (int ct = 0; ct < 16; ++ct)
@@ -663,6 +668,10 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_bf16_kernel(DecodeArgs a) 
     e0 = e1;
     e1 = e2;
     e2 = e3;
+  };
+  for (int y = 0; y < n_steps; y += 2) {   // n_steps is even: two half pages per page
+    step(y, std::integral_constant<int, 0>{});
+    step(y + 1, std::integral_constant<int, 1>{});
   }
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));   // no page load may land after the workgroup ends
 }
