@@ -253,13 +253,14 @@ __device__ __forceinline__ void o_fence(f32x16* o) {
 // sequence marks its first page, a prefix maximum over the marks gives every page its
 // sequence, and one gather per page fetches the ids.  The step loop then needs no cursor
 // walking and no scalar loads.
-// Scratch space is the start of stage 0 (not in use yet): 3 KiB of per-sequence arrays, then
-// 4 KiB of page marks.  Every thread of the workgroup calls it; n_pages <= 1024.
-__device__ void build_page_table(const DecodeArgs& a, uint8_t* smem, int4* tab, int n_pages, long long x0, int b0,
-                                 long long s_first) {
+// `scratch` (LDS not in use yet) holds 3 KiB of per-sequence arrays, then 4 KiB of page marks.
+// Every thread of the workgroup calls it; n_pages <= 1024.  The barriers wait only for LDS
+// traffic, so page loads already in flight keep going.
+__device__ void build_page_table(const DecodeArgs& a, uint8_t* scratch, int4* tab, int n_pages, long long x0,
+                                 int b0, long long s_first) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  int* s_start = reinterpret_cast<int*>(smem);          // [256] stage 0 as scratch
+  int* s_start = reinterpret_cast<int*>(scratch);       // [256]
   int* s_len = s_start + 256;                           // [256]
   int* s_nb = s_start + 512;                            // [256]
   int* s_wsum = s_start + 768;                          // [4]
@@ -280,7 +281,7 @@ __device__ void build_page_table(const DecodeArgs& a, uint8_t* smem, int4* tab, 
       if (lane >= o) incl += v;
     }
     if (lane == 63) s_wsum[wave] = incl;
-    __syncthreads();
+    lds_barrier();
     int before = 0, total = 0;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
@@ -295,9 +296,9 @@ __device__ void build_page_table(const DecodeArgs& a, uint8_t* smem, int4* tab, 
     const long long k_end_ll = rel_base + total;       // range pages covered by this chunk
     const int k_end = (int)(k_end_ll < n_pages ? k_end_ll : n_pages);
     for (int k = k_done + t; k < k_end; k += 256) s_mark[k] = -1;
-    __syncthreads();
+    lds_barrier();
     if (nb > 0 && start >= k_done && start < k_end) s_mark[start] = t;   // sequence t starts at page start
-    __syncthreads();
+    lds_barrier();
     // pages k_done .. k_end-1: sequence = last mark at or before k (page k_done may continue
     // the sequence of the previous chunk's last page, or of chunk_b itself at the range start)
     {
@@ -317,9 +318,9 @@ __device__ void build_page_table(const DecodeArgs& a, uint8_t* smem, int4* tab, 
         const int v = __shfl_up(inc, o, 64);
         if (lane >= o) inc = v > inc ? v : inc;
       }
-      __syncthreads();                                   // everyone has read its marks
+      lds_barrier();                                   // everyone has read its marks
       if (lane == 63) s_wsum[wave] = inc;
-      __syncthreads();
+      lds_barrier();
       int prev = __shfl_up(inc, 1, 64);
       if (lane == 0) prev = -1;
 #pragma unroll
@@ -332,7 +333,7 @@ __device__ void build_page_table(const DecodeArgs& a, uint8_t* smem, int4* tab, 
         if (k < k_end) s_mark[k] = r < 0 ? 0 : r;        // no mark yet: sequence chunk_b
       }
     }
-    __syncthreads();
+    lds_barrier();
 #pragma unroll
     for (int i = 0; i < 4; ++i) {                       // k_end - k_done <= 1024
       const int k = k_done + t + 256 * i;
@@ -346,7 +347,7 @@ __device__ void build_page_table(const DecodeArgs& a, uint8_t* smem, int4* tab, 
       }
     }
     k_done = k_end;
-    __syncthreads();
+    lds_barrier();
     if (k_done >= n_pages || chunk_b + 256 >= a.B) break;
     chunk_b += 256;
     rel_base += total;
@@ -415,7 +416,6 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_bf16_kernel(DecodeArgs a) 
   // the host sizes the ranges to fit the table; the clamp only keeps LDS accesses in bounds
   const int n_pages = (int)(x1 - x0 < kTabCap ? x1 - x0 : kTabCap);
   const int n_steps = 2 * n_pages;               // half pages of this range
-  build_page_table(a, smem, reinterpret_cast<int4*>(smem + kTabOff), n_pages, x0, b0, s_first);
 
   bf16x8 qf[36];
   auto load_q = [&](int bb) {
@@ -599,12 +599,23 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_bf16_kernel(DecodeArgs a) 
   };
 
   // prologue: queries, half pages 0..2 in flight, scores and probabilities of half page 0.
-  // e0..e3: table entries of half pages y .. y+3.
+  // The first page needs no table: its queries and both halves are requested before the
+  // table is built (in stage 3, not yet in use), so that the build overlaps their latency.
+  load_q(b0);
+  {
+    const int tb0 = (int)(x0 - s_first);
+    int L0;
+    seq_tiles(a.kv_lens, b0, a.max_blocks, &L0);
+    const int4 f0 = int4{ld_const(a.block_table, (size_t)b0 * a.max_blocks + tb0), L0 - kBlock * tb0, b0, 0};
+    issue(load_for(0, f0.x, nvalid(f0, 0), 0));
+    issue(load_for(1, f0.x, nvalid(f0, 1), 1));
+  }
+  build_page_table(a, smem + 3 * kStageBytes, reinterpret_cast<int4*>(smem + kTabOff), n_pages, x0, b0, s_first);
+  // e0..e3: table entries of half pages y .. y+3
   int4 e0 = entry(0), e1 = entry(1), e2 = entry(2), e3;
-  u32x4 e3_raw = entry_raw(3);   // read a step ahead: the page-table read never waits
-  load_q(e0.z);
-  issue(load_for(0, e0.x, nvalid(e0, 0), 0));
-  issue(load_for(1, e1.x, nvalid(e1, 1), 1));
+  // the entry of half page y+3 is read during step y-1 and made scalar at its end, so the
+  // page-table read never waits
+  int4 e3_next = entry(3);
   issue(load_for(2, e2.x, nvalid(e2, 2), 0));
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
   lds_barrier();
@@ -622,8 +633,8 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_bf16_kernel(DecodeArgs a) 
     // stay in flight), then everyone's
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(9));
     lds_barrier();   // stage (y+3)%4 == (y-1)%4 is no longer read by anyone
-    e3 = entry_of(e3_raw, y + 3);
-    e3_raw = entry_raw(y + 4);
+    e3 = e3_next;
+    const u32x4 e4_raw = entry_raw(y + 4);
     // the nine page loads of half page y+3 go out one after every fourth score MFMA, so that
     // their issue (which may wait for queue space) overlaps matrix work
     const PageLoad pl = load_for((y + 3) & 3, e3.x, nvalid(e3, y + 3), 1 - P);
@@ -634,16 +645,12 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_bf16_kernel(DecodeArgs a) 
       load_q(e1.z);
       __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     }
-    f32x16 sv = scores(smem + ((y + 1) & 3) * kStageBytes, [&](int st) {   // stale data if !has_next
-      if ((st & 3) == 0) load_row<Aux>(pl, st >> 2, wave, src[st >> 2]);
-    });
+    // values of half page y first: a segment's stores then go out before this step's page
+    // loads (the wait at the top of the next step covers both) and have the score MFMAs to
+    // drain, and the probabilities of y are dead during the scores of y+1
     const float m_old = m_ref, l_old = l_run;
     const bool over_old = over;
     values(smem + (y & 3) * kStageBytes, pf);
-    // softmax of half page y+1 (a compact block: on one wave per SIMD, vector instructions
-    // cost the same wherever they sit between the matrix instructions)
-    softmax(sv, last_visible(e1, y + 1), seg_end, sm);
-
     if (seg_end) {
       // unnormalised O and (m, l) of this segment into its slot; the combine normalises
       const float l_tot = pair_sum(l_old);
@@ -664,7 +671,18 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_bf16_kernel(DecodeArgs a) 
         for (int t = 0; t < 16; ++t) mfma_zero(oacc[t], zero8);
       }
     }
+    f32x16 sv = scores(smem + ((y + 1) & 3) * kStageBytes, [&](int st) {   // stale data if !has_next
+      if ((st & 3) == 0) load_row<Aux>(pl, st >> 2, wave, src[st >> 2]);
+    });
+    // softmax of half page y+1 (a compact block: on one wave per SIMD, vector instructions
+    // cost the same wherever they sit between the matrix instructions)
+    softmax(sv, last_visible(e1, y + 1), seg_end, sm);
+
     soft_commit(sm);
+    // all four words stay live until here (a word the compiler finds unused would otherwise
+    // have its register recycled while the read is still in flight, which forces a wait)
+    asm volatile("" ::"v"(e4_raw));
+    e3_next = entry_of(e4_raw, y + 4);
     e0 = e1;
     e1 = e2;
     e2 = e3;
@@ -800,7 +818,7 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_fp8_kernel(DecodeArgs a) {
   }
   if (b0 < 0) return;
   const int n_steps = (int)(x1 - x0 < kTabCap8 ? x1 - x0 : kTabCap8);   // pages of this range
-  build_page_table(a, smem, reinterpret_cast<int4*>(smem + kTabOff8), n_steps, x0, b0, s_first);
+  build_page_table(a, smem, reinterpret_cast<int4*>(smem + kTabOff8), n_steps, x0, b0, s_first);   // stage 0 scratch
 
   // The folded query (bf16) becomes two e4m3 operands per K-step: with s = amax/448 over the
   // head's 576 values and x = q/s, hi = e4m3(x) and lo = e4m3(16 (x - hi)), so that
