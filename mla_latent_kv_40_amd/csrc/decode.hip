@@ -1218,7 +1218,8 @@ __global__ void __launch_bounds__(256) combine_kernel(DecodeArgs a) {
   auto slot = [&](int g) { return ((size_t)(g + b) * a.Sq + j); };
   float M = -INFINITY;
   bool redo = false;
-  for (int g = g_lo; g <= g_hi; ++g) {
+#pragma unroll 4
+  for (int g = g_lo; g <= g_hi; ++g) {   // independent loads: several in flight
     if (empty(g)) continue;
     const float2 v = ml[slot(g) * kH + h];
     if (v.y < 0.f) redo = true;
@@ -1229,15 +1230,35 @@ __global__ void __launch_bounds__(256) combine_kernel(DecodeArgs a) {
   for (int i = 0; i < 16; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   float L = 0.f;
   if (!redo && M != -INFINITY) {
-    for (int g = g_lo; g <= g_hi; ++g) {
-      if (empty(g)) continue;
-      const float2 v = ml[slot(g) * kH + h];
-      if (!(v.y > 0.f)) continue;
-      const float wg = __builtin_amdgcn_exp2f(v.x - M);
-      L += wg * v.y;
+    // slots in order, the next one's partials and (m, l) loading while the current one is
+    // accumulated; a segment with nothing visible (l = 0) holds zeros and gets weight 0
+    auto next_slot = [&](int g) {
+      while (g <= g_hi && empty(g)) ++g;
+      return g;
+    };
+    auto fetch = [&](int g, f32x4* d, float2& v) {
       const f32x4* src = reinterpret_cast<const f32x4*>(a.part_o + slot(g) * (kH * kDC) + (size_t)w * (32 * kDC));
 #pragma unroll
-      for (int i = 0; i < 16; ++i) acc[i] += wg * src[t + 256 * i];
+      for (int i = 0; i < 16; ++i) d[i] = src[t + 256 * i];
+      v = ml[slot(g) * kH + h];
+    };
+    int g = next_slot(g_lo);
+    f32x4 cur[16];
+    float2 vc;
+    fetch(g, cur, vc);
+    while (g <= g_hi) {
+      const int gn = next_slot(g + 1);
+      f32x4 nxt[16];
+      float2 vn = float2{0.f, 0.f};
+      if (gn <= g_hi) fetch(gn, nxt, vn);
+      const float wg = vc.y > 0.f ? __builtin_amdgcn_exp2f(vc.x - M) : 0.0f;
+      L += vc.y > 0.f ? wg * vc.y : 0.0f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[i] += wg * cur[i];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) cur[i] = nxt[i];
+      vc = vn;
+      g = gn;
     }
   }
   bool fin = __builtin_isfinite(L);
