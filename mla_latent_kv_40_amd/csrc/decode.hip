@@ -46,6 +46,7 @@ struct DecodeArgs {
   int num_blocks, max_blocks, B, Sq, G;
   float scale_log2;           // softmax_scale * log2(e)
   int fp8;                    // cache and queries are e4m3 codes with scales
+  int seg_w;                  // per-segment overhead in pages, for cutting the ranges
 };
 
 // Read-only kernel inputs are read through the constant address space: with a uniform index
@@ -69,45 +70,95 @@ __device__ __forceinline__ int seq_tiles(const int32_t* kv_lens, int b, int max_
   return (len + kBlock - 1) / kBlock;
 }
 
-// Owner of global tile x when T tiles are split evenly over G ranges [g*T/G, (g+1)*T/G).
-__device__ __forceinline__ int range_of_tile(long long x, long long T, int G) {
-  return (int)(((x + 1) * (long long)G - 1) / T);
+// Ranges are cut in cost units rather than pages.  A sequence with n > 0 pages costs w + n
+// units: w units of per-segment overhead (a segment's partial output stores, the query reload
+// of the next segment, its ragged last page, a reference maximum), then one per page.  Page x
+// of the r-th non-empty sequence (r = 0, 1, ..) sits at cost position c(x) = x + w (r + 1), and
+// range g owns the pages with floor(g C / G) <= c(x) < floor((g+1) C / G), C the total cost.
+// With w = 0 this is the even split of pages.  A range whose interval holds only overhead
+// units or is empty owns no page.
+
+// Owner of cost position c when C units are split over G ranges.
+__device__ __forceinline__ int range_of_tile(long long c, long long C, int G) {
+  return (int)(((c + 1) * (long long)G - 1) / C);
 }
 
-// Wave-level scan over the batch: total tiles, and (if want >= 0) the sequence holding
-// global tile `want` with that sequence's first tile index.  Every lane gets the results.
-__device__ void scan_batch(const int32_t* kv_lens, int B, int max_blocks, long long want, long long* total,
-                           int* seq, long long* seq_first) {
+// Page a cost boundary maps to (the first page at or after it), with its sequence.
+struct CostHit {
+  long long page;      // page index; the total page count when the boundary is at or past the end
+  int seq;             // sequence of that page (-1 past the end)
+  long long seq_first; // first page of that sequence
+};
+
+// Wave-level scan over the batch: total cost and pages, and (for each boundary >= 0) the page
+// it maps to.  Every lane gets the results.
+__device__ void scan_batch(const int32_t* kv_lens, int B, int max_blocks, int w, long long want0, long long want1,
+                           long long* cost_total, long long* page_total, CostHit* h0, CostHit* h1) {
   const int lane = threadIdx.x & 63;
-  long long run = 0;
-  int found_b = -1;
-  long long found_s = 0;
+  long long run_c = 0, run_n = 0;
+  CostHit hit[2] = {{-1, -1, 0}, {-1, -1, 0}};
+  const long long want[2] = {want0, want1};
   for (int base = 0; base < B; base += 64) {
     const int b = base + lane;
     int L;
     const int n = b < B ? seq_tiles(kv_lens, b, max_blocks, &L) : 0;
-    int incl = n;
+    const int c = n > 0 ? n + w : 0;
+    int incl_n = n, incl_c = c;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
-      const int y = __shfl_up(incl, o, 64);
-      if (lane >= o) incl += y;
+      const int yn = __shfl_up(incl_n, o, 64), yc = __shfl_up(incl_c, o, 64);
+      if (lane >= o) {
+        incl_n += yn;
+        incl_c += yc;
+      }
     }
-    const int excl = incl - n;
-    const bool mine = n > 0 && want >= run + excl && want < run + incl;
-    const unsigned long long mask = __ballot(mine);
-    if (mask) {
-      const int src = __ffsll((long long)mask) - 1;
-      found_b = __shfl(b, src, 64);
-      found_s = run + __shfl(excl, src, 64);
+    const int excl_n = incl_n - n, excl_c = incl_c - c;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const bool mine = n > 0 && want[k] >= run_c + excl_c && want[k] < run_c + incl_c;
+      const unsigned long long mask = __ballot(mine);
+      if (mask) {
+        const int src = __ffsll((long long)mask) - 1;
+        const long long cstart = run_c + __shfl(excl_c, src, 64);
+        const long long first = run_n + __shfl(excl_n, src, 64);
+        const long long off = want[k] - cstart - w;
+        hit[k] = CostHit{first + (off > 0 ? off : 0), __shfl(b, src, 64), first};
+      }
     }
-    run += __shfl(incl, 63, 64);
+    run_n += __shfl(incl_n, 63, 64);
+    run_c += __shfl(incl_c, 63, 64);
   }
   // wave-uniform results: hand them back as scalars
-  *total = ((long long)__builtin_amdgcn_readfirstlane((int)(run >> 32)) << 32) |
-           (unsigned)__builtin_amdgcn_readfirstlane((int)run);
-  *seq = __builtin_amdgcn_readfirstlane(found_b);
-  *seq_first = ((long long)__builtin_amdgcn_readfirstlane((int)(found_s >> 32)) << 32) |
-               (unsigned)__builtin_amdgcn_readfirstlane((int)found_s);
+  auto uni64 = [](long long v) {
+    return ((long long)__builtin_amdgcn_readfirstlane((int)(v >> 32)) << 32) |
+           (unsigned)__builtin_amdgcn_readfirstlane((int)v);
+  };
+  *cost_total = uni64(run_c);
+  *page_total = uni64(run_n);
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    CostHit* h = k == 0 ? h0 : h1;
+    if (h == nullptr) continue;
+    if (hit[k].seq < 0) hit[k].page = run_n;   // at or past the end (or want < 0)
+    *h = CostHit{uni64(hit[k].page), __builtin_amdgcn_readfirstlane(hit[k].seq), uni64(hit[k].seq_first)};
+  }
+}
+
+// Pages [x0, x1) of range g and the sequence b0 (first page s_first) holding x0; false when the
+// range owns no page.
+__device__ bool range_pages(const DecodeArgs& a, int g, long long* x0, long long* x1, int* b0, long long* s_first) {
+  long long C_all, T_all;
+  scan_batch(a.kv_lens, a.B, a.max_blocks, a.seg_w, -1, -1, &C_all, &T_all, nullptr, nullptr);
+  const long long c0 = (long long)g * C_all / a.G;
+  const long long c1 = (long long)(g + 1) * C_all / a.G;
+  if (c0 >= c1) return false;
+  CostHit h0, h1;
+  scan_batch(a.kv_lens, a.B, a.max_blocks, a.seg_w, c0, c1, &C_all, &T_all, &h0, &h1);
+  *x0 = h0.page;
+  *x1 = h1.seq < 0 ? T_all : h1.page;
+  *b0 = h0.seq;
+  *s_first = h0.seq_first;
+  return *x0 < *x1 && h0.seq >= 0;
 }
 
 // ---------------------------------------------------------------------------------------
@@ -397,21 +448,9 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_bf16_kernel(DecodeArgs a) 
   const int g = lid / a.Sq;
   const int j = lid - g * a.Sq;
 
-  long long T_all, s_first;
+  long long x0, x1, s_first;
   int b0;
-  {
-    int db;
-    long long ds;
-    scan_batch(a.kv_lens, a.B, a.max_blocks, -1, &T_all, &db, &ds);
-  }
-  const long long x0 = (long long)g * T_all / a.G;
-  const long long x1 = (long long)(g + 1) * T_all / a.G;
-  if (x0 >= x1) return;
-  {
-    long long tot;
-    scan_batch(a.kv_lens, a.B, a.max_blocks, x0, &tot, &b0, &s_first);
-  }
-  if (b0 < 0) return;                             // unreachable: x0 < T_all lies in some sequence
+  if (!range_pages(a, g, &x0, &x1, &b0, &s_first)) return;
 
   // the host sizes the ranges to fit the table; the clamp only keeps LDS accesses in bounds
   const int n_pages = (int)(x1 - x0 < kTabCap ? x1 - x0 : kTabCap);
@@ -598,26 +637,21 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_bf16_kernel(DecodeArgs a) 
     return valid_page(e) ? (v < kHalf - 1 ? v : kHalf - 1) : -1;
   };
 
-  // prologue: queries, half pages 0..2 in flight, scores and probabilities of half page 0.
-  // The first page needs no table: its queries and both halves are requested before the
-  // table is built (in stage 3, not yet in use), so that the build overlaps their latency.
-  load_q(b0);
-  {
-    const int tb0 = (int)(x0 - s_first);
-    int L0;
-    seq_tiles(a.kv_lens, b0, a.max_blocks, &L0);
-    const int4 f0 = int4{ld_const(a.block_table, (size_t)b0 * a.max_blocks + tb0), L0 - kBlock * tb0, b0, 0};
-    issue(load_for(0, f0.x, nvalid(f0, 0), 0));
-    issue(load_for(1, f0.x, nvalid(f0, 1), 1));
-  }
+  // prologue: the range's page table (built in stage 3, not yet in use) comes first, so that
+  // its own loads wait for nothing else (vector loads complete in order); then the queries and
+  // half pages 0..2 are requested, and the scores and probabilities of half page 0 wait only
+  // for the queries and that half page.
   build_page_table(a, smem + 3 * kStageBytes, reinterpret_cast<int4*>(smem + kTabOff), n_pages, x0, b0, s_first);
   // e0..e3: table entries of half pages y .. y+3
   int4 e0 = entry(0), e1 = entry(1), e2 = entry(2), e3;
   // the entry of half page y+3 is read during step y-1 and made scalar at its end, so the
   // page-table read never waits
   int4 e3_next = entry(3);
+  load_q(b0);
+  issue(load_for(0, e0.x, nvalid(e0, 0), 0));
+  issue(load_for(1, e1.x, nvalid(e1, 1), 1));
   issue(load_for(2, e2.x, nvalid(e2, 2), 0));
-  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(18));
   lds_barrier();
   {
     f32x16 s0 = scores(smem, [](int) {});
@@ -802,21 +836,9 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_fp8_kernel(DecodeArgs a) {
   const int g = lid / a.Sq;
   const int j = lid - g * a.Sq;
 
-  long long T_all, s_first;
+  long long x0, x1, s_first;
   int b0;
-  {
-    int db;
-    long long ds;
-    scan_batch(a.kv_lens, a.B, a.max_blocks, -1, &T_all, &db, &ds);
-  }
-  const long long x0 = (long long)g * T_all / a.G;
-  const long long x1 = (long long)(g + 1) * T_all / a.G;
-  if (x0 >= x1) return;
-  {
-    long long tot;
-    scan_batch(a.kv_lens, a.B, a.max_blocks, x0, &tot, &b0, &s_first);
-  }
-  if (b0 < 0) return;
+  if (!range_pages(a, g, &x0, &x1, &b0, &s_first)) return;
   const int n_steps = (int)(x1 - x0 < kTabCap8 ? x1 - x0 : kTabCap8);   // pages of this range
   build_page_table(a, smem, reinterpret_cast<int4*>(smem + kTabOff8), n_steps, x0, b0, s_first);   // stage 0 scratch
 
@@ -1055,10 +1077,11 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_fp8_kernel(DecodeArgs a) {
   };
 
   int4 e0 = entry(0), e1 = entry(1), e2 = entry(2), e3;
-  load_q(e0.z);
+  // pages 0..2 are requested first: they land while the queries are split
   issue(load_for(0, e0.x, nvalid(e0)));
   issue(load_for(1, e1.x, nvalid(e1)));
   issue(load_for(2, e2.x, nvalid(e2)));
+  load_q(e0.z);
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
   lds_barrier();
   {
@@ -1120,8 +1143,9 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_fp8_kernel(DecodeArgs a) {
 // Exact attention of one (query row, head) by one wave, two passes over the visible tokens in
 // fp32 (scores in the exp2 domain).  Used by the combine for heads whose fast-path segments
 // were marked (a score far above the segment's reference); slow, but right for any input.
-// Lane l handles columns 9l .. 9l+8 of the score and 8l .. 8l+7 of the output.
-__device__ void exact_head(const DecodeArgs& a, int b, int j, int h, int L, float* out) {
+// Lane l handles columns 9l .. 9l+8 of the score and c0 + 2l, c0 + 2l + 1 of the output (one
+// quarter of the latent row); the log-sum-exp is written when `with_lse`.
+__device__ void exact_head(const DecodeArgs& a, int b, int j, int h, int L, int c0, bool with_lse) {
   const int lane = threadIdx.x & 63;
   const int row = b * a.Sq + j;
   const int last = L - a.Sq + j;                     // last visible position
@@ -1152,7 +1176,8 @@ __device__ void exact_head(const DecodeArgs& a, int b, int j, int h, int L, floa
     if (sl >= 0) mx = fmaxf(mx, score(sl));
   }
   float l = 0.f;
-  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float acc0 = 0.f, acc1 = 0.f;
+  const int col = c0 + 2 * lane;
   if (mx != -INFINITY) {
     for (int t = 0; t < n; ++t) {
       const long long sl = slot(t);
@@ -1160,129 +1185,140 @@ __device__ void exact_head(const DecodeArgs& a, int b, int j, int h, int L, floa
       const float w = __builtin_amdgcn_exp2f(score(sl) - mx);
       l += w;
       const float wc = a.fp8 ? w * a.cache_scale[sl] : w;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] += wc * elem(sl, 8 * lane + i);
+      acc0 += wc * elem(sl, col);
+      acc1 += wc * elem(sl, col + 1);
     }
   }
   const float inv = l > 0.f ? 1.0f / l : 0.0f;
-  *reinterpret_cast<f32x4*>(out) = f32x4{acc[0], acc[1], acc[2], acc[3]} * inv;
-  *reinterpret_cast<f32x4*>(out + 4) = f32x4{acc[4], acc[5], acc[6], acc[7]} * inv;
-  if (lane == 0) a.lse[(size_t)row * kH + h] = l > 0.f ? (mx + __log2f(l)) * 0.69314718055994531f : -INFINITY;
+  *reinterpret_cast<float2*>(a.o_lat + qrow * kDC + col) = float2{acc0 * inv, acc1 * inv};
+  if (with_lse && lane == 0) a.lse[qrow] = l > 0.f ? (mx + __log2f(l)) * 0.69314718055994531f : -INFINITY;
 }
 
 
-// One workgroup per (query row, group of 32 heads).  Every segment left its unnormalised
-// O_g (in register order) and (m_g, l_g) per head in slot g + b; with M = max m_g over the
-// non-empty ones and w_g = 2^(m_g - M):  o = sum w_g O_g / sum w_g l_g,
-// lse = ln 2 * (M + log2 sum w_g l_g).  Thread t reads 16-byte pieces t + 256i of the
-// group's 64 KiB block (coalesced); all of them belong to head 32w + t%32, so each thread
-// needs one head's weights.  The result goes through LDS so that the rows of o_lat are
-// written contiguously.  Heads marked by the fast path are then recomputed exactly.
-constexpr int kCombineLds = 32 * kDC * 4 + 64;
+// One workgroup per (query row, group of 32 heads, quarter of the latent columns).  Every
+// segment left its unnormalised O_g (in register order) and (m_g, l_g) per head in slot g + b;
+// with M = max m_g over the non-empty ones and w_g = 2^(m_g - M):  o = sum w_g O_g / sum w_g l_g,
+// lse = ln 2 * (M + log2 sum w_g l_g).  Quarter c of a group's 64 KiB block is its 1 KiB blocks
+// 16c .. 16c+15 (column tiles 4c .. 4c+3, so columns 128c .. 128c+127), contiguous in every
+// slot: thread t reads its 16-byte pieces t + 256i (i < 4), all of head 32w + t%32, so each
+// thread needs one head's weights.  The pieces of kCombineBatch slots are requested together,
+// so a sequence's slots cost about one memory latency rather than one each.  The result goes
+// through LDS so that each head's 128 columns are written contiguously.  Heads marked by the
+// fast path (or whose sums are not finite) are then recomputed exactly, quarter by quarter.
+constexpr int kCombineBatch = 4;
+constexpr int kCombinePitch = 128 + 4;   // fp32 words per head in the LDS tile (spreads heads over banks)
 
 __global__ void __launch_bounds__(256) combine_kernel(DecodeArgs a) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t cl[];
-  float* tile = reinterpret_cast<float*>(cl);                 // [32 heads][512]
-  int* redo_mask = reinterpret_cast<int*>(cl + 32 * kDC * 4);  // heads to recompute
+  __shared__ __attribute__((aligned(16))) float tile[32 * kCombinePitch];   // [32 heads][128 columns]
+  __shared__ int redo_mask;                                                 // heads to recompute
   const int row = blockIdx.x;          // b*Sq + j
   const int b = row / a.Sq, j = row - b * a.Sq;
   const int w = blockIdx.y;            // heads 32w .. 32w+31
+  const int c = blockIdx.z;            // columns 128c .. 128c+127
   const int t = threadIdx.x, lane = t & 63;
   const int hh = t & 31, h = 32 * w + hh, hl = (t >> 5) & 1;
-  long long T_all, S_b;
-  int bb;
-  scan_batch(a.kv_lens, a.B, a.max_blocks, -1, &T_all, &bb, &S_b);
-  long long first = 0;                 // first tile of sequence b
+  long long C_all, T_all;
+  scan_batch(a.kv_lens, a.B, a.max_blocks, a.seg_w, -1, -1, &C_all, &T_all, nullptr, nullptr);
+  long long first = 0;                 // first page of sequence b
+  int rank = 0;                        // non-empty sequences before b
   for (int base = 0; base < b; base += 64) {
     const int q = base + lane;
     int L;
     const int n = q < b ? seq_tiles(a.kv_lens, q, a.max_blocks, &L) : 0;
     first += wave_sum_i(n);
+    rank += wave_sum_i(n > 0 ? 1 : 0);
   }
+  const long long cfirst = first + (long long)a.seg_w * (rank + 1);   // cost position of that page
   int Lb;
   const int nb = seq_tiles(a.kv_lens, b, a.max_blocks, &Lb);
-  if (t == 0) *redo_mask = 0;
+  if (t == 0) redo_mask = 0;
   __syncthreads();
-  float* out_row = a.o_lat + ((size_t)row * kH + 32 * w) * kDC;
+  // head 32w + k of this row starts at out_base + k * kDC
+  float* out_base = a.o_lat + ((size_t)row * kH + 32 * w) * kDC + 128 * c;
   if (nb == 0) {
-    for (int i = t; i < 32 * kDC / 4; i += 256) reinterpret_cast<f32x4*>(out_row)[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (t < 32) a.lse[(size_t)row * kH + 32 * w + t] = -INFINITY;
+    for (int i = t; i < 32 * 32; i += 256)
+      *reinterpret_cast<f32x4*>(out_base + (i >> 5) * kDC + 4 * (i & 31)) = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (c == 0 && t < 32) a.lse[(size_t)row * kH + 32 * w + t] = -INFINITY;
     return;
   }
-  const int g_lo = range_of_tile(first, T_all, a.G);
-  const int g_hi = range_of_tile(first + nb - 1, T_all, a.G);
-  // Ranges between g_lo and g_hi that hold no page at all (possible when the batch has fewer
-  // pages than ranges) wrote nothing: skip them.
-  auto empty = [&](int g) { return (long long)g * T_all / a.G == (long long)(g + 1) * T_all / a.G; };
+  const int g_lo = range_of_tile(cfirst, C_all, a.G);
+  const int g_hi = range_of_tile(cfirst + nb - 1, C_all, a.G);
+  // Ranges between g_lo and g_hi with an empty cost interval (possible when the batch costs
+  // fewer units than there are ranges) wrote nothing: skip them.
+  auto empty = [&](int g) { return (long long)g * C_all / a.G == (long long)(g + 1) * C_all / a.G; };
   const float2* ml = reinterpret_cast<const float2*>(a.part_ml);
   auto slot = [&](int g) { return ((size_t)(g + b) * a.Sq + j); };
+  // partials and (m, l) of the slots g .. g + kCombineBatch - 1 (zeros past g_hi)
+  const size_t piece = (size_t)w * (32 * kDC) + (size_t)c * (16 * 256) + 4 * t;
+  f32x4 v[kCombineBatch][4];
+  float2 mv[kCombineBatch];
+  auto fetch = [&](int g) {
+#pragma unroll
+    for (int k = 0; k < kCombineBatch; ++k) {
+      const int gk = g + k;
+      if (gk <= g_hi && !empty(gk)) {
+        const float* src = a.part_o + slot(gk) * (kH * kDC) + piece;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[k][i] = *reinterpret_cast<const f32x4*>(src + 1024 * i);
+        mv[k] = ml[slot(gk) * kH + h];
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[k][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+        mv[k] = float2{0.f, 0.f};
+      }
+    }
+  };
   float M = -INFINITY;
   bool redo = false;
 #pragma unroll 4
   for (int g = g_lo; g <= g_hi; ++g) {   // independent loads: several in flight
     if (empty(g)) continue;
-    const float2 v = ml[slot(g) * kH + h];
-    if (v.y < 0.f) redo = true;
-    else if (v.y > 0.f) M = fmaxf(M, v.x);
+    const float2 u = ml[slot(g) * kH + h];
+    if (u.y < 0.f) redo = true;
+    else if (u.y > 0.f) M = fmaxf(M, u.x);
   }
-  f32x4 acc[16];
+  f32x4 acc[4];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < 4; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   float L = 0.f;
   if (!redo && M != -INFINITY) {
-    // slots in order, the next one's partials and (m, l) loading while the current one is
-    // accumulated; a segment with nothing visible (l = 0) holds zeros and gets weight 0
-    auto next_slot = [&](int g) {
-      while (g <= g_hi && empty(g)) ++g;
-      return g;
-    };
-    auto fetch = [&](int g, f32x4* d, float2& v) {
-      const f32x4* src = reinterpret_cast<const f32x4*>(a.part_o + slot(g) * (kH * kDC) + (size_t)w * (32 * kDC));
+    // a segment with nothing visible (l = 0) holds zeros and gets weight 0
+    for (int g = g_lo;;) {
+      fetch(g);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) d[i] = src[t + 256 * i];
-      v = ml[slot(g) * kH + h];
-    };
-    int g = next_slot(g_lo);
-    f32x4 cur[16];
-    float2 vc;
-    fetch(g, cur, vc);
-    while (g <= g_hi) {
-      const int gn = next_slot(g + 1);
-      f32x4 nxt[16];
-      float2 vn = float2{0.f, 0.f};
-      if (gn <= g_hi) fetch(gn, nxt, vn);
-      const float wg = vc.y > 0.f ? __builtin_amdgcn_exp2f(vc.x - M) : 0.0f;
-      L += vc.y > 0.f ? wg * vc.y : 0.0f;
+      for (int k = 0; k < kCombineBatch; ++k) {
+        const float wg = mv[k].y > 0.f ? __builtin_amdgcn_exp2f(mv[k].x - M) : 0.0f;
+        L += mv[k].y > 0.f ? wg * mv[k].y : 0.0f;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) acc[i] += wg * cur[i];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) cur[i] = nxt[i];
-      vc = vn;
-      g = gn;
+        for (int i = 0; i < 4; ++i) acc[i] += wg * v[k][i];
+      }
+      g += kCombineBatch;
+      if (g > g_hi) break;
     }
   }
   bool fin = __builtin_isfinite(L);
 #pragma unroll
-  for (int i = 0; i < 16; ++i)
+  for (int i = 0; i < 4; ++i)
     fin = fin && __builtin_isfinite(acc[i][0]) && __builtin_isfinite(acc[i][1]) && __builtin_isfinite(acc[i][2]) &&
           __builtin_isfinite(acc[i][3]);
   redo = redo || !fin;
   const float inv = L > 0.f ? 1.0f / L : 0.0f;
-  // piece t + 256i: block (ct, q4) = (t + 256i) / 64, lane t%64 -> columns 32ct + 8q4 + 4hl
+  // piece t + 256i is 1 KiB block 16c + t/64 + 4i = (column tile 4c + ct, quad q4) with
+  // ct = (t/64 + 4i) / 4 = i and q4 = t/64: columns 128c + 32i + 8q4 + 4hl .. +3 of head hh
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int blk = (t >> 6) + 4 * i, ct = blk >> 2, q4 = blk & 3;
-    *reinterpret_cast<f32x4*>(tile + hh * kDC + 32 * ct + 8 * q4 + 4 * hl) = acc[i] * inv;
-  }
-  if (redo) atomicOr(redo_mask, 1 << hh);
+  for (int i = 0; i < 4; ++i)
+    *reinterpret_cast<f32x4*>(tile + hh * kCombinePitch + 32 * i + 8 * (t >> 6) + 4 * hl) = acc[i] * inv;
+  if (redo) atomicOr(&redo_mask, 1 << hh);
   __syncthreads();
-  for (int i = t; i < 32 * kDC / 4; i += 256) reinterpret_cast<f32x4*>(out_row)[i] = reinterpret_cast<const f32x4*>(tile)[i];
-  if (t < 32) a.lse[(size_t)row * kH + h] = L > 0.f ? (M + __log2f(L)) * 0.69314718055994531f : -INFINITY;
-  const int mask = *redo_mask;
+  for (int i = t; i < 32 * 32; i += 256)
+    *reinterpret_cast<f32x4*>(out_base + (i >> 5) * kDC + 4 * (i & 31)) =
+        *reinterpret_cast<const f32x4*>(tile + (i >> 5) * kCombinePitch + 4 * (i & 31));
+  if (c == 0 && t < 32) a.lse[(size_t)row * kH + h] = L > 0.f ? (M + __log2f(L)) * 0.69314718055994531f : -INFINITY;
+  const int mask = redo_mask;
   if (mask) {
     __syncthreads();   // the plain results are written before any exact row replaces them
     for (int k = t >> 6; k < 32; k += 4)
-      if (mask & (1 << k)) exact_head(a, b, j, 32 * w + k, Lb, a.o_lat + ((size_t)row * kH + 32 * w + k) * kDC + 8 * lane);
+      if (mask & (1 << k)) exact_head(a, b, j, 32 * w + k, Lb, 128 * c, c == 0);
   }
 }
 
@@ -1369,12 +1405,17 @@ bool is_dsv2_shape(const mla_config_t& c);
 // unit (each holds all 160 KiB of LDS), so G = CUs / Sq, capped by the number of pages, and
 // raised where needed so that no range exceeds the LDS page table (kTabCap pages for bf16,
 // kTabCap8 for fp8: the pages of the batch are at most B * max_blocks).
+// Per-segment overhead in pages for cutting the ranges, fitted to measured workgroup times (a
+// range with one more segment ran ~20K cycles longer: ~3 bf16 pages, ~2 fp8 pages).
+constexpr int kSegCost = 3, kSegCost8 = 2;
+
 int decode_num_ranges(int num_cus, int B, int Sq, int max_blocks, bool fp8) {
   const long long cap = (long long)B * max_blocks;
   const int tab = fp8 ? kTabCap8 : kTabCap;
   long long G = num_cus / (Sq > 0 ? Sq : 1);
   if (G < 1) G = 1;
-  const long long need = (cap + tab - 1) / tab;
+  // a range owns at most ceil(C / G) pages, C <= B (max_blocks + w) the total cost
+  const long long need = ((long long)B * (max_blocks + (fp8 ? kSegCost8 : kSegCost)) + tab - 1) / tab;
   if (G < need) G = need;
   if (cap < G) G = cap < 1 ? 1 : cap;
   return (int)G;
@@ -1416,6 +1457,7 @@ hipError_t launch_decode(const mla_config_t& cfg, int num_cus, const void* q_abs
     a.G = G;
     a.scale_log2 = scale * 1.4426950408889634f;
     a.fp8 = fp8 ? 1 : 0;
+    a.seg_w = fp8 ? kSegCost8 : kSegCost;
     static bool attr_set = false;   // idempotent; races only repeat the same call
     if (!attr_set) {
       const void* kernels[4] = {(const void*)decode_mfma_bf16_kernel<0>, (const void*)decode_mfma_bf16_kernel<2>,
@@ -1445,14 +1487,7 @@ hipError_t launch_decode(const mla_config_t& cfg, int num_cus, const void* q_abs
       if (e != hipSuccess) return e;
     }
     if (phases & 2) {
-      static bool cattr = false;
-      if (!cattr) {
-        hipError_t e = hipFuncSetAttribute((const void*)combine_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                           kCombineLds);
-        if (e != hipSuccess) return e;
-        cattr = true;
-      }
-      hipLaunchKernelGGL(combine_kernel, dim3(B * Sq, kH / 32), dim3(256), kCombineLds, stream, a);
+      hipLaunchKernelGGL(combine_kernel, dim3(B * Sq, kH / 32, 4), dim3(256), 0, stream, a);
     }
     return hipGetLastError();
   }
