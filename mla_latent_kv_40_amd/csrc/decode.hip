@@ -246,6 +246,10 @@ __device__ __forceinline__ u32x4 lds_b128(uint32_t addr) {
   const MLA_LDS u32x4* __restrict__ p = (const MLA_LDS u32x4*)(size_t)addr;
   return *p;
 }
+__device__ __forceinline__ uint32_t lds_u16(uint32_t addr) {
+  const MLA_LDS uint16_t* __restrict__ p = (const MLA_LDS uint16_t*)(size_t)addr;
+  return *p;
+}
 __device__ __forceinline__ bf16x4 lds_tr16(const uint8_t* __restrict__ base, uint32_t off) {
   const MLA_LDS uint8_t* __restrict__ lb = (const MLA_LDS uint8_t*)base;
   return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)(lb + off));
@@ -752,7 +756,8 @@ constexpr int kPage8 = kBlock * kRow;                // 36864: one page of codes
 constexpr int kStage8 = kPage8 + kWaves * 256;       // + one copy of the page's 64 scales per wave
 constexpr int kTabOff8 = kStages * kStage8;          // 151552
 constexpr int kTabCap8 = 512;
-constexpr int kDecodeLds8 = kTabOff8 + 16 * kTabCap8;   // 159744
+constexpr int kSrcTab8 = kTabOff8 + 16 * kTabCap8;   // 159744: per-lane source offsets of the row loads
+constexpr int kDecodeLds8 = kSrcTab8 + 2 * 9 * 64 * 2;   // 162048
 constexpr int kE8M0One = 127;                        // E8M0 code of 1.0
 
 // LDS layout of a page of codes: row r (576 B = 36 chunks of 16 B) at 576r, chunk c stored at
@@ -801,12 +806,19 @@ __device__ __forceinline__ int page8_src(int wave, int i, int lane) {
   const int r = ch / 36, pos = ch - 36 * r;
   return r * kRow + 16 * (pos ^ key8(r));
 }
+// Wave w's nine row loads cover rows 16w .. 16w+15 (9 x 64 chunks = 16 rows of 36), so their
+// source offsets are 16w rows (the scalar offset) plus a per-lane part that depends on w only
+// through the parity of w (row bit 4 enters key8).  That part, below 9216, is computed once per
+// workgroup into an LDS table [w%2][i][lane] of 16-bit entries; a load then reads its entry
+// (one LDS read) instead of recomputing the division and the key.
+__device__ __forceinline__ int page8_src_lane(int par, int i, int lane) {
+  return page8_src(par, i, lane) - 16 * par * kRow;
+}
 template <int Aux>
-__device__ __forceinline__ void load_row8(const PageLoad8& p, int i, int wave, int lane) {
-  asm volatile("" : "+v"(lane));   // rebuild the per-lane offset here rather than keep it live
+__device__ __forceinline__ void load_row8(const PageLoad8& p, int i, int wave, int lane, int off) {
   if (i < 9) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(p.rows, (MLA_LDS void*)(p.stage + 1024 * (9 * wave + i)), 16,
-                                             page8_src(wave, i, lane), 0, 0, Aux);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(p.rows, (MLA_LDS void*)(p.stage + 1024 * (9 * wave + i)), 16, off,
+                                             16 * kRow * wave, 0, Aux);
   } else {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(p.scales, (MLA_LDS void*)(p.stage + kPage8 + 256 * wave), 4, 4 * lane,
                                              0, 0, Aux);
@@ -840,6 +852,11 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_fp8_kernel(DecodeArgs a) {
   int b0;
   if (!range_pages(a, g, &x0, &x1, &b0, &s_first)) return;
   const int n_steps = (int)(x1 - x0 < kTabCap8 ? x1 - x0 : kTabCap8);   // pages of this range
+  {
+    uint16_t* st = reinterpret_cast<uint16_t*>(smem + kSrcTab8);
+    for (int e = threadIdx.x; e < 2 * 9 * 64; e += 256) st[e] = (uint16_t)page8_src_lane(e / 576, (e / 64) % 9, e % 64);
+  }
+  // (the table build's barriers also publish the source-offset table)
   build_page_table(a, smem, reinterpret_cast<int4*>(smem + kTabOff8), n_steps, x0, b0, s_first);   // stage 0 scratch
 
   // The folded query (bf16) becomes two e4m3 operands per K-step: with s = amax/448 over the
@@ -1059,9 +1076,15 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_fp8_kernel(DecodeArgs a) {
   auto load_for = [&](int stage, int pg, int nv) {
     return page_load8(smem + stage * kStage8, a.cache, a.cache_scale, nv > 0 ? pg : 0, nv);
   };
+  // this lane's entry of row load i in the source-offset table
+  const uint32_t src_addr = lds_addr(smem + kSrcTab8) + (uint32_t)(1152 * (wave & 1) + 2 * lane);
+  auto src_off = [&](int i) -> int { return (int)lds_u16(src_addr + 128u * (uint32_t)i); };
   auto issue = [&](const PageLoad8& pl) {
+    int off[9];
 #pragma unroll
-    for (int i = 0; i < 10; ++i) load_row8<Aux>(pl, i, wave, lane);
+    for (int i = 0; i < 9; ++i) off[i] = src_off(i);
+#pragma unroll
+    for (int i = 0; i < 10; ++i) load_row8<Aux>(pl, i, wave, lane, i < 9 ? off[i] : 0);
   };
   const uint32_t tab_addr = lds_addr(smem + kTabOff8);
   auto entry = [&](int z) -> int4 {
@@ -1106,9 +1129,15 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_fp8_kernel(DecodeArgs a) {
     values(smem + (y & 3) * kStage8, pf, psb);
     const uint8_t* next = smem + ((y + 1) & 3) * kStage8;
     f32x16 s0, s1;
+    // row load k goes out after score MFMA 4k, its table entry having been read one load ahead
+    int off_next = src_off(0);
     scores(next, [&](int st) {   // stale data if !has_next
-      if ((st & 3) == 0) load_row8<Aux>(pl, st >> 2, wave, lane);   // st = 0, 4, .., 32
-      if (st == 34) load_row8<Aux>(pl, 9, wave, lane);
+      if ((st & 3) == 0) {   // st = 0, 4, .., 32
+        const int k = st >> 2, off = off_next;
+        if (k + 1 < 9) off_next = src_off(k + 1);
+        load_row8<Aux>(pl, k, wave, lane, off);
+      }
+      if (st == 34) load_row8<Aux>(pl, 9, wave, lane, 0);
     }, s0, s1);
     const float m_old = m_ref, l_old = l_run;
     const bool over_old = over;
