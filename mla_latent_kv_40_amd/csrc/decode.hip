@@ -944,7 +944,7 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_fp8_kernel(DecodeArgs a) {
     }
     // fragment f = (K-step f/2, token block f%2) feeds two consecutive MFMAs (hi, lo); the next
     // two fragments are read ahead
-    constexpr int D = 2;
+    constexpr int D = 1;
     i32x8 kr[D + 1];
 #pragma unroll
     for (int d = 0; d < D; ++d) kr[d] = kfrag(d);
@@ -964,71 +964,109 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_fp8_kernel(DecodeArgs a) {
   };
 
   // ---- softmax of one page: raw scores -> e4m3 Pt and the B block scale, against the segment
-  // reference (log2 units).  y = raw * token scale; log2-domain score = kq * y.
+  // reference (log2 units).  y = raw * token scale; log2-domain score = kq * y.  It runs in
+  // pieces -1 .. 22: -1 .. 5 scale the scores and find the page maximum and the block-scale
+  // exponent as one block; 6 .. 21 each turn two scores into probabilities and e4m3 Pt, and in
+  // the steps piece 6 + c follows value MFMA c of the previous page, so that their vector
+  // instructions issue in the shadow of the 16-pass matrix instructions (about ten per MFMA
+  // cost a fraction of what they cost as one block); 22 finishes.  Scales are read one piece
+  // ahead of their use.
   struct Soft {
     float m_new, l_new;
     bool over_new;
     i32x8 p;
     int sb;
   };
-  auto softmax = [&](f32x16& s0, f32x16& s1, const uint8_t* tile, int vis, bool fresh, Soft& st) {
-    const uint32_t sbase = lds_addr(tile) + kPage8 + 256 * wave + 16 * hl;
-    // scales of tokens 32tb + 8u + 4hl + 0..3 (block d = 4tb + u); read where they are used
-    auto scales = [&](int d) { return __builtin_bit_cast(f32x4, lds_b128(sbase + 128 * (d >> 2) + 32 * (d & 3))); };
-    float cm = 0.f;
-#pragma unroll
-    for (int d = 0; d < 8; ++d) {
-      const f32x4 c4 = scales(d);
-      f32x16& sv = (d < 4) ? s0 : s1;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        sv[4 * (d & 3) + k] *= c4[k];
-        cm = fmaxf(cm, c4[k]);
-      }
-    }
-    if (vis < kBlock - 1) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int t = 8 * (i >> 2) + 4 * hl + (i & 3);
-        if (t > vis) s0[i] = -INFINITY;
-        if (t + 32 > vis) s1[i] = -INFINITY;
-      }
-    }
-    float mx = fmaxf(s0[0], s1[0]);
-#pragma unroll
-    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, fmaxf(s0[i], s1[i]));
-    const float tmax = pair_max(mx) * kq;
-    cm = pair_max(cm);
-    const float m_in = fresh ? -INFINITY : m_ref;
-    st.m_new = (m_in == -INFINITY) ? tmax : m_in;
-    st.over_new = (fresh ? false : over) || (tmax > st.m_new + kRescaleLog2);
-    const float m_use = (st.m_new == -INFINITY) ? 0.0f : st.m_new;
-    // largest Pt of the page <= 2^(tmax - m) * max scale < 2^frexp_exp(...): shift it to <= 256
-    int e = __builtin_amdgcn_frexp_expf(__builtin_amdgcn_exp2f(tmax - m_use) * cm) - 8;
-    e = e < -120 ? -120 : (e > 120 ? 120 : e);
-    const float neg = -(m_use + (float)e);
-    float lsum = 0.f;
+  struct SoftState {
+    uint32_t cmu;   // largest token scale of the page (non-negative floats order as integers)
+    float mx;       // largest y of this lane's tokens
+    float neg;      // -(reference + e)
+    int e;          // block-scale exponent of Pt
+    float lsum;
+    f32x4 c[2];     // scales: in use / in flight
+    int w;          // first half of a block's packed Pt
     int pk[8];
-#pragma unroll
-    for (int d = 0; d < 8; ++d) {
-      const f32x16& sv = (d < 4) ? s0 : s1;
-      const f32x4 c4 = scales(d);
-      float u[4];
+  };
+  auto soft_piece = [&](int p, f32x16& s0, f32x16& s1, const uint8_t* tile, int vis, bool fresh, SoftState& q,
+                        Soft& st) {
+    const uint32_t sbase = lds_addr(tile) + kPage8 + 256 * wave + 16 * hl;
+    // scales of tokens 32tb + 8u + 4hl + 0..3 (block d = 4tb + u)
+    auto scales = [&](int d) { return __builtin_bit_cast(f32x4, lds_b128(sbase + 128 * (d >> 2) + 32 * (d & 3))); };
+    auto umax = [](uint32_t x, uint32_t y) { return x > y ? x : y; };
+    if (p == -1) {
+      q.c[0] = scales(0);
+      q.c[1] = scales(1);
+      q.cmu = 0;
+    } else if (p < 4) {   // y of blocks 2p, 2p+1 (elements 8(p&1) .. +7 of s0 or s1)
+      f32x16& sv = p < 2 ? s0 : s1;
+      const f32x4 ca = q.c[0], cb = q.c[1];
+      if (p < 3) {
+        q.c[0] = scales(2 * p + 2);
+        q.c[1] = scales(2 * p + 3);
+      }
+      const int i0 = 8 * (p & 1);
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        u[k] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[4 * (d & 3) + k], kq, neg));
-        lsum += u[k];
+        sv[i0 + k] *= ca[k];
+        sv[i0 + 4 + k] *= cb[k];
       }
-      int w = __builtin_amdgcn_cvt_pk_fp8_f32(u[0] * c4[0], u[1] * c4[1], 0, false);
-      pk[d] = __builtin_amdgcn_cvt_pk_fp8_f32(u[2] * c4[2], u[3] * c4[3], w, true);
+      uint32_t m = q.cmu;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) m = umax(m, umax(__float_as_uint(ca[k]), __float_as_uint(cb[k])));
+      q.cmu = m;
+    } else if (p == 4) {
+      if (vis < kBlock - 1) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int t = 8 * (i >> 2) + 4 * hl + (i & 3);
+          if (t > vis) s0[i] = -INFINITY;
+          if (t + 32 > vis) s1[i] = -INFINITY;
+        }
+      }
+      float mx = s0[0];
+#pragma unroll
+      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s0[i]);
+      q.mx = mx;
+    } else if (p == 5) {
+      float mx = q.mx;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s1[i]);
+      const float tmax = pair_max(mx) * kq;
+      const float cm = pair_max(__uint_as_float(q.cmu));
+      const float m_in = fresh ? -INFINITY : m_ref;
+      st.m_new = (m_in == -INFINITY) ? tmax : m_in;
+      st.over_new = (fresh ? false : over) || (tmax > st.m_new + kRescaleLog2);
+      const float m_use = (st.m_new == -INFINITY) ? 0.0f : st.m_new;
+      // largest Pt of the page <= 2^(tmax - m) * max scale < 2^frexp_exp(...): shift it to <= 256
+      int e = __builtin_amdgcn_frexp_expf(__builtin_amdgcn_exp2f(tmax - m_use) * cm) - 8;
+      e = e < -120 ? -120 : (e > 120 ? 120 : e);
+      q.e = e;
+      q.neg = -(m_use + (float)e);
+      q.lsum = 0.f;
+      q.c[1] = scales(0);
+    } else if (p < 22) {   // tokens 2h, 2h+1 of block d = h/2 (h = p - 6)
+      const int h = p - 6, d = h >> 1, k0 = 2 * (h & 1);
+      const f32x16& sv = (d < 4) ? s0 : s1;
+      if ((h & 1) == 0) {
+        q.c[0] = q.c[1];
+        if (d + 1 < 8) q.c[1] = scales(d + 1);
+      }
+      const f32x4 c4 = q.c[0];
+      const float u0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[4 * (d & 3) + k0], kq, q.neg));
+      const float u1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[4 * (d & 3) + k0 + 1], kq, q.neg));
+      q.lsum += u0;
+      q.lsum += u1;
+      if ((h & 1) == 0) q.w = __builtin_amdgcn_cvt_pk_fp8_f32(u0 * c4[0], u1 * c4[1], 0, false);
+      else q.pk[d] = __builtin_amdgcn_cvt_pk_fp8_f32(u0 * c4[2], u1 * c4[3], q.w, true);
+    } else if (p == 22) {
+      st.l_new = (fresh ? 0.0f : l_run) + __builtin_ldexpf(q.lsum, q.e);
+      st.p = i32x8{q.pk[0], q.pk[1], q.pk[2], q.pk[3], q.pk[4], q.pk[5], q.pk[6], q.pk[7]};
+      st.sb = q.e + kE8M0One;
     }
-    st.l_new = (fresh ? 0.0f : l_run) + __builtin_ldexpf(lsum, e);
-    st.p = i32x8{pk[0], pk[1], pk[2], pk[3], pk[4], pk[5], pk[6], pk[7]};
-    st.sb = e + kE8M0One;
   };
 
   // ---- O^T += Codes^T . Pt^T for the page in `tile`
-  auto values = [&](const uint8_t* tile, const i32x8& pf, int sb) {
+  auto values = [&](const uint8_t* tile, const i32x8& pf, int sb, auto hook) {
     o_fence<3>(oacc);
     int ln = lane;
     asm volatile("" : "+v"(ln));
@@ -1049,15 +1087,17 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_fp8_kernel(DecodeArgs a) {
       const i32x2 t3 = lds_tr8(xv[2 + (ct & 1)], o + 32 * kRow);
       return i32x8{t0[0], t0[1], t1[0], t1[1], t2[0], t2[1], t3[0], t3[1]};
     };
-    constexpr int D = 2;
+    constexpr int D = 1;
     i32x8 vr[D + 1];
 #pragma unroll
     for (int d = 0; d < D; ++d) vr[d] = vfrag(d);
+    hook(-1);
 #pragma unroll
     for (int ct = 0; ct < 16; ++ct) {
       if (ct + D < 16) vr[(ct + D) % (D + 1)] = vfrag(ct + D);
       __builtin_amdgcn_sched_barrier(0);
       mfma8_acc(oacc[ct], vr[ct % (D + 1)], pf, one, sb);
+      hook(ct);
       __builtin_amdgcn_sched_barrier(0);
     }
     o_fence<20>(oacc);
@@ -1110,7 +1150,9 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_fp8_kernel(DecodeArgs a) {
   {
     f32x16 s0, s1;
     scores(smem, [](int) {}, s0, s1);
-    softmax(s0, s1, smem, last_visible(e0), true, sm);
+    SoftState ss;
+#pragma unroll
+    for (int p = -1; p < 23; ++p) soft_piece(p, s0, s1, smem, last_visible(e0), true, ss, sm);
     soft_commit(sm);
   }
 
@@ -1125,8 +1167,8 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_fp8_kernel(DecodeArgs a) {
       load_q(e1.z);
       __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     }
-    // values of page y first, so that its probabilities are dead before the scores of y+1
-    values(smem + (y & 3) * kStage8, pf, psb);
+    // scores of page y+1, then the values of page y with the softmax of page y+1 spread over
+    // its MFMAs
     const uint8_t* next = smem + ((y + 1) & 3) * kStage8;
     f32x16 s0, s1;
     // row load k goes out after score MFMA 4k, its table entry having been read one load ahead
@@ -1141,7 +1183,14 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_fp8_kernel(DecodeArgs a) {
     }, s0, s1);
     const float m_old = m_ref, l_old = l_run;
     const bool over_old = over;
-    softmax(s0, s1, next, last_visible(e1), seg_end, sm);
+    const int vis = last_visible(e1);
+    SoftState ss;
+#pragma unroll
+    for (int p = -1; p < 6; ++p) soft_piece(p, s0, s1, next, vis, seg_end, ss, sm);
+    values(smem + (y & 3) * kStage8, pf, psb, [&](int c) {
+      if (c >= 0) soft_piece(c + 6, s0, s1, next, vis, seg_end, ss, sm);
+    });
+    soft_piece(22, s0, s1, next, vis, seg_end, ss, sm);
 
     if (seg_end) {
       const float l_tot = pair_sum(l_old);
