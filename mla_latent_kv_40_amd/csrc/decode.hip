@@ -1056,8 +1056,15 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_fp8_kernel(DecodeArgs a) {
       const float u1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[4 * (d & 3) + k0 + 1], kq, q.neg));
       q.lsum += u0;
       q.lsum += u1;
-      if ((h & 1) == 0) q.w = __builtin_amdgcn_cvt_pk_fp8_f32(u0 * c4[0], u1 * c4[1], 0, false);
-      else q.pk[d] = __builtin_amdgcn_cvt_pk_fp8_f32(u0 * c4[2], u1 * c4[3], q.w, true);
+      // the empty asm statements pin the piece between its MFMAs (otherwise the compiler sinks
+      // this arithmetic below the loop, next to the first use of its results)
+      if ((h & 1) == 0) {
+        q.w = __builtin_amdgcn_cvt_pk_fp8_f32(u0 * c4[0], u1 * c4[1], 0, false);
+        asm volatile("" : "+v"(q.lsum), "+v"(q.w));
+      } else {
+        q.pk[d] = __builtin_amdgcn_cvt_pk_fp8_f32(u0 * c4[2], u1 * c4[3], q.w, true);
+        asm volatile("" : "+v"(q.lsum), "+v"(q.pk[d]));
+      }
     } else if (p == 22) {
       st.l_new = (fresh ? 0.0f : l_run) + __builtin_ldexpf(q.lsum, q.e);
       st.p = i32x8{q.pk[0], q.pk[1], q.pk[2], q.pk[3], q.pk[4], q.pk[5], q.pk[6], q.pk[7]};
