@@ -490,6 +490,9 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_bf16_kernel(DecodeArgs a) 
   // 4ct + 2(gg&1) + uu/2, byte 8(uu&1)
   const uint32_t vb = (uint32_t)((4 * hl + ((lane & 15) >> 2)) * 1024 + 8 * (lane & 1)) |
                       (uint32_t)(16 * ((2 * ((lane >> 4) & 1) + ((lane >> 1) & 1)) ^ (4 * ((lane & 15) >> 2)) ^ hl));
+  uint32_t vbx[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) vbx[e] = vb ^ (64u * (e & 3) ^ 32u * (e >> 2));
   auto scores = [&](const uint8_t* tile, auto hook) -> f32x16 {
     // the eight swizzle variants of this lane's row address, stage offset included once (the
     // XOR touches bits 5..7 only and stages start at multiples of 256); the rest of each
@@ -567,11 +570,12 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_bf16_kernel(DecodeArgs a) 
   // ---- O^T += V^T . P^T for the half page in `tile`
   auto values = [&](const uint8_t* tile, const bf16x8* pf) {
     o_fence<3>(oacc);   // MFMA writes of O settled
-    // eight swizzle variants (column tile mod 4, token half E), stage offset included once
-    const uint32_t T = (uint32_t)(tile - smem);   // stage offset, a multiple of 256
+    // eight swizzle variants (column tile mod 4, token half E): the stage offset T is a multiple
+    // of 256 and the XOR touches bits 5..7 only, so (vb + T) ^ c = (vb ^ c) + T with vb ^ c
+    // loop-invariant
     const uint8_t* xv[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) xv[e] = smem + ((vb + T) ^ (64u * (e & 3) ^ 32u * (e >> 2)));
+    for (int e = 0; e < 8; ++e) xv[e] = tile + vbx[e];
     auto vfrag = [&](int it) -> bf16x8 {
       const int k = it >> 4, ct = it & 15;
       const bf16x4 lo = lds_tr16(xv[ct & 3], 16384u * k + 256u * (ct >> 2));
