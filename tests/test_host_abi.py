@@ -28,7 +28,7 @@ def test_exports_every_declared_symbol(L):
     assert set(syms) == set(B.EXPORTS), syms
     for s in syms:
         assert hasattr(L, s), s
-    assert B.mla_abi_version() == 2
+    assert B.mla_abi_version() == B.ABI_VERSION == 2
 
 
 def cfg(**kw):
