@@ -41,7 +41,7 @@ struct DecodeArgs {
   const int32_t* kv_lens;     // [B]
   float* o_lat;               // [T, H, 512]
   float* lse;                 // [T, H]
-  float* part_o;              // [slots*Sq] x 256 KiB unnormalised segment outputs (register order)
+  uint16_t* part_o;           // [slots*Sq] x 128 KiB unnormalised segment outputs, bf16 (register order)
   float* part_ml;             // [slots*Sq, H, 2]   (reference max m in log2 units, l)
   int num_blocks, max_blocks, B, Sq, G;
   float scale_log2;           // softmax_scale * log2(e)
@@ -299,6 +299,42 @@ __device__ __forceinline__ void o_fence(f32x16* o) {
                  : "i"(N - 1));
 }
 
+// A segment's unnormalised O in bf16 (fp32 range, relative rounding 2^-9; the segments of a
+// sequence are summed in fp32 by the combine), in register order: lane l's oacc[ct][8qp .. +7]
+// (columns 32ct + 8(2qp) + 4hl + 0..3 and 32ct + 8(2qp + 1) + 4hl + 0..3 of its head) goes to
+// 1 KiB block 2ct + qp at 16 bytes per lane, so every store writes 1 KiB contiguously.
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t cvt_bf16x2(float lo, float hi) {   // v_cvt_pk_bf16_f32, nearest-even
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
+}
+__device__ __forceinline__ f32x16 read_acc(const f32x16& x) {   // accumulation registers -> VGPRs
+  f32x16 r;
+  asm volatile("v_accvgpr_read_b32 %0, %16\n\tv_accvgpr_read_b32 %1, %17\n\tv_accvgpr_read_b32 %2, %18\n\t"
+               "v_accvgpr_read_b32 %3, %19\n\tv_accvgpr_read_b32 %4, %20\n\tv_accvgpr_read_b32 %5, %21\n\t"
+               "v_accvgpr_read_b32 %6, %22\n\tv_accvgpr_read_b32 %7, %23\n\tv_accvgpr_read_b32 %8, %24\n\t"
+               "v_accvgpr_read_b32 %9, %25\n\tv_accvgpr_read_b32 %10, %26\n\tv_accvgpr_read_b32 %11, %27\n\t"
+               "v_accvgpr_read_b32 %12, %28\n\tv_accvgpr_read_b32 %13, %29\n\tv_accvgpr_read_b32 %14, %30\n\t"
+               "v_accvgpr_read_b32 %15, %31"
+               : "=v"(r[0]), "=v"(r[1]), "=v"(r[2]), "=v"(r[3]), "=v"(r[4]), "=v"(r[5]), "=v"(r[6]), "=v"(r[7]),
+                 "=v"(r[8]), "=v"(r[9]), "=v"(r[10]), "=v"(r[11]), "=v"(r[12]), "=v"(r[13]), "=v"(r[14]), "=v"(r[15])
+               : "a"(x[0]), "a"(x[1]), "a"(x[2]), "a"(x[3]), "a"(x[4]), "a"(x[5]), "a"(x[6]), "a"(x[7]), "a"(x[8]),
+                 "a"(x[9]), "a"(x[10]), "a"(x[11]), "a"(x[12]), "a"(x[13]), "a"(x[14]), "a"(x[15]));
+  return r;
+}
+__device__ __forceinline__ void store_partial(uint16_t* so, const f32x16* oacc) {
+#pragma unroll
+  for (int ct = 0; ct < 16; ++ct) {
+    __builtin_amdgcn_sched_barrier(0);   // one column tile at a time: few registers in flight
+    const f32x16 o = read_acc(oacc[ct]);
+#pragma unroll
+    for (int qp = 0; qp < 2; ++qp)
+      *reinterpret_cast<u32x4*>(so + 512 * (2 * ct + qp)) =
+          u32x4{cvt_bf16x2(o[8 * qp], o[8 * qp + 1]), cvt_bf16x2(o[8 * qp + 2], o[8 * qp + 3]),
+                cvt_bf16x2(o[8 * qp + 4], o[8 * qp + 5]), cvt_bf16x2(o[8 * qp + 6], o[8 * qp + 7])};
+  }
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 // ---- page table of the range, built once in LDS: entry k describes range page k
 //   pg     page id in the cache (out-of-range ids are treated as holding no valid token)
 //   r      tokens from the page's first row to the end of its sequence (kv_len - 64 tb)
@@ -470,8 +506,8 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_bf16_kernel(DecodeArgs a) 
   // this lane's part of workspace slot (g + b, j), stored in register order: wave block of
   // 64 KiB, then (column tile ct, quad q4) blocks of 1 KiB, then 16 bytes per lane, so that
   // every store instruction writes 1 KiB contiguously
-  auto slot_o = [&](int bb) -> float* {
-    return a.part_o + ((size_t)(g + bb) * a.Sq + j) * (kH * kDC) + (size_t)wave * (32 * kDC) + 4 * lane;
+  auto slot_o = [&](int bb) -> uint16_t* {
+    return a.part_o + ((size_t)(g + bb) * a.Sq + j) * (kH * kDC) + (size_t)wave * (32 * kDC) + 8 * lane;
   };
 
   f32x16 oacc[16];
@@ -699,15 +735,9 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_bf16_kernel(DecodeArgs a) 
       const bool over_seg = pair_sum(over_old ? 1.0f : 0.0f) > 0.0f;   // either half of the head
       const size_t row = ((size_t)(g + e0.z) * a.Sq + j) * kH + head;
       if (hl == 0) reinterpret_cast<float2*>(a.part_ml)[row] = float2{m_old, over_seg ? -1.0f : l_tot};
-      float* so = slot_o(e0.z);
+      uint16_t* so = slot_o(e0.z);
       o_fence<20>(oacc);   // results of the last accumulation settled before the stores
-      // oacc[ct][4q4 + i] is column 32ct + 8q4 + 4hl + i of this lane's head
-#pragma unroll
-      for (int ct = 0; ct < 16; ++ct)
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4)
-          *reinterpret_cast<f32x4*>(so + 256 * (4 * ct + q4)) =
-              f32x4{oacc[ct][4 * q4], oacc[ct][4 * q4 + 1], oacc[ct][4 * q4 + 2], oacc[ct][4 * q4 + 3]};
+      store_partial(so, oacc);
       if (has_next) {
 #pragma unroll
         for (int t = 0; t < 16; ++t) mfma_zero(oacc[t], zero8);
@@ -914,8 +944,8 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_fp8_kernel(DecodeArgs a) {
       qlo[k] = i32x8{lw[0], lw[1], lw[2], lw[3], lw[4], lw[5], lw[6], lw[7]};
     }
   };
-  auto slot_o = [&](int bb) -> float* {
-    return a.part_o + ((size_t)(g + bb) * a.Sq + j) * (kH * kDC) + (size_t)wave * (32 * kDC) + 4 * lane;
+  auto slot_o = [&](int bb) -> uint16_t* {
+    return a.part_o + ((size_t)(g + bb) * a.Sq + j) * (kH * kDC) + (size_t)wave * (32 * kDC) + 8 * lane;
   };
 
   f32x16 oacc[16];
@@ -1207,13 +1237,8 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_fp8_kernel(DecodeArgs a) {
       const float l_tot = pair_sum(l_old);
       const size_t row = ((size_t)(g + e0.z) * a.Sq + j) * kH + head;
       if (hl == 0) reinterpret_cast<float2*>(a.part_ml)[row] = float2{m_old, over_old ? -1.0f : l_tot};
-      float* so = slot_o(e0.z);
-#pragma unroll
-      for (int ct = 0; ct < 16; ++ct)
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4)
-          *reinterpret_cast<f32x4*>(so + 256 * (4 * ct + q4)) =
-              f32x4{oacc[ct][4 * q4], oacc[ct][4 * q4 + 1], oacc[ct][4 * q4 + 2], oacc[ct][4 * q4 + 3]};
+      uint16_t* so = slot_o(e0.z);
+      store_partial(so, oacc);
       if (has_next) {
 #pragma unroll
         for (int t = 0; t < 16; ++t) mfma_zero(oacc[t], zero8);
@@ -1337,22 +1362,22 @@ __global__ void __launch_bounds__(256) combine_kernel(DecodeArgs a) {
   auto empty = [&](int g) { return (long long)g * C_all / a.G == (long long)(g + 1) * C_all / a.G; };
   const float2* ml = reinterpret_cast<const float2*>(a.part_ml);
   auto slot = [&](int g) { return ((size_t)(g + b) * a.Sq + j); };
-  // partials and (m, l) of the slots g .. g + kCombineBatch - 1 (zeros past g_hi)
-  const size_t piece = (size_t)w * (32 * kDC) + (size_t)c * (16 * 256) + 4 * t;
-  f32x4 v[kCombineBatch][4];
+  // partials (bf16) and (m, l) of the slots g .. g + kCombineBatch - 1 (zeros past g_hi)
+  const size_t piece = (size_t)w * (32 * kDC) + (size_t)c * (8 * 512) + 8 * t;
+  u32x4 v[kCombineBatch][2];
   float2 mv[kCombineBatch];
   auto fetch = [&](int g) {
 #pragma unroll
     for (int k = 0; k < kCombineBatch; ++k) {
       const int gk = g + k;
       if (gk <= g_hi && !empty(gk)) {
-        const float* src = a.part_o + slot(gk) * (kH * kDC) + piece;
+        const uint16_t* src = a.part_o + slot(gk) * (kH * kDC) + piece;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) v[k][i] = *reinterpret_cast<const f32x4*>(src + 1024 * i);
+        for (int i = 0; i < 2; ++i) v[k][i] = *reinterpret_cast<const u32x4*>(src + 2048 * i);
         mv[k] = ml[slot(gk) * kH + h];
       } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) v[k][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int i = 0; i < 2; ++i) v[k][i] = u32x4{0u, 0u, 0u, 0u};
         mv[k] = float2{0.f, 0.f};
       }
     }
@@ -1379,7 +1404,12 @@ __global__ void __launch_bounds__(256) combine_kernel(DecodeArgs a) {
         const float wg = mv[k].y > 0.f ? __builtin_amdgcn_exp2f(mv[k].x - M) : 0.0f;
         L += mv[k].y > 0.f ? wg * mv[k].y : 0.0f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[i] += wg * v[k][i];
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            acc[2 * i + (e >> 1)][2 * (e & 1)] += wg * __uint_as_float(v[k][i][e] << 16);
+            acc[2 * i + (e >> 1)][2 * (e & 1) + 1] += wg * __uint_as_float(v[k][i][e] & 0xFFFF0000u);
+          }
       }
       g += kCombineBatch;
       if (g > g_hi) break;
@@ -1392,11 +1422,14 @@ __global__ void __launch_bounds__(256) combine_kernel(DecodeArgs a) {
           __builtin_isfinite(acc[i][3]);
   redo = redo || !fin;
   const float inv = L > 0.f ? 1.0f / L : 0.0f;
-  // piece t + 256i is 1 KiB block 16c + t/64 + 4i = (column tile 4c + ct, quad q4) with
-  // ct = (t/64 + 4i) / 4 = i and q4 = t/64: columns 128c + 32i + 8q4 + 4hl .. +3 of head hh
+  // piece t + 256i is 1 KiB block 8c + bq, bq = t/64 + 4i = 2ct + qp (column tile 4c + ct):
+  // acc[2i] holds columns 128c + 32ct + 16qp + 4hl .. +3 of head hh, acc[2i+1] the same + 8
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    *reinterpret_cast<f32x4*>(tile + hh * kCombinePitch + 32 * i + 8 * (t >> 6) + 4 * hl) = acc[i] * inv;
+  for (int i = 0; i < 2; ++i) {
+    const int bq = (t >> 6) + 4 * i, col = 32 * (bq >> 1) + 16 * (bq & 1) + 4 * hl;
+    *reinterpret_cast<f32x4*>(tile + hh * kCombinePitch + col) = acc[2 * i] * inv;
+    *reinterpret_cast<f32x4*>(tile + hh * kCombinePitch + col + 8) = acc[2 * i + 1] * inv;
+  }
   if (redo) atomicOr(&redo_mask, 1 << hh);
   __syncthreads();
   for (int i = t; i < 32 * 32; i += 256)
@@ -1514,7 +1547,7 @@ size_t decode_workspace_bytes(const mla_config_t& cfg, int num_cus, int B, int S
   if (!(cfg.cache_dtype != MLA_F32 && is_dsv2_shape(cfg))) return 256;   // generic path: none needed
   const int G = decode_num_ranges(num_cus, B, Sq, max_blocks, cfg.cache_dtype == MLA_FP8_E4M3);
   const size_t slots = (size_t)(G + B - 1) * Sq;
-  const size_t o_bytes = slots * kH * kDC * sizeof(float);
+  const size_t o_bytes = slots * kH * kDC * sizeof(uint16_t);
   const size_t l_bytes = slots * kH * 2 * sizeof(float);
   return ((o_bytes + 255) & ~(size_t)255) + ((l_bytes + 255) & ~(size_t)255);
 }
@@ -1536,9 +1569,9 @@ hipError_t launch_decode(const mla_config_t& cfg, int num_cus, const void* q_abs
     a.lse = lse;
     const int G = decode_num_ranges(num_cus, B, Sq, max_blocks, fp8);
     const size_t slots = (size_t)(G + B - 1) * Sq;
-    a.part_o = static_cast<float*>(workspace);
+    a.part_o = static_cast<uint16_t*>(workspace);
     a.part_ml = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) +
-                                          ((slots * kH * kDC * sizeof(float) + 255) & ~(size_t)255));
+                                          ((slots * kH * kDC * sizeof(uint16_t) + 255) & ~(size_t)255));
     a.num_blocks = num_blocks;
     a.max_blocks = max_blocks;
     a.B = B;
