@@ -34,8 +34,10 @@ struct RopeTheta {
 // q_abs[t, h, 128qc + c'] for c' < 128: wave w computes columns 128qc + 32w .. +31 with its
 // eight weight fragments (K = d_h = 128) held in registers, B[k = d, n = c] = W_UK[c, h, d]
 // (16 contiguous bytes per lane); A[m = t, k = d] = q^C[t, h, d].  Quarter qc also rotates the
-// positional part of the rows t with t % 4 == qc.  The loads of the next pass are issued
-// before the current pass's results are written.
+// positional part of the rows t with t % 4 == qc.  Every load of a pass (weights, query rows,
+// positional inputs) is issued before anything waits, so a pass costs one memory round trip;
+// the rotation runs while the matrix instructions execute, and the loads of the next pass are
+// issued before the current pass's results are written.
 __global__ void __launch_bounds__(256) absorb_q_mfma_kernel(
     const uint16_t* __restrict__ q_nope, const uint16_t* __restrict__ q_rope,
     const int32_t* __restrict__ q_pos, const uint16_t* __restrict__ w_uk, uint16_t* __restrict__ q_abs, int T,
@@ -66,29 +68,28 @@ __global__ void __launch_bounds__(256) absorb_q_mfma_kernel(
       }
     }
   };
-  load_a(0);
-
-  for (int t0 = 0; t0 < T; t0 += kPassRows) {
-    // positional part: rows t0 + 4i + qc (i < 16) x 32 pairs.  The angle pos * base^(-2j/d_R)
-    // and its reduction modulo 2 pi are taken in fp64 (positions reach 2^15, so an fp32 angle
-    // would be off by milliradians); cosine and sine of the reduced angle (|r| <= pi) in fp32
-    // are then accurate to a few fp32 ulps, far below the bf16 rounding of the result.
+  // positional part of a pass at t0: rows t0 + 4i + qc (i < 16) x 32 pairs, pair e = tid +
+  // 256i' (i' < 2) being row t0 + 4(e/32) + qc, pair e%32 = tid%32
+  const int jp = tid & 31;
+  const double th = theta.v[jp];
+  uint32_t rx[2];
+  int rpos[2];
+  auto load_rope = [&](int t0) {
 #pragma unroll
-    for (int e = tid; e < 16 * (kAbsDR / 2); e += 256) {
-      const int t = t0 + 4 * (e >> 5) + qc, jp = e & 31;
+    for (int i = 0; i < 2; ++i) {
+      const int t = t0 + 4 * ((tid + 256 * i) >> 5) + qc;
+      rx[i] = 0u;
+      rpos[i] = 0;
       if (t < T) {
-        const uint16_t* src = q_rope + ((size_t)t * kAbsH + h) * kAbsDR + 2 * jp;
-        const double ang = (double)q_pos[t] * theta.v[jp];
-        const double k = rint(ang * 0.15915494309189535);                   // ang / (2 pi)
-        const double red = fma(-k, 6.283185307179586, ang) - k * 2.4492935982947064e-16;   // 2 pi = hi + lo
-        float sn, cs;
-        sincosf((float)red, &sn, &cs);
-        const uint32_t xx = *reinterpret_cast<const uint32_t*>(src);
-        const float x0 = bf16_bits_to_f32(xx & 0xFFFFu), x1 = bf16_bits_to_f32(xx >> 16);
-        *reinterpret_cast<uint32_t*>(q_abs + ((size_t)t * kAbsH + h) * kAbsRow + kAbsDC + 2 * jp) =
-            pack_bf16x2(x0 * cs - x1 * sn, x0 * sn + x1 * cs);
+        rx[i] = *reinterpret_cast<const uint32_t*>(q_rope + ((size_t)t * kAbsH + h) * kAbsDR + 2 * jp);
+        rpos[i] = q_pos[t];
       }
     }
+  };
+  load_a(0);
+  load_rope(0);
+
+  for (int t0 = 0; t0 < T; t0 += kPassRows) {
     f32x16 acc[2] = {};
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt)
@@ -96,7 +97,28 @@ __global__ void __launch_bounds__(256) absorb_q_mfma_kernel(
       for (int ks = 0; ks < 8; ++ks)
         acc[rt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[rt][ks], __builtin_bit_cast(bf16x8, wv[ks]), acc[rt], 0,
                                                           0, 0);
-    if (t0 + kPassRows < T) load_a(t0 + kPassRows);
+    // The angle pos * base^(-2j/d_R) and its reduction modulo 2 pi are taken in fp64
+    // (positions reach 2^15, so an fp32 angle would be off by milliradians); cosine and sine
+    // of the reduced angle (|r| <= pi) in fp32 are then accurate to a few fp32 ulps, far below
+    // the bf16 rounding of the result.
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int t = t0 + 4 * ((tid + 256 * i) >> 5) + qc;
+      if (t < T) {
+        const double ang = (double)rpos[i] * th;
+        const double k = rint(ang * 0.15915494309189535);                   // ang / (2 pi)
+        const double red = fma(-k, 6.283185307179586, ang) - k * 2.4492935982947064e-16;   // 2 pi = hi + lo
+        float sn, cs;
+        sincosf((float)red, &sn, &cs);
+        const float x0 = bf16_bits_to_f32(rx[i] & 0xFFFFu), x1 = bf16_bits_to_f32(rx[i] >> 16);
+        *reinterpret_cast<uint32_t*>(q_abs + ((size_t)t * kAbsH + h) * kAbsRow + kAbsDC + 2 * jp) =
+            pack_bf16x2(x0 * cs - x1 * sn, x0 * sn + x1 * cs);
+      }
+    }
+    if (t0 + kPassRows < T) {
+      load_a(t0 + kPassRows);
+      load_rope(t0 + kPassRows);
+    }
     __syncthreads();   // the previous pass's stage reads are done
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt)
