@@ -176,14 +176,15 @@ __global__ void __launch_bounds__(256) absorb_q_generic_kernel(
 
 constexpr int kOutDV = 128;
 
-// out^T[v, t] = W_UV,h^T[v, c] . o_lat^T[c, t] for one head h and output columns
-// v = 32qv .. 32qv+31, all query rows.  The weight slice W_UV[:, h, 32qv .. +31] (512 rows of
-// 64 bytes) is copied to LDS once; the A operand (rows v, K = c) comes from it through
-// transposing reads, with the 64-byte pitch putting the four rows of one read on four
-// different 64-byte bank groups.  The B operand (K = c, contiguous in o_lat) comes straight
-// from global memory.  The four waves split the contraction (wave w: c = 128w .. 128w+127), so
-// each lane's share of o_lat for a pass of 64 rows is requested at once, and their partial
-// tiles are summed through LDS.
+// out^T[v, t] = W_UV,h^T[v, c] . o_lat^T[c, t] for one head h, output columns
+// v = 32qv .. 32qv+31 and the 64 query rows of block z.  The weight slice W_UV[:, h, 32qv .. +31]
+// (512 rows of 64 bytes) is copied to LDS once; the A operand (rows v, K = c) comes from it
+// through transposing reads, with the 64-byte pitch putting the four rows of one read on four
+// different 64-byte bank groups.  o_lat is read with each load instruction covering 1 KB of
+// one row (a fragment-shaped read, 32 rows of 32 bytes per instruction, costs the memory
+// pipeline about twice as long) and reaches the B operand (K = c, N = t) through an LDS stage
+// in bf16, 32 rows at a time.  The four waves split the contraction (wave w: c = 128w ..
+// 128w+127) and sum their partial tiles through LDS.
 
 // ds_read_b64_tr_b16 (gfx950): within each group of 16 lanes, output lane i gets element i%4
 // of the four values read by source lane 4j + i/4, as its element j.
@@ -191,90 +192,88 @@ __device__ __forceinline__ bf16x4 op_tr16(const uint8_t* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)(const MLA_LDS uint8_t*)p);
 }
 
+constexpr int kOPitch = kAbsDC * 2 + 16;   // bytes per staged o_lat row (bf16; the pad spreads rows over banks)
+
 __global__ void __launch_bounds__(256) out_proj_mfma_kernel(
     const float* __restrict__ o_lat, const uint16_t* __restrict__ w_uv, uint16_t* __restrict__ out,
     int T) {
-  __shared__ __attribute__((aligned(16))) uint8_t wl[kAbsDC * 64];          // [c][32 v] bf16
-  __shared__ __attribute__((aligned(16))) f32x4 red[4][8][kPassRows];      // [wave][v/4][t]
-  const int h = blockIdx.x, qv = blockIdx.y;
+  __shared__ __attribute__((aligned(16))) uint8_t wl[kAbsDC * 64];        // [c][32 v] bf16
+  __shared__ __attribute__((aligned(16))) uint8_t ost[32 * kOPitch];      // [32 t][512 c] bf16, then the reduction
+  static_assert(sizeof(f32x4) * 4 * 8 * kPassRows <= sizeof(ost), "reduction tile fits the stage");
+  f32x4 (*red)[8][kPassRows] = reinterpret_cast<f32x4 (*)[8][kPassRows]>(ost);   // [wave][v/4][t]
+  const int h = blockIdx.x, qv = blockIdx.y, t0 = kPassRows * blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 5;                // K group of this lane: c = 16ks + 8g .. +7
-  // B fragments of the pass at t0: rows t0 + 32rt + lane%32, c = 128w + 16ks + 8g .. +7 (rows
-  // past T read row 0 and are zeroed before use)
-  f32x4 ox[2][8][2];
-  auto load_b = [&](int t0) {
+  // weight slice: piece p = tid + 256i is row p/4, bytes 16(p%4) .. of that row
+  u32x4 r[8];
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
-      const int t = t0 + 32 * rt + (lane & 31);
-      const float* orow = o_lat + ((size_t)(t < T ? t : 0) * kAbsH + h) * kAbsDC + 128 * wave + 8 * g;
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        ox[rt][ks][0] = *reinterpret_cast<const f32x4*>(orow + 16 * ks);
-        ox[rt][ks][1] = *reinterpret_cast<const f32x4*>(orow + 16 * ks + 4);
-      }
-    }
-  };
-  // weight slice: piece p = tid + 256i is row p/4, bytes 16(p%4) .. of that row; the first
-  // pass's o_lat fragments are requested before it is written to LDS
-  {
-    u32x4 r[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int p = tid + 256 * i;
-      r[i] = *reinterpret_cast<const u32x4*>(w_uv + (size_t)(p >> 2) * (kAbsH * kOutDV) + h * kOutDV + 32 * qv +
-                                             8 * (p & 3));
-    }
-    load_b(0);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) *reinterpret_cast<u32x4*>(wl + 16 * (tid + 256 * i)) = r[i];
+  for (int i = 0; i < 8; ++i) {
+    const int p = tid + 256 * i;
+    r[i] = *reinterpret_cast<const u32x4*>(w_uv + (size_t)(p >> 2) * (kAbsH * kOutDV) + h * kOutDV + 32 * qv +
+                                           8 * (p & 3));
   }
+  // o_lat rows t0 .. t0+63 of head h: piece p = tid + 256i is row p/128 (= 2i + tid/128), floats
+  // 4(p%128) .. +3; rows past T are zeros
+  f32x4 ov[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    const int p = tid + 256 * i, t = t0 + (p >> 7);
+    ov[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (t < T) ov[i] = *reinterpret_cast<const f32x4*>(o_lat + ((size_t)t * kAbsH + h) * kAbsDC + 4 * (p & 127));
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) *reinterpret_cast<u32x4*>(wl + 16 * (tid + 256 * i)) = r[i];
   // A operand: source lane s = 16G + 4j + a reads row 128w + 16ks + 8(G/2) + j (+4 for the high
   // half) at columns 16(G%2) + 4a .. +3, so that output lane l holds column l%32 of the tile
   // and rows 8(l/32) .. +7 of the K-step, matching B.
   const int G = lane >> 4, jr = (lane >> 2) & 3, ac = lane & 3;
   const uint8_t* wb = wl + (128 * wave + 8 * (G >> 1) + jr) * 64 + 2 * (16 * (G & 1) + 4 * ac);
-  for (int t0 = 0; t0 < T; t0 += kPassRows) {
-    __syncthreads();   // weight slice in LDS; the previous pass's reduction reads are done
-    f32x16 acc[2] = {};
+  // B operand: lane l reads staged row l%32, columns 128w + 16ks + 8g .. +7
+  const uint8_t* ob = ost + (lane & 31) * kOPitch + 2 * (128 * wave + 8 * g);
+  f32x16 acc[2] = {};
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt) {
+    // stage rows 32rt .. 32rt+31 (pieces i = 16rt .. 16rt+15)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const f32x4 x = ov[16 * rt + i];
+      const int p = tid + 256 * i;
+      *reinterpret_cast<u32x2*>(ost + (p >> 7) * kOPitch + 8 * (p & 127)) =
+          u32x2{cvt_pk_bf16(x[0], x[1]), cvt_pk_bf16(x[2], x[3])};
+    }
+    __syncthreads();   // weight slice and stage written
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
       const bf16x4 lo = op_tr16(wb + 16 * ks * 64);
       const bf16x4 hi = op_tr16(wb + (16 * ks + 4) * 64);
       const bf16x8 a = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-#pragma unroll
-      for (int rt = 0; rt < 2; ++rt) {
-        const bool ok = t0 + 32 * rt + (lane & 31) < T;
-        const f32x4 x0 = ok ? ox[rt][ks][0] : f32x4{0.f, 0.f, 0.f, 0.f};
-        const f32x4 x1 = ok ? ox[rt][ks][1] : f32x4{0.f, 0.f, 0.f, 0.f};
-        const u32x4 bq = u32x4{pack_bf16x2(x0[0], x0[1]), pack_bf16x2(x0[2], x0[3]), pack_bf16x2(x1[0], x1[1]),
-                               pack_bf16x2(x1[2], x1[3])};
-        acc[rt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8, bq), acc[rt], 0, 0, 0);
-      }
+      const bf16x8 b = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(ob + 32 * ks));
+      acc[rt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[rt], 0, 0, 0);
     }
-    if (t0 + kPassRows < T) load_b(t0 + kPassRows);
-    // acc[rt][4m + i] = partial out^T[v = 8m + 4g + i, t = 32rt + lane%32]
+    __syncthreads();   // stage reads done before it is rewritten (or reused for the reduction)
+  }
+  // acc[rt][4m + i] = partial out^T[v = 8m + 4g + i, t = 32rt + lane%32]
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
+  for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-      for (int m = 0; m < 4; ++m)
-        red[wave][2 * m + g][32 * rt + (lane & 31)] =
-            f32x4{acc[rt][4 * m], acc[rt][4 * m + 1], acc[rt][4 * m + 2], acc[rt][4 * m + 3]};
-    __syncthreads();
-    // thread tid: row t0 + tid/4, columns 32qv + 8(tid%4) .. +7
-    {
-      const int r = tid >> 2, vc = tid & 3;
-      f32x4 s0 = red[0][2 * vc][r], s1 = red[0][2 * vc + 1][r];
+    for (int m = 0; m < 4; ++m)
+      red[wave][2 * m + g][32 * rt + (lane & 31)] =
+          f32x4{acc[rt][4 * m], acc[rt][4 * m + 1], acc[rt][4 * m + 2], acc[rt][4 * m + 3]};
+  __syncthreads();
+  // thread tid: row t0 + tid/4, columns 32qv + 8(tid%4) .. +7
+  {
+    const int rr = tid >> 2, vc = tid & 3;
+    f32x4 s0 = red[0][2 * vc][rr], s1 = red[0][2 * vc + 1][rr];
 #pragma unroll
-      for (int w = 1; w < 4; ++w) {
-        s0 += red[w][2 * vc][r];
-        s1 += red[w][2 * vc + 1][r];
-      }
-      const int t = t0 + r;
-      if (t < T)
-        *reinterpret_cast<u32x4*>(out + ((size_t)t * kAbsH + h) * kOutDV + 32 * qv + 8 * vc) =
-            u32x4{pack_bf16x2(s0[0], s0[1]), pack_bf16x2(s0[2], s0[3]), pack_bf16x2(s1[0], s1[1]),
-                  pack_bf16x2(s1[2], s1[3])};
+    for (int w = 1; w < 4; ++w) {
+      s0 += red[w][2 * vc][rr];
+      s1 += red[w][2 * vc + 1][rr];
     }
+    const int t = t0 + rr;
+    if (t < T)
+      *reinterpret_cast<u32x4*>(out + ((size_t)t * kAbsH + h) * kOutDV + 32 * qv + 8 * vc) =
+          u32x4{pack_bf16x2(s0[0], s0[1]), pack_bf16x2(s0[2], s0[3]), pack_bf16x2(s1[0], s1[1]),
+                pack_bf16x2(s1[2], s1[3])};
   }
 }
 
@@ -340,7 +339,8 @@ hipError_t launch_out_proj(const mla_config_t& cfg, const float* o_lat, const vo
                            hipStream_t stream) {
   if (T == 0) return hipSuccess;
   if (cfg.act_dtype == MLA_BF16 && is_dsv2_shape(cfg)) {
-    hipLaunchKernelGGL(out_proj_mfma_kernel, dim3(kAbsH, kOutDV / 32), dim3(256), 0, stream, o_lat,
+    hipLaunchKernelGGL(out_proj_mfma_kernel, dim3(kAbsH, kOutDV / 32, (T + kPassRows - 1) / kPassRows), dim3(256), 0,
+                       stream, o_lat,
                        static_cast<const uint16_t*>(w_uv), static_cast<uint16_t*>(out), T);
     return hipGetLastError();
   }

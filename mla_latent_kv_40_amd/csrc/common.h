@@ -37,6 +37,12 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
 }
 
+// The same rounding (nearest even, finite values) in one instruction: v_cvt_pk_bf16_f32.
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
+}
+
 // ------------------------------------------------------------------ OCP e4m3fn
 
 // Nearest e4m3fn code of x (ties to even), saturating to +-448.  Exact arithmetic only

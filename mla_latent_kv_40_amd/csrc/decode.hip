@@ -303,10 +303,6 @@ __device__ __forceinline__ void o_fence(f32x16* o) {
 // sequence are summed in fp32 by the combine), in register order: lane l's oacc[ct][8qp .. +7]
 // (columns 32ct + 8(2qp) + 4hl + 0..3 and 32ct + 8(2qp + 1) + 4hl + 0..3 of its head) goes to
 // 1 KiB block 2ct + qp at 16 bytes per lane, so every store writes 1 KiB contiguously.
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ uint32_t cvt_bf16x2(float lo, float hi) {   // v_cvt_pk_bf16_f32, nearest-even
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
-}
 __device__ __forceinline__ f32x16 read_acc(const f32x16& x) {   // accumulation registers -> VGPRs
   f32x16 r;
   asm volatile("v_accvgpr_read_b32 %0, %16\n\tv_accvgpr_read_b32 %1, %17\n\tv_accvgpr_read_b32 %2, %18\n\t"
@@ -329,8 +325,8 @@ __device__ __forceinline__ void store_partial(uint16_t* so, const f32x16* oacc) 
 #pragma unroll
     for (int qp = 0; qp < 2; ++qp)
       *reinterpret_cast<u32x4*>(so + 512 * (2 * ct + qp)) =
-          u32x4{cvt_bf16x2(o[8 * qp], o[8 * qp + 1]), cvt_bf16x2(o[8 * qp + 2], o[8 * qp + 3]),
-                cvt_bf16x2(o[8 * qp + 4], o[8 * qp + 5]), cvt_bf16x2(o[8 * qp + 6], o[8 * qp + 7])};
+          u32x4{cvt_pk_bf16(o[8 * qp], o[8 * qp + 1]), cvt_pk_bf16(o[8 * qp + 2], o[8 * qp + 3]),
+                cvt_pk_bf16(o[8 * qp + 4], o[8 * qp + 5]), cvt_pk_bf16(o[8 * qp + 6], o[8 * qp + 7])};
   }
   __builtin_amdgcn_sched_barrier(0);
 }
