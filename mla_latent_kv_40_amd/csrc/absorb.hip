@@ -9,10 +9,10 @@
 // rows of one step) and are bound by reading the 16.8 MB weight once.
 //
 // Matrix-core path (DeepSeek-V2 shape, bf16): v_mfma_f32_32x32x16_bf16, one workgroup per
-// (head, quarter of the output columns) over all query rows, so that each weight byte is read
-// by one workgroup and 512 workgroups keep every compute unit busy; every load of a pass of 64
-// query rows is issued before the first matrix instruction.  32x32 accumulator layout: lane l
-// holds column l%32 and rows 8*(k/4) + 4*(l/32) + k%4 for k = 0..15.
+// (head, quarter of the output columns, block of 64 query rows), so that each weight byte is
+// read by one workgroup per row block and 512 workgroups (at up to 64 rows) keep every compute
+// unit busy; every load of a workgroup is issued before the first matrix instruction.  32x32
+// accumulator layout: lane l holds column l%32 and rows 8*(k/4) + 4*(l/32) + k%4 for k = 0..15.
 #include "common.h"
 
 #include <cmath>
@@ -31,112 +31,118 @@ struct RopeTheta {
   double v[kAbsDR / 2];
 };
 
-// q_abs[t, h, 128qc + c'] for c' < 128: wave w computes columns 128qc + 32w .. +31 with its
-// eight weight fragments (K = d_h = 128) held in registers, B[k = d, n = c] = W_UK[c, h, d]
-// (16 contiguous bytes per lane); A[m = t, k = d] = q^C[t, h, d].  Quarter qc also rotates the
-// positional part of the rows t with t % 4 == qc.  Every load of a pass (weights, query rows,
-// positional inputs) is issued before anything waits, so a pass costs one memory round trip;
-// the rotation runs while the matrix instructions execute, and the loads of the next pass are
-// issued before the current pass's results are written.
+// q_abs[t, h, 128qc + c'] for c' < 128 and the 64 query rows t of block z: wave w computes
+// columns 128qc + 32w .. +31; B[k = d, n = c] = W_UK[c, h, d], A[m = t, k = d] = q^C[t, h, d],
+// both read from LDS, where they arrive through loads that each cover 4 x 256 contiguous
+// bytes (the weight rows of head h are 256 bytes, 32 KB apart; a fragment-shaped read would
+// touch 32 rows per instruction).  Quarter qc also rotates the positional part of the rows
+// t with t % 4 == qc.  Every load (weights, query rows, positional inputs) is issued before
+// anything waits, and the rotation runs while the matrix instructions execute.
+constexpr int kRowPitch = 2 * kAbsDH + 16;    // bytes per staged weight / query row (the pad spreads rows over banks)
+
 __global__ void __launch_bounds__(256) absorb_q_mfma_kernel(
     const uint16_t* __restrict__ q_nope, const uint16_t* __restrict__ q_rope,
     const int32_t* __restrict__ q_pos, const uint16_t* __restrict__ w_uk, uint16_t* __restrict__ q_abs, int T,
     RopeTheta theta) {
-  __shared__ __attribute__((aligned(16))) uint16_t stage[kPassRows * kAbsPitch];
-  const int h = blockIdx.x, qc = blockIdx.y;
+  __shared__ __attribute__((aligned(16))) uint8_t wst[128 * kRowPitch];           // [c'][d] bf16
+  __shared__ __attribute__((aligned(16))) uint8_t qst[kPassRows * kRowPitch];     // [t - t0][d] bf16
+  __shared__ __attribute__((aligned(16))) uint16_t stage[kPassRows * kAbsPitch];  // results [t - t0][c']
+  const int h = blockIdx.x, qc = blockIdx.y, t0 = kPassRows * blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int li = lane & 31, lg = lane >> 5;
 
+  // weight rows c = 128qc + p/16, bytes 16(p%16) .. for piece p = tid + 256i
   u32x4 wv[8];
-  {
-    const uint16_t* wsrc = w_uk + (size_t)(128 * qc + 32 * wave + li) * (kAbsH * kAbsDH) + h * kAbsDH + 8 * lg;
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) wv[ks] = *reinterpret_cast<const u32x4*>(wsrc + 16 * ks);
+  for (int i = 0; i < 8; ++i) {
+    const int p = tid + 256 * i;
+    wv[i] = *reinterpret_cast<const u32x4*>(w_uk + (size_t)(128 * qc + (p >> 4)) * (kAbsH * kAbsDH) + h * kAbsDH +
+                                            8 * (p & 15));
   }
-  // A fragments of both row tiles of the pass at t0: rows t0 + 32rt + li, d = 16ks + 8lg .. +7
-  bf16x8 af[2][8];
-  auto load_a = [&](int t0) {
+  // query rows t0 + p/16 (zeros past T)
+  u32x4 qv[4];
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
-      const int t = t0 + 32 * rt + li;
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        u32x4 v = {0u, 0u, 0u, 0u};
-        if (t < T)
-          v = *reinterpret_cast<const u32x4*>(q_nope + ((size_t)t * kAbsH + h) * kAbsDH + 16 * ks + 8 * lg);
-        af[rt][ks] = __builtin_bit_cast(bf16x8, v);
-      }
-    }
-  };
-  // positional part of a pass at t0: rows t0 + 4i + qc (i < 16) x 32 pairs, pair e = tid +
-  // 256i' (i' < 2) being row t0 + 4(e/32) + qc, pair e%32 = tid%32
+  for (int i = 0; i < 4; ++i) {
+    const int p = tid + 256 * i, t = t0 + (p >> 4);
+    qv[i] = u32x4{0u, 0u, 0u, 0u};
+    if (t < T) qv[i] = *reinterpret_cast<const u32x4*>(q_nope + ((size_t)t * kAbsH + h) * kAbsDH + 8 * (p & 15));
+  }
+  // positional part: rows t0 + 4i + qc (i < 16) x 32 pairs, pair e = tid + 256i' (i' < 2) being
+  // row t0 + 4(e/32) + qc, pair e%32 = tid%32
   const int jp = tid & 31;
   const double th = theta.v[jp];
   uint32_t rx[2];
   int rpos[2];
-  auto load_rope = [&](int t0) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int t = t0 + 4 * ((tid + 256 * i) >> 5) + qc;
-      rx[i] = 0u;
-      rpos[i] = 0;
-      if (t < T) {
-        rx[i] = *reinterpret_cast<const uint32_t*>(q_rope + ((size_t)t * kAbsH + h) * kAbsDR + 2 * jp);
-        rpos[i] = q_pos[t];
-      }
+  for (int i = 0; i < 2; ++i) {
+    const int t = t0 + 4 * ((tid + 256 * i) >> 5) + qc;
+    rx[i] = 0u;
+    rpos[i] = 0;
+    if (t < T) {
+      rx[i] = *reinterpret_cast<const uint32_t*>(q_rope + ((size_t)t * kAbsH + h) * kAbsDR + 2 * jp);
+      rpos[i] = q_pos[t];
     }
-  };
-  load_a(0);
-  load_rope(0);
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int p = tid + 256 * i;
+    *reinterpret_cast<u32x4*>(wst + (p >> 4) * kRowPitch + 16 * (p & 15)) = wv[i];
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int p = tid + 256 * i;
+    *reinterpret_cast<u32x4*>(qst + (p >> 4) * kRowPitch + 16 * (p & 15)) = qv[i];
+  }
+  __syncthreads();
 
-  for (int t0 = 0; t0 < T; t0 += kPassRows) {
-    f32x16 acc[2] = {};
+  // A fragments: rows 32rt + li, d = 16ks + 8lg .. +7; B fragments: weight row 32w + li, same d
+  f32x16 acc[2] = {};
+  const uint8_t* wb = wst + (32 * wave + li) * kRowPitch + 16 * lg;
+  const uint8_t* qb = qst + li * kRowPitch + 16 * lg;
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
+  for (int ks = 0; ks < 8; ++ks) {
+    const bf16x8 b = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(wb + 32 * ks));
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks)
-        acc[rt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[rt][ks], __builtin_bit_cast(bf16x8, wv[ks]), acc[rt], 0,
-                                                          0, 0);
-    // The angle pos * base^(-2j/d_R) and its reduction modulo 2 pi are taken in fp64
-    // (positions reach 2^15, so an fp32 angle would be off by milliradians); cosine and sine
-    // of the reduced angle (|r| <= pi) in fp32 are then accurate to a few fp32 ulps, far below
-    // the bf16 rounding of the result.
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int t = t0 + 4 * ((tid + 256 * i) >> 5) + qc;
-      if (t < T) {
-        const double ang = (double)rpos[i] * th;
-        const double k = rint(ang * 0.15915494309189535);                   // ang / (2 pi)
-        const double red = fma(-k, 6.283185307179586, ang) - k * 2.4492935982947064e-16;   // 2 pi = hi + lo
-        float sn, cs;
-        sincosf((float)red, &sn, &cs);
-        const float x0 = bf16_bits_to_f32(rx[i] & 0xFFFFu), x1 = bf16_bits_to_f32(rx[i] >> 16);
-        *reinterpret_cast<uint32_t*>(q_abs + ((size_t)t * kAbsH + h) * kAbsRow + kAbsDC + 2 * jp) =
-            pack_bf16x2(x0 * cs - x1 * sn, x0 * sn + x1 * cs);
-      }
+    for (int rt = 0; rt < 2; ++rt) {
+      const bf16x8 a = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qb + 32 * rt * kRowPitch + 32 * ks));
+      acc[rt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[rt], 0, 0, 0);
     }
-    if (t0 + kPassRows < T) {
-      load_a(t0 + kPassRows);
-      load_rope(t0 + kPassRows);
+  }
+  // The angle pos * base^(-2j/d_R) and its reduction modulo 2 pi are taken in fp64 (positions
+  // reach 2^15, so an fp32 angle would be off by milliradians); cosine and sine of the reduced
+  // angle (|r| <= pi) in fp32 are then accurate to a few fp32 ulps, far below the bf16 rounding
+  // of the result.
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int t = t0 + 4 * ((tid + 256 * i) >> 5) + qc;
+    if (t < T) {
+      const double ang = (double)rpos[i] * th;
+      const double k = rint(ang * 0.15915494309189535);                   // ang / (2 pi)
+      const double red = fma(-k, 6.283185307179586, ang) - k * 2.4492935982947064e-16;   // 2 pi = hi + lo
+      float sn, cs;
+      sincosf((float)red, &sn, &cs);
+      const float x0 = bf16_bits_to_f32(rx[i] & 0xFFFFu), x1 = bf16_bits_to_f32(rx[i] >> 16);
+      *reinterpret_cast<uint32_t*>(q_abs + ((size_t)t * kAbsH + h) * kAbsRow + kAbsDC + 2 * jp) =
+          pack_bf16x2(x0 * cs - x1 * sn, x0 * sn + x1 * cs);
     }
-    __syncthreads();   // the previous pass's stage reads are done
+  }
+  // 32x32 accumulator layout: lane l holds column l%32 and rows 8(k/4) + 4(l/32) + k%4
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
+  for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-      for (int k = 0; k < 16; ++k) {
-        const int r = 32 * rt + 8 * (k >> 2) + 4 * lg + (k & 3);
-        stage[r * kAbsPitch + 32 * wave + li] = (uint16_t)f32_to_bf16_bits(acc[rt][k]);
-      }
-    __syncthreads();
-    // 64 rows x 256 bytes: piece p = tid + 256i is row p/16, bytes 16(p%16) ..
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int p = tid + 256 * i, r = p >> 4;
-      const int t = t0 + r;
-      if (t < T)
-        *reinterpret_cast<u32x4*>(q_abs + ((size_t)t * kAbsH + h) * kAbsRow + 128 * qc + 8 * (p & 15)) =
-            *reinterpret_cast<const u32x4*>(stage + r * kAbsPitch + 8 * (p & 15));
+    for (int k = 0; k < 16; ++k) {
+      const int r = 32 * rt + 8 * (k >> 2) + 4 * lg + (k & 3);
+      stage[r * kAbsPitch + 32 * wave + li] = (uint16_t)f32_to_bf16_bits(acc[rt][k]);
     }
+  __syncthreads();
+  // 64 rows x 256 bytes: piece p = tid + 256i is row p/16, bytes 16(p%16) ..
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int p = tid + 256 * i, r = p >> 4;
+    const int t = t0 + r;
+    if (t < T)
+      *reinterpret_cast<u32x4*>(q_abs + ((size_t)t * kAbsH + h) * kAbsRow + 128 * qc + 8 * (p & 15)) =
+          *reinterpret_cast<const u32x4*>(stage + r * kAbsPitch + 8 * (p & 15));
   }
 }
 
@@ -311,7 +317,7 @@ hipError_t launch_absorb_q(const mla_config_t& cfg, const void* q_nope, const vo
                            const int32_t* q_pos, const void* w_uk, void* q_abs, int T, hipStream_t stream) {
   if (T == 0) return hipSuccess;
   if (cfg.act_dtype == MLA_BF16 && is_dsv2_shape(cfg)) {
-    dim3 grid(kAbsH, kAbsDC / 128);
+    dim3 grid(kAbsH, kAbsDC / 128, (T + kPassRows - 1) / kPassRows);
     auto* qn = static_cast<const uint16_t*>(q_nope);
     auto* qr = static_cast<const uint16_t*>(q_rope);
     auto* w = static_cast<const uint16_t*>(w_uk);
