@@ -1308,10 +1308,11 @@ __device__ void exact_head(const DecodeArgs& a, int b, int j, int h, int L, int 
 // One workgroup per (query row, group of 32 heads, quarter of the latent columns).  Every
 // segment left its unnormalised O_g (in register order) and (m_g, l_g) per head in slot g + b;
 // with M = max m_g over the non-empty ones and w_g = 2^(m_g - M):  o = sum w_g O_g / sum w_g l_g,
-// lse = ln 2 * (M + log2 sum w_g l_g).  Quarter c of a group's 64 KiB block is its 1 KiB blocks
-// 16c .. 16c+15 (column tiles 4c .. 4c+3, so columns 128c .. 128c+127), contiguous in every
-// slot: thread t reads its 16-byte pieces t + 256i (i < 4), all of head 32w + t%32, so each
-// thread needs one head's weights.  The pieces of kCombineBatch slots are requested together,
+// lse = ln 2 * (M + log2 sum w_g l_g).  The partials are bf16 (summed here in fp32).  Quarter c
+// of a group's 32 KiB block is its 1 KiB blocks 8c .. 8c+7 (column tiles 4c .. 4c+3, so columns
+// 128c .. 128c+127), contiguous in every slot: thread t reads its 16-byte pieces t + 256i
+// (i < 2, eight values each), all of head 32w + t%32, so each thread needs one head's
+// weights.  The pieces of kCombineBatch slots are requested together,
 // so a sequence's slots cost about one memory latency rather than one each.  The result goes
 // through LDS so that each head's 128 columns are written contiguously.  Heads marked by the
 // fast path (or whose sums are not finite) are then recomputed exactly, quarter by quarter.
