@@ -128,6 +128,21 @@ def test_split_ranges_and_combine_poisoned_workspace():
         compare_seq(w, bt, seqs, got, b, heads=range(0, 128, 5))
 
 
+def test_ragged_row_blocks_absorb_and_out_proj():
+    log("case dsv2 bf16 B=100 short sequences: 100 query rows = one full 64-row block + 36")
+    rng = np.random.default_rng(41)
+    lengths = rng.integers(1, 90, size=100)
+    w, bt, seqs = dsv2(100, lengths, seed=41)
+    st = run_state(w, bt, seqs)
+    got = host(st)
+    # every row of the folded query, then the layer output on rows at and around the block edge
+    qa = np.concatenate([orc.absorbed_query(s["q_c"], s["q_r"], bt.weights["W_UK"],
+                                            [int(bt.kv_lens[b]) - 1], w.rope_base) for b, s in enumerate(seqs)])
+    check("q_abs", st.q_abs.float().cpu().numpy(), qa)
+    for b in (0, 63, 64, 99):
+        compare_seq(w, bt, seqs, got, b, heads=range(b % 3, 128, 9))
+
+
 def test_causal_multi_query_sq4():
     log("case dsv2 bf16 Sq=4 causal, lengths [4, 68, 129, 300]")
     w, bt, seqs = dsv2(4, [4, 68, 129, 300], sq=4, seed=13)
