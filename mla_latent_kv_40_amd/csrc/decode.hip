@@ -1312,11 +1312,11 @@ __device__ void exact_head(const DecodeArgs& a, int b, int j, int h, int L, int 
 // of a group's 32 KiB block is its 1 KiB blocks 8c .. 8c+7 (column tiles 4c .. 4c+3, so columns
 // 128c .. 128c+127), contiguous in every slot: thread t reads its 16-byte pieces t + 256i
 // (i < 2, eight values each), all of head 32w + t%32, so each thread needs one head's
-// weights.  The pieces of kCombineBatch slots are requested together,
+// weights.  The pieces and (m, l) of kCombineBatch slots are requested together,
 // so a sequence's slots cost about one memory latency rather than one each.  The result goes
 // through LDS so that each head's 128 columns are written contiguously.  Heads marked by the
 // fast path (or whose sums are not finite) are then recomputed exactly, quarter by quarter.
-constexpr int kCombineBatch = 4;
+constexpr int kCombineBatch = 8;
 constexpr int kCombinePitch = 128 + 4;   // fp32 words per head in the LDS tile (spreads heads over banks)
 
 __global__ void __launch_bounds__(256) combine_kernel(DecodeArgs a) {
@@ -1379,14 +1379,25 @@ __global__ void __launch_bounds__(256) combine_kernel(DecodeArgs a) {
       }
     }
   };
+  // the first batch (all of a sequence's slots when it has at most kCombineBatch) is requested
+  // before anything waits: the maxima then come from the same loads
+  fetch(g_lo);
   float M = -INFINITY;
   bool redo = false;
+  if (g_hi - g_lo < kCombineBatch) {
+#pragma unroll
+    for (int k = 0; k < kCombineBatch; ++k) {   // (m, l) = (0, 0) for slots past g_hi or empty
+      if (mv[k].y < 0.f) redo = true;
+      else if (mv[k].y > 0.f) M = fmaxf(M, mv[k].x);
+    }
+  } else {
 #pragma unroll 4
-  for (int g = g_lo; g <= g_hi; ++g) {   // independent loads: several in flight
-    if (empty(g)) continue;
-    const float2 u = ml[slot(g) * kH + h];
-    if (u.y < 0.f) redo = true;
-    else if (u.y > 0.f) M = fmaxf(M, u.x);
+    for (int g = g_lo; g <= g_hi; ++g) {   // independent loads: several in flight
+      if (empty(g)) continue;
+      const float2 u = ml[slot(g) * kH + h];
+      if (u.y < 0.f) redo = true;
+      else if (u.y > 0.f) M = fmaxf(M, u.x);
+    }
   }
   f32x4 acc[4];
 #pragma unroll
@@ -1395,7 +1406,7 @@ __global__ void __launch_bounds__(256) combine_kernel(DecodeArgs a) {
   if (!redo && M != -INFINITY) {
     // a segment with nothing visible (l = 0) holds zeros and gets weight 0
     for (int g = g_lo;;) {
-      fetch(g);
+      if (g != g_lo) fetch(g);
 #pragma unroll
       for (int k = 0; k < kCombineBatch; ++k) {
         const float wg = mv[k].y > 0.f ? __builtin_amdgcn_exp2f(mv[k].x - M) : 0.0f;
