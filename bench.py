@@ -1,7 +1,8 @@
 """MLA decode benchmark on one MI355X: one JSON line.
 
-A step is the whole decode path for one batch: mla_cache_append (the step's new tokens),
-mla_absorb_q, mla_decode_split + mla_decode_combine (= mla_decode_attn), mla_out_proj.
+A step is the whole decode path for one batch: mla_append_absorb (= mla_cache_append of the
+step's new tokens and mla_absorb_q, in one launch), mla_decode_split + mla_decode_combine
+(= mla_decode_attn), mla_out_proj.
 The default workload is DeepSeek-V2-shaped bf16 decode at batch 64 with context lengths
 drawn uniformly from [1024, 32768] (synthetic, seeded).  Inputs are resident in HBM before
 the timed region.
@@ -141,8 +142,7 @@ def main() -> int:
     stream = torch.cuda.current_stream()
 
     def step(ev=None):
-        st.append(st.new_c, st.new_k, st.new_pos, st.new_seq, st.T)
-        st.absorb()
+        st.append_absorb()
         if ev is not None:
             ev[0].record(stream)
         st.decode_split()

@@ -125,6 +125,20 @@ mla_status_t mla_absorb_q(const mla_config_t* cfg, const void* q_nope, const voi
                           const int32_t* q_pos, const void* w_uk, void* q_abs, int32_t T, void* stream);
 
 /*
+ * mla_append_absorb -- mla_cache_append and mla_absorb_q of one decode step in a single
+ * launch (the two are independent: the append writes cache rows, the absorption reads the
+ * step's queries and writes q_abs).  Arguments, layouts and results are exactly those of the
+ * two calls (see their passages above); validation is theirs, and on any error nothing is
+ * launched.  For the DeepSeek-V2 shape with bf16 activations one kernel does both; otherwise
+ * the two kernels are launched in order.  n = 0 or T = 0 skips that half.
+ */
+mla_status_t mla_append_absorb(const mla_config_t* cfg, void* cache, float* cache_scale, int32_t num_blocks,
+                               const void* c_kv, const void* k_r, const int32_t* pos, const int32_t* seq_of,
+                               const int32_t* block_table, int32_t batch, int32_t max_blocks, int32_t n,
+                               const void* q_nope, const void* q_rope, const int32_t* q_pos, const void* w_uk,
+                               void* q_abs, int32_t T, void* stream);
+
+/*
  * mla_decode_workspace_size -- bytes of scratch mla_decode_attn needs for batch B,
  * Sq queries per sequence and block tables of width max_blocks on the current device.
  * Returns 0 for invalid arguments.  The value depends only on these arguments and the

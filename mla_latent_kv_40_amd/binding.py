@@ -13,13 +13,13 @@ from typing import Optional
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmla.so")
 
-ABI_VERSION = 2   # what mla_abi_version() returns for the argument lists below
+ABI_VERSION = 3   # what mla_abi_version() returns for the argument lists below
 
 MLA_OK, MLA_ERR_INVALID_ARG, MLA_ERR_UNSUPPORTED, MLA_ERR_WORKSPACE, MLA_ERR_HIP = range(5)
 MLA_F32, MLA_BF16, MLA_FP8_E4M3 = range(3)
 DTYPES = {"f32": MLA_F32, "bf16": MLA_BF16, "fp8": MLA_FP8_E4M3}
 
-EXPORTS = ("mla_cache_append", "mla_absorb_q", "mla_decode_workspace_size", "mla_decode_attn",
+EXPORTS = ("mla_cache_append", "mla_absorb_q", "mla_append_absorb", "mla_decode_workspace_size", "mla_decode_attn",
            "mla_decode_split", "mla_decode_combine", "mla_out_proj", "mla_status_string", "mla_abi_version")
 
 
@@ -51,6 +51,8 @@ def lib() -> ctypes.CDLL:
         cfgp = ctypes.POINTER(MlaConfig)
         L.mla_cache_append.argtypes = [cfgp, vp, f32p, i32, vp, vp, vp, vp, vp, i32, i32, i32, vp]
         L.mla_absorb_q.argtypes = [cfgp, vp, vp, vp, vp, vp, i32, vp]
+        L.mla_append_absorb.argtypes = [cfgp, vp, f32p, i32, vp, vp, vp, vp, vp, i32, i32, i32, vp, vp, vp, vp, vp,
+                                        i32, vp]
         L.mla_decode_workspace_size.argtypes = [cfgp, i32, i32, i32]
         L.mla_decode_workspace_size.restype = ctypes.c_size_t
         for name in ("mla_decode_attn", "mla_decode_split", "mla_decode_combine"):
@@ -60,7 +62,7 @@ def lib() -> ctypes.CDLL:
         L.mla_status_string.argtypes = [ctypes.c_int]
         L.mla_status_string.restype = ctypes.c_char_p
         L.mla_abi_version.restype = ctypes.c_int32
-        for name in ("mla_cache_append", "mla_absorb_q", "mla_decode_attn", "mla_decode_split", "mla_decode_combine",
+        for name in ("mla_cache_append", "mla_absorb_q", "mla_append_absorb", "mla_decode_attn", "mla_decode_split", "mla_decode_combine",
                      "mla_out_proj"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -122,6 +124,17 @@ def mla_absorb_q(cfg: Config, q_nope, q_rope, q_pos, w_uk, q_abs, T, stream=None
                             _ptr(q_abs), T, _stream(stream))
     if check:
         _check("mla_absorb_q", st)
+    return st
+
+
+def mla_append_absorb(cfg: Config, cache, cache_scale, num_blocks, c_kv, k_r, pos, seq_of, block_table, batch,
+                      max_blocks, n, q_nope, q_rope, q_pos, w_uk, q_abs, T, stream=None, check=True) -> int:
+    st = lib().mla_append_absorb(ctypes.byref(cfg.c()), _ptr(cache), _ptr(cache_scale), num_blocks, _ptr(c_kv),
+                                 _ptr(k_r), _ptr(pos), _ptr(seq_of), _ptr(block_table), batch, max_blocks, n,
+                                 _ptr(q_nope), _ptr(q_rope), _ptr(q_pos), _ptr(w_uk), _ptr(q_abs), T,
+                                 _stream(stream))
+    if check:
+        _check("mla_append_absorb", st)
     return st
 
 

@@ -13,7 +13,7 @@
 // read by one workgroup per row block and 512 workgroups (at up to 64 rows) keep every compute
 // unit busy; every load of a workgroup is issued before the first matrix instruction.  32x32
 // accumulator layout: lane l holds column l%32 and rows 8*(k/4) + 4*(l/32) + k%4 for k = 0..15.
-#include "common.h"
+#include "append_dsv2.h"
 
 #include <cmath>
 
@@ -31,6 +31,12 @@ struct RopeTheta {
   double v[kAbsDR / 2];
 };
 
+static RopeTheta rope_theta(const mla_config_t& cfg) {
+  RopeTheta theta;
+  for (int j = 0; j < kAbsDR / 2; ++j) theta.v[j] = std::pow((double)cfg.rope_base, -2.0 * j / (double)kAbsDR);
+  return theta;
+}
+
 // q_abs[t, h, 128qc + c'] for c' < 128 and the 64 query rows t of block z: wave w computes
 // columns 128qc + 32w .. +31; B[k = d, n = c] = W_UK[c, h, d], A[m = t, k = d] = q^C[t, h, d],
 // both read from LDS, where they arrive through loads that each cover 4 x 256 contiguous
@@ -40,14 +46,27 @@ struct RopeTheta {
 // anything waits, and the rotation runs while the matrix instructions execute.
 constexpr int kRowPitch = 2 * kAbsDH + 16;    // bytes per staged weight / query row (the pad spreads rows over banks)
 
-__global__ void __launch_bounds__(256) absorb_q_mfma_kernel(
-    const uint16_t* __restrict__ q_nope, const uint16_t* __restrict__ q_rope,
-    const int32_t* __restrict__ q_pos, const uint16_t* __restrict__ w_uk, uint16_t* __restrict__ q_abs, int T,
-    RopeTheta theta) {
+struct AbsorbArgs {
+  const uint16_t* q_nope;
+  const uint16_t* q_rope;
+  const int32_t* q_pos;
+  const uint16_t* w_uk;
+  uint16_t* q_abs;
+  int T;
+};
+
+// Workgroup (h, qc, z) of the absorption; every thread of the workgroup calls it.
+__device__ __forceinline__ void absorb_q_block(const AbsorbArgs& aq, const RopeTheta& theta, int h, int qc, int z) {
   __shared__ __attribute__((aligned(16))) uint8_t wst[128 * kRowPitch];           // [c'][d] bf16
-  __shared__ __attribute__((aligned(16))) uint8_t qst[kPassRows * kRowPitch];     // [t - t0][d] bf16
-  __shared__ __attribute__((aligned(16))) uint16_t stage[kPassRows * kAbsPitch];  // results [t - t0][c']
-  const int h = blockIdx.x, qc = blockIdx.y, t0 = kPassRows * blockIdx.z;
+  __shared__ __attribute__((aligned(16))) uint8_t qst[kPassRows * kRowPitch];     // [t - t0][d] bf16, then
+  static_assert(kPassRows * kAbsPitch * 2 <= sizeof(qst), "result tile fits the query stage");
+  uint16_t* stage = reinterpret_cast<uint16_t*>(qst);   // the results [t - t0][c'] (52 KB in all: 3 per CU)
+  const uint16_t* __restrict__ q_nope = aq.q_nope;
+  const uint16_t* __restrict__ q_rope = aq.q_rope;
+  const int32_t* __restrict__ q_pos = aq.q_pos;
+  const uint16_t* __restrict__ w_uk = aq.w_uk;
+  uint16_t* __restrict__ q_abs = aq.q_abs;
+  const int T = aq.T, t0 = kPassRows * z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int li = lane & 31, lg = lane >> 5;
 
@@ -127,6 +146,7 @@ __global__ void __launch_bounds__(256) absorb_q_mfma_kernel(
     }
   }
   // 32x32 accumulator layout: lane l holds column l%32 and rows 8(k/4) + 4(l/32) + k%4
+  __syncthreads();   // every wave's query-fragment reads are done before the results overwrite them
 #pragma unroll
   for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
@@ -143,6 +163,26 @@ __global__ void __launch_bounds__(256) absorb_q_mfma_kernel(
     if (t < T)
       *reinterpret_cast<u32x4*>(q_abs + ((size_t)t * kAbsH + h) * kAbsRow + 128 * qc + 8 * (p & 15)) =
           *reinterpret_cast<const u32x4*>(stage + r * kAbsPitch + 8 * (p & 15));
+  }
+}
+
+__global__ void __launch_bounds__(256) absorb_q_mfma_kernel(AbsorbArgs aq, RopeTheta theta) {
+  absorb_q_block(aq, theta, blockIdx.x, blockIdx.y, blockIdx.z);
+}
+
+// One launch for a step's cache append and query absorption (independent work): the first
+// n_append workgroups append four tokens each and go out first, the rest are the absorption's
+// (h, qc, z).  At three workgroups per CU (the absorption's 52 KB of LDS) up to 256 append
+// workgroups and 512 absorption workgroups all run at once.
+template <int CacheFmt>
+__global__ void __launch_bounds__(256) append_absorb_kernel(AppendArgs ap, AppendTheta ath, AbsorbArgs aq,
+                                                            RopeTheta theta, int n_append) {
+  const int bid = blockIdx.x;
+  if (bid < n_append) {
+    append_dsv2_token<CacheFmt>(ap, ath, bid * 4 + (threadIdx.x >> 6));
+  } else {
+    const int a = bid - n_append;
+    absorb_q_block(aq, theta, a % kAbsH, (a / kAbsH) % (kAbsDC / 128), a / (kAbsH * (kAbsDC / 128)));
   }
 }
 
@@ -318,13 +358,9 @@ hipError_t launch_absorb_q(const mla_config_t& cfg, const void* q_nope, const vo
   if (T == 0) return hipSuccess;
   if (cfg.act_dtype == MLA_BF16 && is_dsv2_shape(cfg)) {
     dim3 grid(kAbsH, kAbsDC / 128, (T + kPassRows - 1) / kPassRows);
-    auto* qn = static_cast<const uint16_t*>(q_nope);
-    auto* qr = static_cast<const uint16_t*>(q_rope);
-    auto* w = static_cast<const uint16_t*>(w_uk);
-    RopeTheta theta;
-    for (int j = 0; j < kAbsDR / 2; ++j) theta.v[j] = std::pow((double)cfg.rope_base, -2.0 * j / (double)kAbsDR);
-    hipLaunchKernelGGL(absorb_q_mfma_kernel, grid, dim3(256), 0, stream, qn, qr, q_pos, w,
-                       static_cast<uint16_t*>(q_abs), T, theta);
+    const AbsorbArgs aq{static_cast<const uint16_t*>(q_nope), static_cast<const uint16_t*>(q_rope), q_pos,
+                        static_cast<const uint16_t*>(w_uk), static_cast<uint16_t*>(q_abs), T};
+    hipLaunchKernelGGL(absorb_q_mfma_kernel, grid, dim3(256), 0, stream, aq, rope_theta(cfg));
     return hipGetLastError();
   }
   const size_t total = (size_t)T * cfg.num_heads * (cfg.d_c + cfg.d_r);
@@ -360,6 +396,38 @@ hipError_t launch_out_proj(const mla_config_t& cfg, const float* o_lat, const vo
                        o_lat, static_cast<const uint16_t*>(w_uv), static_cast<uint16_t*>(out), T, cfg.num_heads,
                        cfg.d_c, cfg.d_v);
   return hipGetLastError();
+}
+
+hipError_t launch_append(const mla_config_t& cfg, void* cache, float* cache_scale, int num_blocks,
+                         const void* c_kv, const void* k_r, const int32_t* pos, const int32_t* seq_of,
+                         const int32_t* block_table, int batch, int max_blocks, int n, hipStream_t stream);
+
+// A step's append and absorption: one launch for the DeepSeek-V2 shape with bf16 activations,
+// else the two launches.
+hipError_t launch_append_absorb(const mla_config_t& cfg, void* cache, float* cache_scale, int num_blocks,
+                                const void* c_kv, const void* k_r, const int32_t* pos, const int32_t* seq_of,
+                                const int32_t* block_table, int batch, int max_blocks, int n, const void* q_nope,
+                                const void* q_rope, const int32_t* q_pos, const void* w_uk, void* q_abs, int T,
+                                hipStream_t stream) {
+  if (n > 0 && T > 0 && append_dsv2_applies(cfg) && is_dsv2_shape(cfg)) {
+    const AppendArgs ap = append_args(cache, cache_scale, num_blocks, c_kv, k_r, pos, seq_of, block_table, batch,
+                                      max_blocks, n);
+    const AbsorbArgs aq{static_cast<const uint16_t*>(q_nope), static_cast<const uint16_t*>(q_rope), q_pos,
+                        static_cast<const uint16_t*>(w_uk), static_cast<uint16_t*>(q_abs), T};
+    const int n_append = (n + 3) / 4;
+    const dim3 grid(n_append + kAbsH * (kAbsDC / 128) * ((T + kPassRows - 1) / kPassRows));
+    if (cfg.cache_dtype == MLA_BF16)
+      hipLaunchKernelGGL(append_absorb_kernel<MLA_BF16>, grid, dim3(256), 0, stream, ap, append_theta(cfg), aq,
+                         rope_theta(cfg), n_append);
+    else
+      hipLaunchKernelGGL(append_absorb_kernel<MLA_FP8_E4M3>, grid, dim3(256), 0, stream, ap, append_theta(cfg), aq,
+                         rope_theta(cfg), n_append);
+    return hipGetLastError();
+  }
+  hipError_t e = launch_append(cfg, cache, cache_scale, num_blocks, c_kv, k_r, pos, seq_of, block_table, batch,
+                               max_blocks, n, stream);
+  if (e != hipSuccess) return e;
+  return launch_absorb_q(cfg, q_nope, q_rope, q_pos, w_uk, q_abs, T, stream);
 }
 
 }  // namespace mla

@@ -14,6 +14,9 @@ hipError_t launch_append(const mla_config_t&, void*, float*, int, const void*, c
                          const int32_t*, const int32_t*, int, int, int, hipStream_t);
 hipError_t launch_absorb_q(const mla_config_t&, const void*, const void*, const int32_t*, const void*, void*, int,
                            hipStream_t);
+hipError_t launch_append_absorb(const mla_config_t&, void*, float*, int, const void*, const void*, const int32_t*,
+                                const int32_t*, const int32_t*, int, int, int, const void*, const void*,
+                                const int32_t*, const void*, void*, int, hipStream_t);
 hipError_t launch_out_proj(const mla_config_t&, const float*, const void*, void*, int, hipStream_t);
 hipError_t launch_decode(const mla_config_t&, int, const void*, const void*, const float*, int,
                          const int32_t*, int, const int32_t*, int, int, void*, float*, float*, hipStream_t,
@@ -68,7 +71,7 @@ mla_status_t from_hip(hipError_t e) { return e == hipSuccess ? MLA_OK : MLA_ERR_
 
 extern "C" {
 
-int32_t mla_abi_version(void) { return 2; }
+int32_t mla_abi_version(void) { return 3; }
 
 const char* mla_status_string(mla_status_t s) {
   switch (s) {
@@ -81,10 +84,9 @@ const char* mla_status_string(mla_status_t s) {
   return "MLA_ERR_UNKNOWN";
 }
 
-mla_status_t mla_cache_append(const mla_config_t* cfg, void* cache, float* cache_scale, int32_t num_blocks,
-                              const void* c_kv, const void* k_r, const int32_t* pos, const int32_t* seq_of,
-                              const int32_t* block_table, int32_t batch, int32_t max_blocks, int32_t n,
-                              void* stream) {
+static mla_status_t check_append(const mla_config_t* cfg, void* cache, float* cache_scale, int32_t num_blocks,
+                                 const void* c_kv, const void* k_r, const int32_t* pos, const int32_t* seq_of,
+                                 const int32_t* block_table, int32_t batch, int32_t max_blocks, int32_t n) {
   mla_status_t st = check_cfg(cfg);
   if (st != MLA_OK) return st;
   if (n < 0 || num_blocks <= 0 || batch <= 0 || max_blocks <= 0) return MLA_ERR_INVALID_ARG;
@@ -93,6 +95,27 @@ mla_status_t mla_cache_append(const mla_config_t* cfg, void* cache, float* cache
   if (!aligned16(cache) || (n > 0 && (!aligned16(c_kv) || !aligned16(k_r)))) return MLA_ERR_INVALID_ARG;
   const bool fp8 = cfg->cache_dtype == MLA_FP8_E4M3;
   if (fp8 != (cache_scale != nullptr)) return MLA_ERR_INVALID_ARG;
+  return MLA_OK;
+}
+
+static mla_status_t check_absorb(const mla_config_t* cfg, const void* q_nope, const void* q_rope,
+                                 const int32_t* q_pos, const void* w_uk, void* q_abs, int32_t T) {
+  mla_status_t st = check_cfg(cfg);
+  if (st != MLA_OK) return st;
+  if (T < 0) return MLA_ERR_INVALID_ARG;
+  if (T == 0) return MLA_OK;
+  if (!q_nope || !q_rope || !q_pos || !w_uk || !q_abs) return MLA_ERR_INVALID_ARG;
+  if (!aligned16(q_nope) || !aligned16(q_rope) || !aligned16(w_uk) || !aligned16(q_abs)) return MLA_ERR_INVALID_ARG;
+  return MLA_OK;
+}
+
+mla_status_t mla_cache_append(const mla_config_t* cfg, void* cache, float* cache_scale, int32_t num_blocks,
+                              const void* c_kv, const void* k_r, const int32_t* pos, const int32_t* seq_of,
+                              const int32_t* block_table, int32_t batch, int32_t max_blocks, int32_t n,
+                              void* stream) {
+  mla_status_t st = check_append(cfg, cache, cache_scale, num_blocks, c_kv, k_r, pos, seq_of, block_table, batch,
+                                 max_blocks, n);
+  if (st != MLA_OK) return st;
   if (n == 0) return MLA_OK;
   return from_hip(mla::launch_append(*cfg, cache, cache_scale, num_blocks, c_kv, k_r, pos, seq_of, block_table,
                                      batch, max_blocks, n, static_cast<hipStream_t>(stream)));
@@ -100,14 +123,32 @@ mla_status_t mla_cache_append(const mla_config_t* cfg, void* cache, float* cache
 
 mla_status_t mla_absorb_q(const mla_config_t* cfg, const void* q_nope, const void* q_rope, const int32_t* q_pos,
                           const void* w_uk, void* q_abs, int32_t T, void* stream) {
-  mla_status_t st = check_cfg(cfg);
+  mla_status_t st = check_absorb(cfg, q_nope, q_rope, q_pos, w_uk, q_abs, T);
   if (st != MLA_OK) return st;
-  if (T < 0) return MLA_ERR_INVALID_ARG;
   if (T == 0) return MLA_OK;
-  if (!q_nope || !q_rope || !q_pos || !w_uk || !q_abs) return MLA_ERR_INVALID_ARG;
-  if (!aligned16(q_nope) || !aligned16(q_rope) || !aligned16(w_uk) || !aligned16(q_abs)) return MLA_ERR_INVALID_ARG;
   return from_hip(mla::launch_absorb_q(*cfg, q_nope, q_rope, q_pos, w_uk, q_abs, T,
                                        static_cast<hipStream_t>(stream)));
+}
+
+mla_status_t mla_append_absorb(const mla_config_t* cfg, void* cache, float* cache_scale, int32_t num_blocks,
+                               const void* c_kv, const void* k_r, const int32_t* pos, const int32_t* seq_of,
+                               const int32_t* block_table, int32_t batch, int32_t max_blocks, int32_t n,
+                               const void* q_nope, const void* q_rope, const int32_t* q_pos, const void* w_uk,
+                               void* q_abs, int32_t T, void* stream) {
+  mla_status_t st = check_append(cfg, cache, cache_scale, num_blocks, c_kv, k_r, pos, seq_of, block_table, batch,
+                                 max_blocks, n);
+  if (st != MLA_OK) return st;
+  st = check_absorb(cfg, q_nope, q_rope, q_pos, w_uk, q_abs, T);
+  if (st != MLA_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (n == 0 && T == 0) return MLA_OK;
+  if (T == 0)
+    return from_hip(mla::launch_append(*cfg, cache, cache_scale, num_blocks, c_kv, k_r, pos, seq_of, block_table,
+                                       batch, max_blocks, n, s));
+  if (n == 0) return from_hip(mla::launch_absorb_q(*cfg, q_nope, q_rope, q_pos, w_uk, q_abs, T, s));
+  return from_hip(mla::launch_append_absorb(*cfg, cache, cache_scale, num_blocks, c_kv, k_r, pos, seq_of,
+                                            block_table, batch, max_blocks, n, q_nope, q_rope, q_pos, w_uk, q_abs,
+                                            T, s));
 }
 
 size_t mla_decode_workspace_size(const mla_config_t* cfg, int32_t B, int32_t Sq, int32_t max_blocks) {

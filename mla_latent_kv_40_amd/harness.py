@@ -3,8 +3,9 @@
 Torch provides device memory and the stream; every computation is a libmla call:
 
     setup (untimed)  mla_cache_append of each sequence's context tokens
-    step             mla_cache_append (the Sq new tokens per sequence)
-                     mla_absorb_q -> mla_decode_attn -> mla_out_proj
+    step             mla_append_absorb (the Sq new tokens per sequence into the cache, and the
+                     folded queries; or mla_cache_append then mla_absorb_q)
+                     -> mla_decode_attn -> mla_out_proj
 
 Inputs come from ``workloads`` (seeded draws, no method arithmetic).  The tiny fp32 case
 starts from hidden states; its caller passes the per-sequence latent and query tensors.
@@ -110,6 +111,12 @@ class DecodeState:
     def absorb(self, stream=None) -> None:
         B.mla_absorb_q(self.cfg, self.q_nope, self.q_rope, self.new_pos, self.w_uk, self.q_abs, self.T, stream)
 
+    def append_absorb(self, stream=None) -> None:
+        """The step's new tokens into the cache and the folded queries, in one call."""
+        B.mla_append_absorb(self.cfg, self.cache, self.cache_scale, self.batch.num_blocks, self.new_c, self.new_k,
+                            self.new_pos, self.new_seq, self.block_table, self.w.batch, self.batch.max_blocks, self.T,
+                            self.q_nope, self.q_rope, self.new_pos, self.w_uk, self.q_abs, self.T, stream)
+
     def decode(self, stream=None) -> None:
         B.mla_decode_attn(self.cfg, self.q_abs, self.cache, self.cache_scale, self.batch.num_blocks,
                           self.block_table, self.batch.max_blocks, self.kv_lens, self.w.batch, self.w.sq,
@@ -129,10 +136,14 @@ class DecodeState:
     def out_proj(self, stream=None) -> None:
         B.mla_out_proj(self.cfg, self.o_lat, self.w_uv, self.out, self.T, stream)
 
-    def step(self, stream=None) -> None:
-        """One decode step: append the new tokens, fold the query, attend, project out."""
-        self.append(self.new_c, self.new_k, self.new_pos, self.new_seq, self.T, stream)
-        self.absorb(stream)
+    def step(self, stream=None, fused: bool = True) -> None:
+        """One decode step: append the new tokens, fold the query, attend, project out.
+        fused=False makes the append and the absorption two calls."""
+        if fused:
+            self.append_absorb(stream)
+        else:
+            self.append(self.new_c, self.new_k, self.new_pos, self.new_seq, self.T, stream)
+            self.absorb(stream)
         self.decode(stream)
         self.out_proj(stream)
 

@@ -26,7 +26,9 @@ def _gpu():
     torch.cuda.set_device(0)
 
 
-def run_state(w, bt, seqs, weights=None, poison=True):
+def run_state(w, bt, seqs, weights=None, poison=True, fused=True):
+    """One step; fused=False runs mla_cache_append and mla_absorb_q as two calls instead of
+    mla_append_absorb."""
     st = harness.DecodeState(w, bt, seqs, device="cuda", weights=weights)
     st.fill_context()
     if poison:
@@ -35,7 +37,7 @@ def run_state(w, bt, seqs, weights=None, poison=True):
         st.o_lat.fill_(float("nan"))
         st.lse.fill_(float("nan"))
         st.q_abs.view(torch.uint8).fill_(0xFF)
-    st.step()
+    st.step(fused=fused)
     torch.cuda.synchronize()
     return st
 
@@ -107,9 +109,9 @@ def dsv2(batch, lengths, sq=1, seed=7, name="dsv2_b16_l4k", fp8=False):
 
 
 def test_dsv2_edge_lengths_all_heads():
-    log("case dsv2 bf16 lengths [1, 63, 64, 65, 200], Sq=1, all heads")
+    log("case dsv2 bf16 lengths [1, 63, 64, 65, 200], Sq=1, all heads (append and absorb as two calls)")
     w, bt, seqs = dsv2(5, [1, 63, 64, 65, 200])
-    st = run_state(w, bt, seqs)
+    st = run_state(w, bt, seqs, fused=False)
     got = host(st)
     for b in range(w.batch):
         compare_seq(w, bt, seqs, got, b)

@@ -28,7 +28,7 @@ def test_exports_every_declared_symbol(L):
     assert set(syms) == set(B.EXPORTS), syms
     for s in syms:
         assert hasattr(L, s), s
-    assert B.mla_abi_version() == B.ABI_VERSION == 2
+    assert B.mla_abi_version() == B.ABI_VERSION == 3
 
 
 def cfg(**kw):
@@ -76,6 +76,25 @@ def test_pointer_and_size_validation(L):
                               check=False) == B.MLA_ERR_INVALID_ARG
     assert B.mla_cache_append(c, FAKE, None, 0, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 4, 3, stream=0,
                               check=False) == B.MLA_ERR_INVALID_ARG
+
+
+def test_append_absorb_validation(L):
+    c = cfg()
+    app = [FAKE, None, 8, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 4]      # cache .. max_blocks (bf16: no scale)
+    absq = [FAKE, FAKE, FAKE, FAKE, FAKE]                          # q_nope, q_rope, q_pos, w_uk, q_abs
+    # either half's validation fails the whole call before anything is launched
+    assert B.mla_append_absorb(c, *app, 3, 0, FAKE, FAKE, FAKE, FAKE, 4, stream=0,
+                               check=False) == B.MLA_ERR_INVALID_ARG          # null q_nope
+    assert B.mla_append_absorb(c, *app, 3, FAKE + 8, FAKE, FAKE, FAKE, FAKE, 4, stream=0,
+                               check=False) == B.MLA_ERR_INVALID_ARG          # misaligned q_nope
+    assert B.mla_append_absorb(c, FAKE, FAKE, 8, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 4, 3, *absq, 4, stream=0,
+                               check=False) == B.MLA_ERR_INVALID_ARG          # scale for a bf16 cache
+    assert B.mla_append_absorb(c, *app, -1, *absq, 4, stream=0, check=False) == B.MLA_ERR_INVALID_ARG
+    assert B.mla_append_absorb(c, *app, 3, *absq, -1, stream=0, check=False) == B.MLA_ERR_INVALID_ARG
+    c8 = cfg(cache_dtype="fp8")
+    assert B.mla_append_absorb(c8, *app, 3, *absq, 4, stream=0, check=False) == B.MLA_ERR_INVALID_ARG
+    # nothing to do on either side is a no-op that touches nothing
+    assert B.mla_append_absorb(c, *app, 0, 0, 0, 0, 0, 0, 0, stream=0, check=False) == B.MLA_OK
 
 
 def test_decode_workspace_checks(L):
