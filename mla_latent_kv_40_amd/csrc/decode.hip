@@ -1312,14 +1312,16 @@ __device__ void exact_head(const DecodeArgs& a, int b, int j, int h, int L, int 
 // of a group's 32 KiB block is its 1 KiB blocks 8c .. 8c+7 (column tiles 4c .. 4c+3, so columns
 // 128c .. 128c+127), contiguous in every slot: thread t reads its 16-byte pieces t + 256i
 // (i < 2, eight values each), all of head 32w + t%32, so each thread needs one head's
-// weights.  The pieces and (m, l) of kCombineBatch slots are requested together,
-// so a sequence's slots cost about one memory latency rather than one each.  The result goes
+// weights.  The pieces and (m, l) of KB slots are requested together, so a sequence's slots
+// cost about one memory latency rather than one each; KB = 8 where sequences span many
+// ranges, else 4 (its registers allow more workgroups per CU).  The result goes
 // through LDS so that each head's 128 columns are written contiguously.  Heads marked by the
 // fast path (or whose sums are not finite) are then recomputed exactly, quarter by quarter.
-constexpr int kCombineBatch = 8;
 constexpr int kCombinePitch = 128 + 4;   // fp32 words per head in the LDS tile (spreads heads over banks)
 
+template <int KB>
 __global__ void __launch_bounds__(256) combine_kernel(DecodeArgs a) {
+  constexpr int kCombineBatch = KB;
   __shared__ __attribute__((aligned(16))) float tile[32 * kCombinePitch];   // [32 heads][128 columns]
   __shared__ int redo_mask;                                                 // heads to recompute
   const int row = blockIdx.x;          // b*Sq + j
@@ -1617,7 +1619,11 @@ hipError_t launch_decode(const mla_config_t& cfg, int num_cus, const void* q_abs
       if (e != hipSuccess) return e;
     }
     if (phases & 2) {
-      hipLaunchKernelGGL(combine_kernel, dim3(B * Sq, kH / 32, 4), dim3(256), 0, stream, a);
+      // a sequence spans about G / B + 1 ranges
+      if (G >= 3 * B)
+        hipLaunchKernelGGL(combine_kernel<8>, dim3(B * Sq, kH / 32, 4), dim3(256), 0, stream, a);
+      else
+        hipLaunchKernelGGL(combine_kernel<4>, dim3(B * Sq, kH / 32, 4), dim3(256), 0, stream, a);
     }
     return hipGetLastError();
   }
