@@ -311,6 +311,7 @@ def test_fp8_extreme_scores_take_the_exact_path():
 @pytest.mark.parametrize("name,sample", [
     ("dsv2_b16_l4k", [(0, None), (15, None)]),
     ("dsv2_b64_l1k_32k", [("shortest", range(0, 128, 16)), ("longest", range(3, 128, 16))]),
+    ("dsv2_b64_l32k", [(0, range(0, 128, 16)), (63, range(7, 128, 16))]),
     ("dsv2_b32_l8k_sq4", [(0, range(0, 128, 8)), (31, range(5, 128, 16))]),
     ("dsv2_b128_l8k_fp8", [(0, range(0, 128, 8)), (127, range(5, 128, 16))]),
 ])
