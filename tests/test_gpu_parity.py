@@ -145,6 +145,19 @@ def test_ragged_row_blocks_absorb_and_out_proj():
         compare_seq(w, bt, seqs, got, b, heads=range(b % 3, 128, 9))
 
 
+def test_many_short_sequences():
+    log("case dsv2 bf16 B=300 sequences of 1..40 tokens: several 256-sequence chunks in the page-table"
+        " build, ranges that own no page or span many sequences, five 64-row blocks")
+    rng = np.random.default_rng(51)
+    lengths = rng.integers(1, 41, size=300)
+    w, bt, seqs = dsv2(300, lengths, seed=51)
+    st = run_state(w, bt, seqs)
+    got = host(st)
+    assert np.all(np.isfinite(got["o"]))
+    for b in (0, 63, 64, 255, 256, 299):
+        compare_seq(w, bt, seqs, got, b, heads=range(b % 5, 128, 11))
+
+
 def test_causal_multi_query_sq4():
     log("case dsv2 bf16 Sq=4 causal, lengths [4, 68, 129, 300]")
     w, bt, seqs = dsv2(4, [4, 68, 129, 300], sq=4, seed=13)
