@@ -158,6 +158,21 @@ def test_many_short_sequences():
         compare_seq(w, bt, seqs, got, b, heads=range(b % 5, 128, 11))
 
 
+@pytest.mark.parametrize("fp8", [False, True])
+def test_split_then_combine_equals_decode_attn(fp8):
+    log(f"case mla_decode_split + mla_decode_combine (the bench's calls) against mla_decode_attn, fp8={fp8}")
+    w, bt, seqs = dsv2(4, [3000, 65, 1, 700], seed=61, fp8=fp8)
+    st = run_state(w, bt, seqs)
+    o_ref, lse_ref = st.o_lat.clone(), st.lse.clone()
+    st.o_lat.fill_(float("nan"))
+    st.lse.fill_(float("nan"))
+    st.workspace.view(torch.float32)[: st.ws_bytes // 4].fill_(float("nan"))
+    st.decode_split()
+    st.decode_combine()
+    torch.cuda.synchronize()
+    assert torch.equal(st.o_lat, o_ref) and torch.equal(st.lse, lse_ref)
+
+
 def test_causal_multi_query_sq4():
     log("case dsv2 bf16 Sq=4 causal, lengths [4, 68, 129, 300]")
     w, bt, seqs = dsv2(4, [4, 68, 129, 300], sq=4, seed=13)
