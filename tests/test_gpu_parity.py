@@ -159,6 +159,24 @@ def test_many_short_sequences():
 
 
 @pytest.mark.parametrize("fp8", [False, True])
+def test_append_absorb_equals_the_two_calls(fp8):
+    log(f"case mla_append_absorb against mla_cache_append + mla_absorb_q (cache rows, scales, q_abs), fp8={fp8}")
+    w, bt, seqs = dsv2(70, np.arange(1, 71) * 7, seed=67, fp8=fp8)   # 70 query rows: two row blocks
+    fused = run_state(w, bt, seqs, fused=True)
+    apart = run_state(w, bt, seqs, fused=False)
+    # the written rows (slots past a sequence's length are never written: uninitialised memory)
+    for b in range(w.batch):
+        L = int(bt.kv_lens[b])
+        pages = torch.as_tensor(bt.block_table[b, (np.arange(L) // 64)], device=fused.cache.device, dtype=torch.long)
+        slots = torch.as_tensor(np.arange(L) % 64, device=fused.cache.device, dtype=torch.long)
+        assert torch.equal(fused.cache[pages, slots], apart.cache[pages, slots]), b
+        if fp8:
+            assert torch.equal(fused.cache_scale[pages, slots], apart.cache_scale[pages, slots]), b
+    assert torch.equal(fused.q_abs, apart.q_abs)
+    assert torch.equal(fused.out, apart.out)
+
+
+@pytest.mark.parametrize("fp8", [False, True])
 def test_split_then_combine_equals_decode_attn(fp8):
     log(f"case mla_decode_split + mla_decode_combine (the bench's calls) against mla_decode_attn, fp8={fp8}")
     w, bt, seqs = dsv2(4, [3000, 65, 1, 700], seed=61, fp8=fp8)
