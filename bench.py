@@ -7,17 +7,25 @@ The default workload is DeepSeek-V2-shaped bf16 decode at batch 64 with context 
 drawn uniformly from [1024, 32768] (synthetic, seeded).  Inputs are resident in HBM before
 the timed region.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--settle-ms MS] [--workload NAME] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--settle-ms MS] [--workload NAME]
+                    [--no-cpu-baseline] [--no-configs] [--warm]
 
-Before the W warm-up steps, untimed steps run for at least MS milliseconds (default 300): from
-idle the GPU's clocks take ~100 steps to settle, and the timed steps measure the steady state.
+Timing.  Before every step (settle, warm-up and timed) a 512 MiB buffer is written, outside
+the timed events, so that no step starts with the latent cache in the 256 MB last-level cache
+(a decode step of one layer follows other layers' work in a model).  Each timed step is
+bracketed by HIP events on the launch stream: step (all kernels), split (K1), combine (K2).
+Untimed steps run for at least MS milliseconds first (default 300): from idle the GPU's clocks
+take ~100 steps to settle.  --warm adds the same measurement without the buffer writes.
 
-value       query tokens decoded per second (B*Sq per step / mean step time)
-roofline    the split-K decode kernel: latent-cache bytes it must read per launch (1152 B per
-            visible cached token in bf16, 580 B in fp8 incl. the scale) / its mean duration,
-            against 8 TB/s; durations from HIP events on the launch stream.  traffic = HBM bytes
-            per launch measured by rocprofv3 counters (profiles/decode_hbm_traffic.md), null
-            when the kernel source differs from the one those counters were taken on
+value       query tokens decoded per second: B*Sq / mean step time (flushed steps)
+roofline    the split-K decode (K1 split + K2 combine): latent-cache bytes it must read per step
+            (1152 B per cached token in bf16, 580 B in fp8 incl. the scale) / mean(K1 + K2),
+            against 8 TB/s; the K1-only figure alongside.  traffic = HBM bytes per step of K1 + K2
+            from rocprofv3 counters (profiles/decode_hbm_traffic.md), null when the kernel source
+            differs from the one those counters were taken on
+configs     the same measurement (shorter) for each DeepSeek-V2-shaped workload and the tiny
+            fp32 case, with its bound and roofline fraction, and the oracle's max error / tolerance
+            on the sequences its CPU sample covers
 cpu_baseline the fp64 oracle on the host cores, on a bounded sample of the same workload
 """
 from __future__ import annotations
@@ -25,6 +33,8 @@ from __future__ import annotations
 import argparse
 import json
 import os
+import shutil
+import subprocess
 import sys
 import time
 
@@ -36,26 +46,30 @@ sys.path.insert(0, ROOT)
 PEAK_HBM_GBS = 8000.0
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_FP8_TFLOPS = 5000.0
+PEAK_FP32_TFLOPS = 157.3
 METRIC = "MLA decode tokens/s + latent-cache GB/s & TFLOP/s (% peak) at B=64, 32k ctx"
+FLUSH_BYTES = 512 << 20
+# the five workloads of the task's configuration list, in its order (the first is latency-bound)
+CONFIGS = ["tiny_f32", "dsv2_b16_l4k", "dsv2_b64_l1k_32k", "dsv2_b32_l8k_sq4", "dsv2_b128_l8k_fp8"]
 
 
 def algorithmic(w, kv_lens):
-    """Bytes the decode kernel must read (the latent cache rows of every visible token) and
-    the FLOPs of the latent-space attention: 2*H*(2*d_c + d_R) per visible (query, token)."""
+    """Bytes the decode must read (the latent cache rows of every cached token) and the FLOPs of
+    the latent-space attention: 2*H*(2*d_c + d_R) per visible (query, token)."""
     kv = kv_lens.astype(np.int64)
     tokens = int(kv.sum())
     per_tok = w.row * (1 if w.dtype == "fp8" else 2 if w.dtype == "bf16" else 4) + (4 if w.dtype == "fp8" else 0)
     visible = 0
     for j in range(w.sq):
-        visible += int((kv - w.sq + j + 1).sum())
+        visible += int(np.maximum(kv - w.sq + j + 1, 0).sum())
     flops = visible * 2 * w.heads * (2 * w.d_c + w.d_r)
     return tokens * per_tok, flops, tokens
 
 
-def measured_traffic(kernel, workload):
-    """HBM bytes per launch of `kernel` on `workload` from the committed rocprofv3 counter summary
-    (FETCH_SIZE and WRITE_SIZE, scaled by a calibration copy), or None when that summary was
-    taken on a different decode.hip than the one built here."""
+def measured_traffic(workload):
+    """HBM bytes per step of the split and combine kernels on `workload` from the committed
+    rocprofv3 counter summary (FETCH_SIZE and WRITE_SIZE, scaled by a calibration copy), or None
+    when that summary was taken on a different decode.hip than the one built here."""
     import hashlib
     src = os.path.join(ROOT, "mla_latent_kv_40_amd", "csrc", "decode.hip")
     prof = os.path.join(ROOT, "profiles", "decode_hbm_traffic.md")
@@ -64,13 +78,32 @@ def measured_traffic(kernel, workload):
     sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
     for line in open(prof):
         f = line.split()
-        if len(f) == 6 and f[0] == "traffic" and f[1] == kernel and f[2] == workload and f[5] == sha:
-            return int(f[3])
+        if len(f) == 5 and f[0] == "traffic" and f[1] == workload and f[4] == sha:
+            return int(f[2])
     return None
 
 
-def cpu_baseline(w, bt, budget_s=20.0):
-    """Time the fp64 oracle on whole sequences near the batch's mean length until ~budget."""
+def gpu_clock_mhz():
+    """Current shader clock of GPU 0 from rocm-smi (None if it cannot be read)."""
+    smi = shutil.which("rocm-smi") or "/opt/rocm/bin/rocm-smi"
+    try:
+        r = subprocess.run([smi, "--showclocks", "--json"], capture_output=True, text=True, timeout=20)
+        d = json.loads(r.stdout)
+    except Exception:
+        return None
+    for card in d.values():
+        for k, v in card.items():
+            if "sclk" in k.lower() and "clock" in k.lower():
+                try:
+                    return float(str(v).strip("()Mhz MHz"))
+                except ValueError:
+                    pass
+    return None
+
+
+def cpu_baseline(w, bt, seqs_gpu_out, budget_s=20.0, heads=None):
+    """Time the fp64 oracle on whole sequences near the batch's mean length until ~budget, and
+    compare its outputs with the GPU's (max error / tolerance of the oracle gate, 4x for fp8)."""
     import oracle.mla_oracle as orc
     from mla_latent_kv_40_amd import workloads as wl
     try:
@@ -79,34 +112,179 @@ def cpu_baseline(w, bt, budget_s=20.0):
     except Exception:
         threads = len(os.sched_getaffinity(0))
     kv = bt.kv_lens.astype(np.int64)
-    order = np.argsort(np.abs(kv - kv.mean()))
-    done, toks, t0 = 0, 0, time.perf_counter()
+    order = np.argsort(np.abs(kv - kv.mean()), kind="stable")
+    done, t0 = 0, time.perf_counter()
     picked = []
+    worst = 0.0
+    factor = 4.0 if w.dtype == "fp8" else 1.0
+    hs = list(range(w.heads)) if heads is None else list(heads)
     for b in order:
-        s = wl.draw_sequence(w, int(b), int(kv[b]))
-        orc.decode(s["c"], s["k_r"], s["q_c"], s["q_r"], bt.weights["W_UK"], bt.weights["W_UV"], int(kv[b]),
-                   w.softmax_scale, w.rope_base)
+        b = int(b)
+        if w.d_model is not None:   # the tiny case starts at hidden states
+            W = bt.weights
+            L = int(kv[b])
+            C, KR, qC, qR = orc.project_from_hidden(W["x"], W["W_down"], W["W_KR"], W["W_Q"], W["W_QR"], w.heads,
+                                                    w.d_h, w.d_r, list(range(L - w.sq, L)))
+            s = {"c": C, "k_r": KR, "q_c": qC, "q_r": qR}
+        else:
+            s = wl.draw_sequence(w, b, int(kv[b]))
+        ref = orc.decode(s["c"], s["k_r"], s["q_c"], s["q_r"], bt.weights["W_UK"], bt.weights["W_UV"], int(kv[b]),
+                         w.softmax_scale, w.rope_base, heads=hs)
         done += w.sq
-        toks += int(kv[b])
         picked.append(int(kv[b]))
+        rows = slice(b * w.sq, (b + 1) * w.sq)
+        for k in ("o", "o_lat", "lse"):
+            got = seqs_gpu_out[k][rows][:, hs].astype(np.float64)
+            tol = factor * (2e-2 * float(np.max(np.abs(ref[k]))) + 1e-3)
+            worst = max(worst, float(np.max(np.abs(got - ref[k]))) / tol)
         if time.perf_counter() - t0 > budget_s:
             break
     dt = time.perf_counter() - t0
-    return {"value": done / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{len(picked)} of {w.batch} sequences (kv_len {picked}, nearest the batch mean "
-                      f"{kv.mean():.0f}), all {w.heads} heads, fp64 numpy, {dt:.1f} s"}
+    scale = w.heads / len(hs)
+    return {"value": done / (dt * scale), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{len(picked)} of {w.batch} sequences (kv_len {picked[:24]}{' ...' if len(picked) > 24 else ''}, "
+                      f"nearest the batch mean {kv.mean():.0f}), {len(hs)} of {w.heads} heads (rate scaled to all "
+                      f"heads), fp64 numpy, {dt:.1f} s",
+            "max_err_over_tol": round(worst, 4)}
+
+
+def run_workload(name, steps, warmup, settle_ms, flush, warm, cpu_budget, log):
+    import torch
+    from mla_latent_kv_40_amd import harness, workloads as wl
+
+    w = wl.get(name)
+    log(f"[bench] workload {w.name}: {w.description}")
+    t = time.perf_counter()
+    bt = wl.draw_batch(w)
+    if w.d_model is not None:
+        W = {k: np.asarray(v, dtype=np.float64) for k, v in bt.weights.items()}
+        L = int(bt.kv_lens[0])
+        x = W["x"]
+        xq = x[L - w.sq:L]
+        seqs = [{"c": (x @ W["W_down"]).astype(np.float32), "k_r": (x @ W["W_KR"]).astype(np.float32),
+                 "q_c": (xq @ W["W_Q"]).reshape(w.sq, w.heads, w.d_h).astype(np.float32),
+                 "q_r": (xq @ W["W_QR"]).reshape(w.sq, w.heads, w.d_r).astype(np.float32)}]
+    else:
+        seqs = harness.draw_all_sequences(w, bt)
+    st = harness.DecodeState(w, bt, seqs, device="cuda:0")
+    del seqs
+    st.fill_context()
+    log(f"[bench] setup {time.perf_counter() - t:.1f} s, cache {st.cache.numel() * st.cache.element_size() / 1e9:.2f} GB")
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        st.append_absorb()
+        if ev is not None:
+            ev[1].record(stream)
+        st.decode_split()
+        if ev is not None:
+            ev[2].record(stream)
+        st.decode_combine()
+        if ev is not None:
+            ev[3].record(stream)
+        st.out_proj()
+        if ev is not None:
+            ev[4].record(stream)
+
+    def timed(n, with_flush):
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(n)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(n):
+            if with_flush:
+                flush.fill_(i & 255)
+            step(evs[i])
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        ms = np.array([[e[0].elapsed_time(e[4]), e[1].elapsed_time(e[2]), e[2].elapsed_time(e[3])] for e in evs])
+        return ms, wall
+
+    # settle (the clocks leave their idle state) and warm up, under the same conditions as the
+    # timed steps
+    t_settle = time.perf_counter()
+    settle_steps = 0
+    while (time.perf_counter() - t_settle) * 1e3 < settle_ms:
+        for _ in range(10):
+            flush.fill_(settle_steps & 255)
+            step()
+            settle_steps += 1
+        torch.cuda.synchronize()
+    for i in range(warmup):
+        flush.fill_(i & 255)
+        step()
+    torch.cuda.synchronize()
+    ms, wall = timed(steps, True)
+    # the shader clock under this load: queue ~200 ms of steps, read the clock while they run
+    n_clk = max(1, int(200.0 / max(float(ms[:, 0].mean()), 1e-3)))
+    for i in range(n_clk):
+        flush.fill_(i & 255)
+        step()
+    clk = gpu_clock_mhz()
+    torch.cuda.synchronize()
+
+    bytes_alg, flops, tokens = algorithmic(w, bt.kv_lens)
+    step_ms, k1_ms, k2_ms = ms[:, 0], ms[:, 1], ms[:, 2]
+    k12_ms = k1_ms + k2_ms
+    peak_mfma = {"fp8": PEAK_FP8_TFLOPS, "bf16": PEAK_BF16_TFLOPS}.get(w.dtype, PEAK_FP32_TFLOPS)
+    intensity = flops / bytes_alg
+    hbm_bound = intensity < peak_mfma * 1e12 / (PEAK_HBM_GBS * 1e9)
+
+    def roof(t_ms):
+        gbs = bytes_alg / (t_ms * 1e-3) / 1e9
+        tfl = flops / (t_ms * 1e-3) / 1e12
+        if hbm_bound:
+            return {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                    "frac": round(gbs / PEAK_HBM_GBS, 4)}
+        return {"bound": "mfma", "achieved": round(tfl, 1), "peak": peak_mfma, "unit": "TFLOP/s",
+                "frac": round(tfl / peak_mfma, 4)}
+
+    def pct(x):
+        return {"mean": round(float(x.mean()), 4), "median": round(float(np.median(x)), 4),
+                "p10": round(float(np.percentile(x, 10)), 4), "p90": round(float(np.percentile(x, 90)), 4),
+                "min": round(float(x.min()), 4)}
+
+    k1_name = ("decode_mfma_fp8_kernel" if w.dtype == "fp8" else "decode_mfma_bf16_kernel" if w.dtype == "bf16"
+               else "decode_generic_kernel")
+    r = {
+        "workload": w.name, "batch": w.batch, "sq": w.sq, "dtype": w.dtype, "kv_tokens": tokens,
+        "kv_len_min": int(bt.kv_lens.min()), "kv_len_max": int(bt.kv_lens.max()),
+        "tokens_per_s": round(w.batch * w.sq / (float(step_ms.mean()) * 1e-3), 1),
+        "ms_per_step": round(float(step_ms.mean()), 4), "wall_ms_per_step_incl_flush": round(wall * 1e3 / steps, 4),
+        "step_ms": pct(step_ms), "k1_split_ms": pct(k1_ms), "k2_combine_ms": pct(k2_ms), "k1_k2_ms": pct(k12_ms),
+        "bytes": bytes_alg, "flops": flops, "flop_per_byte": round(intensity, 1),
+        "roofline": dict(roof(float(k12_ms.mean())), kernel=f"{k1_name} + combine_kernel"),
+        "roofline_k1_only": dict(roof(float(k1_ms.mean())), kernel=k1_name),
+        "mfma_frac_k1_k2": round(flops / (float(k12_ms.mean()) * 1e-3) / 1e12 / peak_mfma, 4),
+        "sclk_mhz_under_load": clk, "settle_steps": settle_steps,
+    }
+    if warm:
+        ms_w, _ = timed(steps, False)
+        r["warm_no_flush"] = {"ms_per_step": round(float(ms_w[:, 0].mean()), 4),
+                              "k1_k2_ms": pct(ms_w[:, 1] + ms_w[:, 2])}
+    if cpu_budget > 0:
+        log(f"[bench] cpu baseline (fp64 oracle, ~{cpu_budget:.0f} s) ...")
+        got = {"o": st.out.float().cpu().numpy(), "o_lat": st.o_lat.cpu().numpy(), "lse": st.lse.cpu().numpy()}
+        heads = None if cpu_budget >= 10 else list(range(0, w.heads, max(1, w.heads // 16)))
+        r["cpu_baseline"] = cpu_baseline(w, bt, got, budget_s=cpu_budget, heads=heads)
+    del st
+    torch.cuda.empty_cache()
+    return r
 
 
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=500)
-    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--settle-ms", type=float, default=300.0,
                     help="untimed steps for at least this long before the warm-up steps (the GPU leaves "
                          "its idle clocks over the first ~100 steps)")
     ap.add_argument("--workload", default="dsv2_b64_l1k_32k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-configs", action="store_true", help="skip the per-configuration measurements")
+    ap.add_argument("--warm", action="store_true", help="also time the steps without the cache flush")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a 256 MiB device-to-device copy 3 times (scales HBM counters)")
     a = ap.parse_args()
@@ -120,88 +298,62 @@ def main() -> int:
         print(json.dumps({"copy_bytes": 1 << 28, "runs": 3}))
         return 0
     if a.gpus != 1:
-        print(f"bench.py runs on one GPU only (got --gpus {a.gpus}): the decode path is a single-GPU "
-              "kernel; a multi-GPU split would shard whole sequences per GPU.", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (got --gpus {a.gpus}): this build measures the decode path on "
+              "one GPU; a multi-GPU run would shard whole sequences per GPU and is not provided.", file=sys.stderr)
         return 2
 
     import torch
-    from mla_latent_kv_40_amd import harness, workloads as wl
+
+    def log(msg):
+        print(msg, file=sys.stderr, flush=True)
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
-    w = wl.get(a.workload)
-    print(f"[bench] workload {w.name}: {w.description}", file=sys.stderr, flush=True)
-    t = time.perf_counter()
-    bt = wl.draw_batch(w)
-    seqs = harness.draw_all_sequences(w, bt)
-    st = harness.DecodeState(w, bt, seqs, device="cuda:0")
-    del seqs
-    st.fill_context()
-    print(f"[bench] setup {time.perf_counter() - t:.1f} s, cache {st.cache.numel() * st.cache.element_size() / 1e9:.2f} GB",
-          file=sys.stderr, flush=True)
-    stream = torch.cuda.current_stream()
+    flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda:0")
+    main_r = run_workload(a.workload, a.steps, a.warmup, a.settle_ms, flush, a.warm,
+                          0.0 if a.no_cpu_baseline else 20.0, log)
+    configs = {}
+    if not a.no_configs:
+        for name in CONFIGS:
+            if name == a.workload:
+                configs[name] = {k: main_r[k] for k in ("tokens_per_s", "ms_per_step", "k1_k2_ms", "roofline",
+                                                        "flop_per_byte", "sclk_mhz_under_load")}
+                if "cpu_baseline" in main_r:
+                    configs[name]["max_err_over_tol"] = main_r["cpu_baseline"]["max_err_over_tol"]
+                continue
+            r = run_workload(name, 50, 10, 100.0, flush, False, 0.0 if a.no_cpu_baseline else 3.0, log)
+            configs[name] = {k: r[k] for k in ("tokens_per_s", "ms_per_step", "k1_k2_ms", "roofline",
+                                               "flop_per_byte", "sclk_mhz_under_load")}
+            if "cpu_baseline" in r:
+                configs[name]["max_err_over_tol"] = r["cpu_baseline"]["max_err_over_tol"]
+                configs[name]["oracle_sample"] = r["cpu_baseline"]["sample"]
 
-    def step(ev=None):
-        st.append_absorb()
-        if ev is not None:
-            ev[0].record(stream)
-        st.decode_split()
-        if ev is not None:
-            ev[1].record(stream)
-        st.decode_combine()
-        st.out_proj()
-
-    # a GPU coming out of idle runs the first ~100 steps ~10% slower while its clocks ramp up;
-    # steady-state throughput is measured after an untimed settle period and the warm-up steps
-    t_settle = time.perf_counter()
-    settle_steps = 0
-    while (time.perf_counter() - t_settle) * 1e3 < a.settle_ms:
-        for _ in range(10):
-            step()
-        settle_steps += 10
-        torch.cuda.synchronize()
-    for _ in range(a.warmup):
-        step()
-    torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(a.steps)]
-    t0 = time.perf_counter()
-    for i in range(a.steps):
-        step(evs[i])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    split_ms = np.array([e0.elapsed_time(e1) for e0, e1 in evs])
-    ms_per_step = wall * 1e3 / a.steps
-
-    bytes_alg, flops, tokens = algorithmic(w, bt.kv_lens)
-    k_s = float(split_ms.mean()) * 1e-3
-    gbs = bytes_alg / k_s / 1e9
-    tflops = flops / k_s / 1e12
-    peak_mfma = PEAK_FP8_TFLOPS if w.dtype == "fp8" else PEAK_BF16_TFLOPS
-    # the kernel is bound by whichever roof it is closer to
-    bound_hbm = gbs / PEAK_HBM_GBS >= tflops / peak_mfma
-    roof = ({"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-             "frac": round(gbs / PEAK_HBM_GBS, 4)} if bound_hbm else
-            {"bound": "mfma", "achieved": round(tflops, 1), "peak": peak_mfma, "unit": "TFLOP/s",
-             "frac": round(tflops / peak_mfma, 4)})
-    roof["kernel"] = "decode_mfma_fp8_kernel" if w.dtype == "fp8" else "decode_mfma_bf16_kernel"
-    roof["traffic"] = measured_traffic(roof["kernel"], w.name)
-    value = w.batch * w.sq / (ms_per_step * 1e-3)
+    roof = dict(main_r["roofline"])
+    roof["traffic"] = measured_traffic(main_r["workload"])
     line = {
-        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": a.steps,
-        "warmup": a.warmup, "settle": {"steps": settle_steps, "ms": a.settle_ms}, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": w.dtype, "data": "synthetic (seeded N(0,1) latents/queries, N(0,1/fan_in) weights)",
-        "config": {"workload": w.name, "batch": w.batch, "sq": w.sq, "kv_tokens": tokens,
-                   "kv_len_min": int(bt.kv_lens.min()), "kv_len_max": int(bt.kv_lens.max()),
-                   "heads": w.heads, "d_c": w.d_c, "d_r": w.d_r, "page_tokens": 64, "parallelism": "none"},
+        "metric": METRIC, "value": main_r["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1, "steps": a.steps,
+        "warmup": a.warmup, "settle": {"steps": main_r["settle_steps"], "ms": a.settle_ms},
+        "ms_per_step": main_r["ms_per_step"], "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": main_r["dtype"],
+        "data": "synthetic (seeded N(0,1) latents/queries, N(0,1/fan_in) weights)",
+        "config": {"workload": main_r["workload"], "batch": main_r["batch"], "sq": main_r["sq"],
+                   "kv_tokens": main_r["kv_tokens"], "kv_len_min": main_r["kv_len_min"],
+                   "kv_len_max": main_r["kv_len_max"], "heads": 128, "d_c": 512, "d_r": 64, "page_tokens": 64,
+                   "parallelism": "none", "llc_flush_bytes_between_steps": FLUSH_BYTES},
         "roofline": roof,
-        "decode_split": {"ms": round(float(split_ms.mean()), 4), "ms_min": round(float(split_ms.min()), 4),
-                         "cache_GBps": round(gbs, 1), "cache_frac_of_8TBps": round(gbs / PEAK_HBM_GBS, 4),
-                         "TFLOPs": round(tflops, 1), "mfma_frac": round(tflops / peak_mfma, 4),
-                         "bytes": bytes_alg, "flops": flops},
+        "roofline_k1_only": main_r["roofline_k1_only"],
+        "timing_ms": {k: main_r[k] for k in ("step_ms", "k1_split_ms", "k2_combine_ms", "k1_k2_ms")},
+        "wall_ms_per_step_incl_flush": main_r["wall_ms_per_step_incl_flush"],
+        "mfma_frac_k1_k2": main_r["mfma_frac_k1_k2"],
+        "sclk_mhz_under_load": main_r["sclk_mhz_under_load"],
+        "bytes_per_step": main_r["bytes"], "flops_per_step": main_r["flops"],
     }
-    if not a.no_cpu_baseline:
-        print("[bench] cpu baseline (fp64 oracle) ...", file=sys.stderr, flush=True)
-        line["cpu_baseline"] = cpu_baseline(w, bt)
+    if "warm_no_flush" in main_r:
+        line["warm_no_flush"] = main_r["warm_no_flush"]
+    if configs:
+        line["configs"] = configs
+    if "cpu_baseline" in main_r:
+        line["cpu_baseline"] = main_r["cpu_baseline"]
     print(json.dumps(line), flush=True)
     return 0
 

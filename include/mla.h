@@ -141,8 +141,10 @@ mla_status_t mla_append_absorb(const mla_config_t* cfg, void* cache, float* cach
 /*
  * mla_decode_workspace_size -- bytes of scratch mla_decode_attn needs for batch B,
  * Sq queries per sequence and block tables of width max_blocks on the current device.
- * Returns 0 for invalid arguments.  The value depends only on these arguments and the
- * device's compute-unit count (it bounds the split-K partial results).
+ * Returns 0 for invalid arguments.  The value depends only on these arguments, the
+ * device's compute-unit count and the test-only environment override MLA_FORCE_SPLITS (a
+ * number of token ranges; it must be the same here and in the decode calls that use the
+ * workspace).  It bounds the split-K partial results.
  */
 size_t mla_decode_workspace_size(const mla_config_t* cfg, int32_t B, int32_t Sq,
                                  int32_t max_blocks);
@@ -158,11 +160,14 @@ size_t mla_decode_workspace_size(const mla_config_t* cfg, int32_t B, int32_t Sq,
  *   lse[t,i]   = log sum_s exp(score[s])                         ([T, H] fp32, natural log)
  * FP8: row values are code*cache_scale.  The matrix instructions take e4m3 operands: each
  * head's query becomes two e4m3 terms (hi + lo/16 with one fp32 scale, about 8 significant
- * bits) and the probabilities one e4m3 term per token with a power-of-two block scale.
+ * bits), and so do the probabilities (hi + lo/16 per token, with a power-of-two block scale).
  * The token range is split across workgroups (split-K); partial results go to `workspace`
- * and are merged by a log-sum-exp combine.  A sequence with kv_len <= 0 gives o_lat = 0 and
- * lse = -inf.  Preconditions: Sq <= kv_len[b] <= 64*max_blocks (longer lengths are clamped
- * to the table), pages in [0, num_blocks) (tokens on other pages are skipped).
+ * and are merged by a log-sum-exp combine.  A query row that sees no token gives o_lat = 0 and
+ * lse = -inf: every row of a sequence with kv_len <= 0, and row j of a sequence with
+ * kv_len < Sq when its position p = kv_len - Sq + j is negative (the rows with p >= 0 attend
+ * to tokens 0 .. p as usual).  kv_len[b] <= 64*max_blocks (longer lengths are clamped to the
+ * table); pages in [0, num_blocks) (tokens on other pages are skipped).  Lengths live in
+ * device memory and are not read on the host, so these cases are results, not errors.
  *
  *   q_abs       [T, H, d_c + d_R] act_dtype (mla_absorb_q output)
  *   cache       [num_blocks, 64, d_c + d_R]                 cache_scale [num_blocks, 64] or NULL
@@ -208,7 +213,7 @@ mla_status_t mla_out_proj(const mla_config_t* cfg, const float* o_lat, const voi
 /* Human-readable name of a status code (static storage). */
 const char* mla_status_string(mla_status_t status);
 
-/* ABI version of this header: 2. */
+/* ABI version of this header: 3. */
 int32_t mla_abi_version(void);
 
 #ifdef __cplusplus

@@ -62,8 +62,8 @@ def lib() -> ctypes.CDLL:
         L.mla_status_string.argtypes = [ctypes.c_int]
         L.mla_status_string.restype = ctypes.c_char_p
         L.mla_abi_version.restype = ctypes.c_int32
-        for name in ("mla_cache_append", "mla_absorb_q", "mla_append_absorb", "mla_decode_attn", "mla_decode_split", "mla_decode_combine",
-                     "mla_out_proj"):
+        for name in ("mla_cache_append", "mla_absorb_q", "mla_append_absorb", "mla_decode_attn", "mla_decode_split",
+                     "mla_decode_combine", "mla_out_proj"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib

@@ -25,6 +25,8 @@
 //             (m, l) per head to workspace slot g + b; the combine normalises.
 #include "common.h"
 
+#include <atomic>
+#include <cstdlib>
 #include <type_traits>
 
 namespace mla {
@@ -1004,7 +1006,7 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_fp8_kernel(DecodeArgs a) {
   struct Soft {
     float m_new, l_new;
     bool over_new;
-    i32x8 p;
+    i32x8 p, plo;   // Pt ~ hi + lo/16, two e4m3 terms
     int sb;
   };
   struct SoftState {
@@ -1014,8 +1016,8 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_fp8_kernel(DecodeArgs a) {
     int e;          // block-scale exponent of Pt
     float lsum;
     f32x4 c[2];     // scales: in use / in flight
-    int w;          // first half of a block's packed Pt
-    int pk[8];
+    int w, wl;      // first half of a block's packed Pt terms
+    int pk[8], pl[8];
   };
   auto soft_piece = [&](int p, f32x16& s0, f32x16& s1, const uint8_t* tile, int vis, bool fresh, SoftState& q,
                         Soft& st) {
@@ -1086,24 +1088,32 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_fp8_kernel(DecodeArgs a) {
       const float u1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[4 * (d & 3) + k0 + 1], kq, q.neg));
       q.lsum += u0;
       q.lsum += u1;
-      // the empty asm statements pin the piece between its MFMAs (otherwise the compiler sinks
-      // this arithmetic below the loop, next to the first use of its results)
-      if ((h & 1) == 0) {
-        q.w = __builtin_amdgcn_cvt_pk_fp8_f32(u0 * c4[0], u1 * c4[1], 0, false);
-        asm volatile("" : "+v"(q.lsum), "+v"(q.w));
-      } else {
-        q.pk[d] = __builtin_amdgcn_cvt_pk_fp8_f32(u0 * c4[2], u1 * c4[3], q.w, true);
-        asm volatile("" : "+v"(q.lsum), "+v"(q.pk[d]));
+      // Pt = hi + lo/16: hi = e4m3(Pt), lo = e4m3(16 (Pt - hi)), so Pt keeps about 8 bits
+      // (one e4m3 term alone moved the output of a few dominant tokens by up to 2^-4 of a
+      // token's weight).  The empty asm statements pin the piece between its MFMAs (otherwise
+      // the compiler sinks this arithmetic below the loop, next to the first use of its results)
+      const float t0 = u0 * c4[k0], t1 = u1 * c4[k0 + 1];
+      if ((h & 1) == 0) {   // low 16 bits of the block's packed words
+        q.w = __builtin_amdgcn_cvt_pk_fp8_f32(t0, t1, 0, false);
+        const auto hv = __builtin_amdgcn_cvt_pk_f32_fp8(q.w, false);
+        q.wl = __builtin_amdgcn_cvt_pk_fp8_f32((t0 - hv[0]) * 16.0f, (t1 - hv[1]) * 16.0f, 0, false);
+        asm volatile("" : "+v"(q.lsum), "+v"(q.w), "+v"(q.wl));
+      } else {              // high 16 bits
+        q.pk[d] = __builtin_amdgcn_cvt_pk_fp8_f32(t0, t1, q.w, true);
+        const auto hv = __builtin_amdgcn_cvt_pk_f32_fp8(q.pk[d], true);
+        q.pl[d] = __builtin_amdgcn_cvt_pk_fp8_f32((t0 - hv[0]) * 16.0f, (t1 - hv[1]) * 16.0f, q.wl, true);
+        asm volatile("" : "+v"(q.lsum), "+v"(q.pk[d]), "+v"(q.pl[d]));
       }
     } else if (p == 22) {
       st.l_new = (fresh ? 0.0f : l_run) + __builtin_ldexpf(q.lsum, q.e);
       st.p = i32x8{q.pk[0], q.pk[1], q.pk[2], q.pk[3], q.pk[4], q.pk[5], q.pk[6], q.pk[7]};
+      st.plo = i32x8{q.pl[0], q.pl[1], q.pl[2], q.pl[3], q.pl[4], q.pl[5], q.pl[6], q.pl[7]};
       st.sb = q.e + kE8M0One;
     }
   };
 
   // ---- O^T += Codes^T . Pt^T for the page in `tile`
-  auto values = [&](const uint8_t* tile, const i32x8& pf, int sb, auto hook) {
+  auto values = [&](const uint8_t* tile, const i32x8& pf, const i32x8& pfl, int sb, auto hook) {
     o_fence<3>(oacc);
     int ln = lane;
     asm volatile("" : "+v"(ln));
@@ -1134,13 +1144,14 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_fp8_kernel(DecodeArgs a) {
       if (ct + D < 16) vr[(ct + D) % (D + 1)] = vfrag(ct + D);
       __builtin_amdgcn_sched_barrier(0);
       mfma8_acc(oacc[ct], vr[ct % (D + 1)], pf, one, sb);
+      mfma8_acc(oacc[ct], vr[ct % (D + 1)], pfl, one, sb - 4);   // lo term: block scale 2^(e-4)
       hook(ct);
       __builtin_amdgcn_sched_barrier(0);
     }
     o_fence<20>(oacc);
   };
 
-  i32x8 pf;
+  i32x8 pf, pfl;
   int psb = kE8M0One;
   Soft sm;
   auto soft_commit = [&](const Soft& st) {
@@ -1148,6 +1159,7 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_fp8_kernel(DecodeArgs a) {
     l_run = st.l_new;
     over = st.over_new;
     pf = st.p;
+    pfl = st.plo;
     psb = st.sb;
   };
   auto load_for = [&](int stage, int pg, int nv) {
@@ -1224,7 +1236,7 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_fp8_kernel(DecodeArgs a) {
     SoftState ss;
 #pragma unroll
     for (int p = -1; p < 6; ++p) soft_piece(p, s0, s1, next, vis, seg_end, ss, sm);
-    values(smem + (y & 3) * kStage8, pf, psb, [&](int c) {
+    values(smem + (y & 3) * kStage8, pf, pfl, psb, [&](int c) {
       if (c >= 0) soft_piece(c + 6, s0, s1, next, vis, seg_end, ss, sm);
     });
     soft_piece(22, s0, s1, next, vis, seg_end, ss, sm);
@@ -1541,11 +1553,26 @@ bool is_dsv2_shape(const mla_config_t& c);
 // range with one more segment ran ~20K cycles longer: ~3 bf16 pages, ~2 fp8 pages).
 constexpr int kSegCost = 3, kSegCost8 = 2;
 
+// Test-only override of the range count: the environment variable MLA_FORCE_SPLITS = G > 0
+// replaces the default count, within the same limits (the page table's capacity, at most one
+// range per page).  It is read at every call, so a workspace size and the decode calls that
+// use it must see the same value.  The result is the same attention for any count, up to the
+// rounding of the probabilities and partials that a different cut changes.
+int forced_ranges() {
+  const char* v = std::getenv("MLA_FORCE_SPLITS");
+  if (v == nullptr || *v == 0) return 0;
+  char* end = nullptr;
+  const long x = std::strtol(v, &end, 10);
+  if (end == v || *end != 0 || x <= 0 || x > (1L << 24)) return 0;
+  return (int)x;
+}
+
 int decode_num_ranges(int num_cus, int B, int Sq, int max_blocks, bool fp8) {
   const long long cap = (long long)B * max_blocks;
   const int tab = fp8 ? kTabCap8 : kTabCap;
   long long G = num_cus / (Sq > 0 ? Sq : 1);
   if (G < 1) G = 1;
+  if (const int f = forced_ranges()) G = f;
   // a range owns at most ceil(C / G) pages, C <= B (max_blocks + w) the total cost
   const long long need = ((long long)B * (max_blocks + (fp8 ? kSegCost8 : kSegCost)) + tab - 1) / tab;
   if (G < need) G = need;
@@ -1560,6 +1587,31 @@ size_t decode_workspace_bytes(const mla_config_t& cfg, int num_cus, int B, int S
   const size_t o_bytes = slots * kH * kDC * sizeof(uint16_t);
   const size_t l_bytes = slots * kH * 2 * sizeof(float);
   return ((o_bytes + 255) & ~(size_t)255) + ((l_bytes + 255) & ~(size_t)255);
+}
+
+// The split kernels take all of a compute unit's LDS, above the default dynamic limit, so the
+// limit is raised once per device before their first launch.  Several host threads may get
+// here at once: each one that finds the device not yet marked repeats the same (idempotent)
+// attribute calls, and the mark is an atomic with release/acquire ordering, so no thread
+// launches before some thread's calls have returned successfully.  A failed call is returned
+// and leaves the device unmarked.
+constexpr int kMaxDev = 64;
+std::atomic<int> g_lds_set[kMaxDev];
+
+hipError_t set_decode_lds_limits() {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::atomic<int>* mark = (dev >= 0 && dev < kMaxDev) ? &g_lds_set[dev] : nullptr;
+  if (mark && mark->load(std::memory_order_acquire)) return hipSuccess;
+  const void* kernels[4] = {(const void*)decode_mfma_bf16_kernel<0>, (const void*)decode_mfma_bf16_kernel<2>,
+                            (const void*)decode_mfma_fp8_kernel<0>, (const void*)decode_mfma_fp8_kernel<2>};
+  for (int k = 0; k < 4; ++k) {
+    e = hipFuncSetAttribute(kernels[k], hipFuncAttributeMaxDynamicSharedMemorySize, k < 2 ? kDecodeLds : kDecodeLds8);
+    if (e != hipSuccess) return e;
+  }
+  if (mark) mark->store(1, std::memory_order_release);
+  return hipSuccess;
 }
 
 hipError_t launch_decode(const mla_config_t& cfg, int num_cus, const void* q_abs, const void* cache, const float* cache_scale, int num_blocks, const int32_t* block_table,
@@ -1590,16 +1642,9 @@ hipError_t launch_decode(const mla_config_t& cfg, int num_cus, const void* q_abs
     a.scale_log2 = scale * 1.4426950408889634f;
     a.fp8 = fp8 ? 1 : 0;
     a.seg_w = fp8 ? kSegCost8 : kSegCost;
-    static bool attr_set = false;   // idempotent; races only repeat the same call
-    if (!attr_set) {
-      const void* kernels[4] = {(const void*)decode_mfma_bf16_kernel<0>, (const void*)decode_mfma_bf16_kernel<2>,
-                                (const void*)decode_mfma_fp8_kernel<0>, (const void*)decode_mfma_fp8_kernel<2>};
-      for (int k = 0; k < 4; ++k) {
-        hipError_t e = hipFuncSetAttribute(kernels[k], hipFuncAttributeMaxDynamicSharedMemorySize,
-                                           k < 2 ? kDecodeLds : kDecodeLds8);
-        if (e != hipSuccess) return e;
-      }
-      attr_set = true;
+    {
+      hipError_t e = set_decode_lds_limits();
+      if (e != hipSuccess) return e;
     }
     if (phases & 1) {
       // non-temporal page loads when no other workgroup reads the same pages (one query)

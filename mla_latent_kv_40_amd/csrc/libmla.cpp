@@ -92,9 +92,12 @@ static mla_status_t check_append(const mla_config_t* cfg, void* cache, float* ca
   if (n < 0 || num_blocks <= 0 || batch <= 0 || max_blocks <= 0) return MLA_ERR_INVALID_ARG;
   if (!cache || !block_table) return MLA_ERR_INVALID_ARG;
   if (n > 0 && (!c_kv || !k_r || !pos || !seq_of)) return MLA_ERR_INVALID_ARG;
-  if (!aligned16(cache) || (n > 0 && (!aligned16(c_kv) || !aligned16(k_r)))) return MLA_ERR_INVALID_ARG;
+  if (!aligned16(cache) || !aligned16(block_table)) return MLA_ERR_INVALID_ARG;
+  if (n > 0 && (!aligned16(c_kv) || !aligned16(k_r) || !aligned16(pos) || !aligned16(seq_of)))
+    return MLA_ERR_INVALID_ARG;
   const bool fp8 = cfg->cache_dtype == MLA_FP8_E4M3;
   if (fp8 != (cache_scale != nullptr)) return MLA_ERR_INVALID_ARG;
+  if (cache_scale && !aligned16(cache_scale)) return MLA_ERR_INVALID_ARG;
   return MLA_OK;
 }
 
@@ -105,7 +108,8 @@ static mla_status_t check_absorb(const mla_config_t* cfg, const void* q_nope, co
   if (T < 0) return MLA_ERR_INVALID_ARG;
   if (T == 0) return MLA_OK;
   if (!q_nope || !q_rope || !q_pos || !w_uk || !q_abs) return MLA_ERR_INVALID_ARG;
-  if (!aligned16(q_nope) || !aligned16(q_rope) || !aligned16(w_uk) || !aligned16(q_abs)) return MLA_ERR_INVALID_ARG;
+  if (!aligned16(q_nope) || !aligned16(q_rope) || !aligned16(q_pos) || !aligned16(w_uk) || !aligned16(q_abs))
+    return MLA_ERR_INVALID_ARG;
   return MLA_OK;
 }
 
@@ -166,9 +170,12 @@ static mla_status_t decode_common(const mla_config_t* cfg, const void* q_abs, co
   if ((long long)B * Sq > (1LL << 30)) return MLA_ERR_INVALID_ARG;
   if (B == 0) return MLA_OK;
   if (!q_abs || !cache || !block_table || !kv_lens || !o_lat || !lse) return MLA_ERR_INVALID_ARG;
-  if (!aligned16(q_abs) || !aligned16(cache) || !aligned16(o_lat)) return MLA_ERR_INVALID_ARG;
+  if (!aligned16(q_abs) || !aligned16(cache) || !aligned16(o_lat) || !aligned16(lse) || !aligned16(kv_lens) ||
+      !aligned16(block_table))
+    return MLA_ERR_INVALID_ARG;
   const bool fp8 = cfg->cache_dtype == MLA_FP8_E4M3;
   if (fp8 != (cache_scale != nullptr)) return MLA_ERR_INVALID_ARG;
+  if (cache_scale && !aligned16(cache_scale)) return MLA_ERR_INVALID_ARG;
   const int cus = current_cu_count();
   const size_t need = mla::decode_workspace_bytes(*cfg, cus, B, Sq, max_blocks);
   if (!workspace || ws_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 255u)) return MLA_ERR_WORKSPACE;

@@ -65,10 +65,16 @@ class DecodeState:
         for b in range(Bn):
             L = int(kv[b])
             s = seqs[b]
-            ctx_c.append(s["c"][:L - Sq]); ctx_k.append(s["k_r"][:L - Sq])
-            ctx_pos.append(np.arange(L - Sq, dtype=np.int32)); ctx_seq.append(np.full(L - Sq, b, np.int32))
-            new_c.append(s["c"][L - Sq:L]); new_k.append(s["k_r"][L - Sq:L])
-            new_pos.append(np.arange(L - Sq, L, dtype=np.int32)); new_seq.append(np.full(Sq, b, np.int32))
+            n_ctx = max(L - Sq, 0)
+            ctx_c.append(s["c"][:n_ctx]); ctx_k.append(s["k_r"][:n_ctx])
+            ctx_pos.append(np.arange(n_ctx, dtype=np.int32)); ctx_seq.append(np.full(n_ctx, b, np.int32))
+            # the step's new tokens sit at positions L - Sq .. L - 1; with L < Sq the first ones
+            # have negative positions: no such token exists, the append skips them (zero rows here)
+            idx = np.arange(L - Sq, L)
+            ok = (idx >= 0)[:, None]
+            new_c.append(np.where(ok, s["c"][np.maximum(idx, 0)], 0).astype(s["c"].dtype))
+            new_k.append(np.where(ok, s["k_r"][np.maximum(idx, 0)], 0).astype(s["k_r"].dtype))
+            new_pos.append(idx.astype(np.int32)); new_seq.append(np.full(Sq, b, np.int32))
             qn.append(s["q_c"]); qr.append(s["q_r"])
         self._ctx = (np.concatenate(ctx_c), np.concatenate(ctx_k), np.concatenate(ctx_pos), np.concatenate(ctx_seq))
         self.new_c = dev(np.concatenate(new_c))

@@ -105,12 +105,16 @@ def up_project(C: np.ndarray, W: np.ndarray, heads: int, d_head: int) -> np.ndar
 # ------------------------------------------------------------------ attention
 
 def decode(C, KRraw, qC, qR, W_UK, W_UV, kv_len, softmax_scale, rope_base=10000.0,
-           heads=None, chunk=2048):
+           heads=None, chunk=2048, keys_rotated=False):
     """Textbook softmax attention for the Sq queries of one sequence, unabsorbed.
 
     Inputs (fp64 after upcast):
       C      [L, d_c]      cached latents (L >= kv_len rows; only the first kv_len are used)
-      KRraw  [L, d_R]      positional keys before RoPE (token t is rotated at position t)
+      KRraw  [L, d_R]      positional keys before RoPE (token t is rotated at position t);
+                           with keys_rotated=True they are taken as already rotated, as the
+                           cache stores them (RoPE applied when the token is written): this
+                           serves attention over rows read back from a cache, e.g. the
+                           dequantised rows of an fp8 cache
       qC     [Sq, H, d_h]  content queries;   qR [Sq, H, d_R] positional queries before RoPE
       W_UK   [d_c, H*d_h]  W_UV [d_c, H*d_v]  head-major up-projections
       heads  optional list of head indices to evaluate (default: all)
@@ -145,7 +149,7 @@ def decode(C, KRraw, qC, qR, W_UK, W_UV, kv_len, softmax_scale, rope_base=10000.
     Wv = W_UV[:, cols_v]
 
     pos_q = L - Sq + np.arange(Sq)                       # reading 4
-    kR = rope(KRraw[:L], np.arange(L), rope_base)        # [L, d_R]
+    kR = KRraw[:L] if keys_rotated else rope(KRraw[:L], np.arange(L), rope_base)   # [L, d_R]
     qRr = rope(qR[:, hs], pos_q[:, None], rope_base)     # [Sq, nh, d_R]
     qCs = qC[:, hs]                                      # [Sq, nh, d_h]
 

@@ -8,7 +8,7 @@ from typing import Dict, List, Optional
 import numpy as np
 
 import oracle.mla_oracle as orc
-from mla_latent_kv_40_amd import workloads as wl
+from mla_latent_kv_40_amd import harness, workloads as wl
 
 
 def bound(ref: np.ndarray, factor: float = 1.0) -> float:
@@ -56,3 +56,46 @@ def oracle_for(w: wl.Workload, bt: wl.Batch, seqs, b: int, heads=None, weights=N
 def log(msg: str) -> None:
     print(msg, flush=True)
     sys.stdout.flush()
+
+
+# --------------------------------------------------------------------------- GPU runs
+
+def run_state(w, bt, seqs, weights=None, poison=True, fused=True):
+    """One step; fused=False runs mla_cache_append and mla_absorb_q as two calls instead of
+    mla_append_absorb."""
+    import torch
+    st = harness.DecodeState(w, bt, seqs, device="cuda", weights=weights)
+    st.fill_context()
+    if poison:
+        # NaN in every scratch and output byte: any value read before it is written shows up
+        st.workspace.view(torch.float32)[: st.ws_bytes // 4].fill_(float("nan"))
+        st.o_lat.fill_(float("nan"))
+        st.lse.fill_(float("nan"))
+        st.q_abs.view(torch.uint8).fill_(0xFF)
+    st.step(fused=fused)
+    torch.cuda.synchronize()
+    return st
+
+
+def host(st):
+    return {"o": st.out.float().cpu().numpy(), "o_lat": st.o_lat.cpu().numpy(), "lse": st.lse.cpu().numpy()}
+
+
+def dsv2(batch, lengths, sq=1, seed=7, name="dsv2_b16_l4k", fp8=False):
+    if fp8:
+        name = "dsv2_b128_l8k_fp8"
+    w = wl.get(name, batch=batch, sq=sq, seed=seed, ctx_lo=0, ctx_hi=0)
+    bt = wl.draw_batch(w)
+    # replace the lengths with the requested ones (context + sq), rebuilding the page table
+    kv = np.asarray(lengths, dtype=np.int32)
+    nblk = (kv + 63) // 64
+    rng = np.random.default_rng(seed + 1000)
+    perm = rng.permutation(int(nblk.sum())).astype(np.int32)
+    table = np.full((batch, int(nblk.max())), -1, np.int32)
+    off = 0
+    for b in range(batch):
+        table[b, :nblk[b]] = perm[off:off + nblk[b]]
+        off += int(nblk[b])
+    bt = wl.Batch(w=w, kv_lens=kv, block_table=table, num_blocks=int(nblk.sum()), weights=bt.weights)
+    seqs = harness.draw_all_sequences(w, bt)
+    return w, bt, seqs

@@ -1,0 +1,195 @@
+"""GPU invariance and adversarial checks (through the C ABI):
+
+* split-count invariance: the same batch decoded with different numbers of token ranges
+  (the test-only override MLA_FORCE_SPLITS) agrees within a bound derived from the rounding
+  that a different cut changes, and every run passes the oracle gate;
+* query rows that see no token (kv_len < Sq) give the defined empty result, the others the
+  oracle's;
+* needle tokens in the longest sequence of the full-size long-context workloads, at the bench's
+  launch configuration: at t = 0, at a range boundary and in the sequence's last page.
+"""
+import os
+
+import numpy as np
+import pytest
+
+import oracle.mla_oracle as orc
+from mla_latent_kv_40_amd import binding as B, harness, workloads as wl
+from _common import check, dsv2, host, log, oracle_for, run_state
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    torch.cuda.set_device(0)
+
+
+def decode_with_ranges(st, G):
+    """mla_decode_attn on the state's inputs with MLA_FORCE_SPLITS = G (None: the default count),
+    a fresh NaN-filled workspace and NaN-filled outputs."""
+    old = os.environ.get("MLA_FORCE_SPLITS")
+    if G is None:
+        os.environ.pop("MLA_FORCE_SPLITS", None)
+    else:
+        os.environ["MLA_FORCE_SPLITS"] = str(G)
+    try:
+        ws_bytes = B.mla_decode_workspace_size(st.cfg, st.w.batch, st.w.sq, st.batch.max_blocks)
+        ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+        ws.view(torch.float32)[: ws_bytes // 4].fill_(float("nan"))
+        st.o_lat.fill_(float("nan"))
+        st.lse.fill_(float("nan"))
+        B.mla_decode_attn(st.cfg, st.q_abs, st.cache, st.cache_scale, st.batch.num_blocks, st.block_table,
+                          st.batch.max_blocks, st.kv_lens, st.w.batch, st.w.sq, ws, ws_bytes, st.o_lat, st.lse)
+        torch.cuda.synchronize()
+        return st.o_lat.cpu().numpy().copy(), st.lse.cpu().numpy().copy(), ws_bytes
+    finally:
+        if old is None:
+            os.environ.pop("MLA_FORCE_SPLITS", None)
+        else:
+            os.environ["MLA_FORCE_SPLITS"] = old
+
+
+def weighted_spread(w, bt, seqs, b, heads):
+    """Per (query, head, latent column): D = sum_t w_t |c_t - o| and A = sum_t w_t |c_t| over the
+    oracle's softmax weights w_t (fp64, scores by the absorbed route), with c_t the latent rows
+    the kernel reads (dequantised for an fp8 cache).  They scale the rounding bound below."""
+    s = seqs[b]
+    L = int(bt.kv_lens[b])
+    t = np.arange(L)
+    rows = np.concatenate([s["c"][:L].astype(np.float64), orc.rope(s["k_r"][:L], t, w.rope_base)], axis=1)
+    if w.dtype == "fp8":
+        codes, scale = orc.quantize_rows_fp8(rows)
+        rows = codes * scale.astype(np.float64)[:, None]
+    pos_q = L - w.sq + np.arange(w.sq)
+    qa = orc.absorbed_query(s["q_c"], s["q_r"], bt.weights["W_UK"], pos_q, w.rope_base)[:, list(heads)]
+    sc = np.einsum("jhk,tk->jht", qa, rows) * w.softmax_scale
+    sc = np.where((t[None, :] <= pos_q[:, None])[:, None, :], sc, -np.inf)
+    wt = np.exp(sc - sc.max(-1, keepdims=True))
+    wt /= wt.sum(-1, keepdims=True)
+    C = rows[:, :w.d_c]
+    o = np.einsum("jht,tc->jhc", wt, C)
+    D = np.einsum("jht,jhtc->jhc", wt, np.abs(C[None, None] - o[:, :, None, :]))
+    A = np.einsum("jht,tc->jhc", wt, np.abs(C))
+    return D, A, float(np.abs(C).max())
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_split_count_invariance(fp8):
+    """A different cut changes each segment's softmax reference and so the rounding of the
+    probabilities fed to the value product (bf16: relative 2^-9, and l sums the same rounded
+    values; fp8: hi + lo/16 e4m3 terms, relative 2^-8, l summed unrounded) and of the bf16
+    segment partials (2^-9).  With u the probability rounding, per latent column of one query
+    and head a run is within u' (D + A) of exact attention over the same inputs (u' = u/(1-u)
+    plus the partial rounding), so two runs differ by at most 2 u' (D + A) (+1e-6 max|c| for the
+    fp32 sums).  lse moves only with l: by at most 2 u'.  Ranges tried: the fewest the page table
+    allows, an odd count that is not a multiple of the XCD count, the default, and one page per
+    range."""
+    log(f"case split-count invariance, fp8={fp8}: lengths [20000, 9000, 3001, 777, 65]")
+    lengths = [20000, 9000, 3001, 777, 65]
+    w, bt, seqs = dsv2(5, lengths, seed=71, fp8=fp8)
+    st = run_state(w, bt, seqs)
+    cap = w.batch * bt.max_blocks
+    runs = {}
+    for G in (1, 37, None, cap):
+        o_lat, lse, ws = decode_with_ranges(st, G)
+        runs[G] = (o_lat, lse)
+        log(f"  ranges {G if G is not None else 'default'}: workspace {ws} B")
+        assert np.all(np.isfinite(o_lat)) and np.all(np.isfinite(lse)), G
+    u = 2.0 ** -9
+    up = (2.0 ** -8 + u) if fp8 else (u / (1 - u) + u)
+    heads = list(range(0, 128, 7))
+    for b in range(w.batch):
+        D, A, cmax = weighted_spread(w, bt, seqs, b, heads)
+        bound_o = 2 * up * (D + A) + 1e-6 * cmax
+        bound_l = 2 * (2.0 ** -8 if fp8 else u / (1 - u)) + 1e-5
+        ref = oracle_for(w, bt, seqs, b, heads=heads)
+        for G, (o_lat, lse) in runs.items():
+            g_o = o_lat[b:b + 1][:, heads]
+            g_l = lse[b:b + 1][:, heads]
+            d_o = np.abs(g_o - runs[None][0][b:b + 1][:, heads])
+            d_l = np.abs(g_l - runs[None][1][b:b + 1][:, heads])
+            ratio = max(float(np.max(d_o / bound_o)), float(np.max(d_l / bound_l)))
+            log(f"  b{b} ranges {G}: max |diff| / bound {ratio:.3f} (o_lat {np.max(d_o):.2e}, lse {np.max(d_l):.2e})")
+            assert np.all(d_o <= bound_o) and np.all(d_l <= bound_l), (b, G)
+            f = 4.0 if fp8 else 1.0
+            check(f"b{b} ranges {G} o_lat", g_o, ref["o_lat"], f)
+            check(f"b{b} ranges {G} lse", g_l, ref["lse"], f)
+
+
+def test_query_rows_without_tokens():
+    """kv_len < Sq: query j sits at p = kv_len - Sq + j; rows with p < 0 see no token and give
+    o_lat = 0, lse = -inf (and a zero layer output); rows with p >= 0 attend to tokens 0 .. p,
+    i.e. equal a one-query decode of length p + 1 (the causal multi-query reduction)."""
+    log("case kv_len < Sq: lengths [2, 3, 1, 9], Sq=4")
+    w, bt, seqs = dsv2(4, [2, 3, 1, 9], sq=4, seed=73)
+    st = run_state(w, bt, seqs)
+    got = host(st)
+    for b in range(w.batch):
+        L = int(bt.kv_lens[b])
+        s = seqs[b]
+        for j in range(w.sq):
+            row = b * w.sq + j
+            p = L - w.sq + j
+            if p < 0:
+                assert np.all(got["o_lat"][row] == 0.0) and np.all(np.isneginf(got["lse"][row])), (b, j)
+                assert np.all(got["o"][row] == 0.0), (b, j)
+                continue
+            ref = orc.decode(s["c"], s["k_r"], s["q_c"][j:j + 1], s["q_r"][j:j + 1], bt.weights["W_UK"],
+                             bt.weights["W_UV"], p + 1, w.softmax_scale, w.rope_base)
+            for k in ("o", "o_lat", "lse"):
+                check(f"b{b} j{j} {k}", got[k][row:row + 1], ref[k])
+
+
+def range_boundary_page(bt, b, G, w_seg=3):
+    """A page of sequence b at which the default cut (G ranges, per-segment cost w_seg pages)
+    starts a new range, or None: page x of the r-th non-empty sequence sits at cost position
+    first_page + x + w_seg (r + 1), and range g starts at floor(g C / G)."""
+    n = (bt.kv_lens.astype(np.int64) + 63) // 64
+    nz = n > 0
+    C = int(n.sum() + w_seg * nz.sum())
+    first = int(n[:b].sum())
+    r = int(nz[:b].sum())
+    lo = first + w_seg * (r + 1)
+    for g in range(1, G):
+        c = g * C // G
+        if lo < c < lo + int(n[b]):
+            return c - lo
+    return None
+
+
+@pytest.mark.parametrize("name", ["dsv2_b64_l1k_32k", "dsv2_b64_l32k"])
+def test_full_size_needles(name):
+    """The full-size long-context workloads at the bench's launch configuration, with three
+    needles (latent x4, exact in bf16) in the longest sequence: at t = 0, on the first token of a
+    page where a range starts, and on the sequence's last token.  A dropped, duplicated or
+    misplaced page holding one moves the output of the heads it dominates far past the gate."""
+    w = wl.get(name)
+    bt = wl.draw_batch(w)
+    b = int(np.argmax(bt.kv_lens))
+    L = int(bt.kv_lens[b])
+    G = torch.cuda.get_device_properties(0).multi_processor_count
+    x = range_boundary_page(bt, b, G)
+    assert x is not None
+    spots = [0, 64 * x, L - 1]
+    log(f"case full-size needles {name}: sequence {b} (kv_len {L}), needles at {spots}")
+    seqs = harness.draw_all_sequences(w, bt)
+    heads = list(range(0, 128, 4))
+    plain = oracle_for(w, bt, seqs, b, heads=heads)
+    seqs[b]["c"] = seqs[b]["c"].copy()
+    for t in spots:
+        seqs[b]["c"][t] = seqs[b]["c"][t] * 4.0
+    st = run_state(w, bt, seqs)
+    got = host(st)
+    assert np.all(np.isfinite(got["o"]))
+    ref = oracle_for(w, bt, seqs, b, heads=heads)
+    # the needles move the output by far more than the gate allows, so losing one would fail
+    moved = float(np.max(np.abs(ref["o_lat"] - plain["o_lat"])))
+    tol = 2e-2 * float(np.max(np.abs(ref["o_lat"]))) + 1e-3
+    log(f"  needles move o_lat by {moved:.3e} (gate {tol:.3e})")
+    assert moved > 10 * tol
+    for k in ("o", "o_lat", "lse"):
+        check(f"needles b{b} {k}", got[k][b:b + 1][:, heads], ref[k])

@@ -11,7 +11,7 @@ import pytest
 
 import oracle.mla_oracle as orc
 from mla_latent_kv_40_amd import harness, workloads as wl
-from _common import check, log, oracle_for, tiny_sequences
+from _common import check, dsv2, host, log, oracle_for, run_state, tiny_sequences
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -26,42 +26,39 @@ def _gpu():
     torch.cuda.set_device(0)
 
 
-def run_state(w, bt, seqs, weights=None, poison=True, fused=True):
-    """One step; fused=False runs mla_cache_append and mla_absorb_q as two calls instead of
-    mla_append_absorb."""
-    st = harness.DecodeState(w, bt, seqs, device="cuda", weights=weights)
-    st.fill_context()
-    if poison:
-        # NaN in every scratch and output byte: any value read before it is written shows up
-        st.workspace.view(torch.float32)[: st.ws_bytes // 4].fill_(float("nan"))
-        st.o_lat.fill_(float("nan"))
-        st.lse.fill_(float("nan"))
-        st.q_abs.view(torch.uint8).fill_(0xFF)
-    st.step(fused=fused)
-    torch.cuda.synchronize()
-    return st
-
-
-def host(st):
-    return {"o": st.out.float().cpu().numpy(), "o_lat": st.o_lat.cpu().numpy(), "lse": st.lse.cpu().numpy()}
-
-
 def compare_seq(w, bt, seqs, got, b, heads=None, factor=1.0, weights=None, tag=""):
-    """The gate on the layer output o; o_lat and lse under the same rule as diagnostics.
-
-    fp8 cache: the gate is 4x the bf16 rule on o.  Storing the latent in e4m3 alone moves
-    o_lat of a short sequence by up to ~3/4 of that bound (three mantissa bits on each of a few
-    dominant tokens; measured by quantising the oracle's own inputs), and the e4m3 query and
-    probabilities add to it, so the diagnostics get 1.25x the gate there."""
+    """The gate on every output of the step: the layer output o, the latent-space output o_lat
+    and lse, each under max|gpu - oracle| <= factor * (2e-2 max|oracle| + 1e-3), factor 4 for
+    an fp8 cache (the oracle then sees the values before quantisation, so the gate covers the
+    whole method).  For an fp8 cache a second check runs the oracle on the dequantised cache
+    rows (codes x scale from the oracle's own quantiser) at the bf16 rule: what remains there is
+    the kernel's own arithmetic (its e4m3 query and probability terms), not the storage."""
     ref = oracle_for(w, bt, seqs, b, heads=heads, weights=weights)
     sl = slice(b * w.sq, (b + 1) * w.sq)
     hs = slice(None) if heads is None else list(heads)
     g = {k: v[sl][:, hs] for k, v in got.items()}
-    diag = factor * (1.25 if factor > 1.0 else 1.0)
     r = check(f"{tag}b{b} o", g["o"], ref["o"], factor)
-    check(f"{tag}b{b} o_lat", g["o_lat"], ref["o_lat"], diag)
-    check(f"{tag}b{b} lse", g["lse"], ref["lse"], diag)
+    check(f"{tag}b{b} o_lat", g["o_lat"], ref["o_lat"], factor)
+    check(f"{tag}b{b} lse", g["lse"], ref["lse"], factor)
+    if w.dtype == "fp8":
+        deq = oracle_dequantised(w, bt, seqs, b, heads=heads, weights=weights)
+        for k in ("o", "o_lat", "lse"):
+            check(f"{tag}b{b} {k} vs dequantised cache", g[k], deq[k])
     return r
+
+
+def oracle_dequantised(w, bt, seqs, b, heads=None, weights=None):
+    """The oracle on the rows an fp8 cache holds: [c ; RoPE(k_R)] quantised by the oracle's
+    e4m3 row quantiser and multiplied back by the scale (the stored k_R is already rotated)."""
+    W = weights if weights is not None else bt.weights
+    s = seqs[b]
+    L = int(bt.kv_lens[b])
+    t = np.arange(L)
+    rows = np.concatenate([s["c"][:L].astype(np.float64), orc.rope(s["k_r"][:L], t, w.rope_base)], axis=1)
+    codes, scale = orc.quantize_rows_fp8(rows)
+    deq = codes * scale.astype(np.float64)[:, None]
+    return orc.decode(deq[:, :w.d_c], deq[:, w.d_c:], s["q_c"], s["q_r"], W["W_UK"], W["W_UV"], L,
+                      w.softmax_scale, w.rope_base, heads=heads, keys_rotated=True)
 
 
 # --------------------------------------------------------------------------- tiny fp32
@@ -87,26 +84,6 @@ def test_tiny_f32_from_hidden_states():
 
 
 # --------------------------------------------------------------------------- DS-V2 shapes, bf16
-
-def dsv2(batch, lengths, sq=1, seed=7, name="dsv2_b16_l4k", fp8=False):
-    if fp8:
-        name = "dsv2_b128_l8k_fp8"
-    w = wl.get(name, batch=batch, sq=sq, seed=seed, ctx_lo=0, ctx_hi=0)
-    bt = wl.draw_batch(w)
-    # replace the lengths with the requested ones (context + sq), rebuilding the page table
-    kv = np.asarray(lengths, dtype=np.int32)
-    nblk = (kv + 63) // 64
-    rng = np.random.default_rng(seed + 1000)
-    perm = rng.permutation(int(nblk.sum())).astype(np.int32)
-    table = np.full((batch, int(nblk.max())), -1, np.int32)
-    off = 0
-    for b in range(batch):
-        table[b, :nblk[b]] = perm[off:off + nblk[b]]
-        off += int(nblk[b])
-    bt = wl.Batch(w=w, kv_lens=kv, block_table=table, num_blocks=int(nblk.sum()), weights=bt.weights)
-    seqs = harness.draw_all_sequences(w, bt)
-    return w, bt, seqs
-
 
 def test_dsv2_edge_lengths_all_heads():
     log("case dsv2 bf16 lengths [1, 63, 64, 65, 200], Sq=1, all heads (append and absorb as two calls)")

@@ -28,7 +28,7 @@ def test_exports_every_declared_symbol(L):
     assert set(syms) == set(B.EXPORTS), syms
     for s in syms:
         assert hasattr(L, s), s
-    assert B.mla_abi_version() == B.ABI_VERSION == 3
+    assert B.mla_abi_version() == B.ABI_VERSION
 
 
 def cfg(**kw):
@@ -112,6 +112,59 @@ def test_decode_workspace_checks(L):
     assert B.mla_decode_attn(*bad, FAKE, ws, FAKE, FAKE, stream=0, check=False) == B.MLA_ERR_INVALID_ARG
     assert B.mla_decode_attn(c, FAKE, FAKE, None, 100, FAKE, 512, FAKE, 0, 1, 0, 0, 0, 0, stream=0,
                              check=False) == B.MLA_OK
+
+
+def test_every_pointer_is_checked_for_alignment(L):
+    """Each array argument must be 16-byte aligned (the header's convention): a pointer 4 bytes
+    off is rejected before anything is launched, argument by argument."""
+    c, c8 = cfg(), cfg(cache_dtype="fp8")
+    ws = B.mla_decode_workspace_size(c, 64, 1, 512)
+    ws8 = B.mla_decode_workspace_size(c8, 64, 1, 512)
+    # decode: q_abs, cache, cache_scale, block_table, kv_lens, o_lat, lse
+    for conf, w, scale in ((c, ws, None), (c8, ws8, FAKE)):
+        good = dict(q=FAKE, cache=FAKE, scale=scale, bt=FAKE, kv=FAKE, o=FAKE, lse=FAKE)
+        def call(**kw):
+            a = dict(good, **kw)
+            return B.mla_decode_attn(conf, a["q"], a["cache"], a["scale"], 100, a["bt"], 512, a["kv"], 64, 1,
+                                     FAKE, w, a["o"], a["lse"], stream=0, check=False)
+        for k in good:
+            if good[k] is None:
+                continue
+            assert call(**{k: good[k] + 4}) == B.MLA_ERR_INVALID_ARG, k
+    # append: cache, cache_scale, c_kv, k_r, pos, seq_of, block_table
+    names = ["cache", "scale", "c", "k", "pos", "seq", "bt"]
+    for k in names:
+        a = {n: FAKE for n in names}
+        a[k] += 4
+        assert B.mla_cache_append(c8, a["cache"], a["scale"], 8, a["c"], a["k"], a["pos"], a["seq"], a["bt"], 2, 4,
+                                  3, stream=0, check=False) == B.MLA_ERR_INVALID_ARG, k
+    # absorb: q_nope, q_rope, q_pos, w_uk, q_abs
+    for i in range(5):
+        a = [FAKE] * 5
+        a[i] += 4
+        assert B.mla_absorb_q(c, *a, 4, stream=0, check=False) == B.MLA_ERR_INVALID_ARG, i
+    # out_proj: o_lat, w_uv, out
+    for i in range(3):
+        a = [FAKE] * 3
+        a[i] += 4
+        assert B.mla_out_proj(c, *a, 4, stream=0, check=False) == B.MLA_ERR_INVALID_ARG, i
+
+
+def test_forced_split_count_changes_only_the_workspace(L, monkeypatch):
+    """MLA_FORCE_SPLITS (test-only) sets the number of token ranges; the workspace follows it,
+    clamped to one range per page at most."""
+    c = cfg()
+    base = B.mla_decode_workspace_size(c, 4, 1, 100)
+    monkeypatch.setenv("MLA_FORCE_SPLITS", "1")
+    one = B.mla_decode_workspace_size(c, 4, 1, 100)
+    monkeypatch.setenv("MLA_FORCE_SPLITS", "400")
+    many = B.mla_decode_workspace_size(c, 4, 1, 100)
+    monkeypatch.setenv("MLA_FORCE_SPLITS", "100000")
+    capped = B.mla_decode_workspace_size(c, 4, 1, 100)
+    monkeypatch.setenv("MLA_FORCE_SPLITS", "junk")
+    ignored = B.mla_decode_workspace_size(c, 4, 1, 100)
+    assert one < base < many == capped      # 4 sequences x 100 pages: at most 400 ranges
+    assert ignored == base
 
 
 def test_status_strings(L):

@@ -144,11 +144,57 @@ def _brute(case):
                        case["kv_len"], case["softmax_scale"], case["rope_base"])
 
 
-@pytest.mark.parametrize("Sq", [1, 3])
+@pytest.mark.parametrize("Sq", [1, 3, 4])
 def test_bruteforce_ten_tokens(Sq):
     case = _small_case(Sq=Sq, base=7.0)   # small base: large angles exercise the rotation
     ref = _brute(case)
     got = orc.decode(**case)
+    for k in ("o", "o_lat", "lse"):
+        assert rel_err(got[k], ref[k]) < 1e-12, k
+
+
+def _brute_projection(x, W, row):
+    """One row of x @ W with scalar loops: out[n] = sum_k x[row][k] W[k][n]."""
+    xr = np.asarray(x, dtype=np.float64)[row].tolist()
+    Wl = np.asarray(W, dtype=np.float64).tolist()
+    return [sum(xr[k] * Wl[k][n] for k in range(len(xr))) for n in range(len(Wl[0]))]
+
+
+def test_projection_from_hidden_states_bruteforce():
+    """The tiny case starts at hidden states (katajob "code": latent = x @ W_down; bembew
+    "Implementation Logic", steps 1, 3 and 4): latent and positional key of every token, and
+    the query parts of the query row only, each head's block of columns in head-major order.
+    Scalar loops rebuild rows 0, 4 and L-1 of c and k_R and the query of row L-1."""
+    w = wl.get("tiny_f32")
+    bt = wl.draw_batch(w)
+    W = bt.weights
+    x = W["x"]
+    L = x.shape[0]
+    C, KR, qC, qR = orc.project_from_hidden(x, W["W_down"], W["W_KR"], W["W_Q"], W["W_QR"], w.heads, w.d_h,
+                                            w.d_r, [L - 1])
+    assert C.shape == (L, w.d_c) and KR.shape == (L, w.d_r)
+    assert qC.shape == (1, w.heads, w.d_h) and qR.shape == (1, w.heads, w.d_r)
+    for t in (0, 4, L - 1):
+        assert rel_err(C[t], _brute_projection(x, W["W_down"], t)) < 1e-13, t
+        assert rel_err(KR[t], _brute_projection(x, W["W_KR"], t)) < 1e-13, t
+    qc = _brute_projection(x, W["W_Q"], L - 1)
+    qr = _brute_projection(x, W["W_QR"], L - 1)
+    for i in (0, 3, w.heads - 1):   # head i owns columns i*d .. i*d + d - 1
+        assert rel_err(qC[0, i], qc[i * w.d_h:(i + 1) * w.d_h]) < 1e-13, i
+        assert rel_err(qR[0, i], qr[i * w.d_r:(i + 1) * w.d_r]) < 1e-13, i
+    # the other query rows differ (a wrong row would not pass the element-wise check above)
+    _, _, qC0, _ = orc.project_from_hidden(x, W["W_down"], W["W_KR"], W["W_Q"], W["W_QR"], w.heads, w.d_h, w.d_r,
+                                           [L - 2])
+    assert rel_err(qC0, qC) > 1e-3
+
+
+def test_pre_rotated_keys_give_the_same_attention():
+    """Keys rotated before the call (as a cache stores them) with keys_rotated=True equal the
+    rotation done inside."""
+    case = _small_case(L=9, Sq=2, base=7.0)
+    ref = orc.decode(**case)
+    kr = np.array([_rot_complex(case["KRraw"][t], t, case["rope_base"]) for t in range(9)])
+    got = orc.decode(**dict(case, KRraw=kr, keys_rotated=True))
     for k in ("o", "o_lat", "lse"):
         assert rel_err(got[k], ref[k]) < 1e-12, k
 
@@ -348,3 +394,29 @@ def test_planted_mistake_fails_bruteforce_pin(kind):
     got = _planted_decode(kind)(**case)
     errs = [rel_err(got[k], ref[k]) if got[k].shape == ref[k].shape else 1.0 for k in ("o", "lse")]
     assert max(errs) > 1e-6, kind
+
+
+def _planted_projection(kind):
+    """A copy of the oracle's projection with one plausible mistake."""
+    def bad(x, W_down, W_KR, W_Q, W_QR, heads, d_h, d_r, query_rows):
+        x = np.asarray(x, float)
+        if kind == "first_row_as_query":
+            query_rows = [0]
+        C, KR, qC, qR = orc.project_from_hidden(x, W_down, W_KR, W_Q, W_QR, heads, d_h, d_r, query_rows)
+        if kind == "dim_major_query":             # columns read as (d_h, H) instead of (H, d_h)
+            qC = qC.reshape(len(query_rows), d_h, heads).transpose(0, 2, 1)
+        return C, KR, qC, qR
+    return bad
+
+
+@pytest.mark.parametrize("kind", ["first_row_as_query", "dim_major_query"])
+def test_planted_mistake_fails_projection_pin(kind):
+    w = wl.get("tiny_f32")
+    W = wl.draw_batch(w).weights
+    x = W["x"]
+    L = x.shape[0]
+    _, _, qC, _ = _planted_projection(kind)(x, W["W_down"], W["W_KR"], W["W_Q"], W["W_QR"], w.heads, w.d_h,
+                                            w.d_r, [L - 1])
+    qc = _brute_projection(x, W["W_Q"], L - 1)
+    errs = [rel_err(qC[0, i], qc[i * w.d_h:(i + 1) * w.d_h]) for i in range(w.heads)]
+    assert max(errs) > 1e-3, kind
