@@ -201,6 +201,24 @@ mla_status_t mla_decode_combine(const mla_config_t* cfg, const void* q_abs,
                                 size_t ws_bytes, float* o_lat, float* lse, void* stream);
 
 /*
+ * mla_decode_attn_noalloc -- mla_decode_attn without a caller workspace, for callers that
+ * cannot allocate device memory (code under HIP graph capture, serving loops or harnesses that
+ * forbid allocation).  Same arguments (minus workspace and ws_bytes), results and validation as
+ * mla_decode_attn; the split-K partials go to a fixed device array inside the library
+ * (MLA_NOALLOC_SCRATCH_BYTES = 64 MiB per device, held until the process ends).  A launch whose
+ * partials exceed it, i.e. mla_decode_workspace_size(cfg, B, Sq, max_blocks) >
+ * MLA_NOALLOC_SCRATCH_BYTES, returns MLA_ERR_WORKSPACE and launches nothing.  Nothing is
+ * allocated or freed.  Every call on one device shares that array: calls that can overlap in
+ * time on one device (other streams, other host threads) race and must be ordered by the caller.
+ */
+#define MLA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+mla_status_t mla_decode_attn_noalloc(const mla_config_t* cfg, const void* q_abs,
+                                     const void* cache, const float* cache_scale, int32_t num_blocks,
+                                     const int32_t* block_table, int32_t max_blocks,
+                                     const int32_t* kv_lens, int32_t B, int32_t Sq,
+                                     float* o_lat, float* lse, void* stream);
+
+/*
  * mla_out_proj -- apply W_UV once per query on the output side:
  * out[t,i] = o_lat[t,i] W_UV,i, W_UV,i = columns i*d_v .. i*d_v+d_v-1 of w_uv
  * (katajob "solid answer": the value up-projection folds into the output projection).
@@ -213,7 +231,7 @@ mla_status_t mla_out_proj(const mla_config_t* cfg, const float* o_lat, const voi
 /* Human-readable name of a status code (static storage). */
 const char* mla_status_string(mla_status_t status);
 
-/* ABI version of this header: 3. */
+/* ABI version of this header: 4. */
 int32_t mla_abi_version(void);
 
 #ifdef __cplusplus

@@ -13,14 +13,16 @@ from typing import Optional
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmla.so")
 
-ABI_VERSION = 3   # what mla_abi_version() returns for the argument lists below
+ABI_VERSION = 4   # what mla_abi_version() returns for the argument lists below
+NOALLOC_SCRATCH_BYTES = 64 << 20   # MLA_NOALLOC_SCRATCH_BYTES
 
 MLA_OK, MLA_ERR_INVALID_ARG, MLA_ERR_UNSUPPORTED, MLA_ERR_WORKSPACE, MLA_ERR_HIP = range(5)
 MLA_F32, MLA_BF16, MLA_FP8_E4M3 = range(3)
 DTYPES = {"f32": MLA_F32, "bf16": MLA_BF16, "fp8": MLA_FP8_E4M3}
 
 EXPORTS = ("mla_cache_append", "mla_absorb_q", "mla_append_absorb", "mla_decode_workspace_size", "mla_decode_attn",
-           "mla_decode_split", "mla_decode_combine", "mla_out_proj", "mla_status_string", "mla_abi_version")
+           "mla_decode_split", "mla_decode_combine", "mla_decode_attn_noalloc", "mla_out_proj", "mla_status_string",
+           "mla_abi_version")
 
 
 class MlaConfig(ctypes.Structure):
@@ -58,12 +60,13 @@ def lib() -> ctypes.CDLL:
         for name in ("mla_decode_attn", "mla_decode_split", "mla_decode_combine"):
             getattr(L, name).argtypes = [cfgp, vp, vp, f32p, i32, vp, i32, vp, i32, i32, vp, ctypes.c_size_t,
                                          f32p, f32p, vp]
+        L.mla_decode_attn_noalloc.argtypes = [cfgp, vp, vp, f32p, i32, vp, i32, vp, i32, i32, f32p, f32p, vp]
         L.mla_out_proj.argtypes = [cfgp, f32p, vp, vp, i32, vp]
         L.mla_status_string.argtypes = [ctypes.c_int]
         L.mla_status_string.restype = ctypes.c_char_p
         L.mla_abi_version.restype = ctypes.c_int32
         for name in ("mla_cache_append", "mla_absorb_q", "mla_append_absorb", "mla_decode_attn", "mla_decode_split",
-                     "mla_decode_combine", "mla_out_proj"):
+                     "mla_decode_combine", "mla_decode_attn_noalloc", "mla_out_proj"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -168,6 +171,16 @@ def mla_decode_combine(cfg: Config, q_abs, cache, cache_scale, num_blocks, block
                        kv_lens, B, Sq, workspace, ws_bytes, o_lat, lse, stream=None, check=True) -> int:
     return _decode("mla_decode_combine", cfg, q_abs, cache, cache_scale, num_blocks, block_table,
                    max_blocks, kv_lens, B, Sq, workspace, ws_bytes, o_lat, lse, stream, check)
+
+
+def mla_decode_attn_noalloc(cfg: Config, q_abs, cache, cache_scale, num_blocks, block_table, max_blocks,
+                            kv_lens, B, Sq, o_lat, lse, stream=None, check=True) -> int:
+    st = lib().mla_decode_attn_noalloc(ctypes.byref(cfg.c()), _ptr(q_abs), _ptr(cache), _ptr(cache_scale),
+                                       num_blocks, _ptr(block_table), max_blocks, _ptr(kv_lens), B, Sq, _ptr(o_lat),
+                                       _ptr(lse), _stream(stream))
+    if check:
+        _check("mla_decode_attn_noalloc", st)
+    return st
 
 
 def mla_out_proj(cfg: Config, o_lat, w_uv, out, T, stream=None, check=True) -> int:

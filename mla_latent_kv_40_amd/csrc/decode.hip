@@ -1689,4 +1689,34 @@ hipError_t launch_decode(const mla_config_t& cfg, int num_cus, const void* q_abs
   return hipErrorInvalidValue;
 }
 
+// ------------------------------------------------------------------------ fixed scratch
+
+// For callers that cannot allocate (code under graph capture, serving loops that forbid it):
+// mla_decode_attn_noalloc puts the split-K partials in this file-scope device array instead of
+// a caller workspace.  Every device the library runs on holds its own copy until the process
+// ends.  In host code the array's name is only a stand-in, so the device address is looked up
+// once per device (hipGetSymbolAddress, with that device current) and kept; kernels get that
+// address.  The decode kernels write every partial before reading it, so the array needs no
+// clearing; calls on one device share it, so calls that overlap in time on one device race.
+constexpr size_t kStaticScratchBytes = (size_t)64 << 20;
+static __device__ __attribute__((aligned(256))) uint8_t scratch[kStaticScratchBytes];
+std::atomic<void*> g_scratch_ptr[kMaxDev];
+
+size_t static_scratch_bytes() { return kStaticScratchBytes; }
+
+hipError_t static_scratch(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDev) return hipErrorInvalidDevice;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev].store(p, std::memory_order_release);   // every thread finds the same address
+  }
+  *out = p;
+  return hipSuccess;
+}
+
 }  // namespace mla

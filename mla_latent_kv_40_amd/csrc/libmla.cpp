@@ -22,6 +22,8 @@ hipError_t launch_decode(const mla_config_t&, int, const void*, const void*, con
                          const int32_t*, int, const int32_t*, int, int, void*, float*, float*, hipStream_t,
                          int phases);
 size_t decode_workspace_bytes(const mla_config_t&, int, int, int, int);
+size_t static_scratch_bytes();
+hipError_t static_scratch(void** out);
 bool is_dsv2_shape(const mla_config_t&);
 }  // namespace mla
 
@@ -71,7 +73,7 @@ mla_status_t from_hip(hipError_t e) { return e == hipSuccess ? MLA_OK : MLA_ERR_
 
 extern "C" {
 
-int32_t mla_abi_version(void) { return 3; }
+int32_t mla_abi_version(void) { return 4; }
 
 const char* mla_status_string(mla_status_t s) {
   switch (s) {
@@ -160,10 +162,11 @@ size_t mla_decode_workspace_size(const mla_config_t* cfg, int32_t B, int32_t Sq,
   return mla::decode_workspace_bytes(*cfg, current_cu_count(), B, Sq, max_blocks);
 }
 
+// use_static: the partials go to the library's fixed device scratch (workspace arguments unused)
 static mla_status_t decode_common(const mla_config_t* cfg, const void* q_abs, const void* cache, const float* cache_scale, int32_t num_blocks,
                                   const int32_t* block_table, int32_t max_blocks, const int32_t* kv_lens, int32_t B,
                                   int32_t Sq, void* workspace, size_t ws_bytes, float* o_lat, float* lse,
-                                  void* stream, int phases) {
+                                  void* stream, int phases, bool use_static = false) {
   mla_status_t st = check_cfg(cfg);
   if (st != MLA_OK) return st;
   if (B < 0 || Sq <= 0 || num_blocks <= 0 || max_blocks <= 0) return MLA_ERR_INVALID_ARG;
@@ -178,6 +181,11 @@ static mla_status_t decode_common(const mla_config_t* cfg, const void* q_abs, co
   if (cache_scale && !aligned16(cache_scale)) return MLA_ERR_INVALID_ARG;
   const int cus = current_cu_count();
   const size_t need = mla::decode_workspace_bytes(*cfg, cus, B, Sq, max_blocks);
+  if (use_static) {   // mla_decode_attn_noalloc
+    if (need > mla::static_scratch_bytes()) return MLA_ERR_WORKSPACE;
+    if (mla::static_scratch(&workspace) != hipSuccess) return MLA_ERR_HIP;
+    ws_bytes = mla::static_scratch_bytes();
+  }
   if (!workspace || ws_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 255u)) return MLA_ERR_WORKSPACE;
   return from_hip(mla::launch_decode(*cfg, cus, q_abs, cache, cache_scale, num_blocks, block_table,
                                      max_blocks, kv_lens, B, Sq, workspace, o_lat, lse,
@@ -206,6 +214,14 @@ mla_status_t mla_decode_combine(const mla_config_t* cfg, const void* q_abs, cons
                                 size_t ws_bytes, float* o_lat, float* lse, void* stream) {
   return decode_common(cfg, q_abs, cache, cache_scale, num_blocks, block_table, max_blocks, kv_lens, B, Sq,
                        workspace, ws_bytes, o_lat, lse, stream, 2);
+}
+
+mla_status_t mla_decode_attn_noalloc(const mla_config_t* cfg, const void* q_abs, const void* cache,
+                                     const float* cache_scale, int32_t num_blocks, const int32_t* block_table,
+                                     int32_t max_blocks, const int32_t* kv_lens, int32_t B, int32_t Sq,
+                                     float* o_lat, float* lse, void* stream) {
+  return decode_common(cfg, q_abs, cache, cache_scale, num_blocks, block_table, max_blocks, kv_lens, B, Sq,
+                       nullptr, 0, o_lat, lse, stream, 3, true);
 }
 
 mla_status_t mla_out_proj(const mla_config_t* cfg, const float* o_lat, const void* w_uv, void* out, int32_t T,

@@ -171,3 +171,19 @@ def test_status_strings(L):
     for code in range(5):
         assert B.mla_status_string(code).startswith("MLA_")
     assert "UNKNOWN" in B.mla_status_string(99)
+
+
+def test_noalloc_decode_validation(L):
+    """mla_decode_attn_noalloc validates like mla_decode_attn and rejects a launch whose partials
+    exceed its fixed 64 MiB scratch, before touching the device."""
+    c = cfg()
+    assert B.mla_decode_workspace_size(c, 2048, 1, 4) > B.NOALLOC_SCRATCH_BYTES
+    assert B.mla_decode_attn_noalloc(c, FAKE, FAKE, None, 100, FAKE, 4, FAKE, 2048, 1, FAKE, FAKE, stream=0,
+                                     check=False) == B.MLA_ERR_WORKSPACE
+    assert B.mla_decode_attn_noalloc(c, FAKE + 4, FAKE, None, 100, FAKE, 4, FAKE, 2, 1, FAKE, FAKE, stream=0,
+                                     check=False) == B.MLA_ERR_INVALID_ARG
+    assert B.mla_decode_attn_noalloc(c, FAKE, FAKE, None, 100, FAKE, 4, FAKE, 0, 1, FAKE, FAKE, stream=0,
+                                     check=False) == B.MLA_OK
+    c8 = cfg(cache_dtype="fp8")
+    assert B.mla_decode_attn_noalloc(c8, FAKE, FAKE, None, 100, FAKE, 4, FAKE, 2, 1, FAKE, FAKE, stream=0,
+                                     check=False) == B.MLA_ERR_INVALID_ARG
