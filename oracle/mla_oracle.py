@@ -238,6 +238,26 @@ def out_project(o_lat, W_UV):
     return np.einsum("jic,civ->jiv", o_lat, W_UV.reshape(d_c, H, -1))
 
 
+def model_output(o, W_O):
+    """The layer's output in the model width: the heads' values concatenated head-major and
+    projected by W_O [H*d_v, d_model], out = concat_i(o_i) W_O = sum_i o_i W_O[i*d_v:(i+1)*d_v].
+    The output projection the value up-projection folds into (katajob "solid answer")."""
+    o = np.asarray(o, dtype=np.float64)
+    Sq, H, d_v = o.shape
+    return o.reshape(Sq, H * d_v) @ np.asarray(W_O, dtype=np.float64)
+
+
+def fold_output_weights(W_UV, W_O, heads):
+    """W_O'_i = W_UV,i W_O,i  [d_c, d_model] for every head i, stacked [H, d_c, d_model]: with it
+    the output is sum_i o_lat_i W_O'_i, the value up-projection folded into the output projection
+    (katajob "solid answer"), straight from the latent-space output."""
+    W_UV = np.asarray(W_UV, dtype=np.float64)
+    W_O = np.asarray(W_O, dtype=np.float64)
+    d_c = W_UV.shape[0]
+    d_v = W_UV.shape[1] // heads
+    return np.stack([W_UV[:, i * d_v:(i + 1) * d_v] @ W_O[i * d_v:(i + 1) * d_v] for i in range(heads)])
+
+
 # --------------------------------------------------------------- fp8 e4m3 storage
 
 def e4m3_round(x: np.ndarray) -> np.ndarray:

@@ -199,6 +199,27 @@ def test_pre_rotated_keys_give_the_same_attention():
         assert rel_err(got[k], ref[k]) < 1e-12, k
 
 
+def test_folded_output_projection_equals_the_unfolded_chain():
+    """Folding W_UV into W_O is exact algebra (katajob "solid answer"): o_lat . W_O' equals
+    (o_lat W_UV,i) then W_O, and the brute-force unabsorbed values projected by W_O, on a
+    10-token case with scalar loops for the projection."""
+    case = _small_case(L=10, Sq=2, H=3, d_h=4, d_c=5, d_r=4, d_v=3, base=7.0)
+    rng = np.random.default_rng(12)
+    d_model = 6
+    W_O = rng.standard_normal((3 * 3, d_model))
+    ref = _brute(case)
+    out_chain = orc.model_output(ref["o"], W_O)
+    Wf = orc.fold_output_weights(case["W_UV"], W_O, 3)
+    assert Wf.shape == (3, 5, d_model)
+    out_fold = np.einsum("jic,icn->jn", ref["o_lat"], Wf)
+    assert rel_err(out_fold, out_chain) < 1e-12
+    # scalar loops: out[j][n] = sum_i sum_v o[j][i][v] W_O[i*d_v + v][n]
+    o = ref["o"].tolist()
+    brute = [[sum(o[j][i][v] * W_O[i * 3 + v][n] for i in range(3) for v in range(3)) for n in range(d_model)]
+             for j in range(2)]
+    assert rel_err(out_chain, brute) < 1e-12
+
+
 def test_lse_is_log_sum_exp_of_scores():
     case = _small_case(L=7)
     got = orc.decode(**case)
@@ -420,3 +441,14 @@ def test_planted_mistake_fails_projection_pin(kind):
     qc = _brute_projection(x, W["W_Q"], L - 1)
     errs = [rel_err(qC[0, i], qc[i * w.d_h:(i + 1) * w.d_h]) for i in range(w.heads)]
     assert max(errs) > 1e-3, kind
+
+
+def test_planted_mistake_fails_fold_pin():
+    """A fold that pairs head i's W_UV block with head i+1's W_O block fails the identity."""
+    case = _small_case(L=10, Sq=1, H=3, d_h=4, d_c=5, d_r=4, d_v=3, base=7.0)
+    W_O = np.random.default_rng(13).standard_normal((9, 6))
+    ref = _brute(case)
+    W_UV = np.asarray(case["W_UV"])
+    bad = np.stack([W_UV[:, i * 3:(i + 1) * 3] @ W_O[((i + 1) % 3) * 3:((i + 1) % 3 + 1) * 3] for i in range(3)])
+    out_bad = np.einsum("jic,icn->jn", ref["o_lat"], bad)
+    assert rel_err(out_bad, orc.model_output(ref["o"], W_O)) > 1e-3
