@@ -219,6 +219,58 @@ mla_status_t mla_decode_attn_noalloc(const mla_config_t* cfg, const void* q_abs,
                                      float* o_lat, float* lse, void* stream);
 
 /*
+ * From the hidden state: the projections upstream of the cache and the query (katajob "code":
+ * latent = x @ W_down; bembew "Multi-head Latent Attention", "Implementation Logic", steps 1, 3
+ * and 4), fused with the step's append and absorption.
+ *
+ * mla_append_absorb_hidden -- for the n new tokens, [c ; k_R raw] = h_kv [W_down | W_KR]; for the
+ * T query rows, [q^C ; q^R] = h_q [W_Q | W_QR]; then exactly mla_append_absorb with those arrays
+ * (RoPE on k_R at pos, the cache write, the fold of W_UK and RoPE on q^R at q_pos).  The
+ * projections accumulate in fp32 and are rounded once to the activation format, the format
+ * mla_cache_append and mla_absorb_q take.
+ *   d_model    model width (a multiple of 16; multiples of 64 take the matrix-core path)
+ *   h_kv       [n, d_model] act_dtype     hidden states of the new tokens
+ *   w_dkv_t    [d_c + d_R, d_model] act_dtype: the transposed weights, row j holding the weights
+ *              of output j: rows 0 .. d_c-1 are W_down^T, rows d_c .. d_c+d_R-1 are W_KR^T
+ *   h_q        [T, d_model] act_dtype     hidden states of the query rows
+ *   w_q_t      [H*(d_h + d_R), d_model] act_dtype: rows 0 .. H*d_h-1 are W_Q^T (head i's
+ *              content query is rows i*d_h ..), then H*d_R rows of W_QR^T (head-major)
+ *   workspace  >= mla_hidden_workspace_size(cfg, d_model, n, T) bytes, 256-byte aligned, contents
+ *              need no initialisation; it holds the projected rows and GEMM partial sums
+ * The other arguments are those of mla_append_absorb, validated the same way before anything is
+ * launched.  The weights are taken transposed so that each output's weights are contiguous: the
+ * matrix-core kernels then read both operands with 16-byte row loads.
+ */
+size_t mla_hidden_workspace_size(const mla_config_t* cfg, int32_t d_model, int32_t n, int32_t T);
+mla_status_t mla_append_absorb_hidden(const mla_config_t* cfg, int32_t d_model, const void* h_kv,
+                                      const void* w_dkv_t, void* cache, float* cache_scale, int32_t num_blocks,
+                                      const int32_t* pos, const int32_t* seq_of, const int32_t* block_table,
+                                      int32_t batch, int32_t max_blocks, int32_t n, const void* h_q,
+                                      const void* w_q_t, const int32_t* q_pos, const void* w_uk, void* q_abs,
+                                      int32_t T, void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * To the model width, with W_UV folded into the output projection (katajob "solid answer": the
+ * value up-projection folds into the output projection).  With W_O [H*d_v, d_model] the layer's
+ * output is concat_i(o_i) W_O = sum_i o_lat_i W_UV,i W_O,i = sum_i o_lat_i W_O'_i.
+ *
+ * mla_fold_output_weights -- W_O'_i = W_UV,i W_O,i, once, into w_fold_t [d_model, H*d_c]
+ *   (transposed: row n holds W_O'[i, c, n] at column i*d_c + c), fp32 sums, one rounding.
+ *   w_uv [d_c, H*d_v], w_o [H*d_v, d_model], all act_dtype.
+ * mla_out_proj_folded -- out [T, d_model] (act_dtype) = o_lat [T, H*d_c] (fp32; rounded to bf16 on
+ *   the matrix-core path) . W_O'.  workspace >= mla_out_proj_folded_workspace_size(cfg, d_model, T)
+ *   bytes (GEMM partial sums), 256-byte aligned.
+ * At decode batch sizes the folded weight (H*d_c*d_model values) is d_c/d_v times the size of
+ * W_O, so applying W_UV with mla_out_proj and then W_O reads fewer bytes; the folded form is the
+ * one-GEMM path.
+ */
+mla_status_t mla_fold_output_weights(const mla_config_t* cfg, int32_t d_model, const void* w_uv, const void* w_o,
+                                     void* w_fold_t, void* stream);
+size_t mla_out_proj_folded_workspace_size(const mla_config_t* cfg, int32_t d_model, int32_t T);
+mla_status_t mla_out_proj_folded(const mla_config_t* cfg, int32_t d_model, const float* o_lat, const void* w_fold_t,
+                                 void* out, int32_t T, void* workspace, size_t ws_bytes, void* stream);
+
+/*
  * mla_out_proj -- apply W_UV once per query on the output side:
  * out[t,i] = o_lat[t,i] W_UV,i, W_UV,i = columns i*d_v .. i*d_v+d_v-1 of w_uv
  * (katajob "solid answer": the value up-projection folds into the output projection).
@@ -231,7 +283,7 @@ mla_status_t mla_out_proj(const mla_config_t* cfg, const float* o_lat, const voi
 /* Human-readable name of a status code (static storage). */
 const char* mla_status_string(mla_status_t status);
 
-/* ABI version of this header: 4. */
+/* ABI version of this header: 5. */
 int32_t mla_abi_version(void);
 
 #ifdef __cplusplus

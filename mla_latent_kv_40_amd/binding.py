@@ -13,7 +13,7 @@ from typing import Optional
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmla.so")
 
-ABI_VERSION = 4   # what mla_abi_version() returns for the argument lists below
+ABI_VERSION = 5   # what mla_abi_version() returns for the argument lists below
 NOALLOC_SCRATCH_BYTES = 64 << 20   # MLA_NOALLOC_SCRATCH_BYTES
 
 MLA_OK, MLA_ERR_INVALID_ARG, MLA_ERR_UNSUPPORTED, MLA_ERR_WORKSPACE, MLA_ERR_HIP = range(5)
@@ -22,7 +22,8 @@ DTYPES = {"f32": MLA_F32, "bf16": MLA_BF16, "fp8": MLA_FP8_E4M3}
 
 EXPORTS = ("mla_cache_append", "mla_absorb_q", "mla_append_absorb", "mla_decode_workspace_size", "mla_decode_attn",
            "mla_decode_split", "mla_decode_combine", "mla_decode_attn_noalloc", "mla_out_proj", "mla_status_string",
-           "mla_abi_version")
+           "mla_abi_version", "mla_hidden_workspace_size", "mla_append_absorb_hidden", "mla_fold_output_weights",
+           "mla_out_proj_folded_workspace_size", "mla_out_proj_folded")
 
 
 class MlaConfig(ctypes.Structure):
@@ -62,11 +63,20 @@ def lib() -> ctypes.CDLL:
                                          f32p, f32p, vp]
         L.mla_decode_attn_noalloc.argtypes = [cfgp, vp, vp, f32p, i32, vp, i32, vp, i32, i32, f32p, f32p, vp]
         L.mla_out_proj.argtypes = [cfgp, f32p, vp, vp, i32, vp]
+        L.mla_hidden_workspace_size.argtypes = [cfgp, i32, i32, i32]
+        L.mla_hidden_workspace_size.restype = ctypes.c_size_t
+        L.mla_append_absorb_hidden.argtypes = [cfgp, i32, vp, vp, vp, f32p, i32, vp, vp, vp, i32, i32, i32, vp, vp,
+                                               vp, vp, vp, i32, vp, ctypes.c_size_t, vp]
+        L.mla_fold_output_weights.argtypes = [cfgp, i32, vp, vp, vp, vp]
+        L.mla_out_proj_folded_workspace_size.argtypes = [cfgp, i32, i32]
+        L.mla_out_proj_folded_workspace_size.restype = ctypes.c_size_t
+        L.mla_out_proj_folded.argtypes = [cfgp, i32, f32p, vp, vp, i32, vp, ctypes.c_size_t, vp]
         L.mla_status_string.argtypes = [ctypes.c_int]
         L.mla_status_string.restype = ctypes.c_char_p
         L.mla_abi_version.restype = ctypes.c_int32
         for name in ("mla_cache_append", "mla_absorb_q", "mla_append_absorb", "mla_decode_attn", "mla_decode_split",
-                     "mla_decode_combine", "mla_decode_attn_noalloc", "mla_out_proj"):
+                     "mla_decode_combine", "mla_decode_attn_noalloc", "mla_out_proj", "mla_append_absorb_hidden",
+                     "mla_fold_output_weights", "mla_out_proj_folded"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -187,6 +197,43 @@ def mla_out_proj(cfg: Config, o_lat, w_uv, out, T, stream=None, check=True) -> i
     st = lib().mla_out_proj(ctypes.byref(cfg.c()), _ptr(o_lat), _ptr(w_uv), _ptr(out), T, _stream(stream))
     if check:
         _check("mla_out_proj", st)
+    return st
+
+
+def mla_hidden_workspace_size(cfg: Config, d_model: int, n: int, T: int) -> int:
+    return int(lib().mla_hidden_workspace_size(ctypes.byref(cfg.c()), d_model, n, T))
+
+
+def mla_append_absorb_hidden(cfg: Config, d_model, h_kv, w_dkv_t, cache, cache_scale, num_blocks, pos, seq_of,
+                             block_table, batch, max_blocks, n, h_q, w_q_t, q_pos, w_uk, q_abs, T, workspace,
+                             ws_bytes, stream=None, check=True) -> int:
+    st = lib().mla_append_absorb_hidden(ctypes.byref(cfg.c()), d_model, _ptr(h_kv), _ptr(w_dkv_t), _ptr(cache),
+                                        _ptr(cache_scale), num_blocks, _ptr(pos), _ptr(seq_of), _ptr(block_table),
+                                        batch, max_blocks, n, _ptr(h_q), _ptr(w_q_t), _ptr(q_pos), _ptr(w_uk),
+                                        _ptr(q_abs), T, _ptr(workspace), ws_bytes, _stream(stream))
+    if check:
+        _check("mla_append_absorb_hidden", st)
+    return st
+
+
+def mla_fold_output_weights(cfg: Config, d_model, w_uv, w_o, w_fold_t, stream=None, check=True) -> int:
+    st = lib().mla_fold_output_weights(ctypes.byref(cfg.c()), d_model, _ptr(w_uv), _ptr(w_o), _ptr(w_fold_t),
+                                       _stream(stream))
+    if check:
+        _check("mla_fold_output_weights", st)
+    return st
+
+
+def mla_out_proj_folded_workspace_size(cfg: Config, d_model: int, T: int) -> int:
+    return int(lib().mla_out_proj_folded_workspace_size(ctypes.byref(cfg.c()), d_model, T))
+
+
+def mla_out_proj_folded(cfg: Config, d_model, o_lat, w_fold_t, out, T, workspace, ws_bytes, stream=None,
+                        check=True) -> int:
+    st = lib().mla_out_proj_folded(ctypes.byref(cfg.c()), d_model, _ptr(o_lat), _ptr(w_fold_t), _ptr(out), T,
+                                   _ptr(workspace), ws_bytes, _stream(stream))
+    if check:
+        _check("mla_out_proj_folded", st)
     return st
 
 

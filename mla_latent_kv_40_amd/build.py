@@ -12,7 +12,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
-SOURCES = ["libmla.cpp", "append.hip", "absorb.hip", "decode.hip"]
+SOURCES = ["libmla.cpp", "append.hip", "absorb.hip", "decode.hip", "project.hip"]
 LIB = os.path.join(HERE, "libmla.so")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -30,6 +30,7 @@ EXTRA = {
     "append.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
     "absorb.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
     "decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+    "project.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
     "libmla.cpp": [],
 }
 

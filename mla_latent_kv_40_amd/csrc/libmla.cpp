@@ -25,6 +25,13 @@ size_t decode_workspace_bytes(const mla_config_t&, int, int, int, int);
 size_t static_scratch_bytes();
 hipError_t static_scratch(void** out);
 bool is_dsv2_shape(const mla_config_t&);
+hipError_t launch_project_hidden(const mla_config_t&, int, int, const void*, const void*, int, const void*,
+                                 const void*, int, void*, void*, void*, void*, void*, hipStream_t);
+size_t project_hidden_workspace(const mla_config_t&, int, int, int, int);
+hipError_t launch_out_proj_folded(const mla_config_t&, int, int, const float*, const void*, void*, int, void*,
+                                  hipStream_t);
+size_t out_proj_folded_workspace(const mla_config_t&, int, int, int);
+hipError_t launch_fold_wo(const mla_config_t&, int, const void*, const void*, void*, hipStream_t);
 }  // namespace mla
 
 namespace {
@@ -73,7 +80,7 @@ mla_status_t from_hip(hipError_t e) { return e == hipSuccess ? MLA_OK : MLA_ERR_
 
 extern "C" {
 
-int32_t mla_abi_version(void) { return 4; }
+int32_t mla_abi_version(void) { return 5; }
 
 const char* mla_status_string(mla_status_t s) {
   switch (s) {
@@ -222,6 +229,88 @@ mla_status_t mla_decode_attn_noalloc(const mla_config_t* cfg, const void* q_abs,
                                      float* o_lat, float* lse, void* stream) {
   return decode_common(cfg, q_abs, cache, cache_scale, num_blocks, block_table, max_blocks, kv_lens, B, Sq,
                        nullptr, 0, o_lat, lse, stream, 3, true);
+}
+
+// ---------------------------------------------------------------- from and to the model width
+
+static bool d_model_ok(int32_t d_model) { return d_model > 0 && d_model % 16 == 0 && d_model <= (1 << 20); }
+
+static size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+size_t mla_hidden_workspace_size(const mla_config_t* cfg, int32_t d_model, int32_t n, int32_t T) {
+  if (check_cfg(cfg) != MLA_OK || !d_model_ok(d_model) || n < 0 || T < 0) return 0;
+  return mla::project_hidden_workspace(*cfg, current_cu_count(), d_model, n, T) + 256;
+}
+
+mla_status_t mla_append_absorb_hidden(const mla_config_t* cfg, int32_t d_model, const void* h_kv,
+                                      const void* w_dkv_t, void* cache, float* cache_scale, int32_t num_blocks,
+                                      const int32_t* pos, const int32_t* seq_of, const int32_t* block_table,
+                                      int32_t batch, int32_t max_blocks, int32_t n, const void* h_q,
+                                      const void* w_q_t, const int32_t* q_pos, const void* w_uk, void* q_abs,
+                                      int32_t T, void* workspace, size_t ws_bytes, void* stream) {
+  mla_status_t st = check_cfg(cfg);
+  if (st != MLA_OK) return st;
+  if (!d_model_ok(d_model) || n < 0 || T < 0) return MLA_ERR_INVALID_ARG;
+  if (n > 0 && (!h_kv || !w_dkv_t || !aligned16(h_kv) || !aligned16(w_dkv_t))) return MLA_ERR_INVALID_ARG;
+  if (T > 0 && (!h_q || !w_q_t || !aligned16(h_q) || !aligned16(w_q_t))) return MLA_ERR_INVALID_ARG;
+  if (n == 0 && T == 0) return MLA_OK;
+  const int cus = current_cu_count();
+  const size_t need = mla::project_hidden_workspace(*cfg, cus, d_model, n, T);
+  if (!workspace || ws_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 255u)) return MLA_ERR_WORKSPACE;
+  // the projections' outputs, laid out as mla_cache_append and mla_absorb_q take them
+  const size_t el = cfg->act_dtype == MLA_F32 ? 4 : 2;
+  uint8_t* w = static_cast<uint8_t*>(workspace);
+  void* kv_c = w;
+  w += align256((size_t)n * cfg->d_c * el);
+  void* kv_r = w;
+  w += align256((size_t)n * cfg->d_r * el);
+  void* q_nope = w;
+  w += align256((size_t)T * cfg->num_heads * cfg->d_h * el);
+  void* q_rope = w;
+  w += align256((size_t)T * cfg->num_heads * cfg->d_r * el);
+  // validate the append and absorption halves (as mla_append_absorb will) with the arrays they
+  // will receive, before anything is launched
+  st = check_append(cfg, cache, cache_scale, num_blocks, kv_c, kv_r, pos, seq_of, block_table, batch, max_blocks, n);
+  if (st != MLA_OK) return st;
+  st = check_absorb(cfg, q_nope, q_rope, q_pos, w_uk, q_abs, T);
+  if (st != MLA_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = mla::launch_project_hidden(*cfg, cus, d_model, h_kv, w_dkv_t, n, h_q, w_q_t, T, kv_c, kv_r, q_nope,
+                                            q_rope, w, s);
+  if (e != hipSuccess) return MLA_ERR_HIP;
+  return mla_append_absorb(cfg, cache, cache_scale, num_blocks, kv_c, kv_r, pos, seq_of, block_table, batch,
+                           max_blocks, n, q_nope, q_rope, q_pos, w_uk, q_abs, T, stream);
+}
+
+mla_status_t mla_fold_output_weights(const mla_config_t* cfg, int32_t d_model, const void* w_uv, const void* w_o,
+                                     void* w_fold_t, void* stream) {
+  mla_status_t st = check_cfg(cfg);
+  if (st != MLA_OK) return st;
+  if (!d_model_ok(d_model)) return MLA_ERR_INVALID_ARG;
+  if (!w_uv || !w_o || !w_fold_t || !aligned16(w_uv) || !aligned16(w_o) || !aligned16(w_fold_t))
+    return MLA_ERR_INVALID_ARG;
+  return from_hip(mla::launch_fold_wo(*cfg, d_model, w_uv, w_o, w_fold_t, static_cast<hipStream_t>(stream)));
+}
+
+size_t mla_out_proj_folded_workspace_size(const mla_config_t* cfg, int32_t d_model, int32_t T) {
+  if (check_cfg(cfg) != MLA_OK || !d_model_ok(d_model) || T < 0) return 0;
+  return mla::out_proj_folded_workspace(*cfg, current_cu_count(), d_model, T) + 256;
+}
+
+mla_status_t mla_out_proj_folded(const mla_config_t* cfg, int32_t d_model, const float* o_lat, const void* w_fold_t,
+                                 void* out, int32_t T, void* workspace, size_t ws_bytes, void* stream) {
+  mla_status_t st = check_cfg(cfg);
+  if (st != MLA_OK) return st;
+  if (!d_model_ok(d_model) || T < 0) return MLA_ERR_INVALID_ARG;
+  if (T == 0) return MLA_OK;
+  if (!o_lat || !w_fold_t || !out || !aligned16(o_lat) || !aligned16(w_fold_t) || !aligned16(out))
+    return MLA_ERR_INVALID_ARG;
+  const int cus = current_cu_count();
+  const size_t need = mla::out_proj_folded_workspace(*cfg, cus, d_model, T);
+  if (need > 0 && (!workspace || ws_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 255u)))
+    return MLA_ERR_WORKSPACE;
+  return from_hip(mla::launch_out_proj_folded(*cfg, cus, d_model, o_lat, w_fold_t, out, T, workspace,
+                                              static_cast<hipStream_t>(stream)));
 }
 
 mla_status_t mla_out_proj(const mla_config_t* cfg, const float* o_lat, const void* w_uv, void* out, int32_t T,

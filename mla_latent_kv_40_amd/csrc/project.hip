@@ -1,0 +1,322 @@
+// Projections from and to the model width, on either side of the latent-space decode:
+//
+//   upstream    [c ; k_R raw] = h [W_down | W_KR]     the latent and the positional key of each new
+//               [q^C ; q^R]   = h [W_Q | W_QR]        token, and the two query parts (katajob
+//                                                     interview page, "code": latent = x @ W_down;
+//                                                     bembew "Multi-head Latent Attention",
+//                                                     "Implementation Logic", steps 1, 3 and 4)
+//   downstream  out = sum_i o_lat_i W_O'_i            the value up-projection folded into the output
+//               W_O'_i = W_UV,i W_O,i  [d_c, d_model]  projection (katajob "solid answer")
+//
+// All are row GEMMs Y[t, n] = sum_k X[t, k] W[k, n] with few rows t (the step's tokens) and a large
+// weight, so they are bound by reading the weight once.  The weight is taken transposed, Wt[n, k]
+// (each output's weights contiguous, the layout of a linear layer's weight matrix), so that both
+// matrix operands are 16-byte row loads: A = Wt rows (32 outputs x 8 consecutive k per lane), B = X
+// rows (32 tokens x 8 consecutive k), D = Y^T on v_mfma_f32_32x32x16_bf16.
+//
+// A workgroup owns 64 outputs x 64 rows and a slice of the contraction; its four waves take
+// interleaved 64-wide chunks of that slice and their tiles are summed through LDS.  With one slice
+// the workgroup writes the result; with S slices each writes fp32 partials and a second kernel adds
+// the S partials in a fixed order (deterministic) and writes the result.
+#include "common.h"
+
+#include <cmath>
+
+namespace mla {
+
+constexpr int kPjN = 64;       // outputs per workgroup
+constexpr int kPjT = 64;       // rows per workgroup
+constexpr int kPjChunk = 64;   // contraction elements per chunk (four MFMA K-steps)
+
+// Result routing: output n < split goes to dst0[t * ld0 + n], the rest to dst1[t * ld1 + n - split]
+// (the latent and the positional key, or the content and the positional query, are separate
+// arrays of the next call).
+struct PjOut {
+  void* dst0;
+  void* dst1;
+  long long ld0, ld1;
+  int split;
+};
+
+template <typename OutT>
+__device__ __forceinline__ void pj_store(const PjOut& o, int t, int n, float v) {
+  OutT* d;
+  size_t i;
+  if (n < o.split) {
+    d = static_cast<OutT*>(o.dst0);
+    i = (size_t)t * o.ld0 + n;
+  } else {
+    d = static_cast<OutT*>(o.dst1);
+    i = (size_t)t * o.ld1 + (n - o.split);
+  }
+  if constexpr (sizeof(OutT) == 4) d[i] = v;
+  else d[i] = (OutT)f32_to_bf16_bits(v);
+}
+
+// 8 consecutive X values as bf16 (fp32 inputs are rounded to bf16, nearest even)
+template <typename XT>
+__device__ __forceinline__ bf16x8 load_x8(const XT* p);
+template <>
+__device__ __forceinline__ bf16x8 load_x8<uint16_t>(const uint16_t* p) {
+  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
+}
+template <>
+__device__ __forceinline__ bf16x8 load_x8<float>(const float* p) {
+  const f32x4 a = *reinterpret_cast<const f32x4*>(p), b = *reinterpret_cast<const f32x4*>(p + 4);
+  return __builtin_bit_cast(bf16x8, u32x4{cvt_pk_bf16(a[0], a[1]), cvt_pk_bf16(a[2], a[3]), cvt_pk_bf16(b[0], b[1]),
+                                          cvt_pk_bf16(b[2], b[3])});
+}
+
+// Workgroup (n-tile, slice s, row block z).  X [T, K] (ldx), Wt [N, K] bf16; K % 64 == 0.
+// out_mode 0: write through `o` (bf16); 1: fp32 partials part[s][t][n] (ld N).
+template <typename XT>
+__global__ void __launch_bounds__(256) rows_gemm_kernel(const XT* __restrict__ X, long long ldx,
+                                                        const uint16_t* __restrict__ Wt, int T, int N, int K,
+                                                        int S, PjOut o, float* __restrict__ part) {
+  __shared__ __attribute__((aligned(16))) float red[4][4][16][64];   // [wave][tile][i][lane]  64 KiB
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n0 = kPjN * blockIdx.x, s = blockIdx.y, t0 = kPjT * blockIdx.z;
+  const int r = lane & 31, g = lane >> 5;
+  // rows of this lane's operands (clamped: rows past N or T read a valid row and are not stored)
+  const int na = n0 + r < N ? n0 + r : N - 1, nb = n0 + 32 + r < N ? n0 + 32 + r : N - 1;
+  const int ta = t0 + r < T ? t0 + r : T - 1, tb = t0 + 32 + r < T ? t0 + 32 + r : T - 1;
+  const uint16_t* wa = Wt + (size_t)na * K + 8 * g;
+  const uint16_t* wb = Wt + (size_t)nb * K + 8 * g;
+  const XT* xa = X + (size_t)ta * ldx + 8 * g;
+  const XT* xb = X + (size_t)tb * ldx + 8 * g;
+  f32x16 acc[4];   // [n tile][t tile]
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[i][e] = 0.f;
+  const int n_chunks = K / kPjChunk;
+  const int stride = 4 * S;
+  for (int c = 4 * s + wave; c < n_chunks; c += stride) {
+    const int k = c * kPjChunk;
+    bf16x8 a0[4], a1[4], b0[4], b1[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {   // every load of the chunk first
+      a0[q] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(wa + k + 16 * q));
+      a1[q] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(wb + k + 16 * q));
+      b0[q] = load_x8(xa + k + 16 * q);
+      b1[q] = load_x8(xb + k + 16 * q);
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0[q], b0[q], acc[0], 0, 0, 0);
+      acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0[q], b1[q], acc[1], 0, 0, 0);
+      acc[2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1[q], b0[q], acc[2], 0, 0, 0);
+      acc[3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1[q], b1[q], acc[3], 0, 0, 0);
+    }
+  }
+  // acc[2 nt + tt][i] = partial Y^T[n = n0 + 32 nt + 8(i/4) + 4g + i%4, t = t0 + 32 tt + r]
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) red[wave][i][e][lane] = acc[i][e];
+  __syncthreads();
+  // thread: tile i = wave, element e = 0..15 of its lane, summed over the four waves
+  {
+    const int i = wave, nt = i >> 1, tt = i & 1;
+    const int t = t0 + 32 * tt + r;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const float v = red[0][i][e][lane] + red[1][i][e][lane] + red[2][i][e][lane] + red[3][i][e][lane];
+      const int n = n0 + 32 * nt + 8 * (e >> 2) + 4 * g + (e & 3);
+      if (n < N && t < T) {
+        if (part != nullptr) part[((size_t)s * T + t) * N + n] = v;
+        else pj_store<uint16_t>(o, t, n, v);
+      }
+    }
+  }
+}
+
+// Y = sum over the S slices of part[s][t][n], in slice order, written through `o`.
+template <typename OutT>
+__global__ void __launch_bounds__(256) rows_reduce_kernel(const float* __restrict__ part, int T, int N, int S,
+                                                          PjOut o) {
+  const size_t total = (size_t)T * N;
+  for (size_t e = (size_t)blockIdx.x * 256 + threadIdx.x; e < total; e += (size_t)gridDim.x * 256) {
+    float v = 0.f;
+    for (int s = 0; s < S; ++s) v += part[(size_t)s * total + e];
+    pj_store<OutT>(o, (int)(e / N), (int)(e % N), v);
+  }
+}
+
+// Generic (fp32 or bf16, any K): one thread per output element, fp32 accumulation.
+template <typename XT, typename WT, typename OutT>
+__global__ void __launch_bounds__(256) rows_gemm_generic_kernel(const XT* __restrict__ X, long long ldx,
+                                                                const WT* __restrict__ Wt, int T, int N, int K,
+                                                                PjOut o) {
+  const size_t total = (size_t)T * N;
+  for (size_t e = (size_t)blockIdx.x * 256 + threadIdx.x; e < total; e += (size_t)gridDim.x * 256) {
+    const int t = (int)(e / N), n = (int)(e % N);
+    float acc = 0.f;
+    for (int k = 0; k < K; ++k) acc += load_act(X, (size_t)t * ldx + k) * load_act(Wt, (size_t)n * K + k);
+    pj_store<OutT>(o, t, n, acc);
+  }
+}
+
+// Slices of the contraction for a row GEMM: enough workgroups to cover the compute units about
+// twice, each slice at least four chunks per wave.
+int rows_gemm_slices(int num_cus, int T, int N, int K) {
+  const long long tiles = (long long)((N + kPjN - 1) / kPjN) * ((T + kPjT - 1) / kPjT);
+  if (tiles <= 0) return 1;   // nothing to compute
+  const int chunks = K / kPjChunk;
+  long long S = (2LL * num_cus + tiles - 1) / tiles;
+  const long long S_max = chunks / 16 > 0 ? chunks / 16 : 1;
+  if (S > S_max) S = S_max;
+  if (S < 1) S = 1;
+  return (int)S;
+}
+
+size_t rows_gemm_workspace(int num_cus, int T, int N, int K) {
+  const int S = rows_gemm_slices(num_cus, T, N, K);
+  if (S <= 1) return 0;
+  return (((size_t)S * T * N * sizeof(float)) + 255) & ~(size_t)255;
+}
+
+// Y = X . Wt^T through `o`, bf16 MFMA path (X bf16 or fp32, Wt bf16, K % 64 == 0).
+template <typename XT>
+hipError_t launch_rows_gemm(int num_cus, const XT* X, long long ldx, const uint16_t* Wt, int T, int N, int K,
+                            const PjOut& o, void* workspace, hipStream_t stream) {
+  const int S = rows_gemm_slices(num_cus, T, N, K);
+  float* part = S > 1 ? static_cast<float*>(workspace) : nullptr;
+  const dim3 grid((N + kPjN - 1) / kPjN, S, (T + kPjT - 1) / kPjT);
+  hipLaunchKernelGGL(rows_gemm_kernel<XT>, grid, dim3(256), 0, stream, X, ldx, Wt, T, N, K, S, o, part);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || S == 1) return e;
+  const size_t total = (size_t)T * N;
+  const unsigned blocks = (unsigned)((total + 255) / 256 < 4096 ? (total + 255) / 256 : 4096);
+  hipLaunchKernelGGL(rows_reduce_kernel<uint16_t>, dim3(blocks), dim3(256), 0, stream, part, T, N, S, o);
+  return hipGetLastError();
+}
+
+template <typename XT, typename WT, typename OutT>
+hipError_t launch_rows_gemm_generic(const XT* X, long long ldx, const WT* Wt, int T, int N, int K, const PjOut& o,
+                                    hipStream_t stream) {
+  const size_t total = (size_t)T * N;
+  const unsigned blocks = (unsigned)((total + 255) / 256 < 8192 ? (total + 255) / 256 : 8192);
+  hipLaunchKernelGGL((rows_gemm_generic_kernel<XT, WT, OutT>), dim3(blocks > 0 ? blocks : 1), dim3(256), 0, stream,
+                     X, ldx, Wt, T, N, K, o);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ fold of W_UV into W_O
+
+// W_O'^T[n, i*d_c + c] = sum_v W_UV[c, i*d_v + v] W_O[i*d_v + v, n]: one thread per element, fp32
+// sums of the products, one rounding to the output format.  Weight preparation, run once.
+template <typename T>
+__global__ void __launch_bounds__(256) fold_wo_kernel(const T* __restrict__ w_uv, const T* __restrict__ w_o,
+                                                      T* __restrict__ w_fold_t, int H, int d_c, int d_v,
+                                                      int d_model) {
+  const size_t total = (size_t)d_model * H * d_c;
+  for (size_t e = (size_t)blockIdx.x * 256 + threadIdx.x; e < total; e += (size_t)gridDim.x * 256) {
+    const int c = (int)(e % d_c);
+    const size_t rest = e / d_c;
+    const int i = (int)(rest % H);
+    const int n = (int)(rest / H);
+    float acc = 0.f;
+    for (int v = 0; v < d_v; ++v)
+      acc += load_act(w_uv, (size_t)c * H * d_v + (size_t)i * d_v + v) * load_act(w_o, ((size_t)i * d_v + v) * d_model + n);
+    if constexpr (sizeof(T) == 4) w_fold_t[e] = acc;
+    else w_fold_t[e] = (T)f32_to_bf16_bits(acc);
+  }
+}
+
+// ------------------------------------------------------------------ launchers (host)
+
+bool is_dsv2_shape(const mla_config_t& c);
+
+// The upstream projections of one step: latent rows (c, k_R raw) of the n new tokens into
+// kv_c [n, d_c] / kv_r [n, d_R], and the queries of the T query rows into q_nope [T, H*d_h] /
+// q_rope [T, H*d_R], all in the activation format.
+hipError_t launch_project_hidden(const mla_config_t& cfg, int num_cus, int d_model, const void* h_kv,
+                                 const void* w_dkv_t, int n, const void* h_q, const void* w_q_t, int T, void* kv_c,
+                                 void* kv_r, void* q_nope, void* q_rope, void* gemm_ws, hipStream_t stream) {
+  const int H = cfg.num_heads, d_c = cfg.d_c, d_r = cfg.d_r, d_h = cfg.d_h;
+  const PjOut okv{kv_c, kv_r, d_c, d_r, d_c};
+  const PjOut oq{q_nope, q_rope, (long long)H * d_h, (long long)H * d_r, H * d_h};
+  const int Nkv = d_c + d_r, Nq = H * (d_h + d_r);
+  hipError_t e = hipSuccess;
+  if (cfg.act_dtype == MLA_BF16 && d_model % kPjChunk == 0) {
+    if (n > 0)
+      e = launch_rows_gemm(num_cus, static_cast<const uint16_t*>(h_kv), d_model, static_cast<const uint16_t*>(w_dkv_t),
+                           n, Nkv, d_model, okv, gemm_ws, stream);
+    if (e == hipSuccess && T > 0)
+      e = launch_rows_gemm(num_cus, static_cast<const uint16_t*>(h_q), d_model, static_cast<const uint16_t*>(w_q_t), T,
+                           Nq, d_model, oq, gemm_ws, stream);
+    return e;
+  }
+  if (cfg.act_dtype == MLA_BF16) {
+    if (n > 0)
+      e = launch_rows_gemm_generic<uint16_t, uint16_t, uint16_t>(static_cast<const uint16_t*>(h_kv), d_model,
+                                                                static_cast<const uint16_t*>(w_dkv_t), n, Nkv,
+                                                                d_model, okv, stream);
+    if (e == hipSuccess && T > 0)
+      e = launch_rows_gemm_generic<uint16_t, uint16_t, uint16_t>(static_cast<const uint16_t*>(h_q), d_model,
+                                                                static_cast<const uint16_t*>(w_q_t), T, Nq, d_model,
+                                                                oq, stream);
+    return e;
+  }
+  if (n > 0)
+    e = launch_rows_gemm_generic<float, float, float>(static_cast<const float*>(h_kv), d_model,
+                                                      static_cast<const float*>(w_dkv_t), n, Nkv, d_model, okv,
+                                                      stream);
+  if (e == hipSuccess && T > 0)
+    e = launch_rows_gemm_generic<float, float, float>(static_cast<const float*>(h_q), d_model,
+                                                      static_cast<const float*>(w_q_t), T, Nq, d_model, oq, stream);
+  return e;
+}
+
+// Workspace of launch_project_hidden: the two projections' outputs plus the GEMM partials.
+size_t project_hidden_workspace(const mla_config_t& cfg, int num_cus, int d_model, int n, int T) {
+  const size_t el = cfg.act_dtype == MLA_F32 ? 4 : 2;
+  auto al = [](size_t b) { return (b + 255) & ~(size_t)255; };
+  size_t ws = al((size_t)n * cfg.d_c * el) + al((size_t)n * cfg.d_r * el) +
+              al((size_t)T * cfg.num_heads * cfg.d_h * el) + al((size_t)T * cfg.num_heads * cfg.d_r * el);
+  if (cfg.act_dtype == MLA_BF16 && d_model % kPjChunk == 0) {
+    const size_t a = rows_gemm_workspace(num_cus, n, cfg.d_c + cfg.d_r, d_model);
+    const size_t b = rows_gemm_workspace(num_cus, T, cfg.num_heads * (cfg.d_h + cfg.d_r), d_model);
+    ws += a > b ? a : b;
+  }
+  return ws;
+}
+
+// out [T, d_model] = o_lat [T, H*d_c] . W_O'  (W_O' given transposed: w_fold_t [d_model, H*d_c]).
+hipError_t launch_out_proj_folded(const mla_config_t& cfg, int num_cus, int d_model, const float* o_lat,
+                                  const void* w_fold_t, void* out, int T, void* workspace, hipStream_t stream) {
+  const int K = cfg.num_heads * cfg.d_c;
+  const PjOut o{out, out, d_model, d_model, d_model};
+  if (cfg.act_dtype == MLA_BF16 && K % kPjChunk == 0)
+    return launch_rows_gemm(num_cus, o_lat, (long long)K, static_cast<const uint16_t*>(w_fold_t), T, d_model, K, o,
+                            workspace, stream);
+  if (cfg.act_dtype == MLA_BF16)
+    return launch_rows_gemm_generic<float, uint16_t, uint16_t>(o_lat, K, static_cast<const uint16_t*>(w_fold_t), T,
+                                                               d_model, K, o, stream);
+  return launch_rows_gemm_generic<float, float, float>(o_lat, K, static_cast<const float*>(w_fold_t), T, d_model, K,
+                                                       o, stream);
+}
+
+size_t out_proj_folded_workspace(const mla_config_t& cfg, int num_cus, int d_model, int T) {
+  const int K = cfg.num_heads * cfg.d_c;
+  if (cfg.act_dtype == MLA_BF16 && K % kPjChunk == 0) return rows_gemm_workspace(num_cus, T, d_model, K);
+  return 0;
+}
+
+hipError_t launch_fold_wo(const mla_config_t& cfg, int d_model, const void* w_uv, const void* w_o, void* w_fold_t,
+                          hipStream_t stream) {
+  const size_t total = (size_t)d_model * cfg.num_heads * cfg.d_c;
+  const unsigned blocks = (unsigned)((total + 255) / 256 < 65536 ? (total + 255) / 256 : 65536);
+  if (cfg.act_dtype == MLA_F32)
+    hipLaunchKernelGGL(fold_wo_kernel<float>, dim3(blocks), dim3(256), 0, stream, static_cast<const float*>(w_uv),
+                       static_cast<const float*>(w_o), static_cast<float*>(w_fold_t), cfg.num_heads, cfg.d_c, cfg.d_v,
+                       d_model);
+  else
+    hipLaunchKernelGGL(fold_wo_kernel<uint16_t>, dim3(blocks), dim3(256), 0, stream,
+                       static_cast<const uint16_t*>(w_uv), static_cast<const uint16_t*>(w_o),
+                       static_cast<uint16_t*>(w_fold_t), cfg.num_heads, cfg.d_c, cfg.d_v, d_model);
+  return hipGetLastError();
+}
+
+}  // namespace mla

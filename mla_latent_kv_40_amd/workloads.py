@@ -164,6 +164,7 @@ def draw_batch(w: Workload) -> Batch:
         weights["W_QR"] = normal((dm, H * dr), dm)
         weights["W_Q"] = normal((dm, H * dh), dm)
         weights["W_KR"] = normal((dm, dr), dm)
+        weights["W_O"] = normal((H * dv, dm), H * dv)
     else:
         weights["W_UK"] = normal((dc, H * dh), dc)
         weights["W_UV"] = normal((dc, H * dv), dc)
@@ -184,3 +185,25 @@ def draw_sequence(w: Workload, b: int, kv_len: int) -> Dict[str, np.ndarray]:
     qc = _as_input(w, g.standard_normal((w.sq, w.heads, w.d_h), dtype=np.float32))
     qr = _as_input(w, g.standard_normal((w.sq, w.heads, w.d_r), dtype=np.float32))
     return {"c": c, "k_r": kr, "q_c": qc, "q_r": qr}
+
+
+def draw_hidden(w: Workload, d_model: int, kv_lens) -> Dict[str, np.ndarray]:
+    """Hidden-state inputs for a DeepSeek-V2-shaped workload run from the model width: the
+    projection weights W_down [d_model, d_c], W_KR [d_model, d_R], W_Q [d_model, H*d_h],
+    W_QR [d_model, H*d_R], the output projection W_O [H*d_v, d_model] (all ~ N(0, 1/fan_in)) and
+    hidden states x_b [kv_len_b, d_model] ~ N(0, 1) per sequence, rounded to the input format.
+    Drawn from their own streams (PCG64(SeedSequence([seed, 2])) for the weights,
+    [seed, 3, b] for sequence b), so the other draws of the workload are unchanged."""
+    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([w.seed, 2])))
+    H, dh, dv, dc, dr = w.heads, w.d_h, w.d_v, w.d_c, w.d_r
+
+    def normal(shape, fan_in):
+        return _as_input(w, g.standard_normal(shape, dtype=np.float32) / np.float32(np.sqrt(fan_in)))
+
+    out = {"W_down": normal((d_model, dc), d_model), "W_KR": normal((d_model, dr), d_model),
+           "W_Q": normal((d_model, H * dh), d_model), "W_QR": normal((d_model, H * dr), d_model),
+           "W_O": normal((H * dv, d_model), H * dv)}
+    for b, L in enumerate(np.asarray(kv_lens)):
+        gb = np.random.Generator(np.random.PCG64(np.random.SeedSequence([w.seed, 3, b])))
+        out[f"x{b}"] = _as_input(w, gb.standard_normal((int(L), d_model), dtype=np.float32))
+    return out

@@ -187,3 +187,37 @@ def test_noalloc_decode_validation(L):
     c8 = cfg(cache_dtype="fp8")
     assert B.mla_decode_attn_noalloc(c8, FAKE, FAKE, None, 100, FAKE, 4, FAKE, 2, 1, FAKE, FAKE, stream=0,
                                      check=False) == B.MLA_ERR_INVALID_ARG
+
+
+def test_hidden_and_folded_calls_validate_first(L):
+    c = cfg()
+    ws = B.mla_hidden_workspace_size(c, 5120, 8, 8)
+    assert ws > 0 and B.mla_hidden_workspace_size(c, 5121, 8, 8) == 0
+    # either side may be empty (context written without queries, or queries only)
+    assert 0 < B.mla_hidden_workspace_size(c, 5120, 200, 0) and 0 < B.mla_hidden_workspace_size(c, 5120, 0, 4)
+    assert B.mla_hidden_workspace_size(c, 5120, 0, 0) > 0
+    assert B.mla_out_proj_folded_workspace_size(c, 5120, 0) > 0
+    app = [FAKE, None, 8, FAKE, FAKE, FAKE, 2, 4]          # cache .. max_blocks (bf16: no scale)
+    good = dict(h_kv=FAKE, w_dkv_t=FAKE, h_q=FAKE, w_q_t=FAKE, q_pos=FAKE, w_uk=FAKE, q_abs=FAKE, ws=FAKE)
+
+    def call(conf=c, d_model=5120, n=8, T=8, ws_bytes=ws, **kw):
+        a = dict(good, **kw)
+        return B.mla_append_absorb_hidden(conf, d_model, a["h_kv"], a["w_dkv_t"], *app, n, a["h_q"], a["w_q_t"],
+                                          a["q_pos"], a["w_uk"], a["q_abs"], T, a["ws"], ws_bytes, stream=0,
+                                          check=False)
+    assert call(h_kv=0) == B.MLA_ERR_INVALID_ARG
+    assert call(w_q_t=FAKE + 4) == B.MLA_ERR_INVALID_ARG
+    assert call(d_model=100) == B.MLA_ERR_INVALID_ARG
+    assert call(ws_bytes=ws - 512) == B.MLA_ERR_WORKSPACE
+    assert call(ws=FAKE + 16) == B.MLA_ERR_WORKSPACE
+    assert call(q_pos=0) == B.MLA_ERR_INVALID_ARG              # the absorption half's own check
+    assert call(n=0, T=0) == B.MLA_OK
+    # folded output projection
+    assert B.mla_fold_output_weights(c, 5120, FAKE, 0, FAKE, stream=0, check=False) == B.MLA_ERR_INVALID_ARG
+    wso = B.mla_out_proj_folded_workspace_size(c, 5120, 64)
+    assert wso > 0
+    assert B.mla_out_proj_folded(c, 5120, FAKE, FAKE, FAKE, 64, FAKE, wso - 512, stream=0,
+                                 check=False) == B.MLA_ERR_WORKSPACE
+    assert B.mla_out_proj_folded(c, 5120, FAKE + 4, FAKE, FAKE, 64, FAKE, wso, stream=0,
+                                 check=False) == B.MLA_ERR_INVALID_ARG
+    assert B.mla_out_proj_folded(c, 5120, 0, 0, 0, 0, 0, 0, stream=0, check=False) == B.MLA_OK
