@@ -51,6 +51,8 @@ METRIC = "MLA decode tokens/s + latent-cache GB/s & TFLOP/s (% peak) at B=64, 32
 FLUSH_BYTES = 512 << 20
 # the five workloads of the task's configuration list, in its order (the first is latency-bound)
 CONFIGS = ["tiny_f32", "dsv2_b16_l4k", "dsv2_b64_l1k_32k", "dsv2_b32_l8k_sq4", "dsv2_b128_l8k_fp8"]
+# measured alongside them: a chunked prefill step (512 new tokens per sequence)
+EXTRA_CONFIGS = ["dsv2_b4_l8k_sq512"]
 
 
 def algorithmic(w, kv_lens):
@@ -266,11 +268,67 @@ def run_workload(name, steps, warmup, settle_ms, flush, warm, cpu_budget, log):
     if cpu_budget > 0:
         log(f"[bench] cpu baseline (fp64 oracle, ~{cpu_budget:.0f} s) ...")
         got = {"o": st.out.float().cpu().numpy(), "o_lat": st.o_lat.cpu().numpy(), "lse": st.lse.cpu().numpy()}
-        heads = None if cpu_budget >= 10 else list(range(0, w.heads, max(1, w.heads // 16)))
+        # a head subset keeps one oracle sequence within the budget (many query rows per sequence
+        # cost the oracle Sq times a decode)
+        n_heads = w.heads if (cpu_budget >= 10 and w.sq <= 4) else (16 if w.sq <= 4 else 4)
+        heads = None if n_heads >= w.heads else list(range(0, w.heads, w.heads // n_heads))
         r["cpu_baseline"] = cpu_baseline(w, bt, got, budget_s=cpu_budget, heads=heads)
     del st
     torch.cuda.empty_cache()
     return r
+
+
+def kv_cache_comparison(name, steps, flush, log, kv_heads=(128, 8)):
+    """The same batch (lengths, pages) decoded from a per-head key/value cache: multi-head attention
+    (128 key/value heads of width 128, 65,536 B per token in bf16) and grouped-query attention
+    (8 key/value heads, 4,096 B per token), with mla_kv_decode_attn.  Cache contents are random
+    (timing only); the split + combine time per step against the bytes each token holds."""
+    import torch
+    from mla_latent_kv_40_amd import binding as B, workloads as wl
+
+    w = wl.get(name)
+    bt = wl.draw_batch(w)
+    kv = bt.kv_lens.astype(np.int64)
+    tokens = int(kv.sum())
+    cfg = B.Config(num_heads=w.heads, d_c=w.d_c, d_r=w.d_r, d_h=128, d_v=128, softmax_scale=128 ** -0.5)
+    table = torch.from_numpy(bt.block_table).to("cuda:0")
+    lens = torch.from_numpy(bt.kv_lens).to("cuda:0")
+    q = torch.randn((w.batch, w.heads, 128), dtype=torch.bfloat16, device="cuda:0")
+    o = torch.empty((w.batch, w.heads, 128), dtype=torch.float32, device="cuda:0")
+    lse = torch.empty((w.batch, w.heads), dtype=torch.float32, device="cuda:0")
+    out = {}
+    for h_kv in kv_heads:
+        per_tok = 2 * h_kv * 128 * 2
+        log(f"[bench] per-head key/value cache, {h_kv} key/value heads: {tokens * per_tok / 1e9:.1f} GB")
+        k = torch.randn((bt.num_blocks, h_kv, 64, 128), dtype=torch.bfloat16, device="cuda:0")
+        v = torch.randn((bt.num_blocks, h_kv, 64, 128), dtype=torch.bfloat16, device="cuda:0")
+        ws = B.mla_kv_decode_workspace_size(cfg, h_kv, w.batch, bt.max_blocks)
+        work = torch.empty(ws, dtype=torch.uint8, device="cuda:0")
+        stream = torch.cuda.current_stream()
+
+        def run():
+            B.mla_kv_decode_attn(cfg, h_kv, q, k, v, bt.num_blocks, table, bt.max_blocks, lens, w.batch, work, ws,
+                                 o, lse)
+        for i in range(3):
+            flush.fill_(i & 255)
+            run()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        for i in range(steps):
+            flush.fill_(i & 255)
+            evs[i][0].record(stream)
+            run()
+            evs[i][1].record(stream)
+        torch.cuda.synchronize()
+        ms = np.array([a.elapsed_time(b) for a, b in evs])
+        gbs = tokens * per_tok / (ms.mean() * 1e-3) / 1e9
+        out[f"{'mha' if h_kv == w.heads else 'gqa'}_{h_kv}_kv_heads"] = {
+            "bytes_per_token": per_tok, "cache_GB": round(tokens * per_tok / 1e9, 2),
+            "ms_mean": round(float(ms.mean()), 4), "ms_median": round(float(np.median(ms)), 4),
+            "GBps": round(gbs, 1), "frac_of_8TBps": round(gbs / PEAK_HBM_GBS, 4),
+            "tokens_per_s": round(w.batch / (ms.mean() * 1e-3), 1)}
+        del k, v, work
+        torch.cuda.empty_cache()
+    return out
 
 
 def main() -> int:
@@ -314,7 +372,7 @@ def main() -> int:
                           0.0 if a.no_cpu_baseline else 20.0, log)
     configs = {}
     if not a.no_configs:
-        for name in CONFIGS:
+        for name in CONFIGS + EXTRA_CONFIGS:
             if name == a.workload:
                 configs[name] = {k: main_r[k] for k in ("tokens_per_s", "ms_per_step", "k1_k2_ms", "roofline",
                                                         "flop_per_byte", "sclk_mhz_under_load")}
@@ -327,6 +385,12 @@ def main() -> int:
             if "cpu_baseline" in r:
                 configs[name]["max_err_over_tol"] = r["cpu_baseline"]["max_err_over_tol"]
                 configs[name]["oracle_sample"] = r["cpu_baseline"]["sample"]
+
+    kv_cmp = None
+    if not a.no_configs and a.workload == "dsv2_b64_l1k_32k":
+        kv_cmp = kv_cache_comparison(a.workload, 10, flush, log)
+        kv_cmp["mla_latent"] = {"bytes_per_token": 1152, "ms_mean_k1_k2": main_r["k1_k2_ms"]["mean"],
+                                "tokens_per_s_k1_k2": round(main_r["batch"] / (main_r["k1_k2_ms"]["mean"] * 1e-3), 1)}
 
     roof = dict(main_r["roofline"])
     roof["traffic"] = measured_traffic(main_r["workload"])
@@ -352,6 +416,8 @@ def main() -> int:
         line["warm_no_flush"] = main_r["warm_no_flush"]
     if configs:
         line["configs"] = configs
+    if kv_cmp:
+        line["kv_cache_comparison"] = kv_cmp
     if "cpu_baseline" in main_r:
         line["cpu_baseline"] = main_r["cpu_baseline"]
     print(json.dumps(line), flush=True)

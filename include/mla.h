@@ -271,6 +271,29 @@ mla_status_t mla_out_proj_folded(const mla_config_t* cfg, int32_t d_model, const
                                  void* out, int32_t T, void* workspace, size_t ws_bytes, void* stream);
 
 /*
+ * Decode over a standard per-head key/value cache, for comparison: the cache MLA replaces
+ * (zenaique "What MLA caches versus what MHA and GQA cache": every head keeps its own key and
+ * value per token; the podcast's grouped-query sizing shares them among groups of query heads).
+ * Same paging, lengths and split-K flash decoding as mla_decode_attn, one query per sequence.
+ *
+ * mla_kv_decode_attn -- for sequence b and query head i (of H = cfg->num_heads), with key/value
+ *   head j = i / (H / num_kv_heads):  o[b,i] = sum_t softmax_t(softmax_scale * q[b,i] . k[t,j]) v[t,j]
+ *   over t < kv_len[b]; lse[b,i] = log sum_t exp(softmax_scale * q . k).
+ *   num_kv_heads = H is multi-head attention.  Head width d = cfg->d_h = cfg->d_v = 128, bf16
+ *   cache and activations, H / num_kv_heads in {1, 2, 4, 8, 16}; other fields of cfg are unused.
+ *   q       [B, H, d] bf16 (positions already encoded)
+ *   k_cache, v_cache  [num_blocks, num_kv_heads, 64, d] bf16 (a head's 64-token page contiguous)
+ *   block_table [B, max_blocks], kv_lens [B] int32 (device)
+ *   o [B, H, d] fp32, lse [B, H] fp32;  workspace >= mla_kv_decode_workspace_size(...) bytes,
+ *   256-byte aligned, no initialisation needed.  Sequences with kv_len <= 0 give o = 0, lse = -inf.
+ */
+size_t mla_kv_decode_workspace_size(const mla_config_t* cfg, int32_t num_kv_heads, int32_t B, int32_t max_blocks);
+mla_status_t mla_kv_decode_attn(const mla_config_t* cfg, int32_t num_kv_heads, const void* q, const void* k_cache,
+                                const void* v_cache, int32_t num_blocks, const int32_t* block_table,
+                                int32_t max_blocks, const int32_t* kv_lens, int32_t B, void* workspace,
+                                size_t ws_bytes, float* o, float* lse, void* stream);
+
+/*
  * mla_out_proj -- apply W_UV once per query on the output side:
  * out[t,i] = o_lat[t,i] W_UV,i, W_UV,i = columns i*d_v .. i*d_v+d_v-1 of w_uv
  * (katajob "solid answer": the value up-projection folds into the output projection).
@@ -283,7 +306,7 @@ mla_status_t mla_out_proj(const mla_config_t* cfg, const float* o_lat, const voi
 /* Human-readable name of a status code (static storage). */
 const char* mla_status_string(mla_status_t status);
 
-/* ABI version of this header: 5. */
+/* ABI version of this header: 6. */
 int32_t mla_abi_version(void);
 
 #ifdef __cplusplus

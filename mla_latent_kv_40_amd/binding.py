@@ -13,7 +13,7 @@ from typing import Optional
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmla.so")
 
-ABI_VERSION = 5   # what mla_abi_version() returns for the argument lists below
+ABI_VERSION = 6   # what mla_abi_version() returns for the argument lists below
 NOALLOC_SCRATCH_BYTES = 64 << 20   # MLA_NOALLOC_SCRATCH_BYTES
 
 MLA_OK, MLA_ERR_INVALID_ARG, MLA_ERR_UNSUPPORTED, MLA_ERR_WORKSPACE, MLA_ERR_HIP = range(5)
@@ -23,7 +23,8 @@ DTYPES = {"f32": MLA_F32, "bf16": MLA_BF16, "fp8": MLA_FP8_E4M3}
 EXPORTS = ("mla_cache_append", "mla_absorb_q", "mla_append_absorb", "mla_decode_workspace_size", "mla_decode_attn",
            "mla_decode_split", "mla_decode_combine", "mla_decode_attn_noalloc", "mla_out_proj", "mla_status_string",
            "mla_abi_version", "mla_hidden_workspace_size", "mla_append_absorb_hidden", "mla_fold_output_weights",
-           "mla_out_proj_folded_workspace_size", "mla_out_proj_folded")
+           "mla_out_proj_folded_workspace_size", "mla_out_proj_folded", "mla_kv_decode_workspace_size",
+           "mla_kv_decode_attn")
 
 
 class MlaConfig(ctypes.Structure):
@@ -71,12 +72,16 @@ def lib() -> ctypes.CDLL:
         L.mla_out_proj_folded_workspace_size.argtypes = [cfgp, i32, i32]
         L.mla_out_proj_folded_workspace_size.restype = ctypes.c_size_t
         L.mla_out_proj_folded.argtypes = [cfgp, i32, f32p, vp, vp, i32, vp, ctypes.c_size_t, vp]
+        L.mla_kv_decode_workspace_size.argtypes = [cfgp, i32, i32, i32]
+        L.mla_kv_decode_workspace_size.restype = ctypes.c_size_t
+        L.mla_kv_decode_attn.argtypes = [cfgp, i32, vp, vp, vp, i32, vp, i32, vp, i32, vp, ctypes.c_size_t, f32p,
+                                         f32p, vp]
         L.mla_status_string.argtypes = [ctypes.c_int]
         L.mla_status_string.restype = ctypes.c_char_p
         L.mla_abi_version.restype = ctypes.c_int32
         for name in ("mla_cache_append", "mla_absorb_q", "mla_append_absorb", "mla_decode_attn", "mla_decode_split",
                      "mla_decode_combine", "mla_decode_attn_noalloc", "mla_out_proj", "mla_append_absorb_hidden",
-                     "mla_fold_output_weights", "mla_out_proj_folded"):
+                     "mla_fold_output_weights", "mla_out_proj_folded", "mla_kv_decode_attn"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -234,6 +239,20 @@ def mla_out_proj_folded(cfg: Config, d_model, o_lat, w_fold_t, out, T, workspace
                                    _ptr(workspace), ws_bytes, _stream(stream))
     if check:
         _check("mla_out_proj_folded", st)
+    return st
+
+
+def mla_kv_decode_workspace_size(cfg: Config, num_kv_heads: int, B: int, max_blocks: int) -> int:
+    return int(lib().mla_kv_decode_workspace_size(ctypes.byref(cfg.c()), num_kv_heads, B, max_blocks))
+
+
+def mla_kv_decode_attn(cfg: Config, num_kv_heads, q, k_cache, v_cache, num_blocks, block_table, max_blocks, kv_lens,
+                       B, workspace, ws_bytes, o, lse, stream=None, check=True) -> int:
+    st = lib().mla_kv_decode_attn(ctypes.byref(cfg.c()), num_kv_heads, _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                  num_blocks, _ptr(block_table), max_blocks, _ptr(kv_lens), B, _ptr(workspace),
+                                  ws_bytes, _ptr(o), _ptr(lse), _stream(stream))
+    if check:
+        _check("mla_kv_decode_attn", st)
     return st
 
 

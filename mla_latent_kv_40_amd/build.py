@@ -12,7 +12,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
-SOURCES = ["libmla.cpp", "append.hip", "absorb.hip", "decode.hip", "project.hip"]
+SOURCES = ["libmla.cpp", "append.hip", "absorb.hip", "decode.hip", "project.hip", "gqa.hip"]
 LIB = os.path.join(HERE, "libmla.so")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -31,6 +31,7 @@ EXTRA = {
     "absorb.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
     "decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
     "project.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+    "gqa.hip": [],
     "libmla.cpp": [],
 }
 

@@ -32,6 +32,11 @@ hipError_t launch_out_proj_folded(const mla_config_t&, int, int, const float*, c
                                   hipStream_t);
 size_t out_proj_folded_workspace(const mla_config_t&, int, int, int);
 hipError_t launch_fold_wo(const mla_config_t&, int, const void*, const void*, void*, hipStream_t);
+size_t gqa_workspace_bytes(int B, int H_q, int H_kv, int max_blocks);
+bool gqa_supported(int H_q, int H_kv, int d);
+hipError_t launch_gqa_decode(int H_q, int H_kv, float softmax_scale, const void* q, const void* k, const void* v,
+                             int num_blocks, const int32_t* block_table, int max_blocks, const int32_t* kv_lens,
+                             int B, void* workspace, float* o, float* lse, hipStream_t stream);
 }  // namespace mla
 
 namespace {
@@ -80,7 +85,7 @@ mla_status_t from_hip(hipError_t e) { return e == hipSuccess ? MLA_OK : MLA_ERR_
 
 extern "C" {
 
-int32_t mla_abi_version(void) { return 5; }
+int32_t mla_abi_version(void) { return 6; }
 
 const char* mla_status_string(mla_status_t s) {
   switch (s) {
@@ -311,6 +316,41 @@ mla_status_t mla_out_proj_folded(const mla_config_t* cfg, int32_t d_model, const
     return MLA_ERR_WORKSPACE;
   return from_hip(mla::launch_out_proj_folded(*cfg, cus, d_model, o_lat, w_fold_t, out, T, workspace,
                                               static_cast<hipStream_t>(stream)));
+}
+
+// ---------------------------------------------------------------- per-head key/value cache (comparison)
+
+static mla_status_t check_kv_cfg(const mla_config_t* cfg, int32_t num_kv_heads) {
+  if (!cfg) return MLA_ERR_INVALID_ARG;
+  if (cfg->num_heads <= 0 || num_kv_heads <= 0 || cfg->d_h <= 0 || !(cfg->softmax_scale > 0.0f)) return MLA_ERR_INVALID_ARG;
+  if (cfg->block_size != 64 || cfg->num_heads % num_kv_heads != 0) return MLA_ERR_INVALID_ARG;
+  if (cfg->cache_dtype != MLA_BF16 || cfg->act_dtype != MLA_BF16 || cfg->d_v != cfg->d_h) return MLA_ERR_UNSUPPORTED;
+  if (!mla::gqa_supported(cfg->num_heads, num_kv_heads, cfg->d_h)) return MLA_ERR_UNSUPPORTED;
+  return MLA_OK;
+}
+
+size_t mla_kv_decode_workspace_size(const mla_config_t* cfg, int32_t num_kv_heads, int32_t B, int32_t max_blocks) {
+  if (check_kv_cfg(cfg, num_kv_heads) != MLA_OK || B <= 0 || max_blocks <= 0) return 0;
+  return mla::gqa_workspace_bytes(B, cfg->num_heads, num_kv_heads, max_blocks);
+}
+
+mla_status_t mla_kv_decode_attn(const mla_config_t* cfg, int32_t num_kv_heads, const void* q, const void* k_cache,
+                                const void* v_cache, int32_t num_blocks, const int32_t* block_table,
+                                int32_t max_blocks, const int32_t* kv_lens, int32_t B, void* workspace,
+                                size_t ws_bytes, float* o, float* lse, void* stream) {
+  mla_status_t st = check_kv_cfg(cfg, num_kv_heads);
+  if (st != MLA_OK) return st;
+  if (B < 0 || num_blocks <= 0 || max_blocks <= 0) return MLA_ERR_INVALID_ARG;
+  if (B == 0) return MLA_OK;
+  if (!q || !k_cache || !v_cache || !block_table || !kv_lens || !o || !lse) return MLA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(block_table) || !aligned16(kv_lens) ||
+      !aligned16(o) || !aligned16(lse))
+    return MLA_ERR_INVALID_ARG;
+  const size_t need = mla::gqa_workspace_bytes(B, cfg->num_heads, num_kv_heads, max_blocks);
+  if (!workspace || ws_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 255u)) return MLA_ERR_WORKSPACE;
+  return from_hip(mla::launch_gqa_decode(cfg->num_heads, num_kv_heads, cfg->softmax_scale, q, k_cache, v_cache,
+                                         num_blocks, block_table, max_blocks, kv_lens, B, workspace, o, lse,
+                                         static_cast<hipStream_t>(stream)));
 }
 
 mla_status_t mla_out_proj(const mla_config_t* cfg, const float* o_lat, const void* w_uv, void* out, int32_t T,

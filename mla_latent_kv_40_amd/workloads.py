@@ -87,6 +87,10 @@ WORKLOADS: Dict[str, Workload] = {
     "dsv2_b128_l8k_fp8": _ds("dsv2_b128_l8k_fp8", 4, 128, 1, "fp8", 8191, 8191,
                              "DeepSeek-V2 shapes, fp8 e4m3 cache with per-token scale, B=128, "
                              "context 8192"),
+    # not one of the decode configurations: a chunk of prompt tokens extended in one step
+    "dsv2_b4_l8k_sq512": _ds("dsv2_b4_l8k_sq512", 5, 4, 512, "bf16", 8192, 8192,
+                             "DeepSeek-V2 shapes, bf16, chunked prefill: B=4, context 8192 + a chunk of "
+                             "512 causal new tokens"),
 }
 
 

@@ -258,6 +258,32 @@ def fold_output_weights(W_UV, W_O, heads):
     return np.stack([W_UV[:, i * d_v:(i + 1) * d_v] @ W_O[i * d_v:(i + 1) * d_v] for i in range(heads)])
 
 
+def attention(q, K, V, softmax_scale):
+    """Textbook softmax attention of one query row per head over a per-head key/value cache, the
+    cache MLA replaces (zenaique "What MLA caches versus what MHA and GQA cache": every head keeps
+    its own key and value per token; grouped-query attention shares one key/value head among a
+    group of query heads).
+
+      q [Hq, d]   K [L, Hkv, d]   V [L, Hkv, dv]   query head i reads key/value head i // (Hq/Hkv)
+    Returns o [Hq, dv] and lse [Hq] (natural log); L = 0 gives o = 0 and lse = -inf.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    K = np.asarray(K, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    Hq = q.shape[0]
+    L, Hkv = K.shape[0], K.shape[1]
+    group = Hq // Hkv
+    kv = np.arange(Hq) // group
+    if L == 0:
+        return {"o": np.zeros((Hq, V.shape[-1])), "lse": np.full(Hq, -np.inf)}
+    s = np.einsum("id,tid->it", q, K[:, kv]) * softmax_scale
+    m = s.max(axis=1, keepdims=True)
+    e = np.exp(s - m)
+    den = e.sum(axis=1, keepdims=True)
+    o = np.einsum("it,tid->id", e / den, V[:, kv])
+    return {"o": o, "lse": (m + np.log(den))[:, 0]}
+
+
 # --------------------------------------------------------------- fp8 e4m3 storage
 
 def e4m3_round(x: np.ndarray) -> np.ndarray:

@@ -193,3 +193,21 @@ def test_full_size_needles(name):
     assert moved > 10 * tol
     for k in ("o", "o_lat", "lse"):
         check(f"needles b{b} {k}", got[k][b:b + 1][:, heads], ref[k])
+
+
+@pytest.mark.parametrize("lengths,sq", [([1064, 364], 64), ([256], 256), ([700, 333], 333)])
+def test_chunked_extend_and_prefill(lengths, sq):
+    """Many query rows per sequence: a chunk of Sq new tokens (positions kv_len - Sq ..) appended
+    and attended causally in one step, up to a whole prompt (kv_len = Sq: prefill).  The range
+    count falls to CUs / Sq, so each query row's workgroup streams its sequence's pages."""
+    log(f"case chunked extend / prefill: lengths {lengths}, Sq={sq}")
+    w, bt, seqs = dsv2(len(lengths), lengths, sq=sq, seed=97)
+    st = run_state(w, bt, seqs)
+    got = host(st)
+    assert np.all(np.isfinite(got["o"]))
+    heads = list(range(3, 128, 25))
+    for b in range(w.batch):
+        ref = oracle_for(w, bt, seqs, b, heads=heads)
+        rows = slice(b * sq, (b + 1) * sq)
+        for k in ("o", "o_lat", "lse"):
+            check(f"b{b} Sq={sq} {k}", got[k][rows][:, heads], ref[k])

@@ -221,3 +221,20 @@ def test_hidden_and_folded_calls_validate_first(L):
     assert B.mla_out_proj_folded(c, 5120, FAKE + 4, FAKE, FAKE, 64, FAKE, wso, stream=0,
                                  check=False) == B.MLA_ERR_INVALID_ARG
     assert B.mla_out_proj_folded(c, 5120, 0, 0, 0, 0, 0, 0, stream=0, check=False) == B.MLA_OK
+
+
+def test_kv_cache_decode_validation(L):
+    c = B.Config(num_heads=128, d_c=512, d_r=64, d_h=128, d_v=128, softmax_scale=128 ** -0.5)
+    assert B.mla_kv_decode_workspace_size(c, 8, 64, 512) > 0
+    assert B.mla_kv_decode_workspace_size(c, 3, 64, 512) == 0          # 128 heads do not group by 3
+    assert B.mla_kv_decode_workspace_size(c, 4, 64, 512) == 0          # groups of 32: unsupported
+    ws = B.mla_kv_decode_workspace_size(c, 8, 4, 16)
+    args = [c, 8, FAKE, FAKE, FAKE, 100, FAKE, 16, FAKE, 4]
+    assert B.mla_kv_decode_attn(*args, FAKE, ws - 256, FAKE, FAKE, stream=0, check=False) == B.MLA_ERR_WORKSPACE
+    assert B.mla_kv_decode_attn(c, 8, FAKE + 4, *args[3:], FAKE, ws, FAKE, FAKE, stream=0,
+                                check=False) == B.MLA_ERR_INVALID_ARG
+    assert B.mla_kv_decode_attn(c, 8, FAKE, FAKE, 0, *args[5:], FAKE, ws, FAKE, FAKE, stream=0,
+                                check=False) == B.MLA_ERR_INVALID_ARG
+    c8 = B.Config(num_heads=128, d_c=512, d_r=64, d_h=128, d_v=128, softmax_scale=0.1, cache_dtype="fp8")
+    assert B.mla_kv_decode_attn(c8, 8, *args[2:], FAKE, ws, FAKE, FAKE, stream=0,
+                                check=False) == B.MLA_ERR_UNSUPPORTED

@@ -220,6 +220,41 @@ def test_folded_output_projection_equals_the_unfolded_chain():
     assert rel_err(out_chain, brute) < 1e-12
 
 
+def test_mla_is_attention_over_reconstructed_per_head_keys_and_values():
+    """MLA's unabsorbed decode is multi-head attention whose per-head keys [c W_UK,i ; RoPE(k_R)]
+    and values c W_UV,i are rebuilt from the latent (zenaique: MHA caches them per head, MLA caches
+    the latent): the oracle's decode equals attention() over the rebuilt cache."""
+    case = _small_case(L=10, Sq=1, H=3, d_h=4, d_c=5, d_r=4, d_v=3, base=7.0)
+    ref = orc.decode(**case)
+    L, H = 10, 3
+    KC = orc.up_project(case["C"], case["W_UK"], H, 4)                       # [L, H, d_h]
+    kR = orc.rope(case["KRraw"], np.arange(L), case["rope_base"])            # [L, d_R]
+    K = np.concatenate([KC, np.repeat(kR[:, None, :], H, axis=1)], axis=2)  # [L, H, d_h + d_R]
+    V = orc.up_project(case["C"], case["W_UV"], H, 3)
+    q = np.concatenate([case["qC"][0], orc.rope(case["qR"][0], L - 1, case["rope_base"])], axis=1)
+    got = orc.attention(q, K, V, case["softmax_scale"])
+    assert rel_err(got["o"], ref["o"][0]) < 1e-12 and rel_err(got["lse"], ref["lse"][0]) < 1e-12
+
+
+def test_grouped_attention_bruteforce():
+    """Grouped-query attention with scalar loops: 4 query heads on 2 key/value heads."""
+    rng = np.random.default_rng(21)
+    q, K, V = rng.standard_normal((4, 3)), rng.standard_normal((5, 2, 3)), rng.standard_normal((5, 2, 2))
+    got = orc.attention(q, K, V, 0.7)
+    for i in range(4):
+        j = i // 2
+        sc = [0.7 * sum(q[i][d] * K[t][j][d] for d in range(3)) for t in range(5)]
+        m = max(sc)
+        z = sum(math.exp(x - m) for x in sc)
+        for c in range(2):
+            o = sum(math.exp(sc[t] - m) / z * V[t][j][c] for t in range(5))
+            assert abs(got["o"][i][c] - o) < 1e-12
+        assert abs(got["lse"][i] - (m + math.log(z))) < 1e-12
+    # a planted mistake (key/value head i % Hkv instead of i // group) fails it
+    bad = orc.attention(q[[0, 2, 1, 3]], K, V, 0.7)["o"][[0, 2, 1, 3]]
+    assert rel_err(bad, got["o"]) > 1e-3
+
+
 def test_lse_is_log_sum_exp_of_scores():
     case = _small_case(L=7)
     got = orc.decode(**case)
