@@ -301,7 +301,7 @@ def kv_cache_comparison(name, steps, flush, log, kv_heads=(128, 8)):
         per_tok = 2 * h_kv * 128 * 2
         log(f"[bench] per-head key/value cache, {h_kv} key/value heads: {tokens * per_tok / 1e9:.1f} GB")
         k = torch.randn((bt.num_blocks, h_kv, 64, 128), dtype=torch.bfloat16, device="cuda:0")
-        v = torch.randn((bt.num_blocks, h_kv, 64, 128), dtype=torch.bfloat16, device="cuda:0")
+        v = torch.randn((bt.num_blocks, h_kv, 128, 64), dtype=torch.bfloat16, device="cuda:0")
         ws = B.mla_kv_decode_workspace_size(cfg, h_kv, w.batch, bt.max_blocks)
         work = torch.empty(ws, dtype=torch.uint8, device="cuda:0")
         stream = torch.cuda.current_stream()

@@ -282,7 +282,9 @@ mla_status_t mla_out_proj_folded(const mla_config_t* cfg, int32_t d_model, const
  *   num_kv_heads = H is multi-head attention.  Head width d = cfg->d_h = cfg->d_v = 128, bf16
  *   cache and activations, H / num_kv_heads in {1, 2, 4, 8, 16}; other fields of cfg are unused.
  *   q       [B, H, d] bf16 (positions already encoded)
- *   k_cache, v_cache  [num_blocks, num_kv_heads, 64, d] bf16 (a head's 64-token page contiguous)
+ *   k_cache [num_blocks, num_kv_heads, 64, d] bf16 (a head's 64-token page contiguous, token-major)
+ *   v_cache [num_blocks, num_kv_heads, d, 64] bf16 (the same pages stored transposed, column-major:
+ *           the value product contracts over tokens and reads them contiguously)
  *   block_table [B, max_blocks], kv_lens [B] int32 (device)
  *   o [B, H, d] fp32, lse [B, H] fp32;  workspace >= mla_kv_decode_workspace_size(...) bytes,
  *   256-byte aligned, no initialisation needed.  Sequences with kv_len <= 0 give o = 0, lse = -inf.

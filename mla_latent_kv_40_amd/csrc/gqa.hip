@@ -6,16 +6,17 @@
 // thousand numbers per token and layer, against one latent) and the podcast's grouped-query
 // sizing (8 key/value heads of width 128).
 //
-//   cache      k, v [num_blocks, H_kv, 64, d] bf16 (one 64-token page per head is contiguous)
+//   cache      k [num_blocks, H_kv, 64, d], v [num_blocks, H_kv, d, 64] bf16 (one head's 64-token
+//              page contiguous; the value page stored transposed, column-major, so that the value
+//              product reads its operand with plain loads)
 //   query      q [B, H_q, d] bf16 (one query per sequence, already rotated)
 //   score      s[t] = softmax_scale * q . k[t];   o = sum_t softmax(s)[t] v[t],  lse
 //
 // Work split (flash decoding): a wave owns (sequence, key/value head, chunk of kChunkPages pages)
-// and all G = H_q / H_kv queries of that head, with lane = token for the scores and lane =
-// column pair for the values; its partial (O unnormalised, running max m and sum l per query)
-// goes to the workspace and a combine kernel merges the chunks of a sequence.  This is
-// bandwidth-bound: a page of one head is 32 KiB of keys and values and serves G queries; two or
-// more waves per SIMD keep several pages in flight.
+// and all G = H_q / H_kv queries of that head on the matrix cores; its partial (O unnormalised,
+// running max m and sum l per query) goes to the workspace and a combine kernel merges the chunks
+// of a sequence.  This is bandwidth-bound: a page of one head is 32 KiB of keys and values and
+// serves G queries; several waves per SIMD keep several pages in flight.
 #include "common.h"
 
 namespace mla {
@@ -58,18 +59,27 @@ __global__ void gqa_plan_kernel(GqaArgs a, int32_t* item_start) {
   item_start[a.B] = acc;
 }
 
-// G queries per work item (a slice of one key/value head's group); G * 2 value accumulators per
-// lane (columns 2 lane, 2 lane + 1).  Groups of 16 queries run as two slices of 8 (the second read
-// of a page comes from cache), which keeps the registers of a wave at two or more waves per SIMD.
+// One wave per work item: (sequence, key/value head, chunk of kChunkPages pages) and the group's
+// G <= 16 queries, on v_mfma_f32_16x16x32_bf16 (A 16x32: lane l holds row l%16 and K values
+// 8(l/16) .. +7; B 32x16: column l%16, the same K values; D 16x16: column l%16, rows 4(l/16) .. +3;
+// the order of K inside one instruction is free as long as A and B agree).  Columns past G are
+// padding (zero queries) and are not stored.  Per page (h = l/16):
+//   scores  S^T[t, q] = K[t, :] . Q^T[:, q] for four groups of 16 tokens x four K-steps of 32: A =
+//           the key rows (16 bytes straight from the page), B = the queries (registers); lane l
+//           holds query l%16 for tokens 16 tg + 4h + i;
+//   softmax per query over the page: the lane's 16 scores, then lanes l^16, l^32 (running max and
+//           sum, O rescaled when the max grows);
+//   values  O^T[c, q] += V^T[c, t] . P^T[t, q] for 8 tiles of 16 columns x two K-steps of 32
+//           tokens: the K-step j takes the tokens the lane's own probabilities belong to,
+//           32 j + 4h + i and 32 j + 16 + 4h + i, so P is the B operand as it stands (bf16), and A
+//           is read from the value page stored transposed ([c][t]: two 8-byte pieces per lane).
 template <int G>
 __global__ void __launch_bounds__(256) gqa_split_kernel(GqaArgs a) {
-  __shared__ float qs[4][G][kGqaD];   // this wave's queries, fp32 (read as broadcasts)
-  __shared__ float ps[4][G][64];      // this page's probabilities
+  typedef float f32x4v __attribute__((ext_vector_type(4)));
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int item = blockIdx.x * 4 + wave;
   if (item >= a.n_items || item >= a.item_start[a.B]) return;   // past this batch's items
-  // sequence of the item: binary search over item_start
-  int lo = 0, hi = a.B - 1;
+  int lo = 0, hi = a.B - 1;                                      // sequence of the item
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
     if (a.item_start[mid] <= item) lo = mid;
@@ -77,116 +87,107 @@ __global__ void __launch_bounds__(256) gqa_split_kernel(GqaArgs a) {
   }
   const int b = lo;
   const int rel = item - a.item_start[b];
-  const int hq = rel % (a.H_kv * a.QS), chunk = rel / (a.H_kv * a.QS);
-  const int hk = hq / a.QS, q0 = (hq % a.QS) * G;   // key/value head, first query of the slice
+  const int hk = rel % a.H_kv, chunk = rel / a.H_kv;
   int L = a.kv_lens[b];
   L = L < 0 ? 0 : (L > 64 * a.max_blocks ? 64 * a.max_blocks : L);
   const int p0 = chunk * kChunkPages;
   const int pages = (L + 63) / 64;
   const int p1 = p0 + kChunkPages < pages ? p0 + kChunkPages : pages;
-  // queries of this head group
-  for (int e = lane; e < G * kGqaD; e += 64) {
-    const int g = e / kGqaD, d = e % kGqaD;
-    qs[wave][g][d] = bf16_bits_to_f32(a.q[((size_t)b * a.H_q + hk * G * a.QS + q0 + g) * kGqaD + d]);
-  }
-  // running max and sum per query are wave-uniform (scalar registers); the value accumulators
-  // hold columns 2 lane, 2 lane + 1
-  float m[G], l[G], acc0[G], acc1[G];
+  const int col = lane & 15, h = lane >> 4;
+  // B operand of the scores: query `col` of the group (zero past G), dims 32k + 8h .. +7
+  bf16x8 qf[4];
+  {
+    const int qi = col < G ? col : 0;
+    const uint16_t* qp = a.q + ((size_t)b * a.H_q + hk * G + qi) * kGqaD + 8 * h;
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
-    m[g] = -INFINITY;
-    l[g] = 0.f;
-    acc0[g] = 0.f;
-    acc1[g] = 0.f;
+    for (int k = 0; k < 4; ++k) {
+      qf[k] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qp + 32 * k));
+      if (col >= G) qf[k] = bf16x8{};
+    }
   }
-  auto page_id = [&](int p) -> int {
-    const int pg = a.block_table[(size_t)b * a.max_blocks + p];
-    return (pg >= 0 && pg < a.num_blocks) ? pg : -1;
-  };
+  float m = -INFINITY, l = 0.f;   // running max (exp2 domain) and sum of query `col`
+  f32x4v o[8];
+#pragma unroll
+  for (int ct = 0; ct < 8; ++ct) o[ct] = f32x4v{0.f, 0.f, 0.f, 0.f};
   for (int p = p0; p < p1; ++p) {
-    const int pid = page_id(p);
-    const size_t off = ((size_t)(pid < 0 ? 0 : pid) * a.H_kv + hk) * 64 * kGqaD;
-    const uint16_t* kp = a.k + off + lane * kGqaD;         // this lane's key row (token = lane)
-    const uint16_t* vp = a.v + off + 2 * lane;             // columns 2 lane, 2 lane + 1 of each token
-    // the key row and the first 16 tokens' values are requested before anything waits
-    u32x4 kc[16];
+    const int pg = a.block_table[(size_t)b * a.max_blocks + p];
+    const bool ok = pg >= 0 && pg < a.num_blocks;
+    const size_t off = ((size_t)(ok ? pg : 0) * a.H_kv + hk) * 64 * kGqaD;
+    // key rows 16 tg + col, dims 32k + 8h: all 16 pieces first, then the value pieces
+    u32x4 kf[4][4];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) kc[i] = *reinterpret_cast<const u32x4*>(kp + 8 * i);
-    uint32_t vv[16];
+    for (int tg = 0; tg < 4; ++tg)
 #pragma unroll
-    for (int t = 0; t < 16; ++t) vv[t] = *reinterpret_cast<const uint32_t*>(vp + t * kGqaD);
-    const bool live = pid >= 0 && lane < L - 64 * p;
-    float s[G];
+      for (int k = 0; k < 4; ++k)
+        kf[tg][k] = *reinterpret_cast<const u32x4*>(a.k + off + (size_t)(16 * tg + col) * kGqaD + 32 * k + 8 * h);
+    // value page transposed: row c = 16 ct + col, tokens 32 j + 4h .. +3 and 32 j + 16 + 4h .. +3
+    u32x2 vf[8][2][2];
 #pragma unroll
-    for (int g = 0; g < G; ++g) s[g] = 0.f;
-#pragma unroll 4
-    for (int i = 0; i < 16; ++i) {
-      float kv[8];
+    for (int ct = 0; ct < 8; ++ct)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        kv[2 * e] = bf16_bits_to_f32(kc[i][e] & 0xFFFFu);
-        kv[2 * e + 1] = bf16_bits_to_f32(kc[i][e] >> 16);
-      }
+      for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int g = 0; g < G; ++g) {
-        const f32x4 q0 = *reinterpret_cast<const f32x4*>(&qs[wave][g][8 * i]);
-        const f32x4 q1 = *reinterpret_cast<const f32x4*>(&qs[wave][g][8 * i + 4]);
-        float d = s[g];
-        d = __builtin_fmaf(q0[0], kv[0], d);
-        d = __builtin_fmaf(q0[1], kv[1], d);
-        d = __builtin_fmaf(q0[2], kv[2], d);
-        d = __builtin_fmaf(q0[3], kv[3], d);
-        d = __builtin_fmaf(q1[0], kv[4], d);
-        d = __builtin_fmaf(q1[1], kv[5], d);
-        d = __builtin_fmaf(q1[2], kv[6], d);
-        d = __builtin_fmaf(q1[3], kv[7], d);
-        s[g] = d;
-      }
-    }
+        for (int u = 0; u < 2; ++u)
+          vf[ct][j][u] = *reinterpret_cast<const u32x2*>(a.v + off + (size_t)(16 * ct + col) * 64 + 32 * j + 16 * u +
+                                                         4 * h);
+    f32x4v sc[4];
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const float sg = live ? s[g] * a.scale_log2 : -INFINITY;
-      const float m_new = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(fmaxf(m[g], wave_max(sg)))));
-      const float pg = live ? __builtin_amdgcn_exp2f(sg - m_new) : 0.f;
-      const float alpha = m[g] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m[g] - m_new);
-      l[g] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(l[g] * alpha + wave_sum(pg))));
-      acc0[g] *= alpha;
-      acc1[g] *= alpha;
-      m[g] = m_new;
-      ps[wave][g][lane] = pg;
-    }
-    // values, 16 tokens at a time (the next group's values in flight)
-#pragma unroll 1
     for (int tg = 0; tg < 4; ++tg) {
-      uint32_t vn[16];
-      if (tg < 3) {
+      sc[tg] = f32x4v{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int t = 0; t < 16; ++t) vn[t] = *reinterpret_cast<const uint32_t*>(vp + (16 * (tg + 1) + t) * kGqaD);
+      for (int k = 0; k < 4; ++k)
+        sc[tg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kf[tg][k]), qf[k], sc[tg], 0, 0, 0);
+    }
+    // softmax of query `col` over this page's tokens 16 tg + 4h + i (masked past the length)
+    const int nv = ok ? L - 64 * p : 0;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int tg = 0; tg < 4; ++tg)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = 16 * tg + 4 * h + i;
+        sc[tg][i] = t < nv ? sc[tg][i] * a.scale_log2 : -INFINITY;
+        mx = fmaxf(mx, sc[tg][i]);
       }
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float m_new = fmaxf(m, mx);
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - m_use);
+    float ps = 0.f;
+    bf16x8 pf[2];
 #pragma unroll
-      for (int t4 = 0; t4 < 4; ++t4) {
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int g = 0; g < G; ++g) {
-          const f32x4 w = *reinterpret_cast<const f32x4*>(&ps[wave][g][16 * tg + 4 * t4]);
+      for (int u = 0; u < 2; ++u)
 #pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const uint32_t x = vv[4 * t4 + u];
-            acc0[g] = __builtin_fmaf(w[u], bf16_bits_to_f32(x & 0xFFFFu), acc0[g]);
-            acc1[g] = __builtin_fmaf(w[u], bf16_bits_to_f32(x >> 16), acc1[g]);
-          }
+        for (int i = 0; i < 4; ++i) {
+          const __bf16 pv = (__bf16)__builtin_amdgcn_exp2f(sc[2 * j + u][i] - m_use);
+          pf[j][4 * u + i] = pv;
+          ps += (float)pv;   // the sum of the rounded values that enter the product
         }
-      }
-      if (tg < 3) {
+    ps += __shfl_xor(ps, 16, 64);
+    ps += __shfl_xor(ps, 32, 64);
+    l = l * alpha + ps;
+    m = m_new;
 #pragma unroll
-        for (int t = 0; t < 16; ++t) vv[t] = vn[t];
+    for (int ct = 0; ct < 8; ++ct) {
+      o[ct] *= alpha;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const bf16x8 va = __builtin_bit_cast(bf16x8, u32x4{vf[ct][j][0][0], vf[ct][j][0][1], vf[ct][j][1][0],
+                                                          vf[ct][j][1][1]});
+        o[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pf[j], o[ct], 0, 0, 0);
       }
     }
   }
-  // partial of this item (an empty chunk leaves m = -inf, l = 0)
+  // partial of this item (an empty chunk leaves m = -inf, l = 0): O^T rows 16 ct + 4h + i of column col
+  if (col < G) {
+    float* po = a.part_o + ((size_t)item * G + col) * kGqaD;
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
-    *reinterpret_cast<float2*>(a.part_o + ((size_t)item * G + g) * kGqaD + 2 * lane) = float2{acc0[g], acc1[g]};
-    if (lane == 0) *reinterpret_cast<float2*>(a.part_ml + ((size_t)item * G + g) * 2) = float2{m[g], l[g]};
+    for (int ct = 0; ct < 8; ++ct)
+      *reinterpret_cast<f32x4v*>(po + 16 * ct + 4 * h) = o[ct];
+    if (h == 0) *reinterpret_cast<float2*>(a.part_ml + ((size_t)item * G + col) * 2) = float2{m, l};
   }
 }
 
@@ -226,9 +227,8 @@ __global__ void __launch_bounds__(256) gqa_combine_kernel(GqaArgs a) {
 
 // queries per work item and slices per key/value head
 static void gqa_slices(int H_q, int H_kv, int* G, int* QS) {
-  const int grp = H_q / H_kv;
-  *G = grp > 8 ? 8 : grp;
-  *QS = grp / *G;
+  *G = H_q / H_kv;   // one work item takes the whole group (at most 16 queries: one MFMA tile)
+  *QS = 1;
 }
 
 // Workspace: item starts, then partials for the most items the batch can have.
@@ -287,6 +287,7 @@ hipError_t launch_gqa_decode(int H_q, int H_kv, float softmax_scale, const void*
     MLA_GQA_CASE(2)
     MLA_GQA_CASE(4)
     MLA_GQA_CASE(8)
+    MLA_GQA_CASE(16)
     default:
       return hipErrorInvalidValue;
   }

@@ -39,7 +39,7 @@ def test_kv_cache_decode(h_kv):
         table[b, :nblk[b]] = perm[off:off + nblk[b]]
         off += int(nblk[b])
     k_pages = np.zeros((pool, h_kv, 64, d), np.float32)
-    v_pages = np.zeros((pool, h_kv, 64, d), np.float32)
+    v_pages = np.zeros((pool, h_kv, d, 64), np.float32)   # value pages stored transposed
     Ks, Vs = [], []
     for b, L in enumerate(kv):
         K = wl.round_bf16(rng.standard_normal((L, h_kv, d), dtype=np.float32))
@@ -47,7 +47,7 @@ def test_kv_cache_decode(h_kv):
         t = np.arange(L)
         pg = table[b, t // 64]
         k_pages[pg, :, t % 64] = K
-        v_pages[pg, :, t % 64] = V
+        v_pages[pg, :, :, t % 64] = V
         Ks.append(K)
         Vs.append(V)
     q = wl.round_bf16(rng.standard_normal((len(kv), H, d), dtype=np.float32))
