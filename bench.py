@@ -331,6 +331,65 @@ def kv_cache_comparison(name, steps, flush, log, kv_heads=(128, 8)):
     return out
 
 
+def model_width_measurement(name, steps, flush, log, d_model=5120):
+    """The projections on either side of the decode for the default batch's step (T = B query rows,
+    B new tokens), from d_model = 5120 (DeepSeek-V2's hidden size): mla_append_absorb_hidden (reads
+    [W_down | W_KR] and [W_Q | W_QR], 257 MB) and mla_out_proj_folded (reads W_O' = H*d_c*d_model
+    values, 671 MB).  Weights are random (timing only); bandwidth = weight bytes / time."""
+    import torch
+    from mla_latent_kv_40_amd import binding as B, harness, workloads as wl
+
+    w = wl.get(name)
+    bt = wl.draw_batch(w)
+    cfg = harness.config_for(w)
+    T = w.batch * w.sq
+    H = w.heads
+    dev = dict(dtype=torch.bfloat16, device="cuda:0")
+    cache = torch.empty((bt.num_blocks, 64, w.row), **dev)
+    table = torch.from_numpy(bt.block_table).to("cuda:0")
+    h = torch.randn((T, d_model), **dev)
+    w_dkv = torch.randn((w.d_c + w.d_r, d_model), **dev) * d_model ** -0.5
+    w_q = torch.randn((H * (w.d_h + w.d_r), d_model), **dev) * d_model ** -0.5
+    w_uk = torch.randn((w.d_c, H * w.d_h), **dev) * w.d_c ** -0.5
+    kv = bt.kv_lens.astype(np.int64)
+    pos = torch.from_numpy((kv - 1).astype(np.int32)).to("cuda:0")
+    seq = torch.arange(T, dtype=torch.int32, device="cuda:0")
+    q_abs = torch.empty((T, H, w.row), **dev)
+    ws = B.mla_hidden_workspace_size(cfg, d_model, T, T)
+    work = torch.empty(ws, dtype=torch.uint8, device="cuda:0")
+    o_lat = torch.randn((T, H, w.d_c), dtype=torch.float32, device="cuda:0") * 0.05
+    w_fold = torch.randn((d_model, H * w.d_c), **dev) * (H * w.d_c) ** -0.5
+    out = torch.empty((T, d_model), **dev)
+    wso = max(B.mla_out_proj_folded_workspace_size(cfg, d_model, T), 256)
+    work_o = torch.empty(wso, dtype=torch.uint8, device="cuda:0")
+    stream = torch.cuda.current_stream()
+    calls = {
+        "append_absorb_hidden": (lambda: B.mla_append_absorb_hidden(
+            cfg, d_model, h, w_dkv, cache, None, bt.num_blocks, pos, seq, table, w.batch, bt.max_blocks, T, h, w_q,
+            pos, w_uk, q_abs, T, work, ws), (w_dkv.numel() + w_q.numel() + w_uk.numel()) * 2),
+        "out_proj_folded": (lambda: B.mla_out_proj_folded(cfg, d_model, o_lat, w_fold, out, T, work_o, wso),
+                            w_fold.numel() * 2),
+    }
+    res = {"d_model": d_model, "rows": T}
+    for key, (fn, wbytes) in calls.items():
+        for i in range(3):
+            flush.fill_(i & 255)
+            fn()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        for i in range(steps):
+            flush.fill_(i & 255)
+            evs[i][0].record(stream)
+            fn()
+            evs[i][1].record(stream)
+        torch.cuda.synchronize()
+        ms = np.array([a.elapsed_time(b) for a, b in evs])
+        gbs = wbytes / (ms.mean() * 1e-3) / 1e9
+        res[key] = {"ms_mean": round(float(ms.mean()), 4), "ms_median": round(float(np.median(ms)), 4),
+                    "weight_bytes": int(wbytes), "GBps": round(gbs, 1), "frac_of_8TBps": round(gbs / PEAK_HBM_GBS, 4)}
+        log(f"[bench] {key}: {ms.mean():.3f} ms, {gbs:.0f} GB/s of weights")
+    return res
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -392,6 +451,10 @@ def main() -> int:
         kv_cmp["mla_latent"] = {"bytes_per_token": 1152, "ms_mean_k1_k2": main_r["k1_k2_ms"]["mean"],
                                 "tokens_per_s_k1_k2": round(main_r["batch"] / (main_r["k1_k2_ms"]["mean"] * 1e-3), 1)}
 
+    width = None
+    if not a.no_configs and a.workload == "dsv2_b64_l1k_32k":
+        width = model_width_measurement(a.workload, 20, flush, log)
+
     roof = dict(main_r["roofline"])
     roof["traffic"] = measured_traffic(main_r["workload"])
     line = {
@@ -418,6 +481,8 @@ def main() -> int:
         line["configs"] = configs
     if kv_cmp:
         line["kv_cache_comparison"] = kv_cmp
+    if width:
+        line["model_width_projections"] = width
     if "cpu_baseline" in main_r:
         line["cpu_baseline"] = main_r["cpu_baseline"]
     print(json.dumps(line), flush=True)

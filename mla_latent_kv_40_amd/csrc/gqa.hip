@@ -47,16 +47,25 @@ __device__ __forceinline__ int gqa_chunks(const int32_t* kv_lens, int b, int max
   return (pages + kChunkPages - 1) / kChunkPages;
 }
 
-// item_start[b] = H_kv * QS * (chunks of sequences 0 .. b-1): one thread, a serial scan (B is small
-// next to the split kernel's work).
+// item_start[b] = H_kv * QS * (chunks of sequences 0 .. b-1), item_start[B] = the total: one wave,
+// an exclusive prefix sum over 64 sequences at a time.
 __global__ void gqa_plan_kernel(GqaArgs a, int32_t* item_start) {
-  if (blockIdx.x != 0 || threadIdx.x != 0) return;
-  int acc = 0;
-  for (int b = 0; b < a.B; ++b) {
-    item_start[b] = acc;
-    acc += a.H_kv * a.QS * gqa_chunks(a.kv_lens, b, a.max_blocks);
+  const int lane = threadIdx.x & 63;
+  if (threadIdx.x >= 64) return;
+  int run = 0;
+  for (int base = 0; base < a.B; base += 64) {
+    const int b = base + lane;
+    const int n = b < a.B ? a.H_kv * a.QS * gqa_chunks(a.kv_lens, b, a.max_blocks) : 0;
+    int incl = n;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int v = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += v;
+    }
+    if (b < a.B) item_start[b] = run + incl - n;
+    run += __shfl(incl, 63, 64);
   }
-  item_start[a.B] = acc;
+  if (lane == 0) item_start[a.B] = run;
 }
 
 // One wave per work item: (sequence, key/value head, chunk of kChunkPages pages) and the group's

@@ -14,17 +14,16 @@
 // matrix operands are 16-byte row loads: A = Wt rows (32 outputs x 8 consecutive k per lane), B = X
 // rows (32 tokens x 8 consecutive k), D = Y^T on v_mfma_f32_32x32x16_bf16.
 //
-// A workgroup owns 64 outputs x 64 rows and a slice of the contraction; its four waves take
-// interleaved 64-wide chunks of that slice and their tiles are summed through LDS.  With one slice
-// the workgroup writes the result; with S slices each writes fp32 partials and a second kernel adds
-// the S partials in a fixed order (deterministic) and writes the result.
+// A workgroup owns 256 outputs x 64 rows and a slice of the contraction (each wave 64 outputs, the
+// rows' X staged once in LDS per 64-wide chunk).  With one slice the workgroup writes the result;
+// with S slices each writes fp32 partials and a second kernel adds the S partials in a fixed order
+// (deterministic) and writes the result.
 #include "common.h"
 
 #include <cmath>
 
 namespace mla {
 
-constexpr int kPjN = 64;       // outputs per workgroup
 constexpr int kPjT = 64;       // rows per workgroup
 constexpr int kPjChunk = 64;   // contraction elements per chunk (four MFMA K-steps)
 
@@ -67,65 +66,106 @@ __device__ __forceinline__ bf16x8 load_x8<float>(const float* p) {
                                           cvt_pk_bf16(b[2], b[3])});
 }
 
-// Workgroup (n-tile, slice s, row block z).  X [T, K] (ldx), Wt [N, K] bf16; K % 64 == 0.
-// out_mode 0: write through `o` (bf16); 1: fp32 partials part[s][t][n] (ld N).
+// Workgroup (output group of 256, slice s, row block z): wave w owns outputs n0 + 64w .. +63 (two
+// 32-row A tiles) and all 64 rows (two 32-column B tiles), over the slice's chunks of 64
+// contraction elements.  Per chunk, the rows' 64 x 64 block of X is staged once in LDS (shared by
+// the four waves: X is read once per 256 outputs) while the waves' weight pieces come straight
+// from memory; the next chunk's loads are in flight while the current one is multiplied.
+// X [T, K] (ldx), Wt [N, K] bf16; K % 64 == 0.  part == nullptr: write through `o` (bf16);
+// else fp32 partials part[s][t][n].
+constexpr int kPjGroup = 256;            // outputs per workgroup
+constexpr int kXPitch = 64 * 2 + 16;     // bytes per staged X row (the pad spreads rows over banks)
+
 template <typename XT>
 __global__ void __launch_bounds__(256) rows_gemm_kernel(const XT* __restrict__ X, long long ldx,
                                                         const uint16_t* __restrict__ Wt, int T, int N, int K,
                                                         int S, PjOut o, float* __restrict__ part) {
-  __shared__ __attribute__((aligned(16))) float red[4][4][16][64];   // [wave][tile][i][lane]  64 KiB
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int n0 = kPjN * blockIdx.x, s = blockIdx.y, t0 = kPjT * blockIdx.z;
+  __shared__ __attribute__((aligned(16))) uint8_t xs[2][kPjT * kXPitch];   // 18 KiB
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n0 = kPjGroup * blockIdx.x + 64 * wave, s = blockIdx.y, t0 = kPjT * blockIdx.z;
   const int r = lane & 31, g = lane >> 5;
-  // rows of this lane's operands (clamped: rows past N or T read a valid row and are not stored)
+  const int n_chunks = K / kPjChunk;
+  const int c0 = (int)((long long)s * n_chunks / S), c1 = (int)((long long)(s + 1) * n_chunks / S);
+  // this lane's weight rows (clamped: rows past N are read but not stored)
   const int na = n0 + r < N ? n0 + r : N - 1, nb = n0 + 32 + r < N ? n0 + 32 + r : N - 1;
-  const int ta = t0 + r < T ? t0 + r : T - 1, tb = t0 + 32 + r < T ? t0 + 32 + r : T - 1;
   const uint16_t* wa = Wt + (size_t)na * K + 8 * g;
   const uint16_t* wb = Wt + (size_t)nb * K + 8 * g;
-  const XT* xa = X + (size_t)ta * ldx + 8 * g;
-  const XT* xb = X + (size_t)tb * ldx + 8 * g;
+  // X staging: thread tid copies row tid/4, elements 16(tid%4) .. +15 of the chunk (rows past T: zeros)
+  const int xr = tid >> 2, xc = 16 * (tid & 3);
+  const bool x_ok = t0 + xr < T;
+  const XT* xp = X + (size_t)(x_ok ? t0 + xr : 0) * ldx + xc;
+  auto load_x = [&](int c, u32x4* v) {
+    if (!x_ok) {
+      v[0] = v[1] = u32x4{0u, 0u, 0u, 0u};
+      return;
+    }
+    const XT* q = xp + c * kPjChunk;
+    v[0] = __builtin_bit_cast(u32x4, load_x8(q));
+    v[1] = __builtin_bit_cast(u32x4, load_x8(q + 8));
+  };
+  auto store_x = [&](int buf, const u32x4* v) {
+    uint8_t* d = xs[buf] + xr * kXPitch + 2 * xc;
+    *reinterpret_cast<u32x4*>(d) = v[0];
+    *reinterpret_cast<u32x4*>(d + 16) = v[1];
+  };
+  auto load_w = [&](int c, bf16x8* a0, bf16x8* a1) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      a0[q] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(wa + c * kPjChunk + 16 * q));
+      a1[q] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(wb + c * kPjChunk + 16 * q));
+    }
+  };
   f32x16 acc[4];   // [n tile][t tile]
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc[i][e] = 0.f;
-  const int n_chunks = K / kPjChunk;
-  const int stride = 4 * S;
-  for (int c = 4 * s + wave; c < n_chunks; c += stride) {
-    const int k = c * kPjChunk;
-    bf16x8 a0[4], a1[4], b0[4], b1[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {   // every load of the chunk first
-      a0[q] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(wa + k + 16 * q));
-      a1[q] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(wb + k + 16 * q));
-      b0[q] = load_x8(xa + k + 16 * q);
-      b1[q] = load_x8(xb + k + 16 * q);
+  bf16x8 a0[4], a1[4], n0w[4], n1w[4];
+  u32x4 xv[2];
+  if (c0 < c1) {
+    load_w(c0, a0, a1);
+    load_x(c0, xv);
+    store_x(0, xv);
+  }
+  __syncthreads();
+  for (int c = c0; c < c1; ++c) {
+    const int buf = (c - c0) & 1;
+    const bool more = c + 1 < c1;
+    if (more) {   // the next chunk's loads go out before this chunk's products
+      load_w(c + 1, n0w, n1w);
+      load_x(c + 1, xv);
     }
+    const uint8_t* xb = xs[buf] + r * kXPitch + 16 * g;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0[q], b0[q], acc[0], 0, 0, 0);
-      acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0[q], b1[q], acc[1], 0, 0, 0);
-      acc[2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1[q], b0[q], acc[2], 0, 0, 0);
-      acc[3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1[q], b1[q], acc[3], 0, 0, 0);
+      const bf16x8 b0 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(xb + 32 * q));
+      const bf16x8 b1 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(xb + 32 * kXPitch + 32 * q));
+      acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0[q], b0, acc[0], 0, 0, 0);
+      acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0[q], b1, acc[1], 0, 0, 0);
+      acc[2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1[q], b0, acc[2], 0, 0, 0);
+      acc[3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1[q], b1, acc[3], 0, 0, 0);
     }
+    if (more) {
+      store_x(buf ^ 1, xv);   // the other buffer: last read before the previous barrier
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        a0[q] = n0w[q];
+        a1[q] = n1w[q];
+      }
+    }
+    __syncthreads();
   }
-  // acc[2 nt + tt][i] = partial Y^T[n = n0 + 32 nt + 8(i/4) + 4g + i%4, t = t0 + 32 tt + r]
+  // acc[2 nt + tt][i] = Y^T[n = n0 + 32 nt + 8(i/4) + 4g + i%4, t = t0 + 32 tt + r]
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) red[wave][i][e][lane] = acc[i][e];
-  __syncthreads();
-  // thread: tile i = wave, element e = 0..15 of its lane, summed over the four waves
-  {
-    const int i = wave, nt = i >> 1, tt = i & 1;
+  for (int i = 0; i < 4; ++i) {
+    const int nt = i >> 1, tt = i & 1;
     const int t = t0 + 32 * tt + r;
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      const float v = red[0][i][e][lane] + red[1][i][e][lane] + red[2][i][e][lane] + red[3][i][e][lane];
       const int n = n0 + 32 * nt + 8 * (e >> 2) + 4 * g + (e & 3);
       if (n < N && t < T) {
-        if (part != nullptr) part[((size_t)s * T + t) * N + n] = v;
-        else pj_store<uint16_t>(o, t, n, v);
+        if (part != nullptr) part[((size_t)s * T + t) * N + n] = acc[i][e];
+        else pj_store<uint16_t>(o, t, n, acc[i][e]);
       }
     }
   }
@@ -157,14 +197,14 @@ __global__ void __launch_bounds__(256) rows_gemm_generic_kernel(const XT* __rest
   }
 }
 
-// Slices of the contraction for a row GEMM: enough workgroups to cover the compute units about
-// twice, each slice at least four chunks per wave.
+// Slices of the contraction for a row GEMM: about one workgroup per compute unit, each slice at
+// least four chunks.
 int rows_gemm_slices(int num_cus, int T, int N, int K) {
-  const long long tiles = (long long)((N + kPjN - 1) / kPjN) * ((T + kPjT - 1) / kPjT);
-  if (tiles <= 0) return 1;   // nothing to compute
+  const long long groups = (long long)((N + kPjGroup - 1) / kPjGroup) * ((T + kPjT - 1) / kPjT);
+  if (groups <= 0) return 1;   // nothing to compute
   const int chunks = K / kPjChunk;
-  long long S = (2LL * num_cus + tiles - 1) / tiles;
-  const long long S_max = chunks / 16 > 0 ? chunks / 16 : 1;
+  long long S = (num_cus + groups - 1) / groups;
+  const long long S_max = chunks / 4 > 0 ? chunks / 4 : 1;
   if (S > S_max) S = S_max;
   if (S < 1) S = 1;
   return (int)S;
@@ -182,7 +222,7 @@ hipError_t launch_rows_gemm(int num_cus, const XT* X, long long ldx, const uint1
                             const PjOut& o, void* workspace, hipStream_t stream) {
   const int S = rows_gemm_slices(num_cus, T, N, K);
   float* part = S > 1 ? static_cast<float*>(workspace) : nullptr;
-  const dim3 grid((N + kPjN - 1) / kPjN, S, (T + kPjT - 1) / kPjT);
+  const dim3 grid((N + kPjGroup - 1) / kPjGroup, S, (T + kPjT - 1) / kPjT);
   hipLaunchKernelGGL(rows_gemm_kernel<XT>, grid, dim3(256), 0, stream, X, ldx, Wt, T, N, K, S, o, part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || S == 1) return e;
