@@ -14,12 +14,14 @@
 // matrix operands are 16-byte row loads: A = Wt rows (32 outputs x 8 consecutive k per lane), B = X
 // rows (32 tokens x 8 consecutive k), D = Y^T on v_mfma_f32_32x32x16_bf16.
 //
-// A workgroup owns 256 outputs x 64 rows and a slice of the contraction (each wave 64 outputs, the
-// rows' X staged once in LDS per 64-wide chunk).  With one slice the workgroup writes the result;
+// A workgroup owns 256 outputs x 64 rows and a slice of the contraction (each wave 64 outputs);
+// weights and X reach LDS by buffer->LDS loads, three chunks deep.  With one slice the workgroup
+// writes the result;
 // with S slices each writes fp32 partials and a second kernel adds the S partials in a fixed order
 // (deterministic) and writes the result.
 #include "common.h"
 
+#include <atomic>
 #include <cmath>
 
 namespace mla {
@@ -52,117 +54,129 @@ __device__ __forceinline__ void pj_store(const PjOut& o, int t, int n, float v) 
   else d[i] = (OutT)f32_to_bf16_bits(v);
 }
 
-// 8 consecutive X values as bf16 (fp32 inputs are rounded to bf16, nearest even)
-template <typename XT>
-__device__ __forceinline__ bf16x8 load_x8(const XT* p);
-template <>
-__device__ __forceinline__ bf16x8 load_x8<uint16_t>(const uint16_t* p) {
-  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
-}
-template <>
-__device__ __forceinline__ bf16x8 load_x8<float>(const float* p) {
-  const f32x4 a = *reinterpret_cast<const f32x4*>(p), b = *reinterpret_cast<const f32x4*>(p + 4);
-  return __builtin_bit_cast(bf16x8, u32x4{cvt_pk_bf16(a[0], a[1]), cvt_pk_bf16(a[2], a[3]), cvt_pk_bf16(b[0], b[1]),
-                                          cvt_pk_bf16(b[2], b[3])});
-}
-
 // Workgroup (output group of 256, slice s, row block z): wave w owns outputs n0 + 64w .. +63 (two
 // 32-row A tiles) and all 64 rows (two 32-column B tiles), over the slice's chunks of 64
-// contraction elements.  Per chunk, the rows' 64 x 64 block of X is staged once in LDS (shared by
-// the four waves: X is read once per 256 outputs) while the waves' weight pieces come straight
-// from memory; the next chunk's loads are in flight while the current one is multiplied.
+// contraction elements.  Every chunk is moved into LDS by buffer->LDS loads (no registers in
+// flight): the wave's own 64 weight rows (8 KiB) and a share of the rows' X block (bf16: 8 KiB,
+// fp32: 16 KiB, converted to bf16 when read), three stages, two chunks in flight while one is
+// multiplied, one barrier per chunk.  Rows are XOR-swizzled at 16-byte granularity so that the
+// fragment reads (32 rows, one 16-byte chunk each) spread over the banks.
 // X [T, K] (ldx), Wt [N, K] bf16; K % 64 == 0.  part == nullptr: write through `o` (bf16);
 // else fp32 partials part[s][t][n].
-constexpr int kPjGroup = 256;            // outputs per workgroup
-constexpr int kXPitch = 64 * 2 + 16;     // bytes per staged X row (the pad spreads rows over banks)
+constexpr int kPjGroup = 256;    // outputs per workgroup
+constexpr int kPjA = 256 * 128;  // A stage bytes: 256 rows x 64 bf16
+
+template <typename XT>
+constexpr int pj_stage_bytes() { return kPjA + kPjT * kPjChunk * (int)sizeof(XT); }
+
+__device__ __forceinline__ int pj_key(int r) { return (r >> 1) & 7; }   // bf16 rows: 8 chunks of 16 B
+
+// s_waitcnt that lets at most n vector-memory operations stay outstanding (gfx9 encoding; other
+// counters untouched)
+constexpr int pj_waitcnt_vm(int n) { return (n & 15) | (((n >> 4) & 3) << 14) | (7 << 4) | (15 << 8); }
 
 template <typename XT>
 __global__ void __launch_bounds__(256) rows_gemm_kernel(const XT* __restrict__ X, long long ldx,
-                                                        const uint16_t* __restrict__ Wt, int T, int N, int K,
-                                                        int S, PjOut o, float* __restrict__ part) {
-  __shared__ __attribute__((aligned(16))) uint8_t xs[2][kPjT * kXPitch];   // 18 KiB
+                                                        const uint16_t* __restrict__ Wt, int T, int N, int K, int S,
+                                                        PjOut o, float* __restrict__ part) {
+  extern __shared__ __attribute__((aligned(256))) uint8_t pj_smem[];
+  constexpr int SB = pj_stage_bytes<XT>();
+  constexpr bool kF32 = sizeof(XT) == 4;
+  constexpr int NX = kF32 ? 4 : 2;   // X loads per wave per chunk (1 KiB each)
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int n0 = kPjGroup * blockIdx.x + 64 * wave, s = blockIdx.y, t0 = kPjT * blockIdx.z;
+  const int n_base = kPjGroup * blockIdx.x, s = blockIdx.y, t0 = kPjT * blockIdx.z;
   const int r = lane & 31, g = lane >> 5;
   const int n_chunks = K / kPjChunk;
   const int c0 = (int)((long long)s * n_chunks / S), c1 = (int)((long long)(s + 1) * n_chunks / S);
-  // this lane's weight rows (clamped: rows past N are read but not stored)
-  const int na = n0 + r < N ? n0 + r : N - 1, nb = n0 + 32 + r < N ? n0 + 32 + r : N - 1;
-  const uint16_t* wa = Wt + (size_t)na * K + 8 * g;
-  const uint16_t* wb = Wt + (size_t)nb * K + 8 * g;
-  // X staging: thread tid copies row tid/4, elements 16(tid%4) .. +15 of the chunk (rows past T: zeros)
-  const int xr = tid >> 2, xc = 16 * (tid & 3);
-  const bool x_ok = t0 + xr < T;
-  const XT* xp = X + (size_t)(x_ok ? t0 + xr : 0) * ldx + xc;
-  auto load_x = [&](int c, u32x4* v) {
-    if (!x_ok) {
-      v[0] = v[1] = u32x4{0u, 0u, 0u, 0u};
-      return;
-    }
-    const XT* q = xp + c * kPjChunk;
-    v[0] = __builtin_bit_cast(u32x4, load_x8(q));
-    v[1] = __builtin_bit_cast(u32x4, load_x8(q + 8));
-  };
-  auto store_x = [&](int buf, const u32x4* v) {
-    uint8_t* d = xs[buf] + xr * kXPitch + 2 * xc;
-    *reinterpret_cast<u32x4*>(d) = v[0];
-    *reinterpret_cast<u32x4*>(d + 16) = v[1];
-  };
-  auto load_w = [&](int c, bf16x8* a0, bf16x8* a1) {
+  // weight rows n_base .. N-1 and X rows t0 .. T-1 of this workgroup (loads past them read zeros)
+  const int a_rows = N - n_base < kPjGroup ? N - n_base : kPjGroup;
+  const int x_rows = T - t0 < kPjT ? T - t0 : kPjT;
+  const __amdgpu_buffer_rsrc_t ar =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(Wt + (size_t)n_base * K), 0, a_rows * K * 2, 0x00020000);
+  const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(X + (size_t)t0 * ldx), 0, (int)(((x_rows - 1) * ldx + K) * (long long)sizeof(XT)), 0x00020000);
+  // per-lane source offsets: A load i writes LDS rows 64w + 8i + lane/8 (position lane%8); X load i
+  // writes rows (bf16) 8(2w + i) + lane/8 or (fp32) 4(4w + i) + lane/16.  x_off has room for
+  // the larger count (an array bound that depends on XT does not compile in the host pass).
+  int a_off[8], x_off[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      a0[q] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(wa + c * kPjChunk + 16 * q));
-      a1[q] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(wb + c * kPjChunk + 16 * q));
+  for (int i = 0; i < 8; ++i) {
+    const int rr = 64 * wave + 8 * i + (lane >> 3);
+    a_off[i] = rr * K * 2 + 16 * ((lane & 7) ^ pj_key(rr));
+  }
+#pragma unroll
+  for (int i = 0; i < NX; ++i) {
+    if constexpr (kF32) {
+      const int xrw = 4 * (4 * wave + i) + (lane >> 4);
+      x_off[i] = (int)(xrw * ldx * 4) + 16 * ((lane & 15) ^ (xrw & 15));
+    } else {
+      const int xrw = 8 * (2 * wave + i) + (lane >> 3);
+      x_off[i] = (int)(xrw * ldx * 2) + 16 * ((lane & 7) ^ pj_key(xrw));
     }
+  }
+  const int x_chunk_bytes = kPjChunk * (int)sizeof(XT);
+  auto issue = [&](int c, int stage) {
+    uint8_t* st = pj_smem + stage * SB;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ar, (MLA_LDS void*)(st + (8 * wave + i) * 1024), 16, a_off[i],
+                                               c * kPjChunk * 2, 0, 0);
+#pragma unroll
+    for (int i = 0; i < NX; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (MLA_LDS void*)(st + kPjA + (NX * wave + i) * 1024), 16, x_off[i],
+                                               c * x_chunk_bytes, 0, 0);
   };
   f32x16 acc[4];   // [n tile][t tile]
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc[i][e] = 0.f;
-  bf16x8 a0[4], a1[4], n0w[4], n1w[4];
-  u32x4 xv[2];
-  if (c0 < c1) {
-    load_w(c0, a0, a1);
-    load_x(c0, xv);
-    store_x(0, xv);
-  }
-  __syncthreads();
+  if (c0 < c1) issue(c0, 0);
+  if (c0 + 1 < c1) issue(c0 + 1, 1);
   for (int c = c0; c < c1; ++c) {
-    const int buf = (c - c0) & 1;
-    const bool more = c + 1 < c1;
-    if (more) {   // the next chunk's loads go out before this chunk's products
-      load_w(c + 1, n0w, n1w);
-      load_x(c + 1, xv);
-    }
-    const uint8_t* xb = xs[buf] + r * kXPitch + 16 * g;
+    const int stage = (c - c0) % 3;
+    if (c + 1 < c1) __builtin_amdgcn_s_waitcnt(pj_waitcnt_vm(8 + NX));   // chunk c landed (c+1 may not)
+    else __builtin_amdgcn_s_waitcnt(pj_waitcnt_vm(0));
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");   // everyone's loads of c, and stage (c+2)%3 free
+    if (c + 2 < c1) issue(c + 2, (c - c0 + 2) % 3);
+    const uint8_t* st = pj_smem + stage * SB;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const bf16x8 b0 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(xb + 32 * q));
-      const bf16x8 b1 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(xb + 32 * kXPitch + 32 * q));
-      acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0[q], b0, acc[0], 0, 0, 0);
-      acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0[q], b1, acc[1], 0, 0, 0);
-      acc[2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1[q], b0, acc[2], 0, 0, 0);
-      acc[3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1[q], b1, acc[3], 0, 0, 0);
-    }
-    if (more) {
-      store_x(buf ^ 1, xv);   // the other buffer: last read before the previous barrier
+      bf16x8 av[2], bv[2];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        a0[q] = n0w[q];
-        a1[q] = n1w[q];
+      for (int nt = 0; nt < 2; ++nt) {
+        const int rr = 64 * wave + 32 * nt + r;
+        av[nt] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(st + rr * 128 + 16 * ((2 * q + g) ^ pj_key(rr))));
       }
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        const int t = 32 * tt + r;
+        if constexpr (kF32) {
+          const uint8_t* xb = st + kPjA + t * 256;
+          const f32x4 x0 = *reinterpret_cast<const f32x4*>(xb + 16 * ((4 * q + 2 * g) ^ (t & 15)));
+          const f32x4 x1 = *reinterpret_cast<const f32x4*>(xb + 16 * ((4 * q + 2 * g + 1) ^ (t & 15)));
+          bv[tt] = __builtin_bit_cast(bf16x8, u32x4{cvt_pk_bf16(x0[0], x0[1]), cvt_pk_bf16(x0[2], x0[3]),
+                                                   cvt_pk_bf16(x1[0], x1[1]), cvt_pk_bf16(x1[2], x1[3])});
+        } else {
+          bv[tt] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(st + kPjA + t * 128 +
+                                                                                16 * ((2 * q + g) ^ pj_key(t))));
+        }
+      }
+      acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[0], bv[0], acc[0], 0, 0, 0);
+      acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[0], bv[1], acc[1], 0, 0, 0);
+      acc[2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[1], bv[0], acc[2], 0, 0, 0);
+      acc[3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[1], bv[1], acc[3], 0, 0, 0);
     }
-    __syncthreads();
   }
-  // acc[2 nt + tt][i] = Y^T[n = n0 + 32 nt + 8(i/4) + 4g + i%4, t = t0 + 32 tt + r]
+  __builtin_amdgcn_s_waitcnt(pj_waitcnt_vm(0));   // no load may land after the workgroup ends
+  // acc[2 nt + tt][i] = Y^T[n = n_base + 64w + 32 nt + 8(i/4) + 4g + i%4, t = t0 + 32 tt + r]
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int nt = i >> 1, tt = i & 1;
     const int t = t0 + 32 * tt + r;
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      const int n = n0 + 32 * nt + 8 * (e >> 2) + 4 * g + (e & 3);
+      const int n = n_base + 64 * wave + 32 * nt + 8 * (e >> 2) + 4 * g + (e & 3);
       if (n < N && t < T) {
         if (part != nullptr) part[((size_t)s * T + t) * N + n] = acc[i][e];
         else pj_store<uint16_t>(o, t, n, acc[i][e]);
@@ -197,17 +211,27 @@ __global__ void __launch_bounds__(256) rows_gemm_generic_kernel(const XT* __rest
   }
 }
 
-// Slices of the contraction for a row GEMM: about one workgroup per compute unit, each slice at
-// least four chunks.
+// Slices of the contraction for a row GEMM.  One workgroup fits a compute unit (its LDS), so the
+// launch runs in rounds of num_cus workgroups: S is chosen to minimise the modelled time, rounds x
+// (chunks per slice + 3 chunks of pipeline fill) chunk loads per compute unit, plus the fp32
+// partials written and read back once (S x T x N x 8 bytes, spread over the whole chip).  Each
+// slice keeps at least four chunks.
 int rows_gemm_slices(int num_cus, int T, int N, int K) {
   const long long groups = (long long)((N + kPjGroup - 1) / kPjGroup) * ((T + kPjT - 1) / kPjT);
-  if (groups <= 0) return 1;   // nothing to compute
+  if (groups <= 0 || num_cus <= 0) return 1;   // nothing to compute
   const int chunks = K / kPjChunk;
-  long long S = (num_cus + groups - 1) / groups;
   const long long S_max = chunks / 4 > 0 ? chunks / 4 : 1;
-  if (S > S_max) S = S_max;
-  if (S < 1) S = 1;
-  return (int)S;
+  const double chunk_bytes = (double)(kPjA + kPjT * kPjChunk * 2);
+  long long best_S = 1;
+  double best = -1.0;
+  for (long long S = 1; S <= S_max; ++S) {
+    const long long rounds = (groups * S + num_cus - 1) / num_cus;
+    const long long per = (chunks + S - 1) / S;
+    const double cost = (double)rounds * (double)(per + 3) * chunk_bytes * num_cus +
+                        (S > 1 ? (double)S * T * N * 8.0 : 0.0);
+    if (best < 0.0 || cost < best) { best = cost; best_S = S; }
+  }
+  return (int)best_S;
 }
 
 size_t rows_gemm_workspace(int num_cus, int T, int N, int K) {
@@ -216,14 +240,50 @@ size_t rows_gemm_workspace(int num_cus, int T, int N, int K) {
   return (((size_t)S * T * N * sizeof(float)) + 255) & ~(size_t)255;
 }
 
+// The row GEMM takes more LDS than the default dynamic limit, raised once per device (an atomic
+// mark per device; racing threads repeat the same idempotent calls).
+constexpr int kPjMaxDev = 64;
+std::atomic<int> g_pj_lds_set[kPjMaxDev];
+
+hipError_t set_rows_gemm_lds_limits() {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::atomic<int>* mark = (dev >= 0 && dev < kPjMaxDev) ? &g_pj_lds_set[dev] : nullptr;
+  if (mark && mark->load(std::memory_order_acquire)) return hipSuccess;
+  e = hipFuncSetAttribute((const void*)rows_gemm_kernel<uint16_t>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                          3 * pj_stage_bytes<uint16_t>());
+  if (e != hipSuccess) return e;
+  e = hipFuncSetAttribute((const void*)rows_gemm_kernel<float>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                          3 * pj_stage_bytes<float>());
+  if (e != hipSuccess) return e;
+  if (mark) mark->store(1, std::memory_order_release);
+  return hipSuccess;
+}
+
+template <typename XT, typename WT, typename OutT>
+hipError_t launch_rows_gemm_generic(const XT* X, long long ldx, const WT* Wt, int T, int N, int K, const PjOut& o,
+                                    hipStream_t stream);
+
+// The MFMA kernel addresses one workgroup's weight rows and X rows with 32-bit buffer offsets.
+template <typename XT>
+bool rows_gemm_offsets_fit(long long ldx, int K) {
+  return (long long)kPjGroup * K * 2 < (1ll << 31) && (long long)kPjT * ldx * (long long)sizeof(XT) < (1ll << 31);
+}
+
 // Y = X . Wt^T through `o`, bf16 MFMA path (X bf16 or fp32, Wt bf16, K % 64 == 0).
 template <typename XT>
 hipError_t launch_rows_gemm(int num_cus, const XT* X, long long ldx, const uint16_t* Wt, int T, int N, int K,
                             const PjOut& o, void* workspace, hipStream_t stream) {
+  if (!rows_gemm_offsets_fit<XT>(ldx, K))
+    return launch_rows_gemm_generic<XT, uint16_t, uint16_t>(X, ldx, Wt, T, N, K, o, stream);
   const int S = rows_gemm_slices(num_cus, T, N, K);
   float* part = S > 1 ? static_cast<float*>(workspace) : nullptr;
   const dim3 grid((N + kPjGroup - 1) / kPjGroup, S, (T + kPjT - 1) / kPjT);
-  hipLaunchKernelGGL(rows_gemm_kernel<XT>, grid, dim3(256), 0, stream, X, ldx, Wt, T, N, K, S, o, part);
+  hipError_t e0 = set_rows_gemm_lds_limits();
+  if (e0 != hipSuccess) return e0;
+  hipLaunchKernelGGL(rows_gemm_kernel<XT>, grid, dim3(256), 3 * pj_stage_bytes<XT>(), stream, X, ldx, Wt, T, N, K, S,
+                     o, part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || S == 1) return e;
   const size_t total = (size_t)T * N;
