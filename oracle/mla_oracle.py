@@ -325,6 +325,70 @@ def quantize_rows_fp8(rows: np.ndarray):
     return codes, scale
 
 
+# ------------------------------------------------- block-scaled fp8 e4m3 storage
+#
+# The katajob page (section "Compression as architecture versus compression as post-processing")
+# names per-block scaling as what makes a quantised cache work and says a latent can itself be
+# stored in a reduced-precision format.  The block-scaled format reads that as: the cache rows of
+# a page are cut into tiles of 32 tokens x 32 columns, each tile has one power-of-two scale
+# 2^e, and each value is stored as the e4m3 code of value / 2^e.  Tokens arrive one call at a
+# time, so a tile's scale is decided by the rows it holds so far: a call takes, for each tile it
+# writes, e = the largest exponent any of the tile's rows needs (its earlier rows' exponent
+# included, unless the call writes the tile's first row), re-encodes the earlier rows' codes at
+# the new scale when e grew, and encodes its own rows at e.
+
+TILE_TOKENS = 32
+TILE_COLS = 32
+BLOCK_E_MIN, BLOCK_E_MAX = -126, 127
+
+
+def block_exponent(amax) -> np.ndarray:
+    """Smallest integer e with amax <= 448 * 2^e (the tile's largest magnitude then encodes without
+    saturating), clamped to [-126, 127]; -126 for amax == 0.  Exact: amax = m 2^x with m in
+    [0.5, 1) lies in [2^(x-1), 2^x), and 448 2^(x-9) = 0.875 2^x, so e is x - 9 or x - 8."""
+    a = np.asarray(amax, dtype=np.float64)
+    _, x = np.frexp(np.where(a > 0, a, 1.0))
+    e = x.astype(np.int64) - 9
+    e = np.where(a > E4M3_MAX * np.exp2(e.astype(np.float64)), e + 1, e)
+    e = np.where(a > 0, e, BLOCK_E_MIN)
+    return np.clip(e, BLOCK_E_MIN, BLOCK_E_MAX).astype(np.int64)
+
+
+def append_block_fp8(codes: np.ndarray, exps: np.ndarray, rows: np.ndarray, p0: int) -> None:
+    """One append call of a sequence into its block-scaled cache, in place.
+
+    codes [capacity, row] float64: the code values (e4m3 values) of every position; exps
+    [capacity / 32, row / 32] int: the tile exponents.  rows [n, row]: the new rows at positions
+    p0 .. p0 + n - 1 (the latent exactly and the rotated positional key, both as the fp32
+    values the cache is written from).  Positions before p0 must already be in the cache."""
+    rows = np.asarray(rows, dtype=np.float64).astype(np.float32).astype(np.float64)
+    n, width = rows.shape
+    nb = width // TILE_COLS
+    p1 = p0 + n
+    for k in range(p0 // TILE_TOKENS, (p1 - 1) // TILE_TOKENS + 1 if n > 0 else 0):
+        t0, t1 = k * TILE_TOKENS, (k + 1) * TILE_TOKENS
+        a, b = max(t0, p0), min(t1, p1)                     # new rows of this tile
+        new = rows[a - p0:b - p0].reshape(b - a, nb, TILE_COLS)
+        e_new = block_exponent(np.abs(new).max(axis=(0, 2)))   # [nb]
+        fresh = a == t0
+        if not fresh:                                       # rows t0 .. a-1 were written earlier
+            e_old = exps[k].astype(np.int64)
+            e_new = np.maximum(e_new, e_old)
+            old = codes[t0:a].reshape(a - t0, nb, TILE_COLS)
+            shift = np.exp2((e_old - e_new).astype(np.float64))[None, :, None]
+            codes[t0:a] = e4m3_round(old * shift).reshape(a - t0, width)
+        codes[a:b] = e4m3_round(new * np.exp2(-e_new.astype(np.float64))[None, :, None]).reshape(b - a, width)
+        exps[k] = e_new
+
+
+def dequantize_block_fp8(codes: np.ndarray, exps: np.ndarray, L: int) -> np.ndarray:
+    """Row values of positions 0 .. L-1: code * 2^e of the tile (token / 32, column / 32)."""
+    t = np.arange(L)
+    e = exps[t // TILE_TOKENS]                                   # [L, nb]
+    scale = np.repeat(np.exp2(e.astype(np.float64)), TILE_COLS, axis=1)
+    return codes[:L] * scale
+
+
 # -------------------------------------------------------------- closed forms
 
 def mha_cache_elements_per_token(heads: int, d_head: int) -> int:

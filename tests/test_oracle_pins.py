@@ -419,6 +419,119 @@ def test_fp8_row_quantiser():
     assert np.array_equal(codes, ref)
 
 
+# ------------------------------------------------------------ block-scaled fp8
+
+def _brute_exponent(amax):
+    """Smallest e in [-126, 127] with amax <= 448 * 2^e, by trying every e in order."""
+    for e in range(-126, 128):
+        if amax <= 448.0 * math.ldexp(1.0, e):
+            return e
+    return 127
+
+
+def _exponent_pin_holds(fn):
+    rng = np.random.default_rng(21)
+    a = np.exp2(rng.uniform(-140, 126, 4000)).astype(np.float32).astype(np.float64)
+    edges = [0.0, 448.0, np.nextafter(448.0, 1e9), 224.0, 1.0, 0.875, np.nextafter(0.875, 1.0),
+             448.0 * 2.0**-126, 448.0 * 2.0**-127, 448.0 * 2.0**127, 1e-45]
+    a = np.concatenate([a, np.asarray(edges)])
+    return np.array_equal(fn(a), np.asarray([_brute_exponent(float(x)) for x in a]))
+
+
+def test_block_exponent_brute_force():
+    assert _exponent_pin_holds(orc.block_exponent)
+
+
+def _tile_rows(rng, n, width=576):
+    """Rows whose 32-column blocks have magnitudes spread over many binades, fp32 values."""
+    mag = np.exp2(rng.integers(-20, 20, size=(n, width // 32))).repeat(32, axis=1)
+    return (rng.standard_normal((n, width)) * mag).astype(np.float32).astype(np.float64)
+
+
+def test_block_quantiser_one_call():
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(22)
+    rows = _tile_rows(rng, 100)
+    rows[32:64, 64:96] = 0.0                                   # one all-zero tile
+    codes = np.zeros((128, 576))
+    exps = np.zeros((4, 18), dtype=np.int64)
+    orc.append_block_fp8(codes, exps, rows, 0)
+    # each tile's exponent is the brute-force exponent of its largest magnitude
+    for k in range(4):
+        blk = np.abs(rows[32 * k:32 * k + 32]).reshape(-1, 18, 32)
+        if blk.shape[0] == 0:
+            continue
+        for cb in range(18):
+            assert exps[k, cb] == _brute_exponent(float(blk[:, cb].max())), (k, cb)
+    assert exps[1, 2] == -126
+    # the codes are torch's e4m3 cast of the fp32 value times 2^-e (exact in fp32 here)
+    e_el = np.repeat(exps[np.arange(100) // 32], 32, axis=1)
+    q = torch.from_numpy((rows * np.exp2(-e_el)).astype(np.float32))
+    assert np.array_equal(codes[:100], q.to(torch.float8_e4m3fn).to(torch.float64).numpy())
+    # error of the stored value: half a step of 3 mantissa bits, or of the subnormal spacing
+    deq = orc.dequantize_block_fp8(codes, exps, 100)
+    assert np.all(np.abs(deq - rows) <= np.abs(rows) * 2.0**-4 + np.exp2(e_el - 10.0))
+    assert np.all(np.abs(codes) <= 448.0)
+
+
+def _regrow_pin_holds(append):
+    """Two calls into one tile: 10 rows, then 5 rows with 64x the magnitude.  The first rows'
+    codes must be the e4m3 cast of (their first-call code x 2^(e1 - e2)), computed with torch."""
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(23)
+    small = rng.standard_normal((10, 576)).astype(np.float32).astype(np.float64)
+    big = (rng.standard_normal((5, 576)) * 64.0).astype(np.float32).astype(np.float64)
+    codes = np.zeros((64, 576))
+    exps = np.zeros((2, 18), dtype=np.int64)
+    append(codes, exps, small, 0)
+    e1, c1 = exps[0].copy(), codes[:10].copy()
+    append(codes, exps, big, 10)
+    e2 = exps[0]
+    if not np.all(e2 >= e1 + 5):
+        return False
+    cast = lambda x: torch.from_numpy(x.astype(np.float32)).to(torch.float8_e4m3fn).to(torch.float64).numpy()
+    shift = np.repeat(np.exp2((e1 - e2).astype(np.float64)), 32)[None, :]
+    ok_old = np.array_equal(codes[:10], cast(c1 * shift))
+    ok_new = np.array_equal(codes[10:15], cast(big * np.repeat(np.exp2(-e2.astype(np.float64)), 32)[None, :]))
+    ok_e = all(e2[cb] == _brute_exponent(float(np.abs(np.concatenate([small, big])[:, 32 * cb:32 * cb + 32]).max()))
+               for cb in range(18))
+    return ok_old and ok_new and ok_e
+
+
+def test_block_append_regrows_earlier_rows():
+    assert _regrow_pin_holds(orc.append_block_fp8)
+
+
+def test_block_append_call_split_and_fresh_tiles():
+    rng = np.random.default_rng(24)
+    rows = _tile_rows(rng, 150)
+    # make the first row of every tile the largest, so no later call grows a tile's exponent:
+    # then any split into calls gives the one-call result exactly
+    for k in range(5):
+        rows[32 * k] = np.sign(rows[32 * k]) * np.abs(rows[32 * k:32 * k + 32]).max(axis=0) + 0.0
+    one_c, one_e = np.zeros((160, 576)), np.zeros((5, 18), dtype=np.int64)
+    orc.append_block_fp8(one_c, one_e, rows, 0)
+    split_c = np.zeros((160, 576))
+    split_e = np.full((5, 18), 100, dtype=np.int64)             # stale exponents: every tile is fresh
+    for a, b in [(0, 1), (1, 31), (31, 33), (33, 96), (96, 97), (97, 150)]:
+        if a % 32 == 0:
+            split_e[a // 32] = 100
+        orc.append_block_fp8(split_c, split_e, rows[a:b], a)
+    assert np.array_equal(one_c[:150], split_c[:150])
+    assert np.array_equal(one_e, split_e)
+
+
+def test_block_planted_mistakes_are_caught():
+    # exponent one too large everywhere (the common ceil/floor slip)
+    assert not _exponent_pin_holds(lambda a: np.minimum(orc.block_exponent(a) + 1, 127))
+    # an append that keeps the earlier rows' codes when the tile's exponent grows
+    def no_rescale(codes, exps, rows, p0):
+        keep = codes[:p0].copy()
+        orc.append_block_fp8(codes, exps, rows, p0)
+        codes[:p0] = keep
+    assert not _regrow_pin_holds(no_rescale)
+
+
 # ------------------------------------------------------ planted mistakes are caught
 
 def _planted_decode(kind):
