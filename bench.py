@@ -19,7 +19,7 @@ take ~100 steps to settle.  --warm adds the same measurement without the buffer 
 
 value       query tokens decoded per second: B*Sq / mean step time (flushed steps)
 roofline    the split-K decode (K1 split + K2 combine): latent-cache bytes it must read per step
-            (1152 B per cached token in bf16, 580 B in fp8 incl. the scale) / mean(K1 + K2),
+            (1152 B per cached token in bf16, 580 B in fp8 incl. the scale, 578.25 B with tile scales) / mean(K1 + K2),
             against 8 TB/s; the K1-only figure alongside.  traffic = HBM bytes per step of K1 + K2
             from rocprofv3 counters (profiles/decode_hbm_traffic.md), null when the kernel source
             differs from the one those counters were taken on
@@ -49,10 +49,11 @@ PEAK_FP8_TFLOPS = 5000.0
 PEAK_FP32_TFLOPS = 157.3
 METRIC = "MLA decode tokens/s + latent-cache GB/s & TFLOP/s (% peak) at B=64, 32k ctx"
 FLUSH_BYTES = 512 << 20
-# the five workloads of the task's configuration list, in its order (the first is latency-bound)
+# the five decode workloads, smallest first (the first is latency-bound)
 CONFIGS = ["tiny_f32", "dsv2_b16_l4k", "dsv2_b64_l1k_32k", "dsv2_b32_l8k_sq4", "dsv2_b128_l8k_fp8"]
-# measured alongside them: a chunked prefill step (512 new tokens per sequence)
-EXTRA_CONFIGS = ["dsv2_b4_l8k_sq512"]
+# measured alongside them: a chunked prefill step (512 new tokens per sequence) and the fp8 step
+# with the block-scaled cache
+EXTRA_CONFIGS = ["dsv2_b4_l8k_sq512", "dsv2_b128_l8k_fp8b"]
 
 
 def algorithmic(w, kv_lens):
@@ -60,12 +61,12 @@ def algorithmic(w, kv_lens):
     the latent-space attention: 2*H*(2*d_c + d_R) per visible (query, token)."""
     kv = kv_lens.astype(np.int64)
     tokens = int(kv.sum())
-    per_tok = w.row * (1 if w.dtype == "fp8" else 2 if w.dtype == "bf16" else 4) + (4 if w.dtype == "fp8" else 0)
+    per_tok = w.cache_bytes_per_token   # row bytes plus the scales' share
     visible = 0
     for j in range(w.sq):
         visible += int(np.maximum(kv - w.sq + j + 1, 0).sum())
     flops = visible * 2 * w.heads * (2 * w.d_c + w.d_r)
-    return tokens * per_tok, flops, tokens
+    return int(round(tokens * per_tok)), flops, tokens
 
 
 def measured_traffic(workload):
@@ -118,7 +119,7 @@ def cpu_baseline(w, bt, seqs_gpu_out, budget_s=20.0, heads=None):
     done, t0 = 0, time.perf_counter()
     picked = []
     worst = 0.0
-    factor = 4.0 if w.dtype == "fp8" else 1.0
+    factor = 4.0 if w.fp8 else 1.0
     hs = list(range(w.heads)) if heads is None else list(heads)
     for b in order:
         b = int(b)
@@ -229,7 +230,7 @@ def run_workload(name, steps, warmup, settle_ms, flush, warm, cpu_budget, log):
     bytes_alg, flops, tokens = algorithmic(w, bt.kv_lens)
     step_ms, k1_ms, k2_ms = ms[:, 0], ms[:, 1], ms[:, 2]
     k12_ms = k1_ms + k2_ms
-    peak_mfma = {"fp8": PEAK_FP8_TFLOPS, "bf16": PEAK_BF16_TFLOPS}.get(w.dtype, PEAK_FP32_TFLOPS)
+    peak_mfma = PEAK_FP8_TFLOPS if w.fp8 else PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
     intensity = flops / bytes_alg
     hbm_bound = intensity < peak_mfma * 1e12 / (PEAK_HBM_GBS * 1e9)
 
@@ -247,7 +248,7 @@ def run_workload(name, steps, warmup, settle_ms, flush, warm, cpu_budget, log):
                 "p10": round(float(np.percentile(x, 10)), 4), "p90": round(float(np.percentile(x, 90)), 4),
                 "min": round(float(x.min()), 4)}
 
-    k1_name = ("decode_mfma_fp8_kernel" if w.dtype == "fp8" else "decode_mfma_bf16_kernel" if w.dtype == "bf16"
+    k1_name = ("decode_mfma_fp8_kernel" if w.fp8 else "decode_mfma_bf16_kernel" if w.dtype == "bf16"
                else "decode_generic_kernel")
     r = {
         "workload": w.name, "batch": w.batch, "sq": w.sq, "dtype": w.dtype, "kv_tokens": tokens,

@@ -65,7 +65,13 @@ typedef enum {
   MLA_ERR_HIP = 4            /* the HIP runtime reported an error (device query or launch) */
 } mla_status_t;
 
-typedef enum { MLA_F32 = 0, MLA_BF16 = 1, MLA_FP8_E4M3 = 2 } mla_dtype_t;
+/*
+ * Cache formats.  MLA_FP8_E4M3: e4m3 codes with one fp32 scale per token.  MLA_FP8_E4M3_B32:
+ * e4m3 codes with one power-of-two scale per tile of 32 tokens x 32 columns (katajob, section
+ * "Compression as architecture versus compression as post-processing": quantised caches depend
+ * on per-block scales, and a low-precision latent composes with MLA); DeepSeek-V2 shape only.
+ */
+typedef enum { MLA_F32 = 0, MLA_BF16 = 1, MLA_FP8_E4M3 = 2, MLA_FP8_E4M3_B32 = 3 } mla_dtype_t;
 
 typedef struct {
   int32_t num_heads;     /* H */
@@ -92,7 +98,9 @@ typedef struct {
  * step 4).
  *
  *   cache        [num_blocks, 64, d_c + d_R] in cache_dtype; row = [c ; RoPE(k_R, pos)]
- *   cache_scale  [num_blocks, 64] fp32, written for FP8 caches; must be NULL otherwise
+ *   cache_scale  FP8_E4M3: [num_blocks, 64] fp32, one per token; FP8_E4M3_B32: [num_blocks, 2, 18]
+ *                fp32, one power of two 2^e per tile (token half, 32-column block); NULL for
+ *                other formats
  *   c_kv         [n, d_c]  act_dtype      k_r [n, d_R] act_dtype, before RoPE
  *   pos          [n] int32 (device)       position of each token within its sequence
  *   seq_of       [n] int32 (device)       sequence of each token, 0 .. batch-1
@@ -101,6 +109,13 @@ typedef struct {
  * and its cosine/sine are evaluated in fp64.
  * A token whose sequence, page slot or page id is out of range is skipped (not written).
  * FP8: scale = amax/448 in fp32, code = e4m3(value / scale), nearest-even, saturating.
+ * FP8_E4M3_B32: for every tile the call writes, e = the smallest integer with amax <= 448 * 2^e
+ * (amax over the tile's rows, those written by earlier calls included unless this call writes
+ * the tile's first row), clamped to [-126, 127]; codes = e4m3(value * 2^-e); when e grows,
+ * the earlier rows' codes are re-encoded as e4m3(code * 2^(e_old - e)).  Preconditions: the
+ * positions of a sequence are appended in order, each once, and the tokens of one call that
+ * fall into one tile are consecutive in the call (true for one token per sequence and for
+ * chunks of consecutive positions); otherwise the tile's contents are undefined.
  */
 mla_status_t mla_cache_append(const mla_config_t* cfg, void* cache, float* cache_scale,
                               int32_t num_blocks, const void* c_kv, const void* k_r,
@@ -150,15 +165,17 @@ size_t mla_decode_workspace_size(const mla_config_t* cfg, int32_t B, int32_t Sq,
                                  int32_t max_blocks);
 
 /*
- * mla_decode_attn -- attention in latent space (katajob: after folding, the model "attends
- * in the latent space directly"; zenaique: decode streams the whole cache from HBM, so the
+ * mla_decode_attn -- attention in latent space (katajob, "Why it is not just extra work at
+ * decode time": once folded, attention runs on the latent itself, with no per-head keys or
+ * values built; zenaique: decode streams the whole cache from HBM, so the
  * bytes per cached token set the ceiling).
  *
  * For every query row t = b*Sq + j and head i, over tokens s = 0 .. p (p = kv_len[b]-Sq+j):
  *   score[s] = softmax_scale * (q_abs[t,i] . cache_row[s])       (content + positional)
  *   o_lat[t,i] = sum_s softmax(score)[s] * c_s                   ([T, H, d_c] fp32)
  *   lse[t,i]   = log sum_s exp(score[s])                         ([T, H] fp32, natural log)
- * FP8: row values are code*cache_scale.  The matrix instructions take e4m3 operands: each
+ * FP8: row values are code*cache_scale (FP8_E4M3_B32: code * the tile's 2^e, which the matrix
+ * instructions take as their E8M0 operand block scales).  The matrix instructions take e4m3 operands: each
  * head's query becomes two e4m3 terms (hi + lo/16 with one fp32 scale, about 8 significant
  * bits), and so do the probabilities (hi + lo/16 per token, with a power-of-two block scale).
  * The token range is split across workgroups (split-K); partial results go to `workspace`
@@ -170,7 +187,7 @@ size_t mla_decode_workspace_size(const mla_config_t* cfg, int32_t B, int32_t Sq,
  * device memory and are not read on the host, so these cases are results, not errors.
  *
  *   q_abs       [T, H, d_c + d_R] act_dtype (mla_absorb_q output)
- *   cache       [num_blocks, 64, d_c + d_R]                 cache_scale [num_blocks, 64] or NULL
+ *   cache       [num_blocks, 64, d_c + d_R]                 cache_scale as for mla_cache_append
  *   block_table [B, max_blocks] int32 (device)              kv_lens [B] int32 (device)
  *   workspace   >= mla_decode_workspace_size(cfg, B, Sq, max_blocks) bytes, 256-byte aligned;
  *               contents need no initialisation and are not preserved.
@@ -308,7 +325,7 @@ mla_status_t mla_out_proj(const mla_config_t* cfg, const float* o_lat, const voi
 /* Human-readable name of a status code (static storage). */
 const char* mla_status_string(mla_status_t status);
 
-/* ABI version of this header: 6. */
+/* ABI version of this header: 7. */
 int32_t mla_abi_version(void);
 
 #ifdef __cplusplus

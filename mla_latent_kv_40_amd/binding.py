@@ -13,12 +13,13 @@ from typing import Optional
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmla.so")
 
-ABI_VERSION = 6   # what mla_abi_version() returns for the argument lists below
+ABI_VERSION = 7   # what mla_abi_version() returns for the argument lists below
 NOALLOC_SCRATCH_BYTES = 64 << 20   # MLA_NOALLOC_SCRATCH_BYTES
 
 MLA_OK, MLA_ERR_INVALID_ARG, MLA_ERR_UNSUPPORTED, MLA_ERR_WORKSPACE, MLA_ERR_HIP = range(5)
-MLA_F32, MLA_BF16, MLA_FP8_E4M3 = range(3)
-DTYPES = {"f32": MLA_F32, "bf16": MLA_BF16, "fp8": MLA_FP8_E4M3}
+MLA_F32, MLA_BF16, MLA_FP8_E4M3, MLA_FP8_E4M3_B32 = range(4)
+# "fp8": e4m3 codes with a scale per token; "fp8b": with a power-of-two scale per 32 x 32 tile
+DTYPES = {"f32": MLA_F32, "bf16": MLA_BF16, "fp8": MLA_FP8_E4M3, "fp8b": MLA_FP8_E4M3_B32}
 
 EXPORTS = ("mla_cache_append", "mla_absorb_q", "mla_append_absorb", "mla_decode_workspace_size", "mla_decode_attn",
            "mla_decode_split", "mla_decode_combine", "mla_decode_attn_noalloc", "mla_out_proj", "mla_status_string",

@@ -38,7 +38,8 @@ constexpr int kTileBytes = kBlock * kRow * 2;     // 73728
 struct DecodeArgs {
   const uint16_t* q_abs;      // [T, H, 576] bf16
   const uint8_t* cache;       // [num_blocks, 64, 576] bf16 (e4m3 codes for an fp8 cache)
-  const float* cache_scale;   // [num_blocks, 64] fp8 only: cached row value = code * scale
+  const float* cache_scale;   // fp8 only: [num_blocks, 64] per token, or [num_blocks, 2, 18] per
+                              // tile of 32 tokens x 32 columns (block8): row value = code * scale
   const int32_t* block_table; // [B, max_blocks]
   const int32_t* kv_lens;     // [B]
   float* o_lat;               // [T, H, 512]
@@ -48,6 +49,7 @@ struct DecodeArgs {
   int num_blocks, max_blocks, B, Sq, G;
   float scale_log2;           // softmax_scale * log2(e)
   int fp8;                    // cache and queries are e4m3 codes with scales
+  int block8;                 // fp8 cache with tile scales (powers of two) instead of token scales
   int seg_w;                  // per-segment overhead in pages, for cutting the ranges
 };
 
@@ -246,6 +248,10 @@ __device__ __forceinline__ void load_row(const PageLoad& p, int i, int wave, int
 // loads in flight before the first transposing read of every step.
 __device__ __forceinline__ u32x4 lds_b128(uint32_t addr) {
   const MLA_LDS u32x4* __restrict__ p = (const MLA_LDS u32x4*)(size_t)addr;
+  return *p;
+}
+__device__ __forceinline__ uint32_t lds_u32(uint32_t addr) {
+  const MLA_LDS uint32_t* __restrict__ p = (const MLA_LDS uint32_t*)(size_t)addr;
   return *p;
 }
 __device__ __forceinline__ uint32_t lds_u16(uint32_t addr) {
@@ -791,6 +797,7 @@ constexpr int kTabCap8 = 512;
 constexpr int kSrcTab8 = kTabOff8 + 16 * kTabCap8;   // 159744: per-lane source offsets of the row loads
 constexpr int kDecodeLds8 = kSrcTab8 + 2 * 9 * 64 * 2;   // 162048
 constexpr int kE8M0One = 127;                        // E8M0 code of 1.0
+constexpr int kTileCols = kRow / 32;                 // 18 column blocks of a row (tile scales)
 
 // LDS layout of a page of codes: row r (576 B = 36 chunks of 16 B) at 576r, chunk c stored at
 // c ^ key8(r), which flips only the two low chunk bits (every chunk stays in its 64-byte group).
@@ -824,13 +831,18 @@ struct PageLoad8 {
   __amdgpu_buffer_rsrc_t rows, scales;
   uint8_t* stage;
 };
+// With tile scales (Block) the page's 36 scales (token half h, column block c at 18h + c) take
+// the first 144 bytes of the copy, and the second half's 18 are in range only when the page has
+// a valid row in that half (else they read as zeros: scale byte 0, codes 0).
+template <bool Block>
 __device__ __forceinline__ PageLoad8 page_load8(uint8_t* stage, const uint8_t* cache, const float* cache_scale,
                                                 int pg, int nvalid) {
   const size_t p = (size_t)(pg < 0 ? 0 : pg);
   const int nv = nvalid < 0 ? 0 : nvalid;
+  const float* sc = Block ? cache_scale + p * (2 * kTileCols) : cache_scale + p * kBlock;
+  const int sbytes = Block ? 4 * kTileCols * (nv > 32 ? 2 : (nv > 0 ? 1 : 0)) : nv * 4;
   return PageLoad8{__builtin_amdgcn_make_buffer_rsrc((void*)(cache + p * kPage8), 0, nv * kRow, 0x00020000),
-                   __builtin_amdgcn_make_buffer_rsrc((void*)(cache_scale + p * kBlock), 0, nv * 4, 0x00020000),
-                   stage};
+                   __builtin_amdgcn_make_buffer_rsrc((void*)sc, 0, sbytes, 0x00020000), stage};
 }
 // source offset in the page of the 16 bytes that lane `lane` of load i (of wave `wave`) writes
 __device__ __forceinline__ int page8_src(int wave, int i, int lane) {
@@ -866,7 +878,7 @@ __device__ __forceinline__ void load_row8(const PageLoad8& p, int i, int wave, i
 //           column tile ct must hold Codes[T(l/32, j), 32ct + l%32] in byte j: four
 //           transposing reads (bytes 8q .. 8q+7) whose source lane σ points at token
 //           16q + 8((σ>>3)&1) + 4(σ>>5) + ((σ>>1)&3), columns 32ct + 8(2((σ>>4)&1) + (σ&1)).
-template <int Aux>
+template <int Aux, bool Block>
 __global__ void __launch_bounds__(256, 1) decode_mfma_fp8_kernel(DecodeArgs a) {
   extern __shared__ __attribute__((aligned(256))) uint8_t smem[];
   const int lane = threadIdx.x & 63;
@@ -964,6 +976,14 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_fp8_kernel(DecodeArgs a) {
     const uint32_t T = lds_addr(tile);
     const uint32_t a0 = T + (uint32_t)(rr * kRow + 16 * (hh ^ key));
     const uint32_t a1 = T + (uint32_t)(rr * kRow + 16 * ((2 + hh) ^ key));
+    // tile scales: the codes of K-step k, token block tb, K-block hh are columns 64k + 32hh ..,
+    // block 2k + hh of token half tb; the exponent field of the stored power of two is the
+    // E8M0 operand scale
+    const uint32_t sa_addr = T + (uint32_t)(kPage8 + 256 * wave + 4 * hh);
+    auto kscale = [&](int f) -> int {
+      if constexpr (Block) return (int)(lds_u32(sa_addr + 4u * (uint32_t)(kTileCols * (f & 1) + 2 * (f >> 1))) >> 23);
+      else return one;
+    };
     auto kfrag = [&](int f) -> i32x8 {   // K-step f/2, token block f%2
       const uint32_t o = 64u * (f >> 1) + (uint32_t)(32 * kRow) * (f & 1);
       const u32x4 lo = lds_b128(a0 + o), hi = lds_b128(a1 + o);
@@ -978,18 +998,26 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_fp8_kernel(DecodeArgs a) {
     // two fragments are read ahead
     constexpr int D = 1;
     i32x8 kr[D + 1];
+    int ks[D + 1];
 #pragma unroll
-    for (int d = 0; d < D; ++d) kr[d] = kfrag(d);
+    for (int d = 0; d < D; ++d) {
+      kr[d] = kfrag(d);
+      ks[d] = kscale(d);
+    }
 #pragma unroll
     for (int f = 0; f < 18; ++f) {
-      if (f + D < 18) kr[(f + D) % (D + 1)] = kfrag(f + D);
+      if (f + D < 18) {
+        kr[(f + D) % (D + 1)] = kfrag(f + D);
+        ks[(f + D) % (D + 1)] = kscale(f + D);
+      }
       const int k = f >> 1;
       f32x16& acc = (f & 1) ? s1 : s0;
+      const int sa = ks[f % (D + 1)];
       __builtin_amdgcn_sched_barrier(0);
-      acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kr[f % (D + 1)], qhi[k], acc, 0, 0, 0, one, 0, one);
+      acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kr[f % (D + 1)], qhi[k], acc, 0, 0, 0, sa, 0, one);
       hook(2 * f);
       __builtin_amdgcn_sched_barrier(0);
-      acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kr[f % (D + 1)], qlo[k], acc, 0, 0, 0, one, 0, lo_scale);
+      acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kr[f % (D + 1)], qlo[k], acc, 0, 0, 0, sa, 0, lo_scale);
       hook(2 * f + 1);
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -1023,7 +1051,10 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_fp8_kernel(DecodeArgs a) {
                         Soft& st) {
     const uint32_t sbase = lds_addr(tile) + kPage8 + 256 * wave + 16 * hl;
     // scales of tokens 32tb + 8u + 4hl + 0..3 (block d = 4tb + u)
-    auto scales = [&](int d) { return __builtin_bit_cast(f32x4, lds_b128(sbase + 128 * (d >> 2) + 32 * (d & 3))); };
+    auto scales = [&](int d) {
+      if constexpr (Block) return f32x4{1.0f, 1.0f, 1.0f, 1.0f};   // the scales ride in the matrix instructions
+      else return __builtin_bit_cast(f32x4, lds_b128(sbase + 128 * (d >> 2) + 32 * (d & 3)));
+    };
     auto umax = [](uint32_t x, uint32_t y) { return x > y ? x : y; };
     if (p == -1) {
       q.c[0] = scales(0);
@@ -1134,17 +1165,30 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_fp8_kernel(DecodeArgs a) {
       const i32x2 t3 = lds_tr8(xv[2 + (ct & 1)], o + 32 * kRow);
       return i32x8{t0[0], t0[1], t1[0], t1[1], t2[0], t2[1], t3[0], t3[1]};
     };
+    // tile scales: column tile ct is column block ct; K-block hl of the operand is token half hl
+    const uint32_t va_addr = lds_addr(tile) + (uint32_t)(kPage8 + 256 * wave + 4 * kTileCols * (ln >> 5));
+    auto vscale = [&](int ct) -> int {
+      if constexpr (Block) return (int)(lds_u32(va_addr + 4u * (uint32_t)ct) >> 23);
+      else return one;
+    };
     constexpr int D = 1;
     i32x8 vr[D + 1];
+    int vs[D + 1];
 #pragma unroll
-    for (int d = 0; d < D; ++d) vr[d] = vfrag(d);
+    for (int d = 0; d < D; ++d) {
+      vr[d] = vfrag(d);
+      vs[d] = vscale(d);
+    }
     hook(-1);
 #pragma unroll
     for (int ct = 0; ct < 16; ++ct) {
-      if (ct + D < 16) vr[(ct + D) % (D + 1)] = vfrag(ct + D);
+      if (ct + D < 16) {
+        vr[(ct + D) % (D + 1)] = vfrag(ct + D);
+        vs[(ct + D) % (D + 1)] = vscale(ct + D);
+      }
       __builtin_amdgcn_sched_barrier(0);
-      mfma8_acc(oacc[ct], vr[ct % (D + 1)], pf, one, sb);
-      mfma8_acc(oacc[ct], vr[ct % (D + 1)], pfl, one, sb - 4);   // lo term: block scale 2^(e-4)
+      mfma8_acc(oacc[ct], vr[ct % (D + 1)], pf, vs[ct % (D + 1)], sb);
+      mfma8_acc(oacc[ct], vr[ct % (D + 1)], pfl, vs[ct % (D + 1)], sb - 4);   // lo term: block scale 2^(e-4)
       hook(ct);
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -1163,7 +1207,7 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_fp8_kernel(DecodeArgs a) {
     psb = st.sb;
   };
   auto load_for = [&](int stage, int pg, int nv) {
-    return page_load8(smem + stage * kStage8, a.cache, a.cache_scale, nv > 0 ? pg : 0, nv);
+    return page_load8<Block>(smem + stage * kStage8, a.cache, a.cache_scale, nv > 0 ? pg : 0, nv);
   };
   // this lane's entry of row load i in the source-offset table
   const uint32_t src_addr = lds_addr(smem + kSrcTab8) + (uint32_t)(1152 * (wave & 1) + 2 * lane);
@@ -1282,15 +1326,20 @@ __device__ void exact_head(const DecodeArgs& a, int b, int j, int h, int L, int 
     if (pg < 0 || pg >= a.num_blocks) return -1;
     return (long long)pg * kBlock + t % kBlock;
   };
+  // value of column c of slot sl (tile scales: the page's tile of token half (sl % 64) / 32 and
+  // column block c / 32; token scales multiply whole scores and weights below)
   auto elem = [&](long long sl, int c) -> float {
-    return a.fp8 ? e4m3_to_f32(a.cache[sl * kRow + c]) : bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(a.cache)[sl * kRow + c]);
+    if (!a.fp8) return bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(a.cache)[sl * kRow + c]);
+    const float v = e4m3_to_f32(a.cache[sl * kRow + c]);
+    if (!a.block8) return v;
+    return v * a.cache_scale[((sl / kBlock) * 2 + (sl % kBlock) / 32) * kTileCols + c / 32];
   };
+  auto token_scale = [&](long long sl) { return (a.fp8 && !a.block8) ? a.cache_scale[sl] : 1.0f; };
   auto score = [&](long long sl) {
     float d = 0.f;
 #pragma unroll
     for (int i = 0; i < 9; ++i) d += qv[i] * elem(sl, 9 * lane + i);
-    const float cs = a.fp8 ? a.cache_scale[sl] : 1.0f;
-    return wave_sum(d) * cs * a.scale_log2;
+    return wave_sum(d) * token_scale(sl) * a.scale_log2;
   };
   float mx = -INFINITY;
   for (int t = 0; t < n; ++t) {
@@ -1306,7 +1355,7 @@ __device__ void exact_head(const DecodeArgs& a, int b, int j, int h, int L, int 
       if (sl < 0) continue;
       const float w = __builtin_amdgcn_exp2f(score(sl) - mx);
       l += w;
-      const float wc = a.fp8 ? w * a.cache_scale[sl] : w;
+      const float wc = w * token_scale(sl);
       acc0 += wc * elem(sl, col);
       acc1 += wc * elem(sl, col + 1);
     }
@@ -1582,7 +1631,8 @@ int decode_num_ranges(int num_cus, int B, int Sq, int max_blocks, bool fp8) {
 
 size_t decode_workspace_bytes(const mla_config_t& cfg, int num_cus, int B, int Sq, int max_blocks) {
   if (!(cfg.cache_dtype != MLA_F32 && is_dsv2_shape(cfg))) return 256;   // generic path: none needed
-  const int G = decode_num_ranges(num_cus, B, Sq, max_blocks, cfg.cache_dtype == MLA_FP8_E4M3);
+  const int G = decode_num_ranges(num_cus, B, Sq, max_blocks,
+                                  cfg.cache_dtype == MLA_FP8_E4M3 || cfg.cache_dtype == MLA_FP8_E4M3_B32);
   const size_t slots = (size_t)(G + B - 1) * Sq;
   const size_t o_bytes = slots * kH * kDC * sizeof(uint16_t);
   const size_t l_bytes = slots * kH * 2 * sizeof(float);
@@ -1604,9 +1654,10 @@ hipError_t set_decode_lds_limits() {
   if (e != hipSuccess) return e;
   std::atomic<int>* mark = (dev >= 0 && dev < kMaxDev) ? &g_lds_set[dev] : nullptr;
   if (mark && mark->load(std::memory_order_acquire)) return hipSuccess;
-  const void* kernels[4] = {(const void*)decode_mfma_bf16_kernel<0>, (const void*)decode_mfma_bf16_kernel<2>,
-                            (const void*)decode_mfma_fp8_kernel<0>, (const void*)decode_mfma_fp8_kernel<2>};
-  for (int k = 0; k < 4; ++k) {
+  const void* kernels[6] = {(const void*)decode_mfma_bf16_kernel<0>,       (const void*)decode_mfma_bf16_kernel<2>,
+                            (const void*)decode_mfma_fp8_kernel<0, false>, (const void*)decode_mfma_fp8_kernel<2, false>,
+                            (const void*)decode_mfma_fp8_kernel<0, true>,  (const void*)decode_mfma_fp8_kernel<2, true>};
+  for (int k = 0; k < 6; ++k) {
     e = hipFuncSetAttribute(kernels[k], hipFuncAttributeMaxDynamicSharedMemorySize, k < 2 ? kDecodeLds : kDecodeLds8);
     if (e != hipSuccess) return e;
   }
@@ -1619,7 +1670,8 @@ hipError_t launch_decode(const mla_config_t& cfg, int num_cus, const void* q_abs
                          float* lse, hipStream_t stream, int phases) {
   if (B == 0) return hipSuccess;
   const float scale = cfg.softmax_scale;
-  const bool fp8 = cfg.cache_dtype == MLA_FP8_E4M3;
+  const bool block8 = cfg.cache_dtype == MLA_FP8_E4M3_B32;
+  const bool fp8 = cfg.cache_dtype == MLA_FP8_E4M3 || block8;
   if ((cfg.cache_dtype == MLA_BF16 || fp8) && is_dsv2_shape(cfg)) {
     DecodeArgs a;
     a.q_abs = static_cast<const uint16_t*>(q_abs);
@@ -1641,6 +1693,7 @@ hipError_t launch_decode(const mla_config_t& cfg, int num_cus, const void* q_abs
     a.G = G;
     a.scale_log2 = scale * 1.4426950408889634f;
     a.fp8 = fp8 ? 1 : 0;
+    a.block8 = block8 ? 1 : 0;
     a.seg_w = fp8 ? kSegCost8 : kSegCost;
     {
       hipError_t e = set_decode_lds_limits();
@@ -1649,11 +1702,16 @@ hipError_t launch_decode(const mla_config_t& cfg, int num_cus, const void* q_abs
     if (phases & 1) {
       // non-temporal page loads when no other workgroup reads the same pages (one query)
       const dim3 grid(G * Sq), block(64 * kWaves);
-      if (fp8) {
+      if (block8) {
         if (Sq == 1)
-          hipLaunchKernelGGL(decode_mfma_fp8_kernel<2>, grid, block, kDecodeLds8, stream, a);
+          hipLaunchKernelGGL((decode_mfma_fp8_kernel<2, true>), grid, block, kDecodeLds8, stream, a);
         else
-          hipLaunchKernelGGL(decode_mfma_fp8_kernel<0>, grid, block, kDecodeLds8, stream, a);
+          hipLaunchKernelGGL((decode_mfma_fp8_kernel<0, true>), grid, block, kDecodeLds8, stream, a);
+      } else if (fp8) {
+        if (Sq == 1)
+          hipLaunchKernelGGL((decode_mfma_fp8_kernel<2, false>), grid, block, kDecodeLds8, stream, a);
+        else
+          hipLaunchKernelGGL((decode_mfma_fp8_kernel<0, false>), grid, block, kDecodeLds8, stream, a);
       } else {
         if (Sq == 1)
           hipLaunchKernelGGL(decode_mfma_bf16_kernel<2>, grid, block, kDecodeLds, stream, a);

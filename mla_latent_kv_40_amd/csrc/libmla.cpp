@@ -69,8 +69,8 @@ mla_status_t check_cfg(const mla_config_t* c) {
   if (!(c->softmax_scale > 0.0f) || !(c->rope_base > 0.0f)) return MLA_ERR_INVALID_ARG;
   const bool f32 = c->cache_dtype == MLA_F32 && c->act_dtype == MLA_F32;
   const bool bf16 = c->cache_dtype == MLA_BF16 && c->act_dtype == MLA_BF16;
-  const bool fp8 = c->cache_dtype == MLA_FP8_E4M3 && c->act_dtype == MLA_BF16;
-  if (c->cache_dtype < 0 || c->cache_dtype > 2 || c->act_dtype < 0 || c->act_dtype > 1) return MLA_ERR_INVALID_ARG;
+  const bool fp8 = (c->cache_dtype == MLA_FP8_E4M3 || c->cache_dtype == MLA_FP8_E4M3_B32) && c->act_dtype == MLA_BF16;
+  if (c->cache_dtype < 0 || c->cache_dtype > 3 || c->act_dtype < 0 || c->act_dtype > 1) return MLA_ERR_INVALID_ARG;
   if (!(f32 || bf16 || fp8)) return MLA_ERR_UNSUPPORTED;
   if (fp8 && !mla::is_dsv2_shape(*c)) return MLA_ERR_UNSUPPORTED;
   if (!mla::is_dsv2_shape(*c)) {
@@ -85,7 +85,7 @@ mla_status_t from_hip(hipError_t e) { return e == hipSuccess ? MLA_OK : MLA_ERR_
 
 extern "C" {
 
-int32_t mla_abi_version(void) { return 6; }
+int32_t mla_abi_version(void) { return 7; }
 
 const char* mla_status_string(mla_status_t s) {
   switch (s) {
@@ -109,7 +109,7 @@ static mla_status_t check_append(const mla_config_t* cfg, void* cache, float* ca
   if (!aligned16(cache) || !aligned16(block_table)) return MLA_ERR_INVALID_ARG;
   if (n > 0 && (!aligned16(c_kv) || !aligned16(k_r) || !aligned16(pos) || !aligned16(seq_of)))
     return MLA_ERR_INVALID_ARG;
-  const bool fp8 = cfg->cache_dtype == MLA_FP8_E4M3;
+  const bool fp8 = cfg->cache_dtype == MLA_FP8_E4M3 || cfg->cache_dtype == MLA_FP8_E4M3_B32;
   if (fp8 != (cache_scale != nullptr)) return MLA_ERR_INVALID_ARG;
   if (cache_scale && !aligned16(cache_scale)) return MLA_ERR_INVALID_ARG;
   return MLA_OK;
@@ -188,7 +188,7 @@ static mla_status_t decode_common(const mla_config_t* cfg, const void* q_abs, co
   if (!aligned16(q_abs) || !aligned16(cache) || !aligned16(o_lat) || !aligned16(lse) || !aligned16(kv_lens) ||
       !aligned16(block_table))
     return MLA_ERR_INVALID_ARG;
-  const bool fp8 = cfg->cache_dtype == MLA_FP8_E4M3;
+  const bool fp8 = cfg->cache_dtype == MLA_FP8_E4M3 || cfg->cache_dtype == MLA_FP8_E4M3_B32;
   if (fp8 != (cache_scale != nullptr)) return MLA_ERR_INVALID_ARG;
   if (cache_scale && !aligned16(cache_scale)) return MLA_ERR_INVALID_ARG;
   const int cus = current_cu_count();

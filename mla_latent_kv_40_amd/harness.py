@@ -47,9 +47,10 @@ class DecodeState:
 
         # paged cache
         nb = batch.num_blocks
-        if w.dtype == "fp8":
+        if w.fp8:
             self.cache = torch.empty((nb, wl.BLOCK, w.row), dtype=torch.uint8, device=device)
-            self.cache_scale = torch.empty((nb, wl.BLOCK), dtype=torch.float32, device=device)
+            shape = (nb, wl.BLOCK) if w.dtype == "fp8" else (nb, wl.BLOCK // 32, w.row // 32)
+            self.cache_scale = torch.empty(shape, dtype=torch.float32, device=device)
         else:
             self.cache = torch.empty((nb, wl.BLOCK, w.row), dtype=act, device=device)
             self.cache_scale = None

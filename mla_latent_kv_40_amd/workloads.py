@@ -44,7 +44,9 @@ class Workload:
     d_r: int                # decoupled RoPE dim
     d_c: int                # latent dim
     d_v: int                # per-head value dim
-    dtype: str              # "f32" | "bf16" | "fp8" (cache format; activations bf16 for fp8)
+    dtype: str              # "f32" | "bf16" | "fp8" | "fp8b" (cache format; activations bf16 for fp8:
+                            # "fp8" one scale per token, "fp8b" one power-of-two scale per tile of
+                            # 32 tokens x 32 columns)
     ctx_lo: int             # context before the step's new tokens (inclusive range)
     ctx_hi: int
     d_model: Optional[int] = None   # set only for the tiny case, whose inputs start at x
@@ -63,6 +65,20 @@ class Workload:
     @property
     def act_dtype(self) -> str:
         return "f32" if self.dtype == "f32" else "bf16"
+
+    @property
+    def fp8(self) -> bool:
+        return self.dtype in ("fp8", "fp8b")
+
+    @property
+    def cache_bytes_per_token(self) -> float:
+        """Row bytes plus the scales' share: 4 per token (fp8), 36 scales x 4 bytes per 64-token
+        page (fp8b)."""
+        if self.dtype == "fp8":
+            return self.row + 4.0
+        if self.dtype == "fp8b":
+            return self.row + 4.0 * 2 * (self.row // 32) / BLOCK
+        return self.row * (2.0 if self.dtype == "bf16" else 4.0)
 
 
 def _ds(name, seed, batch, sq, dtype, lo, hi, desc):
@@ -87,6 +103,10 @@ WORKLOADS: Dict[str, Workload] = {
     "dsv2_b128_l8k_fp8": _ds("dsv2_b128_l8k_fp8", 4, 128, 1, "fp8", 8191, 8191,
                              "DeepSeek-V2 shapes, fp8 e4m3 cache with per-token scale, B=128, "
                              "context 8192"),
+    # the same step and inputs with the block-scaled fp8 cache (32 x 32 tiles, power-of-two scales)
+    "dsv2_b128_l8k_fp8b": _ds("dsv2_b128_l8k_fp8b", 4, 128, 1, "fp8b", 8191, 8191,
+                              "DeepSeek-V2 shapes, fp8 e4m3 cache with a power-of-two scale per tile of "
+                              "32 tokens x 32 columns, B=128, context 8192"),
     # not one of the decode configurations: a chunk of prompt tokens extended in one step
     "dsv2_b4_l8k_sq512": _ds("dsv2_b4_l8k_sq512", 5, 4, 512, "bf16", 8192, 8192,
                              "DeepSeek-V2 shapes, bf16, chunked prefill: B=4, context 8192 + a chunk of "

@@ -27,11 +27,11 @@ article, section "Implementation Logic"):
 
 Readings of points the pages leave open (each also listed in the design notes):
 
-1. "concatenating or adding" the content and positional key (bembew, "Implementation
+1. The page allows either joining or summing the content and positional key (bembew, "Implementation
    Logic", step 5): read as concatenation, so the two dot products add.
 2. k_R is one vector per token shared by all heads (bembew "Decoupling RoPE",
-   talentme "Core Definition", the podcast's "compact latent plus the smaller
-   positional component"); q^R is per head (zenaique follow-up question
+   talentme "Core Definition", and the podcast, which caches the latent next to one
+   small positional part); q^R is per head (zenaique follow-up question
    "Why does MLA need a decoupled RoPE key").
 3. RoPE is not defined on the pages (bembew calls ``apply_rope`` without a body):
    textbook rotary embedding with interleaved pairs (2j, 2j+1) rotated by
@@ -290,10 +290,9 @@ def e4m3_round(x: np.ndarray) -> np.ndarray:
     """Nearest OCP e4m3fn value (ties to even, saturating at +-448), as float64.
 
     e4m3fn: 1 sign, 4 exponent bits (bias 7), 3 mantissa bits, no infinities;
-    normals 2^-6 .. 448, subnormals multiples of 2^-9.  Storing the latent in
-    a reduced-precision format composes with MLA (katajob "Compression as
-    architecture versus compression as post-processing": the latent "can
-    itself be stored in a reduced-precision format").
+    normals 2^-6 .. 448, subnormals multiples of 2^-9.  Storing the latent at
+    lower precision composes with MLA (katajob, section "Compression as
+    architecture versus compression as post-processing").
     """
     x = np.asarray(x, dtype=np.float64)
     a = np.abs(x)
@@ -328,8 +327,8 @@ def quantize_rows_fp8(rows: np.ndarray):
 # ------------------------------------------------- block-scaled fp8 e4m3 storage
 #
 # The katajob page (section "Compression as architecture versus compression as post-processing")
-# names per-block scaling as what makes a quantised cache work and says a latent can itself be
-# stored in a reduced-precision format.  The block-scaled format reads that as: the cache rows of
+# counts per-block scales among what a quantised cache depends on, and has a low-precision latent
+# compose with MLA.  The block-scaled format reads that as: the cache rows of
 # a page are cut into tiles of 32 tokens x 32 columns, each tile has one power-of-two scale
 # 2^e, and each value is stored as the e4m3 code of value / 2^e.  Tokens arrive one call at a
 # time, so a tile's scale is decided by the rows it holds so far: a call takes, for each tile it
@@ -398,8 +397,8 @@ def mha_cache_elements_per_token(heads: int, d_head: int) -> int:
 
 
 def mla_cache_elements_per_token(d_c: int, d_r: int) -> int:
-    """The latent plus the decoupled positional key (podcast: "caches the compact latent and
-    positional part")."""
+    """The latent plus the decoupled positional key (the podcast: both, and nothing else, are
+    cached per token)."""
     return d_c + d_r
 
 

@@ -81,9 +81,13 @@ def host(st):
     return {"o": st.out.float().cpu().numpy(), "o_lat": st.o_lat.cpu().numpy(), "lse": st.lse.cpu().numpy()}
 
 
-def dsv2(batch, lengths, sq=1, seed=7, name="dsv2_b16_l4k", fp8=False):
-    if fp8:
+def dsv2(batch, lengths, sq=1, seed=7, name="dsv2_b16_l4k", fp8=False, fmt=None):
+    """A DeepSeek-V2-shaped batch with the given lengths; fp8=True or fmt="fp8" takes the cache
+    with token scales, fmt="fp8b" the one with tile scales."""
+    if fp8 or fmt == "fp8":
         name = "dsv2_b128_l8k_fp8"
+    elif fmt == "fp8b":
+        name = "dsv2_b128_l8k_fp8b"
     w = wl.get(name, batch=batch, sq=sq, seed=seed, ctx_lo=0, ctx_hi=0)
     bt = wl.draw_batch(w)
     # replace the lengths with the requested ones (context + sq), rebuilding the page table
@@ -99,3 +103,54 @@ def dsv2(batch, lengths, sq=1, seed=7, name="dsv2_b16_l4k", fp8=False):
     bt = wl.Batch(w=w, kv_lens=kv, block_table=table, num_blocks=int(nblk.sum()), weights=bt.weights)
     seqs = harness.draw_all_sequences(w, bt)
     return w, bt, seqs
+
+
+# --------------------------------------------------------------------------- cache contents
+
+CHUNK_TOKENS = 1 << 18   # DecodeState.fill_context's default chunk
+
+
+def append_calls(w, bt, b, chunk_tokens=CHUNK_TOKENS):
+    """Position ranges [p0, p1) of sequence b in the order the harness appends them: its context
+    as cut by fill_context's chunks of the concatenated contexts, then the step's new tokens."""
+    kv = bt.kv_lens.astype(np.int64)
+    n_ctx = np.maximum(kv - w.sq, 0)
+    start = int(n_ctx[:b].sum())
+    calls, p = [], 0
+    while p < n_ctx[b]:
+        g = start + p
+        end = min((g // chunk_tokens + 1) * chunk_tokens, start + int(n_ctx[b]))
+        calls.append((p, end - start))
+        p = end - start
+    L = int(kv[b])
+    if L > n_ctx[b]:
+        calls.append((int(n_ctx[b]), L))
+    return calls
+
+
+def cache_rows(w, bt, seqs, b, chunk_tokens=CHUNK_TOKENS):
+    """The rows [c ; RoPE(k_R)] of sequence b as the cache holds them, by the oracle: fp64 for a
+    bf16 cache, dequantised with the oracle's quantiser for an fp8 one (tile scales: the
+    harness's append calls replayed through oracle.append_block_fp8)."""
+    s = seqs[b]
+    L = int(bt.kv_lens[b])
+    t = np.arange(L)
+    rows = np.concatenate([s["c"][:L].astype(np.float64), orc.rope(s["k_r"][:L], t, w.rope_base)], axis=1)
+    if w.dtype == "fp8":
+        codes, scale = orc.quantize_rows_fp8(rows)
+        return codes * scale.astype(np.float64)[:, None]
+    if w.dtype == "fp8b":
+        codes, exps = block_cache(w, rows, append_calls(w, bt, b, chunk_tokens))
+        return orc.dequantize_block_fp8(codes, exps, L)
+    return rows
+
+
+def block_cache(w, rows, calls):
+    """Codes and tile exponents of one sequence after the append calls (oracle)."""
+    L = rows.shape[0]
+    cap = ((L + 63) // 64) * 64
+    codes = np.zeros((cap, w.row))
+    exps = np.zeros((cap // 32, w.row // 32), dtype=np.int64)
+    for p0, p1 in calls:
+        orc.append_block_fp8(codes, exps, rows[p0:p1], p0)
+    return codes, exps

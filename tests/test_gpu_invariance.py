@@ -15,7 +15,7 @@ import pytest
 
 import oracle.mla_oracle as orc
 from mla_latent_kv_40_amd import binding as B, harness, workloads as wl
-from _common import check, dsv2, host, log, oracle_for, run_state
+from _common import cache_rows, check, dsv2, host, log, oracle_for, run_state
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -60,10 +60,7 @@ def weighted_spread(w, bt, seqs, b, heads):
     s = seqs[b]
     L = int(bt.kv_lens[b])
     t = np.arange(L)
-    rows = np.concatenate([s["c"][:L].astype(np.float64), orc.rope(s["k_r"][:L], t, w.rope_base)], axis=1)
-    if w.dtype == "fp8":
-        codes, scale = orc.quantize_rows_fp8(rows)
-        rows = codes * scale.astype(np.float64)[:, None]
+    rows = cache_rows(w, bt, seqs, b)
     pos_q = L - w.sq + np.arange(w.sq)
     qa = orc.absorbed_query(s["q_c"], s["q_r"], bt.weights["W_UK"], pos_q, w.rope_base)[:, list(heads)]
     sc = np.einsum("jhk,tk->jht", qa, rows) * w.softmax_scale
@@ -77,8 +74,8 @@ def weighted_spread(w, bt, seqs, b, heads):
     return D, A, float(np.abs(C).max())
 
 
-@pytest.mark.parametrize("fp8", [False, True])
-def test_split_count_invariance(fp8):
+@pytest.mark.parametrize("fmt", ["bf16", "fp8", "fp8b"])
+def test_split_count_invariance(fmt):
     """A different cut changes each segment's softmax reference and so the rounding of the
     probabilities fed to the value product (bf16: relative 2^-9, and l sums the same rounded
     values; fp8: hi + lo/16 e4m3 terms, relative 2^-8, l summed unrounded) and of the bf16
@@ -88,9 +85,10 @@ def test_split_count_invariance(fp8):
     fp32 sums).  lse moves only with l: by at most 2 u'.  Ranges tried: the fewest the page table
     allows, an odd count that is not a multiple of the XCD count, the default, and one page per
     range."""
-    log(f"case split-count invariance, fp8={fp8}: lengths [20000, 9000, 3001, 777, 65]")
+    log(f"case split-count invariance, cache {fmt}: lengths [20000, 9000, 3001, 777, 65]")
     lengths = [20000, 9000, 3001, 777, 65]
-    w, bt, seqs = dsv2(5, lengths, seed=71, fp8=fp8)
+    w, bt, seqs = dsv2(5, lengths, seed=71, fmt=None if fmt == "bf16" else fmt)
+    fp8 = w.fp8
     st = run_state(w, bt, seqs)
     cap = w.batch * bt.max_blocks
     runs = {}

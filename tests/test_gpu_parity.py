@@ -11,7 +11,7 @@ import pytest
 
 import oracle.mla_oracle as orc
 from mla_latent_kv_40_amd import harness, workloads as wl
-from _common import check, dsv2, host, log, oracle_for, run_state, tiny_sequences
+from _common import bound, cache_rows, check, dsv2, host, log, oracle_for, run_state, tiny_sequences
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -31,17 +31,28 @@ def compare_seq(w, bt, seqs, got, b, heads=None, factor=1.0, weights=None, tag="
     and lse, each under max|gpu - oracle| <= factor * (2e-2 max|oracle| + 1e-3), factor 4 for
     an fp8 cache (the oracle then sees the values before quantisation, so the gate covers the
     whole method).  For an fp8 cache a second check runs the oracle on the dequantised cache
-    rows (codes x scale from the oracle's own quantiser) at the bf16 rule: what remains there is
-    the kernel's own arithmetic (its e4m3 query and probability terms), not the storage."""
+    rows (codes x scales from the oracle's own quantiser) at the bf16 rule: what remains there is
+    the kernel's own arithmetic (its e4m3 query and probability terms), not the storage.  Where
+    the storage alone (the oracle on the dequantised rows against the oracle on the exact ones)
+    already exceeds the x4 bound, the format cannot meet it whatever the kernel does: that output
+    is logged and left to the second check."""
     ref = oracle_for(w, bt, seqs, b, heads=heads, weights=weights)
     sl = slice(b * w.sq, (b + 1) * w.sq)
     hs = slice(None) if heads is None else list(heads)
     g = {k: v[sl][:, hs] for k, v in got.items()}
-    r = check(f"{tag}b{b} o", g["o"], ref["o"], factor)
-    check(f"{tag}b{b} o_lat", g["o_lat"], ref["o_lat"], factor)
-    check(f"{tag}b{b} lse", g["lse"], ref["lse"], factor)
-    if w.dtype == "fp8":
-        deq = oracle_dequantised(w, bt, seqs, b, heads=heads, weights=weights)
+    deq = oracle_dequantised(w, bt, seqs, b, heads=heads, weights=weights) if w.fp8 else None
+    r = 0.0
+    for k in ("o", "o_lat", "lse"):
+        if deq is not None:
+            storage = float(np.max(np.abs(deq[k] - ref[k]))) / bound(ref[k], factor)
+            if storage > 1.0:
+                log(f"  {tag}b{b} {k}: storage alone is {storage:.3f} of the x{factor:g} bound (format limit); "
+                    f"gpu is {float(np.max(np.abs(g[k] - ref[k]))) / bound(ref[k], factor):.3f} of it")
+                continue
+        rk = check(f"{tag}b{b} {k}", g[k], ref[k], factor)
+        if k == "o":
+            r = rk
+    if deq is not None:
         for k in ("o", "o_lat", "lse"):
             check(f"{tag}b{b} {k} vs dequantised cache", g[k], deq[k])
     return r
@@ -49,14 +60,12 @@ def compare_seq(w, bt, seqs, got, b, heads=None, factor=1.0, weights=None, tag="
 
 def oracle_dequantised(w, bt, seqs, b, heads=None, weights=None):
     """The oracle on the rows an fp8 cache holds: [c ; RoPE(k_R)] quantised by the oracle's
-    e4m3 row quantiser and multiplied back by the scale (the stored k_R is already rotated)."""
+    e4m3 quantiser (per token, or per tile over the harness's append calls) and multiplied back
+    by the scales (the stored k_R is already rotated)."""
     W = weights if weights is not None else bt.weights
     s = seqs[b]
     L = int(bt.kv_lens[b])
-    t = np.arange(L)
-    rows = np.concatenate([s["c"][:L].astype(np.float64), orc.rope(s["k_r"][:L], t, w.rope_base)], axis=1)
-    codes, scale = orc.quantize_rows_fp8(rows)
-    deq = codes * scale.astype(np.float64)[:, None]
+    deq = cache_rows(w, bt, seqs, b)
     return orc.decode(deq[:, :w.d_c], deq[:, w.d_c:], s["q_c"], s["q_r"], W["W_UK"], W["W_UV"], L,
                       w.softmax_scale, w.rope_base, heads=heads, keys_rotated=True)
 
@@ -337,6 +346,7 @@ def test_fp8_extreme_scores_take_the_exact_path():
     ("dsv2_b64_l32k", [(0, range(0, 128, 16)), (63, range(7, 128, 16))]),
     ("dsv2_b32_l8k_sq4", [(0, range(0, 128, 8)), (31, range(5, 128, 16))]),
     ("dsv2_b128_l8k_fp8", [(0, range(0, 128, 8)), (127, range(5, 128, 16))]),
+    ("dsv2_b128_l8k_fp8b", [(0, range(0, 128, 8)), (127, range(5, 128, 16))]),
 ])
 def test_full_size_sampled(name, sample):
     w = wl.get(name)
@@ -352,4 +362,4 @@ def test_full_size_sampled(name, sample):
         elif b == "longest":
             b = int(np.argmax(bt.kv_lens))
         log(f"  oracle on sequence {b} (kv_len {int(bt.kv_lens[b])})")
-        compare_seq(w, bt, seqs, got, b, heads=heads, factor=FP8 if w.dtype == "fp8" else 1.0)
+        compare_seq(w, bt, seqs, got, b, heads=heads, factor=FP8 if w.fp8 else 1.0)
