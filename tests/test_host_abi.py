@@ -49,6 +49,8 @@ FAKE = 1 << 20   # aligned non-null address: never dereferenced because validati
     (dict(cache_dtype="fp8", act_dtype="f32"), B.MLA_ERR_UNSUPPORTED),
     (dict(cache_dtype="bf16", act_dtype="f32"), B.MLA_ERR_UNSUPPORTED),
     (dict(cache_dtype="fp8", num_heads=64), B.MLA_ERR_UNSUPPORTED),
+    (dict(cache_dtype="fp8b", act_dtype="f32"), B.MLA_ERR_UNSUPPORTED),
+    (dict(cache_dtype="fp8b", num_heads=64), B.MLA_ERR_UNSUPPORTED),
     (dict(cache_dtype="f32", act_dtype="f32", num_heads=256, d_c=64, d_r=16, d_h=64, d_v=64),
      B.MLA_ERR_UNSUPPORTED),
 ])
@@ -71,6 +73,12 @@ def test_pointer_and_size_validation(L):
     c8 = cfg(cache_dtype="fp8")
     dec = [100, FAKE, 512, FAKE, 64, 1, FAKE, 1 << 30, FAKE, FAKE]
     assert B.mla_decode_attn(c8, FAKE, FAKE, None, *dec, stream=0, check=False) == B.MLA_ERR_INVALID_ARG
+    c8b = cfg(cache_dtype="fp8b")
+    assert B.mla_decode_attn(c8b, FAKE, FAKE, None, *dec, stream=0, check=False) == B.MLA_ERR_INVALID_ARG
+    assert B.mla_cache_append(c8b, FAKE, None, 8, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 4, 3, stream=0,
+                              check=False) == B.MLA_ERR_INVALID_ARG
+    assert B.mla_cache_append(c8b, FAKE, FAKE + 4, 8, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 4, 3, stream=0,
+                              check=False) == B.MLA_ERR_INVALID_ARG          # misaligned scales
     assert B.mla_decode_attn(c, FAKE, FAKE, FAKE, *dec, stream=0, check=False) == B.MLA_ERR_INVALID_ARG
     assert B.mla_cache_append(c, FAKE, FAKE, 8, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 4, 3, stream=0,
                               check=False) == B.MLA_ERR_INVALID_ARG
