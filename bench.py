@@ -86,8 +86,13 @@ def measured_traffic(workload):
     return None
 
 
+READ_CLOCK = True   # --no-clock: no rocm-smi child (under a profiler, whose preload covers children)
+
+
 def gpu_clock_mhz():
-    """Current shader clock of GPU 0 from rocm-smi (None if it cannot be read)."""
+    """Current shader clock of GPU 0 from rocm-smi (None if it cannot be read or --no-clock)."""
+    if not READ_CLOCK:
+        return None
     smi = shutil.which("rocm-smi") or "/opt/rocm/bin/rocm-smi"
     try:
         r = subprocess.run([smi, "--showclocks", "--json"], capture_output=True, text=True, timeout=20)
@@ -402,10 +407,13 @@ def main() -> int:
     ap.add_argument("--workload", default="dsv2_b64_l1k_32k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-configs", action="store_true", help="skip the per-configuration measurements")
+    ap.add_argument("--no-clock", action="store_true", help="do not read the shader clock with rocm-smi")
     ap.add_argument("--warm", action="store_true", help="also time the steps without the cache flush")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a 256 MiB device-to-device copy 3 times (scales HBM counters)")
     a = ap.parse_args()
+    global READ_CLOCK
+    READ_CLOCK = not a.no_clock
     if a.calibrate_copy:
         import torch
         x = torch.empty(1 << 28, dtype=torch.uint8, device="cuda:0").fill_(1)
