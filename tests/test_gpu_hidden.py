@@ -50,9 +50,10 @@ class HiddenRun:
             off += int(nblk[b])
         self.block_table = dev(table, torch.int32)
         self.kv_lens = dev(kv.astype(np.int32), torch.int32)
-        if w.dtype == "fp8":
+        if w.fp8:
             self.cache = torch.empty((self.num_blocks, 64, w.row), dtype=torch.uint8, device="cuda")
-            self.cache_scale = torch.empty((self.num_blocks, 64), dtype=torch.float32, device="cuda")
+            shape = (self.num_blocks, 64) if w.dtype == "fp8" else (self.num_blocks, 2, w.row // 32)
+            self.cache_scale = torch.empty(shape, dtype=torch.float32, device="cuda")
         else:
             self.cache = torch.empty((self.num_blocks, 64, w.row), dtype=act, device="cuda")
             self.cache_scale = None
@@ -134,13 +135,14 @@ def test_tiny_f32_layer_from_hidden_states():
     check("tiny folded weights", got_f, Wf, extra_rel=1e-4)
 
 
-@pytest.mark.parametrize("fp8", [False, True])
-def test_dsv2_layer_from_hidden_states(fp8):
+@pytest.mark.parametrize("fmt", ["bf16", "fp8", "fp8b"])
+def test_dsv2_layer_from_hidden_states(fmt):
     d_model = 5120
     lengths = [300, 65, 1, 130]
-    name = "dsv2_b128_l8k_fp8" if fp8 else "dsv2_b16_l4k"
+    name = {"bf16": "dsv2_b16_l4k", "fp8": "dsv2_b128_l8k_fp8", "fp8b": "dsv2_b128_l8k_fp8b"}[fmt]
     w = wl.get(name, batch=len(lengths), seed=91)
-    log(f"case DeepSeek-V2 shapes from hidden states, d_model {d_model}, fp8={fp8}, lengths {lengths}")
+    fp8 = w.fp8
+    log(f"case DeepSeek-V2 shapes from hidden states, d_model {d_model}, cache {fmt}, lengths {lengths}")
     bt = wl.draw_batch(w)
     Hd = wl.draw_hidden(w, d_model, lengths)
     W = dict(Hd, W_UK=bt.weights["W_UK"], W_UV=bt.weights["W_UV"])

@@ -28,11 +28,12 @@ def _noalloc(st):
     return st.o_lat.clone(), st.lse.clone()
 
 
-@pytest.mark.parametrize("fp8", [False, True])
-def test_noalloc_equals_decode_attn_twice(fp8):
-    log(f"case mla_decode_attn_noalloc vs mla_decode_attn, fp8={fp8}: a batch of 6, then a batch of 2")
-    big = dsv2(6, [5000, 3001, 77, 1, 640, 2049], seed=81, fp8=fp8)
-    small = dsv2(2, [130, 64], seed=83, fp8=fp8)
+@pytest.mark.parametrize("fmt", ["bf16", "fp8", "fp8b"])
+def test_noalloc_equals_decode_attn_twice(fmt):
+    log(f"case mla_decode_attn_noalloc vs mla_decode_attn, cache {fmt}: a batch of 6, then a batch of 2")
+    f = None if fmt == "bf16" else fmt
+    big = dsv2(6, [5000, 3001, 77, 1, 640, 2049], seed=81, fmt=f)
+    small = dsv2(2, [130, 64], seed=83, fmt=f)
     states = [run_state(*big), run_state(*small)]   # each ran mla_decode_attn with its own workspace
     for st in states:
         assert st.ws_bytes <= B.NOALLOC_SCRATCH_BYTES
