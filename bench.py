@@ -51,9 +51,9 @@ METRIC = "MLA decode tokens/s + latent-cache GB/s & TFLOP/s (% peak) at B=64, 32
 FLUSH_BYTES = 512 << 20
 # the five decode workloads, smallest first (the first is latency-bound)
 CONFIGS = ["tiny_f32", "dsv2_b16_l4k", "dsv2_b64_l1k_32k", "dsv2_b32_l8k_sq4", "dsv2_b128_l8k_fp8"]
-# measured alongside them: a chunked prefill step (512 new tokens per sequence) and the fp8 step
-# with the block-scaled cache
-EXTRA_CONFIGS = ["dsv2_b4_l8k_sq512", "dsv2_b128_l8k_fp8b"]
+# measured alongside them: every context at 32768, a chunked prefill step (512 new tokens per
+# sequence) and the fp8 step with the block-scaled cache
+EXTRA_CONFIGS = ["dsv2_b64_l32k", "dsv2_b4_l8k_sq512", "dsv2_b128_l8k_fp8b"]
 
 
 def algorithmic(w, kv_lens):
@@ -396,6 +396,39 @@ def model_width_measurement(name, steps, flush, log, d_model=5120):
     return res
 
 
+def attainable(log):
+    """What the box reaches on plain library work, next to the published peaks: a 1 GiB
+    device-to-device copy (bytes read + written / time) and an 8192^3 bf16 matrix product
+    (torch.matmul, i.e. the vendor GEMM library).  Reference points only: neither is part of the
+    decode path."""
+    import torch
+    x = torch.empty(1 << 30, dtype=torch.uint8, device="cuda:0").fill_(1)
+    y = torch.empty_like(x)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(20)]
+    for _ in range(3):
+        y.copy_(x)
+    for a, b in evs:
+        a.record(); y.copy_(x); b.record()
+    torch.cuda.synchronize()
+    copy_ms = float(np.median([a.elapsed_time(b) for a, b in evs]))
+    del x, y
+    n = 8192
+    A = torch.randn((n, n), dtype=torch.bfloat16, device="cuda:0")
+    Bm = torch.randn((n, n), dtype=torch.bfloat16, device="cuda:0")
+    for _ in range(3):
+        C = A @ Bm
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(20)]
+    for a, b in evs:
+        a.record(); C = A @ Bm; b.record()
+    torch.cuda.synchronize()
+    mm_ms = float(np.median([a.elapsed_time(b) for a, b in evs]))
+    del A, Bm, C
+    r = {"copy_GBps": round(2 * (1 << 30) / (copy_ms * 1e-3) / 1e9, 1),
+         "bf16_gemm_8192_TFLOPs": round(2 * n ** 3 / (mm_ms * 1e-3) / 1e12, 1)}
+    log(f"[bench] attainable: {r}")
+    return r
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -463,6 +496,7 @@ def main() -> int:
     width = None
     if not a.no_configs and a.workload == "dsv2_b64_l1k_32k":
         width = model_width_measurement(a.workload, 20, flush, log)
+    reach = attainable(log) if not a.no_configs else None
 
     roof = dict(main_r["roofline"])
     roof["traffic"] = measured_traffic(main_r["workload"])
@@ -492,6 +526,8 @@ def main() -> int:
         line["kv_cache_comparison"] = kv_cmp
     if width:
         line["model_width_projections"] = width
+    if reach:
+        line["attainable"] = reach
     if "cpu_baseline" in main_r:
         line["cpu_baseline"] = main_r["cpu_baseline"]
     print(json.dumps(line), flush=True)
