@@ -75,16 +75,40 @@ __device__ __forceinline__ int pj_key(int r) { return (r >> 1) & 7; }   // bf16 
 // counters untouched)
 constexpr int pj_waitcnt_vm(int n) { return (n & 15) | (((n >> 4) & 3) << 14) | (7 << 4) | (15 << 8); }
 
+// One row GEMM of a launch.  A launch runs up to two of them (the latent and the query
+// projections of a step share one grid): workgroups wg0 .. wg0 + groups_n * S * row blocks - 1
+// belong to this one, as (output group, slice, row block) with the output group fastest.
 template <typename XT>
-__global__ void __launch_bounds__(256) rows_gemm_kernel(const XT* __restrict__ X, long long ldx,
-                                                        const uint16_t* __restrict__ Wt, int T, int N, int K, int S,
-                                                        PjOut o, float* __restrict__ part) {
+struct PjGemm {
+  const XT* X;
+  long long ldx;
+  const uint16_t* Wt;
+  PjOut o;
+  float* part;   // S > 1: fp32 partials [S][T][N]
+  int T, N, K, S, groups_n, wg0;
+};
+template <typename XT>
+struct PjJob {
+  PjGemm<XT> g[2];
+  int np;
+};
+
+template <typename XT>
+__global__ void __launch_bounds__(256) rows_gemm_kernel(PjJob<XT> job) {
   extern __shared__ __attribute__((aligned(256))) uint8_t pj_smem[];
   constexpr int SB = pj_stage_bytes<XT>();
   constexpr bool kF32 = sizeof(XT) == 4;
   constexpr int NX = kF32 ? 4 : 2;   // X loads per wave per chunk (1 KiB each)
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int n_base = kPjGroup * blockIdx.x, s = blockIdx.y, t0 = kPjT * blockIdx.z;
+  const int bid = blockIdx.x;
+  const PjGemm<XT> P = (job.np > 1 && bid >= job.g[1].wg0) ? job.g[1] : job.g[0];
+  const XT* __restrict__ X = P.X;
+  const uint16_t* __restrict__ Wt = P.Wt;
+  float* __restrict__ part = P.part;
+  const long long ldx = P.ldx;
+  const int T = P.T, N = P.N, K = P.K, S = P.S;
+  const int local = bid - P.wg0, xg = local % P.groups_n, rest = local / P.groups_n;
+  const int n_base = kPjGroup * xg, s = rest % S, t0 = kPjT * (rest / S);
   const int r = lane & 31, g = lane >> 5;
   const int n_chunks = K / kPjChunk;
   const int c0 = (int)((long long)s * n_chunks / S), c1 = (int)((long long)(s + 1) * n_chunks / S);
@@ -178,22 +202,26 @@ __global__ void __launch_bounds__(256) rows_gemm_kernel(const XT* __restrict__ X
     for (int e = 0; e < 16; ++e) {
       const int n = n_base + 64 * wave + 32 * nt + 8 * (e >> 2) + 4 * g + (e & 3);
       if (n < N && t < T) {
-        if (part != nullptr) part[((size_t)s * T + t) * N + n] = acc[i][e];
-        else pj_store<uint16_t>(o, t, n, acc[i][e]);
+        if (S > 1) part[((size_t)s * T + t) * N + n] = acc[i][e];
+        else pj_store<uint16_t>(P.o, t, n, acc[i][e]);
       }
     }
   }
 }
 
-// Y = sum over the S slices of part[s][t][n], in slice order, written through `o`.
-template <typename OutT>
-__global__ void __launch_bounds__(256) rows_reduce_kernel(const float* __restrict__ part, int T, int N, int S,
-                                                          PjOut o) {
-  const size_t total = (size_t)T * N;
-  for (size_t e = (size_t)blockIdx.x * 256 + threadIdx.x; e < total; e += (size_t)gridDim.x * 256) {
-    float v = 0.f;
-    for (int s = 0; s < S; ++s) v += part[(size_t)s * total + e];
-    pj_store<OutT>(o, (int)(e / N), (int)(e % N), v);
+// Y = sum over the S slices of part[s][t][n], in slice order, written through `o`, for every
+// GEMM of the job with S > 1 (their elements one after the other).
+template <typename XT>
+__global__ void __launch_bounds__(256) rows_reduce_kernel(PjJob<XT> job) {
+  for (int p = 0; p < job.np; ++p) {   // uniform: each GEMM's fields stay scalar
+    const PjGemm<XT> P = p == 0 ? job.g[0] : job.g[1];
+    if (P.S <= 1) continue;
+    const size_t total = (size_t)P.T * P.N;
+    for (size_t e = (size_t)blockIdx.x * 256 + threadIdx.x; e < total; e += (size_t)gridDim.x * 256) {
+      float v = 0.f;
+      for (int s = 0; s < P.S; ++s) v += P.part[(size_t)s * total + e];
+      pj_store<uint16_t>(P.o, (int)(e / P.N), (int)(e % P.N), v);
+    }
   }
 }
 
@@ -211,16 +239,27 @@ __global__ void __launch_bounds__(256) rows_gemm_generic_kernel(const XT* __rest
   }
 }
 
-// Slices of the contraction for a row GEMM.  One workgroup fits a compute unit (its LDS), so the
-// launch runs in rounds of num_cus workgroups: S is chosen to minimise the modelled time, rounds x
-// (chunks per slice + 3 chunks of pipeline fill) chunk loads per compute unit, plus the fp32
-// partials written and read back once (S x T x N x 8 bytes, spread over the whole chip).  Each
-// slice keeps at least four chunks.
-int rows_gemm_slices(int num_cus, int T, int N, int K) {
-  const long long groups = (long long)((N + kPjGroup - 1) / kPjGroup) * ((T + kPjT - 1) / kPjT);
+// Slices of the contraction for the row GEMMs of one launch (one S for all of them).  One
+// workgroup fits a compute unit (its LDS), so the launch runs in rounds of num_cus workgroups: S
+// minimises the modelled time, rounds x (chunks per slice + 3 chunks of pipeline fill) chunk loads
+// per compute unit, plus the fp32 partials written and read back once (S x T x N x 8 bytes, spread
+// over the whole chip).  Each slice keeps at least four chunks.
+struct PjShape {
+  int T, N, K;
+};
+int rows_gemm_slices(int num_cus, const PjShape* sh, int np) {
+  long long groups = 0, outputs = 0;
+  int chunks = 0;
+  for (int i = 0; i < np; ++i) {
+    groups += (long long)((sh[i].N + kPjGroup - 1) / kPjGroup) * ((sh[i].T + kPjT - 1) / kPjT);
+    outputs += (long long)sh[i].T * sh[i].N;
+    if (sh[i].K / kPjChunk > chunks) chunks = sh[i].K / kPjChunk;
+  }
   if (groups <= 0 || num_cus <= 0) return 1;   // nothing to compute
-  const int chunks = K / kPjChunk;
-  const long long S_max = chunks / 4 > 0 ? chunks / 4 : 1;
+  int min_chunks = chunks;
+  for (int i = 0; i < np; ++i)
+    if (sh[i].K / kPjChunk < min_chunks) min_chunks = sh[i].K / kPjChunk;
+  const long long S_max = min_chunks / 4 > 0 ? min_chunks / 4 : 1;
   const double chunk_bytes = (double)(kPjA + kPjT * kPjChunk * 2);
   long long best_S = 1;
   double best = -1.0;
@@ -228,16 +267,19 @@ int rows_gemm_slices(int num_cus, int T, int N, int K) {
     const long long rounds = (groups * S + num_cus - 1) / num_cus;
     const long long per = (chunks + S - 1) / S;
     const double cost = (double)rounds * (double)(per + 3) * chunk_bytes * num_cus +
-                        (S > 1 ? (double)S * T * N * 8.0 : 0.0);
+                        (S > 1 ? (double)S * outputs * 8.0 : 0.0);
     if (best < 0.0 || cost < best) { best = cost; best_S = S; }
   }
   return (int)best_S;
 }
 
-size_t rows_gemm_workspace(int num_cus, int T, int N, int K) {
-  const int S = rows_gemm_slices(num_cus, T, N, K);
+// Partials of the GEMMs of one launch, each in its own 256-byte aligned block.
+size_t rows_gemm_workspace(int num_cus, const PjShape* sh, int np) {
+  const int S = rows_gemm_slices(num_cus, sh, np);
   if (S <= 1) return 0;
-  return (((size_t)S * T * N * sizeof(float)) + 255) & ~(size_t)255;
+  size_t ws = 0;
+  for (int i = 0; i < np; ++i) ws += (((size_t)S * sh[i].T * sh[i].N * sizeof(float)) + 255) & ~(size_t)255;
+  return ws;
 }
 
 // The row GEMM takes more LDS than the default dynamic limit, raised once per device (an atomic
@@ -271,24 +313,53 @@ bool rows_gemm_offsets_fit(long long ldx, int K) {
   return (long long)kPjGroup * K * 2 < (1ll << 31) && (long long)kPjT * ldx * (long long)sizeof(XT) < (1ll << 31);
 }
 
-// Y = X . Wt^T through `o`, bf16 MFMA path (X bf16 or fp32, Wt bf16, K % 64 == 0).
+// One row GEMM's operands: Y = X . Wt^T through `o` (X [T, K] with row stride ldx, Wt [N, K] bf16).
 template <typename XT>
-hipError_t launch_rows_gemm(int num_cus, const XT* X, long long ldx, const uint16_t* Wt, int T, int N, int K,
-                            const PjOut& o, void* workspace, hipStream_t stream) {
-  if (!rows_gemm_offsets_fit<XT>(ldx, K))
-    return launch_rows_gemm_generic<XT, uint16_t, uint16_t>(X, ldx, Wt, T, N, K, o, stream);
-  const int S = rows_gemm_slices(num_cus, T, N, K);
-  float* part = S > 1 ? static_cast<float*>(workspace) : nullptr;
-  const dim3 grid((N + kPjGroup - 1) / kPjGroup, S, (T + kPjT - 1) / kPjT);
+struct PjArgs {
+  const XT* X;
+  long long ldx;
+  const uint16_t* Wt;
+  int T, N, K;
+  PjOut o;
+};
+
+// The row GEMMs in `a` (one or two, K % 64 == 0, every T > 0), bf16 MFMA path, in one launch
+// (plus one launch adding the slices' partials when S > 1).
+template <typename XT>
+hipError_t launch_rows_gemm(int num_cus, const PjArgs<XT>* a, int np, void* workspace, hipStream_t stream) {
+  for (int i = 0; i < np; ++i)
+    if (!rows_gemm_offsets_fit<XT>(a[i].ldx, a[i].K)) {   // too large for 32-bit buffer offsets
+      for (int j = 0; j < np; ++j) {
+        const hipError_t e =
+            launch_rows_gemm_generic<XT, uint16_t, uint16_t>(a[j].X, a[j].ldx, a[j].Wt, a[j].T, a[j].N, a[j].K, a[j].o,
+                                                             stream);
+        if (e != hipSuccess) return e;
+      }
+      return hipSuccess;
+    }
+  PjShape sh[2];
+  for (int i = 0; i < np; ++i) sh[i] = PjShape{a[i].T, a[i].N, a[i].K};
+  const int S = rows_gemm_slices(num_cus, sh, np);
+  PjJob<XT> job{};
+  job.np = np;
+  int wgs = 0;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  for (int i = 0; i < np; ++i) {
+    const int groups_n = (a[i].N + kPjGroup - 1) / kPjGroup;
+    job.g[i] = PjGemm<XT>{a[i].X, a[i].ldx, a[i].Wt, a[i].o, S > 1 ? reinterpret_cast<float*>(ws) : nullptr,
+                          a[i].T, a[i].N, a[i].K, S, groups_n, wgs};
+    wgs += groups_n * S * ((a[i].T + kPjT - 1) / kPjT);
+    if (S > 1) ws += (((size_t)S * a[i].T * a[i].N * sizeof(float)) + 255) & ~(size_t)255;
+  }
   hipError_t e0 = set_rows_gemm_lds_limits();
   if (e0 != hipSuccess) return e0;
-  hipLaunchKernelGGL(rows_gemm_kernel<XT>, grid, dim3(256), 3 * pj_stage_bytes<XT>(), stream, X, ldx, Wt, T, N, K, S,
-                     o, part);
+  hipLaunchKernelGGL(rows_gemm_kernel<XT>, dim3(wgs), dim3(256), 3 * pj_stage_bytes<XT>(), stream, job);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || S == 1) return e;
-  const size_t total = (size_t)T * N;
+  size_t total = 0;
+  for (int i = 0; i < np; ++i) total += (size_t)a[i].T * a[i].N;
   const unsigned blocks = (unsigned)((total + 255) / 256 < 4096 ? (total + 255) / 256 : 4096);
-  hipLaunchKernelGGL(rows_reduce_kernel<uint16_t>, dim3(blocks), dim3(256), 0, stream, part, T, N, S, o);
+  hipLaunchKernelGGL(rows_reduce_kernel<XT>, dim3(blocks), dim3(256), 0, stream, job);
   return hipGetLastError();
 }
 
@@ -340,13 +411,16 @@ hipError_t launch_project_hidden(const mla_config_t& cfg, int num_cus, int d_mod
   const int Nkv = d_c + d_r, Nq = H * (d_h + d_r);
   hipError_t e = hipSuccess;
   if (cfg.act_dtype == MLA_BF16 && d_model % kPjChunk == 0) {
+    // both projections in one launch
+    PjArgs<uint16_t> a[2];
+    int np = 0;
     if (n > 0)
-      e = launch_rows_gemm(num_cus, static_cast<const uint16_t*>(h_kv), d_model, static_cast<const uint16_t*>(w_dkv_t),
-                           n, Nkv, d_model, okv, gemm_ws, stream);
-    if (e == hipSuccess && T > 0)
-      e = launch_rows_gemm(num_cus, static_cast<const uint16_t*>(h_q), d_model, static_cast<const uint16_t*>(w_q_t), T,
-                           Nq, d_model, oq, gemm_ws, stream);
-    return e;
+      a[np++] = PjArgs<uint16_t>{static_cast<const uint16_t*>(h_kv), d_model, static_cast<const uint16_t*>(w_dkv_t), n,
+                                 Nkv, d_model, okv};
+    if (T > 0)
+      a[np++] = PjArgs<uint16_t>{static_cast<const uint16_t*>(h_q), d_model, static_cast<const uint16_t*>(w_q_t), T,
+                                 Nq, d_model, oq};
+    return np > 0 ? launch_rows_gemm(num_cus, a, np, gemm_ws, stream) : hipSuccess;
   }
   if (cfg.act_dtype == MLA_BF16) {
     if (n > 0)
@@ -376,9 +450,11 @@ size_t project_hidden_workspace(const mla_config_t& cfg, int num_cus, int d_mode
   size_t ws = al((size_t)n * cfg.d_c * el) + al((size_t)n * cfg.d_r * el) +
               al((size_t)T * cfg.num_heads * cfg.d_h * el) + al((size_t)T * cfg.num_heads * cfg.d_r * el);
   if (cfg.act_dtype == MLA_BF16 && d_model % kPjChunk == 0) {
-    const size_t a = rows_gemm_workspace(num_cus, n, cfg.d_c + cfg.d_r, d_model);
-    const size_t b = rows_gemm_workspace(num_cus, T, cfg.num_heads * (cfg.d_h + cfg.d_r), d_model);
-    ws += a > b ? a : b;
+    PjShape sh[2];
+    int np = 0;
+    if (n > 0) sh[np++] = PjShape{n, cfg.d_c + cfg.d_r, d_model};
+    if (T > 0) sh[np++] = PjShape{T, cfg.num_heads * (cfg.d_h + cfg.d_r), d_model};
+    ws += rows_gemm_workspace(num_cus, sh, np);
   }
   return ws;
 }
@@ -388,9 +464,10 @@ hipError_t launch_out_proj_folded(const mla_config_t& cfg, int num_cus, int d_mo
                                   const void* w_fold_t, void* out, int T, void* workspace, hipStream_t stream) {
   const int K = cfg.num_heads * cfg.d_c;
   const PjOut o{out, out, d_model, d_model, d_model};
-  if (cfg.act_dtype == MLA_BF16 && K % kPjChunk == 0)
-    return launch_rows_gemm(num_cus, o_lat, (long long)K, static_cast<const uint16_t*>(w_fold_t), T, d_model, K, o,
-                            workspace, stream);
+  if (cfg.act_dtype == MLA_BF16 && K % kPjChunk == 0) {
+    const PjArgs<float> a{o_lat, (long long)K, static_cast<const uint16_t*>(w_fold_t), T, d_model, K, o};
+    return T > 0 ? launch_rows_gemm(num_cus, &a, 1, workspace, stream) : hipSuccess;
+  }
   if (cfg.act_dtype == MLA_BF16)
     return launch_rows_gemm_generic<float, uint16_t, uint16_t>(o_lat, K, static_cast<const uint16_t*>(w_fold_t), T,
                                                                d_model, K, o, stream);
@@ -400,7 +477,10 @@ hipError_t launch_out_proj_folded(const mla_config_t& cfg, int num_cus, int d_mo
 
 size_t out_proj_folded_workspace(const mla_config_t& cfg, int num_cus, int d_model, int T) {
   const int K = cfg.num_heads * cfg.d_c;
-  if (cfg.act_dtype == MLA_BF16 && K % kPjChunk == 0) return rows_gemm_workspace(num_cus, T, d_model, K);
+  if (cfg.act_dtype == MLA_BF16 && K % kPjChunk == 0) {
+    const PjShape sh{T, d_model, K};
+    return rows_gemm_workspace(num_cus, &sh, 1);
+  }
   return 0;
 }
 
