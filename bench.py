@@ -457,7 +457,7 @@ def main() -> int:
         print(json.dumps({"copy_bytes": 1 << 28, "runs": 3}))
         return 0
     if a.gpus != 1:
-        print(f"bench.py runs on one GPU only (got --gpus {a.gpus}): this build measures the decode path on "
+        print(f"bench.py runs on one GPU only (got --gpus {a.gpus}): the decode path is measured on "
               "one GPU; a multi-GPU run would shard whole sequences per GPU and is not provided.", file=sys.stderr)
         return 2
 
