@@ -15,7 +15,7 @@ import pytest
 
 import oracle.mla_oracle as orc
 from mla_latent_kv_40_amd import binding as B, harness, workloads as wl
-from _common import cache_rows, check, dsv2, host, log, oracle_for, run_state
+from _common import bound, cache_rows, check, dsv2, host, log, oracle_for, run_state
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -118,17 +118,21 @@ def test_split_count_invariance(fmt):
             check(f"b{b} ranges {G} lse", g_l, ref["lse"], f)
 
 
-def test_query_rows_without_tokens():
+@pytest.mark.parametrize("fmt", ["bf16", "fp8b"])
+def test_query_rows_without_tokens(fmt):
     """kv_len < Sq: query j sits at p = kv_len - Sq + j; rows with p < 0 see no token and give
     o_lat = 0, lse = -inf (and a zero layer output); rows with p >= 0 attend to tokens 0 .. p,
-    i.e. equal a one-query decode of length p + 1 (the causal multi-query reduction)."""
-    log("case kv_len < Sq: lengths [2, 3, 1, 9], Sq=4")
-    w, bt, seqs = dsv2(4, [2, 3, 1, 9], sq=4, seed=73)
+    i.e. equal a one-query decode of length p + 1 (the causal multi-query reduction).  With the
+    tile-scaled cache the rows are also checked against the oracle on the rows the cache holds
+    (1x), and the exact oracle at 4x where the storage alone stays within it."""
+    log(f"case kv_len < Sq: lengths [2, 3, 1, 9], Sq=4, cache {fmt}")
+    w, bt, seqs = dsv2(4, [2, 3, 1, 9], sq=4, seed=73, fmt=None if fmt == "bf16" else fmt)
     st = run_state(w, bt, seqs)
     got = host(st)
     for b in range(w.batch):
         L = int(bt.kv_lens[b])
         s = seqs[b]
+        deq = cache_rows(w, bt, seqs, b) if w.fp8 else None
         for j in range(w.sq):
             row = b * w.sq + j
             p = L - w.sq + j
@@ -138,8 +142,17 @@ def test_query_rows_without_tokens():
                 continue
             ref = orc.decode(s["c"], s["k_r"], s["q_c"][j:j + 1], s["q_r"][j:j + 1], bt.weights["W_UK"],
                              bt.weights["W_UV"], p + 1, w.softmax_scale, w.rope_base)
+            if deq is None:
+                for k in ("o", "o_lat", "lse"):
+                    check(f"b{b} j{j} {k}", got[k][row:row + 1], ref[k])
+                continue
+            rd = orc.decode(deq[:p + 1, :w.d_c], deq[:p + 1, w.d_c:], s["q_c"][j:j + 1], s["q_r"][j:j + 1],
+                            bt.weights["W_UK"], bt.weights["W_UV"], p + 1, w.softmax_scale, w.rope_base,
+                            keys_rotated=True)
             for k in ("o", "o_lat", "lse"):
-                check(f"b{b} j{j} {k}", got[k][row:row + 1], ref[k])
+                check(f"b{b} j{j} {k} vs dequantised cache", got[k][row:row + 1], rd[k])
+                if np.max(np.abs(rd[k] - ref[k])) <= bound(ref[k], 4.0):
+                    check(f"b{b} j{j} {k}", got[k][row:row + 1], ref[k], 4.0)
 
 
 def range_boundary_page(bt, b, G, w_seg=3):
@@ -193,18 +206,25 @@ def test_full_size_needles(name):
         check(f"needles b{b} {k}", got[k][b:b + 1][:, heads], ref[k])
 
 
-@pytest.mark.parametrize("lengths,sq", [([1064, 364], 64), ([256], 256), ([700, 333], 333)])
-def test_chunked_extend_and_prefill(lengths, sq):
+@pytest.mark.parametrize("lengths,sq,fmt", [([1064, 364], 64, "bf16"), ([256], 256, "bf16"), ([700, 333], 333, "bf16"),
+                                            ([1064, 364], 64, "fp8b"), ([256], 256, "fp8")])
+def test_chunked_extend_and_prefill(lengths, sq, fmt):
     """Many query rows per sequence: a chunk of Sq new tokens (positions kv_len - Sq ..) appended
     and attended causally in one step, up to a whole prompt (kv_len = Sq: prefill).  The range
-    count falls to CUs / Sq, so each query row's workgroup streams its sequence's pages."""
-    log(f"case chunked extend / prefill: lengths {lengths}, Sq={sq}")
-    w, bt, seqs = dsv2(len(lengths), lengths, sq=sq, seed=97)
+    count falls to CUs / Sq, so each query row's workgroup streams its sequence's pages.  The fp8
+    cases append the chunk in the step (for tile scales, runs of up to 32 tokens per tile) and
+    take the fp8 gate (the oracle on the rows the cache holds at 1x as well)."""
+    from test_gpu_parity import compare_seq
+    log(f"case chunked extend / prefill: lengths {lengths}, Sq={sq}, cache {fmt}")
+    w, bt, seqs = dsv2(len(lengths), lengths, sq=sq, seed=97, fmt=None if fmt == "bf16" else fmt)
     st = run_state(w, bt, seqs)
     got = host(st)
     assert np.all(np.isfinite(got["o"]))
     heads = list(range(3, 128, 25))
     for b in range(w.batch):
+        if w.fp8:
+            compare_seq(w, bt, seqs, got, b, heads=heads, factor=4.0, tag=f"Sq={sq} ")
+            continue
         ref = oracle_for(w, bt, seqs, b, heads=heads)
         rows = slice(b * sq, (b + 1) * sq)
         for k in ("o", "o_lat", "lse"):

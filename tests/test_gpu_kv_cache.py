@@ -22,7 +22,7 @@ def kv_cfg():
     return B.Config(num_heads=128, d_c=512, d_r=64, d_h=128, d_v=128, softmax_scale=128 ** -0.5)
 
 
-@pytest.mark.parametrize("h_kv", [128, 32, 8])
+@pytest.mark.parametrize("h_kv", [128, 64, 32, 16, 8])   # 1, 2, 4, 8 and 16 query heads per key/value head
 def test_kv_cache_decode(h_kv):
     lengths = [1, 63, 64, 65, 200, 3000, 0]
     log(f"case per-head key/value cache decode: H=128, H_kv={h_kv}, lengths {lengths}")
