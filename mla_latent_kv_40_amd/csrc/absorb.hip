@@ -203,6 +203,8 @@ __global__ void __launch_bounds__(256) absorb_q_generic_kernel(
     float out;
     if (k < d_c) {
       float acc = 0.f;
+      // unrolled so that several iterations' loads are in flight at once (the sum keeps its order)
+#pragma unroll 8
       for (int d = 0; d < d_h; ++d)
         acc += load_act(q_nope, th * d_h + d) * load_act(w_uk, (size_t)k * H * d_h + (size_t)h * d_h + d);
       out = acc;
@@ -335,6 +337,8 @@ __global__ void __launch_bounds__(256) out_proj_generic_kernel(
     const size_t th = e / d_v;
     const int h = (int)(th % H);
     float acc = 0.f;
+    // unrolled so that several iterations' loads are in flight at once (the sum keeps its order)
+#pragma unroll 8
     for (int c = 0; c < d_c; ++c)
       acc += o_lat[th * d_c + c] * load_act(w_uv, (size_t)c * H * d_v + (size_t)h * d_v + v);
     if constexpr (sizeof(ActT) == 4) out[e] = acc;

@@ -234,6 +234,7 @@ __global__ void __launch_bounds__(256) rows_gemm_generic_kernel(const XT* __rest
   for (size_t e = (size_t)blockIdx.x * 256 + threadIdx.x; e < total; e += (size_t)gridDim.x * 256) {
     const int t = (int)(e / N), n = (int)(e % N);
     float acc = 0.f;
+#pragma unroll 8   // several iterations' loads in flight at once (the sum keeps its order)
     for (int k = 0; k < K; ++k) acc += load_act(X, (size_t)t * ldx + k) * load_act(Wt, (size_t)n * K + k);
     pj_store<OutT>(o, t, n, acc);
   }
@@ -388,6 +389,7 @@ __global__ void __launch_bounds__(256) fold_wo_kernel(const T* __restrict__ w_uv
     const int i = (int)(rest % H);
     const int n = (int)(rest / H);
     float acc = 0.f;
+#pragma unroll 8   // several iterations' loads in flight at once (the sum keeps its order)
     for (int v = 0; v < d_v; ++v)
       acc += load_act(w_uv, (size_t)c * H * d_v + (size_t)i * d_v + v) * load_act(w_o, ((size_t)i * d_v + v) * d_model + n);
     if constexpr (sizeof(T) == 4) w_fold_t[e] = acc;
