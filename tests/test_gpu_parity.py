@@ -272,6 +272,45 @@ def test_zero_length_sequence_gives_empty_result():
         check(f"b{b} lse", lse[b:b + 1], r["lse"])
 
 
+@pytest.mark.parametrize("fmt", ["bf16", "fp8b"])
+def test_out_of_range_page_ids_are_skipped(fmt):
+    """Block-table entries outside [0, num_blocks) (a negative id, an id past the pool) hold no
+    tokens: the decode skips their tokens (also in the combine's exact path) and attends to the
+    rest.  Reference: textbook attention over per-head keys and values rebuilt from the latent
+    rows that remain (the tokens keep their positions), the identity the oracle pins state."""
+    log(f"case out-of-range page ids, cache {fmt}: lengths [700, 3000, 130], one page of each invalid")
+    w, bt, seqs = dsv2(3, [700, 3000, 130], seed=31, fmt=None if fmt == "bf16" else fmt)
+    st = harness.DecodeState(w, bt, seqs, device="cuda")
+    st.fill_context()
+    bad = {0: (3, -1), 1: (10, bt.num_blocks + 7), 2: (1, -5)}   # sequence: (page index, id)
+    table = bt.block_table.copy()
+    for b, (pg, pid) in bad.items():
+        table[b, pg] = pid
+    st.block_table.copy_(torch.from_numpy(table))
+    st.step()
+    torch.cuda.synchronize()
+    got = host(st)
+    W = bt.weights
+    H, d_h, d_v = w.heads, w.d_h, w.d_v
+    heads = list(range(2, 128, 9))
+    for b, (pg, _) in bad.items():
+        L = int(bt.kv_lens[b])
+        rows = cache_rows(w, bt, seqs, b)                       # [L, 576], positional part rotated
+        keep = np.ones(L, bool)
+        keep[64 * pg:64 * (pg + 1)] = False
+        C, KR = rows[keep, :w.d_c], rows[keep, w.d_c:]
+        s = seqs[b]
+        qa = orc.absorbed_query(s["q_c"], s["q_r"], W["W_UK"], [L - 1], w.rope_base)[0]   # [H, 576]
+        qR = qa[:, w.d_c:]
+        K = np.concatenate([orc.up_project(C, W["W_UK"], H, d_h), np.repeat(KR[:, None, :], H, axis=1)], axis=2)
+        V = orc.up_project(C, W["W_UV"], H, d_v)
+        q = np.concatenate([np.asarray(s["q_c"][0], np.float64), qR], axis=1)             # [H, d_h + d_R]
+        ref = orc.attention(q, K, V, w.softmax_scale)
+        o = ref["o"][heads]
+        check(f"b{b} o (page {pg} skipped)", got["o"][b][heads], o)
+        check(f"b{b} lse (page {pg} skipped)", got["lse"][b][heads], ref["lse"][heads])
+
+
 # --------------------------------------------------------------------------- DS-V2 shapes, fp8 cache
 
 def test_fp8_edge_lengths_all_heads():
