@@ -1391,16 +1391,18 @@ __global__ void __launch_bounds__(256) combine_kernel(DecodeArgs a) {
   const int c = blockIdx.z;            // columns 128c .. 128c+127
   const int t = threadIdx.x, lane = t & 63;
   const int hh = t & 31, h = 32 * w + hh, hl = (t >> 5) & 1;
-  long long C_all, T_all;
-  scan_batch(a.kv_lens, a.B, a.max_blocks, a.seg_w, -1, -1, &C_all, &T_all, nullptr, nullptr);
+  // One pass over the lengths: the batch's total cost, and the pages and non-empty sequences
+  // before b (the same units the split's cut uses).
+  long long C_all = 0;
   long long first = 0;                 // first page of sequence b
   int rank = 0;                        // non-empty sequences before b
-  for (int base = 0; base < b; base += 64) {
+  for (int base = 0; base < a.B; base += 64) {
     const int q = base + lane;
     int L;
-    const int n = q < b ? seq_tiles(a.kv_lens, q, a.max_blocks, &L) : 0;
-    first += wave_sum_i(n);
-    rank += wave_sum_i(n > 0 ? 1 : 0);
+    const int n = q < a.B ? seq_tiles(a.kv_lens, q, a.max_blocks, &L) : 0;
+    C_all += wave_sum_i(n > 0 ? n + a.seg_w : 0);
+    first += wave_sum_i(q < b ? n : 0);
+    rank += wave_sum_i(q < b && n > 0 ? 1 : 0);
   }
   const long long cfirst = first + (long long)a.seg_w * (rank + 1);   // cost position of that page
   int Lb;
