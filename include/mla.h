@@ -29,6 +29,13 @@
  *   Calls on the same device may run from several host threads; calls that write the
  *   same buffers must be ordered by the caller (same stream or events).
  *
+ * Size limits (MLA_ERR_INVALID_ARG beyond them; a workspace-size query returns 0)
+ *   At most 2^20 query rows per call (B*Sq, T), 2^20 appended tokens (n) and batch entries,
+ *   and 2^24 pages in the pool (num_blocks) or in a block-table row (max_blocks): a sequence
+ *   holds up to 2^30 tokens.  A decode whose split plan would need more than 2^23 workgroups
+ *   (very wide block tables) returns MLA_ERR_UNSUPPORTED and a workspace size of 0; so does a
+ *   per-head cache decode past 2^24 (sequence, query head) pairs or 2^25 work items.
+ *
  * Positions and the causal mask
  *   Sequence b holds kv_len[b] tokens at positions 0 .. kv_len[b]-1; token t lives at
  *   page block_table[b*max_blocks + t/64], slot t%64.  A step has Sq new query tokens per
@@ -156,10 +163,10 @@ mla_status_t mla_append_absorb(const mla_config_t* cfg, void* cache, float* cach
 /*
  * mla_decode_workspace_size -- bytes of scratch mla_decode_attn needs for batch B,
  * Sq queries per sequence and block tables of width max_blocks on the current device.
- * Returns 0 for invalid arguments.  The value depends only on these arguments, the
- * device's compute-unit count and the test-only environment override MLA_FORCE_SPLITS (a
- * number of token ranges; it must be the same here and in the decode calls that use the
- * workspace).  It bounds the split-K partial results.
+ * Returns 0 for invalid arguments or sizes past the limits above.  The value depends only
+ * on these arguments, the device's compute-unit count and the test-only environment
+ * override MLA_FORCE_SPLITS (a number of token ranges; it must be the same here and in the
+ * decode calls that use the workspace).  It bounds the split-K partial results.
  */
 size_t mla_decode_workspace_size(const mla_config_t* cfg, int32_t B, int32_t Sq,
                                  int32_t max_blocks);
@@ -322,10 +329,11 @@ mla_status_t mla_kv_decode_attn(const mla_config_t* cfg, int32_t num_kv_heads, c
 mla_status_t mla_out_proj(const mla_config_t* cfg, const float* o_lat, const void* w_uv,
                           void* out, int32_t T, void* stream);
 
-/* Human-readable name of a status code (static storage). */
-const char* mla_status_string(mla_status_t status);
+/* Human-readable name of a status code (static storage).  Takes any integer: a value that is not
+ * an mla_status_t gives "MLA_ERR_UNKNOWN" (an enum parameter could not hold such values safely). */
+const char* mla_status_string(int32_t status);
 
-/* ABI version of this header: 7. */
+/* ABI version of this header: 8. */
 int32_t mla_abi_version(void);
 
 #ifdef __cplusplus

@@ -11,9 +11,10 @@ from dataclasses import dataclass
 from typing import Optional
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libmla.so")
+# MLA_LIBRARY names another build of the same library (the host-sanitizer check loads one)
+LIB_PATH = os.environ.get("MLA_LIBRARY") or os.path.join(HERE, "libmla.so")
 
-ABI_VERSION = 7   # what mla_abi_version() returns for the argument lists below
+ABI_VERSION = 8   # what mla_abi_version() returns for the argument lists below
 NOALLOC_SCRATCH_BYTES = 64 << 20   # MLA_NOALLOC_SCRATCH_BYTES
 
 MLA_OK, MLA_ERR_INVALID_ARG, MLA_ERR_UNSUPPORTED, MLA_ERR_WORKSPACE, MLA_ERR_HIP = range(5)
@@ -77,7 +78,7 @@ def lib() -> ctypes.CDLL:
         L.mla_kv_decode_workspace_size.restype = ctypes.c_size_t
         L.mla_kv_decode_attn.argtypes = [cfgp, i32, vp, vp, vp, i32, vp, i32, vp, i32, vp, ctypes.c_size_t, f32p,
                                          f32p, vp]
-        L.mla_status_string.argtypes = [ctypes.c_int]
+        L.mla_status_string.argtypes = [ctypes.c_int32]
         L.mla_status_string.restype = ctypes.c_char_p
         L.mla_abi_version.restype = ctypes.c_int32
         for name in ("mla_cache_append", "mla_absorb_q", "mla_append_absorb", "mla_decode_attn", "mla_decode_split",

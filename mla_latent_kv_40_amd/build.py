@@ -1,6 +1,7 @@
 """Build libmla.so in-tree with hipcc for gfx950 (cross-compiles without a GPU).
 
     python -m mla_latent_kv_40_amd.build [--save-temps DIR]
+    python -m mla_latent_kv_40_amd.build --host-sanitize OUT.so   # host code under ASan + UBSan
 """
 from __future__ import annotations
 
@@ -47,33 +48,44 @@ def _run(cmd, cwd=None, verbose=False, remarks=False):
         sys.stderr.write(r.stderr)
 
 
-def build(verbose: bool = False, save_temps: str | None = None) -> str:
-    """Compile every source to an object (own flags) and link libmla.so; always recompiles."""
-    objdir = os.path.join(HERE, "_build")
+# Host-side sanitizers for a checking build: each flag applies to the host pass only (device code
+# is built as usual).  The library then needs the ASan runtime loaded first in the process.
+HOST_SANITIZE = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                 "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-fno-sanitize-recover=all"]
+
+
+def build(verbose: bool = False, save_temps: str | None = None, host_sanitize: str | None = None) -> str:
+    """Compile every source to an object (own flags) and link libmla.so; always recompiles.
+    host_sanitize: build instead a copy with the host code under ASan and UBSan, at that path."""
+    objdir = os.path.join(HERE, "_build_san" if host_sanitize else "_build")
     os.makedirs(objdir, exist_ok=True)
+    san = HOST_SANITIZE if host_sanitize else []
     if save_temps:
         os.makedirs(save_temps, exist_ok=True)
     objs = []
     for src in SOURCES:
         obj = os.path.join(objdir, src + ".o")
-        cmd = [HIPCC, *FLAGS, *EXTRA[src], "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [HIPCC, *FLAGS, *EXTRA[src], *san, "-c", os.path.join(CSRC, src), "-o", obj]
         if save_temps:
             cmd.insert(1, "-save-temps=cwd")
             cmd += ["-Rpass-analysis=kernel-resource-usage"]
         _run(cmd, cwd=save_temps, verbose=verbose, remarks=bool(save_temps))
         objs.append(obj)
-    tmp = LIB + ".tmp"
-    _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp], verbose=verbose)
-    os.replace(tmp, LIB)
-    return LIB
+    out = host_sanitize or LIB
+    tmp = out + ".tmp"
+    _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *san, *objs, "-o", tmp], verbose=verbose)
+    os.replace(tmp, out)
+    return out
 
 
 def main() -> None:
     ap = argparse.ArgumentParser()
     ap.add_argument("--save-temps", default=None, help="keep intermediate files (ISA) in this folder")
+    ap.add_argument("--host-sanitize", default=None, metavar="OUT.so",
+                    help="build a copy with the host code under ASan + UBSan at this path")
     ap.add_argument("-v", "--verbose", action="store_true")
     a = ap.parse_args()
-    print(build(verbose=a.verbose, save_temps=a.save_temps))
+    print(build(verbose=a.verbose, save_temps=a.save_temps, host_sanitize=a.host_sanitize))
 
 
 if __name__ == "__main__":

@@ -1550,7 +1550,7 @@ __global__ void __launch_bounds__(256) decode_generic_kernel(
     if (t <= p && t < L) {
       const int pg = block_table[(size_t)b * max_blocks + t / kBlock];
       if (pg >= 0 && pg < num_blocks) {
-        rowidx = pg * kBlock + (t % kBlock);
+        rowidx = pg * kBlock + (t % kBlock);   // pages < 2^24: fits an int
         const CacheT* r = cache + (size_t)rowidx * width;
         float d = 0.f;
         for (int k = 0; k < width; ++k) d += qs[k] * load_act(r, k);
@@ -1624,7 +1624,10 @@ int forced_ranges() {
 // combine against 67 us for 256 ranges of 4 (64 ranges: 76 us).
 constexpr int kMinRangePages = 8;
 
-int decode_num_ranges(int num_cus, int B, int Sq, int max_blocks, bool fp8) {
+// Most split workgroups (ranges x queries per sequence) a plan may launch; wider plans are refused.
+constexpr long long kMaxSplitGrid = 1LL << 23;
+
+long long decode_num_ranges(int num_cus, int B, int Sq, int max_blocks, bool fp8) {
   const long long cap = (long long)B * max_blocks;
   const int tab = fp8 ? kTabCap8 : kTabCap;
   long long G = num_cus / (Sq > 0 ? Sq : 1);
@@ -1632,16 +1635,17 @@ int decode_num_ranges(int num_cus, int B, int Sq, int max_blocks, bool fp8) {
   if (G < 1) G = 1;
   if (const int f = forced_ranges()) G = f;
   // a range owns at most ceil(C / G) pages, C <= B (max_blocks + w) the total cost
-  const long long need = ((long long)B * (max_blocks + (fp8 ? kSegCost8 : kSegCost)) + tab - 1) / tab;
+  const long long need = ((long long)B * ((long long)max_blocks + (fp8 ? kSegCost8 : kSegCost)) + tab - 1) / tab;
   if (G < need) G = need;
   if (cap < G) G = cap < 1 ? 1 : cap;
-  return (int)G;
+  return G;
 }
 
 size_t decode_workspace_bytes(const mla_config_t& cfg, int num_cus, int B, int Sq, int max_blocks) {
   if (!(cfg.cache_dtype != MLA_F32 && is_dsv2_shape(cfg))) return 256;   // generic path: none needed
-  const int G = decode_num_ranges(num_cus, B, Sq, max_blocks,
-                                  cfg.cache_dtype == MLA_FP8_E4M3 || cfg.cache_dtype == MLA_FP8_E4M3_B32);
+  const long long G = decode_num_ranges(num_cus, B, Sq, max_blocks,
+                                        cfg.cache_dtype == MLA_FP8_E4M3 || cfg.cache_dtype == MLA_FP8_E4M3_B32);
+  if (G > kMaxSplitGrid / (Sq > 0 ? Sq : 1)) return 0;   // refused: too many workgroups
   const size_t slots = (size_t)(G + B - 1) * Sq;
   const size_t o_bytes = slots * kH * kDC * sizeof(uint16_t);
   const size_t l_bytes = slots * kH * 2 * sizeof(float);
@@ -1690,7 +1694,8 @@ hipError_t launch_decode(const mla_config_t& cfg, int num_cus, const void* q_abs
     a.kv_lens = kv_lens;
     a.o_lat = o_lat;
     a.lse = lse;
-    const int G = decode_num_ranges(num_cus, B, Sq, max_blocks, fp8);
+    // the caller has checked the plan against kMaxSplitGrid (a zero workspace size)
+    const int G = (int)decode_num_ranges(num_cus, B, Sq, max_blocks, fp8);
     const size_t slots = (size_t)(G + B - 1) * Sq;
     a.part_o = static_cast<uint16_t*>(workspace);
     a.part_ml = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) +

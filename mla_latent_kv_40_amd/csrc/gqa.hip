@@ -240,11 +240,15 @@ static void gqa_slices(int H_q, int H_kv, int* G, int* QS) {
   *QS = 1;
 }
 
-// Workspace: item starts, then partials for the most items the batch can have.
+// Most work items one launch may take (four per workgroup); larger batches are refused.
+constexpr size_t kMaxItems = (size_t)1 << 25;
+
+// Workspace: item starts, then partials for the most items the batch can have (0: refused).
 size_t gqa_workspace_bytes(int B, int H_q, int H_kv, int max_blocks) {
   int G, QS;
   gqa_slices(H_q, H_kv, &G, &QS);
   const size_t items = (size_t)B * H_kv * QS * ((max_blocks + kChunkPages - 1) / kChunkPages);
+  if (items > kMaxItems) return 0;
   auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
   return al((size_t)(B + 1) * 4) + al(items * G * kGqaD * 4) + al(items * G * 2 * 4);
 }

@@ -59,6 +59,16 @@ int current_cu_count() {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// Size limits checked before anything is launched.  Within them every row, token-slot and page
+// index fits the kernels' 32-bit arithmetic and every launch keeps far below the 2^32
+// work-items one grid dimension can hold.
+constexpr int32_t kMaxRows = 1 << 20;    // query rows (B*Sq, T), appended tokens, batch entries
+constexpr int32_t kMaxPages = 1 << 24;   // pages in the pool, and in one block-table row
+constexpr long long kMaxKvPairs = 1LL << 24;   // (sequence, query head) pairs of a per-head decode
+
+bool rows_ok(long long r) { return r >= 0 && r <= kMaxRows; }
+bool pages_ok(int32_t p) { return p > 0 && p <= kMaxPages; }
+
 
 // Shape and format checks shared by every call.
 mla_status_t check_cfg(const mla_config_t* c) {
@@ -85,9 +95,9 @@ mla_status_t from_hip(hipError_t e) { return e == hipSuccess ? MLA_OK : MLA_ERR_
 
 extern "C" {
 
-int32_t mla_abi_version(void) { return 7; }
+int32_t mla_abi_version(void) { return 8; }
 
-const char* mla_status_string(mla_status_t s) {
+const char* mla_status_string(int32_t s) {
   switch (s) {
     case MLA_OK: return "MLA_OK";
     case MLA_ERR_INVALID_ARG: return "MLA_ERR_INVALID_ARG: invalid argument";
@@ -103,7 +113,8 @@ static mla_status_t check_append(const mla_config_t* cfg, void* cache, float* ca
                                  const int32_t* block_table, int32_t batch, int32_t max_blocks, int32_t n) {
   mla_status_t st = check_cfg(cfg);
   if (st != MLA_OK) return st;
-  if (n < 0 || num_blocks <= 0 || batch <= 0 || max_blocks <= 0) return MLA_ERR_INVALID_ARG;
+  if (!rows_ok(n) || !pages_ok(num_blocks) || batch <= 0 || !rows_ok(batch) || !pages_ok(max_blocks))
+    return MLA_ERR_INVALID_ARG;
   if (!cache || !block_table) return MLA_ERR_INVALID_ARG;
   if (n > 0 && (!c_kv || !k_r || !pos || !seq_of)) return MLA_ERR_INVALID_ARG;
   if (!aligned16(cache) || !aligned16(block_table)) return MLA_ERR_INVALID_ARG;
@@ -119,7 +130,7 @@ static mla_status_t check_absorb(const mla_config_t* cfg, const void* q_nope, co
                                  const int32_t* q_pos, const void* w_uk, void* q_abs, int32_t T) {
   mla_status_t st = check_cfg(cfg);
   if (st != MLA_OK) return st;
-  if (T < 0) return MLA_ERR_INVALID_ARG;
+  if (!rows_ok(T)) return MLA_ERR_INVALID_ARG;
   if (T == 0) return MLA_OK;
   if (!q_nope || !q_rope || !q_pos || !w_uk || !q_abs) return MLA_ERR_INVALID_ARG;
   if (!aligned16(q_nope) || !aligned16(q_rope) || !aligned16(q_pos) || !aligned16(w_uk) || !aligned16(q_abs))
@@ -170,7 +181,8 @@ mla_status_t mla_append_absorb(const mla_config_t* cfg, void* cache, float* cach
 }
 
 size_t mla_decode_workspace_size(const mla_config_t* cfg, int32_t B, int32_t Sq, int32_t max_blocks) {
-  if (check_cfg(cfg) != MLA_OK || B <= 0 || Sq <= 0 || max_blocks <= 0) return 0;
+  if (check_cfg(cfg) != MLA_OK || B <= 0 || Sq <= 0 || !rows_ok((long long)B * Sq) || !pages_ok(max_blocks))
+    return 0;
   return mla::decode_workspace_bytes(*cfg, current_cu_count(), B, Sq, max_blocks);
 }
 
@@ -181,8 +193,8 @@ static mla_status_t decode_common(const mla_config_t* cfg, const void* q_abs, co
                                   void* stream, int phases, bool use_static = false) {
   mla_status_t st = check_cfg(cfg);
   if (st != MLA_OK) return st;
-  if (B < 0 || Sq <= 0 || num_blocks <= 0 || max_blocks <= 0) return MLA_ERR_INVALID_ARG;
-  if ((long long)B * Sq > (1LL << 30)) return MLA_ERR_INVALID_ARG;
+  if (B < 0 || Sq <= 0 || !rows_ok((long long)B * Sq) || !pages_ok(num_blocks) || !pages_ok(max_blocks))
+    return MLA_ERR_INVALID_ARG;
   if (B == 0) return MLA_OK;
   if (!q_abs || !cache || !block_table || !kv_lens || !o_lat || !lse) return MLA_ERR_INVALID_ARG;
   if (!aligned16(q_abs) || !aligned16(cache) || !aligned16(o_lat) || !aligned16(lse) || !aligned16(kv_lens) ||
@@ -193,6 +205,7 @@ static mla_status_t decode_common(const mla_config_t* cfg, const void* q_abs, co
   if (cache_scale && !aligned16(cache_scale)) return MLA_ERR_INVALID_ARG;
   const int cus = current_cu_count();
   const size_t need = mla::decode_workspace_bytes(*cfg, cus, B, Sq, max_blocks);
+  if (need == 0) return MLA_ERR_UNSUPPORTED;   // the split plan needs too many workgroups
   if (use_static) {   // mla_decode_attn_noalloc
     if (need > mla::static_scratch_bytes()) return MLA_ERR_WORKSPACE;
     if (mla::static_scratch(&workspace) != hipSuccess) return MLA_ERR_HIP;
@@ -243,7 +256,7 @@ static bool d_model_ok(int32_t d_model) { return d_model > 0 && d_model % 16 == 
 static size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
 size_t mla_hidden_workspace_size(const mla_config_t* cfg, int32_t d_model, int32_t n, int32_t T) {
-  if (check_cfg(cfg) != MLA_OK || !d_model_ok(d_model) || n < 0 || T < 0) return 0;
+  if (check_cfg(cfg) != MLA_OK || !d_model_ok(d_model) || !rows_ok(n) || !rows_ok(T)) return 0;
   return mla::project_hidden_workspace(*cfg, current_cu_count(), d_model, n, T) + 256;
 }
 
@@ -255,7 +268,7 @@ mla_status_t mla_append_absorb_hidden(const mla_config_t* cfg, int32_t d_model, 
                                       int32_t T, void* workspace, size_t ws_bytes, void* stream) {
   mla_status_t st = check_cfg(cfg);
   if (st != MLA_OK) return st;
-  if (!d_model_ok(d_model) || n < 0 || T < 0) return MLA_ERR_INVALID_ARG;
+  if (!d_model_ok(d_model) || !rows_ok(n) || !rows_ok(T)) return MLA_ERR_INVALID_ARG;
   if (n > 0 && (!h_kv || !w_dkv_t || !aligned16(h_kv) || !aligned16(w_dkv_t))) return MLA_ERR_INVALID_ARG;
   if (T > 0 && (!h_q || !w_q_t || !aligned16(h_q) || !aligned16(w_q_t))) return MLA_ERR_INVALID_ARG;
   if (n == 0 && T == 0) return MLA_OK;
@@ -298,7 +311,7 @@ mla_status_t mla_fold_output_weights(const mla_config_t* cfg, int32_t d_model, c
 }
 
 size_t mla_out_proj_folded_workspace_size(const mla_config_t* cfg, int32_t d_model, int32_t T) {
-  if (check_cfg(cfg) != MLA_OK || !d_model_ok(d_model) || T < 0) return 0;
+  if (check_cfg(cfg) != MLA_OK || !d_model_ok(d_model) || !rows_ok(T)) return 0;
   return mla::out_proj_folded_workspace(*cfg, current_cu_count(), d_model, T) + 256;
 }
 
@@ -306,7 +319,7 @@ mla_status_t mla_out_proj_folded(const mla_config_t* cfg, int32_t d_model, const
                                  void* out, int32_t T, void* workspace, size_t ws_bytes, void* stream) {
   mla_status_t st = check_cfg(cfg);
   if (st != MLA_OK) return st;
-  if (!d_model_ok(d_model) || T < 0) return MLA_ERR_INVALID_ARG;
+  if (!d_model_ok(d_model) || !rows_ok(T)) return MLA_ERR_INVALID_ARG;
   if (T == 0) return MLA_OK;
   if (!o_lat || !w_fold_t || !out || !aligned16(o_lat) || !aligned16(w_fold_t) || !aligned16(out))
     return MLA_ERR_INVALID_ARG;
@@ -330,7 +343,8 @@ static mla_status_t check_kv_cfg(const mla_config_t* cfg, int32_t num_kv_heads) 
 }
 
 size_t mla_kv_decode_workspace_size(const mla_config_t* cfg, int32_t num_kv_heads, int32_t B, int32_t max_blocks) {
-  if (check_kv_cfg(cfg, num_kv_heads) != MLA_OK || B <= 0 || max_blocks <= 0) return 0;
+  if (check_kv_cfg(cfg, num_kv_heads) != MLA_OK || B <= 0 || !rows_ok(B) || !pages_ok(max_blocks)) return 0;
+  if ((long long)B * cfg->num_heads > kMaxKvPairs) return 0;
   return mla::gqa_workspace_bytes(B, cfg->num_heads, num_kv_heads, max_blocks);
 }
 
@@ -340,13 +354,15 @@ mla_status_t mla_kv_decode_attn(const mla_config_t* cfg, int32_t num_kv_heads, c
                                 size_t ws_bytes, float* o, float* lse, void* stream) {
   mla_status_t st = check_kv_cfg(cfg, num_kv_heads);
   if (st != MLA_OK) return st;
-  if (B < 0 || num_blocks <= 0 || max_blocks <= 0) return MLA_ERR_INVALID_ARG;
+  if (!rows_ok(B) || !pages_ok(num_blocks) || !pages_ok(max_blocks)) return MLA_ERR_INVALID_ARG;
   if (B == 0) return MLA_OK;
+  if ((long long)B * cfg->num_heads > kMaxKvPairs) return MLA_ERR_UNSUPPORTED;
   if (!q || !k_cache || !v_cache || !block_table || !kv_lens || !o || !lse) return MLA_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(block_table) || !aligned16(kv_lens) ||
       !aligned16(o) || !aligned16(lse))
     return MLA_ERR_INVALID_ARG;
   const size_t need = mla::gqa_workspace_bytes(B, cfg->num_heads, num_kv_heads, max_blocks);
+  if (need == 0) return MLA_ERR_UNSUPPORTED;   // more work items than one launch takes
   if (!workspace || ws_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 255u)) return MLA_ERR_WORKSPACE;
   return from_hip(mla::launch_gqa_decode(cfg->num_heads, num_kv_heads, cfg->softmax_scale, q, k_cache, v_cache,
                                          num_blocks, block_table, max_blocks, kv_lens, B, workspace, o, lse,
@@ -357,7 +373,7 @@ mla_status_t mla_out_proj(const mla_config_t* cfg, const float* o_lat, const voi
                           void* stream) {
   mla_status_t st = check_cfg(cfg);
   if (st != MLA_OK) return st;
-  if (T < 0) return MLA_ERR_INVALID_ARG;
+  if (!rows_ok(T)) return MLA_ERR_INVALID_ARG;
   if (T == 0) return MLA_OK;
   if (!o_lat || !w_uv || !out) return MLA_ERR_INVALID_ARG;
   if (!aligned16(o_lat) || !aligned16(w_uv) || !aligned16(out)) return MLA_ERR_INVALID_ARG;

@@ -246,3 +246,63 @@ def test_kv_cache_decode_validation(L):
     c8 = B.Config(num_heads=128, d_c=512, d_r=64, d_h=128, d_v=128, softmax_scale=0.1, cache_dtype="fp8")
     assert B.mla_kv_decode_attn(c8, 8, *args[2:], FAKE, ws, FAKE, FAKE, stream=0,
                                 check=False) == B.MLA_ERR_UNSUPPORTED
+
+
+def test_size_limits(L):
+    """The documented size limits: at most 2^20 query rows, appended tokens and batch entries per
+    call, 2^24 pages in the pool or a table row, and split plans of at most 2^23 workgroups.
+    Sizes past them are refused before anything is launched, and the size queries stay exact
+    (no wrap-around) up to them."""
+    rows, pages = 1 << 20, 1 << 24
+    for fmt in ("bf16", "fp8", "fp8b"):
+        c = cfg(cache_dtype=fmt)
+        sc = None if fmt == "bf16" else FAKE
+        # at the limits the sizes are real (huge) byte counts, past them 0
+        one = B.mla_decode_workspace_size(c, 1, rows, 1)
+        assert one >= rows * 128 * 512 * 2
+        assert B.mla_decode_workspace_size(c, 1, rows + 1, 1) == 0
+        assert B.mla_decode_workspace_size(c, 2, rows // 2 + 1, 1) == 0
+        wide = B.mla_decode_workspace_size(c, 128, 1, pages)
+        assert wide >= 128 * pages // 1024 * 128 * 512 * 2         # one partial per range of <= 1024 pages
+        assert B.mla_decode_workspace_size(c, 128, 1, pages + 1) == 0
+        assert B.mla_decode_workspace_size(c, rows, 1, pages) == 0  # plan past 2^23 workgroups
+        for b, sq, mb in [(2**31 - 1, 1, 1), (1, 2**31 - 1, 1), (2**31 - 1, 2**31 - 1, 2**31 - 1), (-1, 1, 1)]:
+            assert B.mla_decode_workspace_size(c, b, sq, mb) == 0
+        dec = lambda b, sq, nb, mb: B.mla_decode_attn(c, FAKE, FAKE, sc, nb, FAKE, mb, FAKE, b, sq, FAKE,
+                                                      1 << 62, FAKE, FAKE, stream=0, check=False)
+        assert dec(rows + 1, 1, 100, 8) == B.MLA_ERR_INVALID_ARG
+        assert dec(1024, 1025, 100, 8) == B.MLA_ERR_INVALID_ARG
+        assert dec(4, 1, pages + 1, 8) == B.MLA_ERR_INVALID_ARG
+        assert dec(4, 1, 100, pages + 1) == B.MLA_ERR_INVALID_ARG
+        assert dec(rows, 1, 100, pages) == B.MLA_ERR_UNSUPPORTED   # refused before any launch
+        assert B.mla_decode_attn_noalloc(c, FAKE, FAKE, sc, 100, FAKE, pages, FAKE, rows, 1, FAKE, FAKE,
+                                         stream=0, check=False) == B.MLA_ERR_UNSUPPORTED
+        app = lambda nb, batch, mb, n: B.mla_cache_append(c, FAKE, sc, nb, FAKE, FAKE, FAKE, FAKE, FAKE, batch,
+                                                          mb, n, stream=0, check=False)
+        assert app(pages + 1, 2, 4, 3) == B.MLA_ERR_INVALID_ARG
+        assert app(8, rows + 1, 4, 3) == B.MLA_ERR_INVALID_ARG
+        assert app(8, 2, pages + 1, 3) == B.MLA_ERR_INVALID_ARG
+        assert app(8, 2, 4, rows + 1) == B.MLA_ERR_INVALID_ARG
+        assert B.mla_absorb_q(c, FAKE, FAKE, FAKE, FAKE, FAKE, rows + 1, stream=0,
+                              check=False) == B.MLA_ERR_INVALID_ARG
+        assert B.mla_out_proj(c, FAKE, FAKE, FAKE, rows + 1, stream=0, check=False) == B.MLA_ERR_INVALID_ARG
+        assert B.mla_hidden_workspace_size(c, 5120, rows, rows) > 0
+        assert B.mla_hidden_workspace_size(c, 5120, rows + 1, 1) == 0
+        assert B.mla_hidden_workspace_size(c, 5120, 1, rows + 1) == 0
+        assert B.mla_hidden_workspace_size(c, 1 << 20, rows, rows) > 0
+        assert B.mla_out_proj_folded_workspace_size(c, 1 << 20, rows) > 0
+        assert B.mla_out_proj_folded_workspace_size(c, 5120, rows + 1) == 0
+        assert B.mla_out_proj_folded(c, 5120, FAKE, FAKE, FAKE, rows + 1, FAKE, 1 << 62, stream=0,
+                                     check=False) == B.MLA_ERR_INVALID_ARG
+    kv = B.Config(num_heads=128, d_c=512, d_r=64, d_h=128, d_v=128, softmax_scale=128 ** -0.5)
+    assert B.mla_kv_decode_workspace_size(kv, 8, rows // 128, 16) > 0
+    assert B.mla_kv_decode_workspace_size(kv, 8, rows // 128 + 1, 16) > 0      # 2^24 pairs is the limit
+    assert B.mla_kv_decode_workspace_size(kv, 8, rows, 16) == 0                # 2^27 pairs
+    assert B.mla_kv_decode_workspace_size(kv, 128, 8192, pages) == 0           # 2^30 work items
+    assert B.mla_kv_decode_workspace_size(kv, 8, 4, pages + 1) == 0
+    kvd = lambda n, b, nb, mb: B.mla_kv_decode_attn(kv, n, FAKE, FAKE, FAKE, nb, FAKE, mb, FAKE, b, FAKE,
+                                                    1 << 62, FAKE, FAKE, stream=0, check=False)
+    assert kvd(8, rows + 1, 100, 16) == B.MLA_ERR_INVALID_ARG
+    assert kvd(8, 4, pages + 1, 16) == B.MLA_ERR_INVALID_ARG
+    assert kvd(8, rows, 100, 16) == B.MLA_ERR_UNSUPPORTED
+    assert kvd(128, 8192, 100, pages) == B.MLA_ERR_UNSUPPORTED
