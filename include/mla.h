@@ -165,8 +165,10 @@ mla_status_t mla_append_absorb(const mla_config_t* cfg, void* cache, float* cach
  * Sq queries per sequence and block tables of width max_blocks on the current device.
  * Returns 0 for invalid arguments or sizes past the limits above.  The value depends only
  * on these arguments, the device's compute-unit count and the test-only environment
- * override MLA_FORCE_SPLITS (a number of token ranges; it must be the same here and in the
- * decode calls that use the workspace).  It bounds the split-K partial results.
+ * overrides MLA_FORCE_SPLITS (a number of token ranges) and MLA_SPLIT_TOKENS (tokens per
+ * range, counted over the block tables' capacity; MLA_FORCE_SPLITS wins when both are set);
+ * they must be the same here and in the decode calls that use the workspace.  It bounds the
+ * split-K partial results.
  */
 size_t mla_decode_workspace_size(const mla_config_t* cfg, int32_t B, int32_t Sq,
                                  int32_t max_blocks);

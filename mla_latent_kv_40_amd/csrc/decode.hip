@@ -1604,19 +1604,24 @@ bool is_dsv2_shape(const mla_config_t& c);
 // range with one more segment ran ~20K cycles longer: ~3 bf16 pages, ~2 fp8 pages).
 constexpr int kSegCost = 3, kSegCost8 = 2;
 
-// Test-only override of the range count: the environment variable MLA_FORCE_SPLITS = G > 0
-// replaces the default count, within the same limits (the page table's capacity, at most one
-// range per page).  It is read at every call, so a workspace size and the decode calls that
-// use it must see the same value.  The result is the same attention for any count, up to the
-// rounding of the probabilities and partials that a different cut changes.
-int forced_ranges() {
-  const char* v = std::getenv("MLA_FORCE_SPLITS");
+// Test-only overrides of the range count, read at every call (so a workspace size and the
+// decode calls that use it must see the same values), applied within the same limits as the
+// default (the page table's capacity, at most one range per page):
+//   MLA_FORCE_SPLITS = G > 0   G ranges;
+//   MLA_SPLIT_TOKENS = n > 0   ranges of about n tokens of the block tables' capacity,
+//                              G = ceil(64 B max_blocks / n) (ignored when MLA_FORCE_SPLITS is set).
+// The result is the same attention for any count, up to the rounding of the probabilities and
+// partials that a different cut changes.  Unset, empty or malformed values are ignored.
+long long env_positive(const char* name, long long max) {
+  const char* v = std::getenv(name);
   if (v == nullptr || *v == 0) return 0;
   char* end = nullptr;
-  const long x = std::strtol(v, &end, 10);
-  if (end == v || *end != 0 || x <= 0 || x > (1L << 24)) return 0;
-  return (int)x;
+  const long long x = std::strtoll(v, &end, 10);
+  if (end == v || *end != 0 || x <= 0 || x > max) return 0;
+  return x;
 }
+int forced_ranges() { return (int)env_positive("MLA_FORCE_SPLITS", 1LL << 24); }
+long long forced_split_tokens() { return env_positive("MLA_SPLIT_TOKENS", 1LL << 40); }
 
 // Small batches: at least this many pages (of the block tables' capacity) per range.  A range
 // costs a fixed ~20K cycles (page table, queries, segment end) and a 128 KiB partial that the
@@ -1634,6 +1639,7 @@ long long decode_num_ranges(int num_cus, int B, int Sq, int max_blocks, bool fp8
   if (G > cap / kMinRangePages) G = cap / kMinRangePages;
   if (G < 1) G = 1;
   if (const int f = forced_ranges()) G = f;
+  else if (const long long n = forced_split_tokens()) G = (cap * kBlock + n - 1) / n;
   // a range owns at most ceil(C / G) pages, C <= B (max_blocks + w) the total cost
   const long long need = ((long long)B * ((long long)max_blocks + (fp8 ? kSegCost8 : kSegCost)) + tab - 1) / tab;
   if (G < need) G = need;

@@ -2,7 +2,8 @@
 
 * split-count invariance: the same batch decoded with different numbers of token ranges
   (the test-only override MLA_FORCE_SPLITS) agrees within a bound derived from the rounding
-  that a different cut changes, and every run passes the oracle gate;
+  that a different cut changes, and every run passes the oracle gate; the range-size override
+  MLA_SPLIT_TOKENS reproduces the equivalent range count bit for bit;
 * query rows that see no token (kv_len < Sq) give the defined empty result, the others the
   oracle's;
 * needle tokens in the longest sequence of the full-size long-context workloads, at the bench's
@@ -28,14 +29,12 @@ def _gpu():
     torch.cuda.set_device(0)
 
 
-def decode_with_ranges(st, G):
-    """mla_decode_attn on the state's inputs with MLA_FORCE_SPLITS = G (None: the default count),
-    a fresh NaN-filled workspace and NaN-filled outputs."""
-    old = os.environ.get("MLA_FORCE_SPLITS")
-    if G is None:
-        os.environ.pop("MLA_FORCE_SPLITS", None)
-    else:
-        os.environ["MLA_FORCE_SPLITS"] = str(G)
+def decode_with_ranges(st, G, var="MLA_FORCE_SPLITS"):
+    """mla_decode_attn on the state's inputs with the test-only override `var` = G (None: the
+    default count), a fresh NaN-filled workspace and NaN-filled outputs."""
+    old = {k: os.environ.pop(k, None) for k in ("MLA_FORCE_SPLITS", "MLA_SPLIT_TOKENS")}
+    if G is not None:
+        os.environ[var] = str(G)
     try:
         ws_bytes = B.mla_decode_workspace_size(st.cfg, st.w.batch, st.w.sq, st.batch.max_blocks)
         ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
@@ -47,10 +46,11 @@ def decode_with_ranges(st, G):
         torch.cuda.synchronize()
         return st.o_lat.cpu().numpy().copy(), st.lse.cpu().numpy().copy(), ws_bytes
     finally:
-        if old is None:
-            os.environ.pop("MLA_FORCE_SPLITS", None)
-        else:
-            os.environ["MLA_FORCE_SPLITS"] = old
+        for k, v in old.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
 
 
 def weighted_spread(w, bt, seqs, b, heads):
@@ -116,6 +116,24 @@ def test_split_count_invariance(fmt):
             f = 4.0 if fp8 else 1.0
             check(f"b{b} ranges {G} o_lat", g_o, ref["o_lat"], f)
             check(f"b{b} ranges {G} lse", g_l, ref["lse"], f)
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "fp8"])
+def test_split_tokens_override_equals_range_count(fmt):
+    """MLA_SPLIT_TOKENS = n gives G = ceil(64 * B * max_blocks / n) ranges: the same cut as
+    MLA_FORCE_SPLITS = G, so the two runs agree bit for bit."""
+    lengths = [20000, 9000, 3001, 777, 65]
+    log(f"case split-tokens override, cache {fmt}: lengths {lengths}")
+    w, bt, seqs = dsv2(5, lengths, seed=72, fmt=None if fmt == "bf16" else fmt)
+    st = run_state(w, bt, seqs)
+    cap_tokens = 64 * w.batch * bt.max_blocks
+    for n in (cap_tokens // 37, 4096, 64 * 3):
+        G = -(-cap_tokens // n)
+        o_t, l_t, ws_t = decode_with_ranges(st, n, var="MLA_SPLIT_TOKENS")
+        o_g, l_g, ws_g = decode_with_ranges(st, G)
+        log(f"  {n} tokens per range -> {G} ranges: workspace {ws_t} B")
+        assert ws_t == ws_g
+        assert np.array_equal(o_t, o_g) and np.array_equal(l_t, l_g), (n, G)
 
 
 @pytest.mark.parametrize("fmt", ["bf16", "fp8b"])

@@ -175,6 +175,28 @@ def test_forced_split_count_changes_only_the_workspace(L, monkeypatch):
     assert ignored == base
 
 
+def test_split_tokens_override_sets_the_range_size(L, monkeypatch):
+    """MLA_SPLIT_TOKENS = n (test-only) asks for ranges of about n tokens of the block tables'
+    capacity: G = ceil(64 * B * max_blocks / n), so the workspace equals the one for that many
+    forced ranges.  MLA_FORCE_SPLITS wins when both are set."""
+    c = cfg()
+    monkeypatch.delenv("MLA_FORCE_SPLITS", raising=False)
+
+    def size(force=None, tokens=None):
+        for k, v in (("MLA_FORCE_SPLITS", force), ("MLA_SPLIT_TOKENS", tokens)):
+            if v is None:
+                monkeypatch.delenv(k, raising=False)
+            else:
+                monkeypatch.setenv(k, str(v))
+        return B.mla_decode_workspace_size(c, 4, 1, 100)   # capacity 400 pages = 25,600 tokens
+
+    base = size()
+    for n, G in ((25_600, 1), (1 << 30, 1), (6_400, 4), (6_399, 5), (700, 37), (64, 400), (1, 400)):
+        assert size(tokens=n) == size(force=G), (n, G)
+    assert size(force=3, tokens=64) == size(force=3)
+    assert size(tokens="junk") == size(tokens=0) == base
+
+
 def test_status_strings(L):
     for code in range(5):
         assert B.mla_status_string(code).startswith("MLA_")
