@@ -396,11 +396,60 @@ def model_width_measurement(name, steps, flush, log, d_model=5120):
     return res
 
 
+ATTAINABLE_LIB = os.path.join(os.path.dirname(os.path.abspath(__file__)), "mla_latent_kv_40_amd",
+                              "libmla_attainable.so")
+LOOP_FLOP = {0: 32 * 32 * 16 * 2, 1: 32 * 32 * 64 * 2}   # per instruction: bf16, scaled fp8
+LDS_PER_CU = 163840
+
+
+def mfma_loop_rates(log, settle_ms=300.0):
+    """The matrix rate the chip sustains: libmla_attainable's loop of independent matrix
+    instructions (no memory traffic) on every compute unit, launched back to back for settle_ms
+    before 20 timed launches (median).  One workgroup of four waves per compute unit (all of its
+    LDS reserved, the decode split's occupancy), and two per compute unit."""
+    import ctypes
+    import torch
+    if not os.path.exists(ATTAINABLE_LIB):
+        raise RuntimeError(f"{ATTAINABLE_LIB} is not built: run __graft_entry__.build()")
+    L = ctypes.CDLL(ATTAINABLE_LIB)
+    fn = L.mla_attainable_mfma_loop
+    fn.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+    fn.restype = ctypes.c_int32
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    stream = torch.cuda.current_stream()
+    out = torch.empty(2 * cus * 256, dtype=torch.float32, device="cuda:0")
+    r = {}
+    for kind, name, iters in ((0, "bf16", 2048), (1, "fp8", 1024)):
+        for per_cu in (1, 2):
+            wgs, it = cus * per_cu, iters // per_cu
+
+            def launch():
+                rc = fn(kind, wgs, it, LDS_PER_CU // per_cu, out.data_ptr(), stream.cuda_stream)
+                if rc != 0:
+                    raise RuntimeError(f"mla_attainable_mfma_loop returned {rc}")
+            t0 = time.perf_counter()
+            while time.perf_counter() - t0 < settle_ms * 1e-3:
+                for _ in range(20):
+                    launch()
+                torch.cuda.synchronize()
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(20)]
+            for e0, e1 in evs:
+                e0.record(stream); launch(); e1.record(stream)
+            torch.cuda.synchronize()
+            ms = float(np.median([e0.elapsed_time(e1) for e0, e1 in evs]))
+            flop = wgs * 4 * it * 4 * LOOP_FLOP[kind]
+            key = f"{name}_mfma_loop_TFLOPs" + ("" if per_cu == 1 else "_2wg_per_cu")
+            r[key] = round(flop / (ms * 1e-3) / 1e12, 1)
+    del out
+    log(f"[bench] matrix-instruction loop: {r}")
+    return r
+
+
 def attainable(log):
-    """What the box reaches on plain library work, next to the published peaks: a 1 GiB
-    device-to-device copy (bytes read + written / time) and an 8192^3 bf16 matrix product
-    (torch.matmul, i.e. the vendor GEMM library).  Reference points only: neither is part of the
-    decode path."""
+    """What the box reaches, next to the published peaks: a 1 GiB device-to-device copy (bytes
+    read + written / time), an 8192^3 bf16 matrix product (torch.matmul, i.e. the vendor GEMM
+    library) and the plain matrix-instruction loop (mfma_loop_rates).  Reference points only:
+    none is part of the decode path."""
     import torch
     x = torch.empty(1 << 30, dtype=torch.uint8, device="cuda:0").fill_(1)
     y = torch.empty_like(x)
@@ -425,6 +474,7 @@ def attainable(log):
     del A, Bm, C
     r = {"copy_GBps": round(2 * (1 << 30) / (copy_ms * 1e-3) / 1e9, 1),
          "bf16_gemm_8192_TFLOPs": round(2 * n ** 3 / (mm_ms * 1e-3) / 1e12, 1)}
+    r.update(mfma_loop_rates(log))
     log(f"[bench] attainable: {r}")
     return r
 
@@ -527,6 +577,11 @@ def main() -> int:
     if width:
         line["model_width_projections"] = width
     if reach:
+        # the split-K decode's matrix rate (K1 + K2, algorithmic FLOPs) against the loop's
+        loop = reach["fp8_mfma_loop_TFLOPs" if main_r["dtype"].startswith("fp8") else "bf16_mfma_loop_TFLOPs"]
+        tfl = main_r["flops"] / (main_r["k1_k2_ms"]["mean"] * 1e-3) / 1e12
+        reach["k1_k2_TFLOPs"] = round(tfl, 1)
+        reach["k1_k2_of_mfma_loop"] = round(tfl / loop, 4)
         line["attainable"] = reach
     if "cpu_baseline" in main_r:
         line["cpu_baseline"] = main_r["cpu_baseline"]

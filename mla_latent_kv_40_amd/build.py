@@ -1,4 +1,5 @@
-"""Build libmla.so in-tree with hipcc for gfx950 (cross-compiles without a GPU).
+"""Build libmla.so (and the measurement aid libmla_attainable.so) in-tree with hipcc for gfx950
+(cross-compiles without a GPU).
 
     python -m mla_latent_kv_40_amd.build [--save-temps DIR]
     python -m mla_latent_kv_40_amd.build --host-sanitize OUT.so   # host code under ASan + UBSan
@@ -15,6 +16,9 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 SOURCES = ["libmla.cpp", "append.hip", "absorb.hip", "decode.hip", "project.hip", "gqa.hip"]
 LIB = os.path.join(HERE, "libmla.so")
+# the matrix-instruction loop the benchmark times for the attainable matrix rate (not in libmla)
+ATTAINABLE_SOURCES = ["attainable.hip"]
+ATTAINABLE_LIB = os.path.join(HERE, "libmla_attainable.so")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -34,6 +38,7 @@ EXTRA = {
     "project.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
     "gqa.hip": [],
     "libmla.cpp": [],
+    "attainable.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
 }
 
 
@@ -55,15 +60,23 @@ HOST_SANITIZE = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize
 
 
 def build(verbose: bool = False, save_temps: str | None = None, host_sanitize: str | None = None) -> str:
-    """Compile every source to an object (own flags) and link libmla.so; always recompiles.
-    host_sanitize: build instead a copy with the host code under ASan and UBSan, at that path."""
-    objdir = os.path.join(HERE, "_build_san" if host_sanitize else "_build")
+    """Compile every source to an object (own flags) and link libmla.so, then libmla_attainable.so;
+    always recompiles.  host_sanitize: build instead a copy of libmla with the host code under
+    ASan and UBSan, at that path (and nothing else)."""
+    out = _link(SOURCES, host_sanitize or LIB, verbose, save_temps, host_sanitize is not None)
+    if not host_sanitize:
+        _link(ATTAINABLE_SOURCES, ATTAINABLE_LIB, verbose, save_temps, False)
+    return out
+
+
+def _link(sources, out, verbose, save_temps, sanitize) -> str:
+    objdir = os.path.join(HERE, "_build_san" if sanitize else "_build")
     os.makedirs(objdir, exist_ok=True)
-    san = HOST_SANITIZE if host_sanitize else []
+    san = HOST_SANITIZE if sanitize else []
     if save_temps:
         os.makedirs(save_temps, exist_ok=True)
     objs = []
-    for src in SOURCES:
+    for src in sources:
         obj = os.path.join(objdir, src + ".o")
         cmd = [HIPCC, *FLAGS, *EXTRA[src], *san, "-c", os.path.join(CSRC, src), "-o", obj]
         if save_temps:
@@ -71,7 +84,6 @@ def build(verbose: bool = False, save_temps: str | None = None, host_sanitize: s
             cmd += ["-Rpass-analysis=kernel-resource-usage"]
         _run(cmd, cwd=save_temps, verbose=verbose, remarks=bool(save_temps))
         objs.append(obj)
-    out = host_sanitize or LIB
     tmp = out + ".tmp"
     _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *san, *objs, "-o", tmp], verbose=verbose)
     os.replace(tmp, out)

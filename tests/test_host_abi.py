@@ -328,3 +328,22 @@ def test_size_limits(L):
     assert kvd(8, 4, pages + 1, 16) == B.MLA_ERR_INVALID_ARG
     assert kvd(8, rows, 100, 16) == B.MLA_ERR_UNSUPPORTED
     assert kvd(128, 8192, 100, pages) == B.MLA_ERR_UNSUPPORTED
+
+
+def test_attainable_library_exports_and_validates():
+    """libmla_attainable (the matrix-instruction loop the benchmark times) exports what its
+    header declares and rejects bad arguments before any HIP call."""
+    path = os.path.join(ROOT, "mla_latent_kv_40_amd", "libmla_attainable.so")
+    if not os.path.exists(path):
+        pytest.fail("libmla_attainable.so is not built (run __graft_entry__.build())")
+    src = open(os.path.join(ROOT, "include", "mla_attainable.h")).read()
+    syms = set(re.findall(r"^\s*[A-Za-z_0-9]+\s*\*?\s*(mla_[a-z_0-9]+)\s*\(", src, re.M))
+    assert syms == {"mla_attainable_mfma_loop"}
+    L = ctypes.CDLL(path)
+    fn = L.mla_attainable_mfma_loop
+    fn.argtypes = [ctypes.c_int32] * 4 + [ctypes.c_void_p, ctypes.c_void_p]
+    fn.restype = ctypes.c_int32
+    for args in [(2, 256, 16, 0, FAKE), (-1, 256, 16, 0, FAKE), (0, 0, 16, 0, FAKE), (0, (1 << 20) + 1, 16, 0, FAKE),
+                 (0, 256, -1, 0, FAKE), (1, 256, (1 << 20) + 1, 0, FAKE), (0, 256, 16, 163841, FAKE),
+                 (1, 256, 16, -1, FAKE), (0, 256, 16, 0, None), (1, 256, 16, 0, FAKE + 4)]:
+        assert fn(*args, None) == -1, args
