@@ -1419,74 +1419,83 @@ __global__ void __launch_bounds__(256) combine_kernel(DecodeArgs a) {
   }
   const int g_lo = range_of_tile(cfirst, C_all, a.G);
   const int g_hi = range_of_tile(cfirst + nb - 1, C_all, a.G);
-  // Ranges between g_lo and g_hi with an empty cost interval (possible when the batch costs
-  // fewer units than there are ranges) wrote nothing: skip them.
-  auto empty = [&](int g) { return (long long)g * C_all / a.G == (long long)(g + 1) * C_all / a.G; };
+  // Walk of the ranges g_lo, g_lo + 1, ..: range g's cost interval starts at floor(g C / G), and
+  // with g C = floor(g C / G) G + rem, the next start is floor(g C / G) + C/G + carry (carry = 1
+  // when rem + C%G >= G).  A range whose interval is empty (possible when the batch costs fewer
+  // units than there are ranges) wrote nothing: it is skipped.  One division per sequence.
+  const long long cq = C_all / a.G, cr = C_all % a.G;
+  long long rem = ((long long)g_lo * C_all) % a.G;
+  auto walk_empty = [&]() {   // is the next range of the walk empty?  (advances the walk)
+    const bool e = cq == 0 && rem + cr < a.G;
+    rem += cr;
+    if (rem >= a.G) rem -= a.G;
+    return e;
+  };
   const float2* ml = reinterpret_cast<const float2*>(a.part_ml);
   auto slot = [&](int g) { return ((size_t)(g + b) * a.Sq + j); };
-  // partials (bf16) and (m, l) of the slots g .. g + kCombineBatch - 1 (zeros past g_hi)
+  // partials (bf16) and (m, l) of the slots g .. g + kCombineBatch - 1.  Every load is issued
+  // (a slot that is past g_hi or empty reads slot g_hi, which the range holding the sequence's
+  // last page wrote, and is then given weight 0), so the loads of a batch share one memory
+  // latency; the flags are wave-uniform.
   const size_t piece = (size_t)w * (32 * kDC) + (size_t)c * (8 * 512) + 8 * t;
   u32x4 v[kCombineBatch][2];
   float2 mv[kCombineBatch];
+  bool use[kCombineBatch];
   auto fetch = [&](int g) {
 #pragma unroll
     for (int k = 0; k < kCombineBatch; ++k) {
       const int gk = g + k;
-      if (gk <= g_hi && !empty(gk)) {
-        const uint16_t* src = a.part_o + slot(gk) * (kH * kDC) + piece;
+      use[k] = gk <= g_hi && !walk_empty();
+      const size_t sl = slot(use[k] ? gk : g_hi);
+      const uint16_t* src = a.part_o + sl * (kH * kDC) + piece;
 #pragma unroll
-        for (int i = 0; i < 2; ++i) v[k][i] = *reinterpret_cast<const u32x4*>(src + 2048 * i);
-        mv[k] = ml[slot(gk) * kH + h];
-      } else {
-#pragma unroll
-        for (int i = 0; i < 2; ++i) v[k][i] = u32x4{0u, 0u, 0u, 0u};
-        mv[k] = float2{0.f, 0.f};
-      }
+      for (int i = 0; i < 2; ++i) v[k][i] = *reinterpret_cast<const u32x4*>(src + 2048 * i);
+      mv[k] = ml[sl * kH + h];
     }
   };
-  // the first batch (all of a sequence's slots when it has at most kCombineBatch) is requested
-  // before anything waits: the maxima then come from the same loads
-  fetch(g_lo);
+  // Running maximum over the batches: acc and L are rescaled when a batch raises it (a
+  // sequence's slots mostly fit one batch, and then nothing is rescaled).  A segment with
+  // nothing visible (l = 0) holds zeros and gets weight 0; one marked by the fast path (l < 0)
+  // sends the head to the exact recomputation.
   float M = -INFINITY;
   bool redo = false;
-  if (g_hi - g_lo < kCombineBatch) {
-#pragma unroll
-    for (int k = 0; k < kCombineBatch; ++k) {   // (m, l) = (0, 0) for slots past g_hi or empty
-      if (mv[k].y < 0.f) redo = true;
-      else if (mv[k].y > 0.f) M = fmaxf(M, mv[k].x);
-    }
-  } else {
-#pragma unroll 4
-    for (int g = g_lo; g <= g_hi; ++g) {   // independent loads: several in flight
-      if (empty(g)) continue;
-      const float2 u = ml[slot(g) * kH + h];
-      if (u.y < 0.f) redo = true;
-      else if (u.y > 0.f) M = fmaxf(M, u.x);
-    }
-  }
   f32x4 acc[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   float L = 0.f;
-  if (!redo && M != -INFINITY) {
-    // a segment with nothing visible (l = 0) holds zeros and gets weight 0
-    for (int g = g_lo;;) {
-      if (g != g_lo) fetch(g);
+  for (int g = g_lo; g <= g_hi; g += kCombineBatch) {
+    fetch(g);
+    float Mb = M;
 #pragma unroll
-      for (int k = 0; k < kCombineBatch; ++k) {
-        const float wg = mv[k].y > 0.f ? __builtin_amdgcn_exp2f(mv[k].x - M) : 0.0f;
-        L += mv[k].y > 0.f ? wg * mv[k].y : 0.0f;
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            acc[2 * i + (e >> 1)][2 * (e & 1)] += wg * __uint_as_float(v[k][i][e] << 16);
-            acc[2 * i + (e >> 1)][2 * (e & 1) + 1] += wg * __uint_as_float(v[k][i][e] & 0xFFFF0000u);
-          }
-      }
-      g += kCombineBatch;
-      if (g > g_hi) break;
+    for (int k = 0; k < kCombineBatch; ++k) {
+      if (use[k] && mv[k].y < 0.f) redo = true;
+      if (use[k] && mv[k].y > 0.f) Mb = fmaxf(Mb, mv[k].x);
     }
+    if (Mb > M) {
+      const float r = M == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(M - Mb);
+      L *= r;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] *= r;
+      M = Mb;
+    }
+#pragma unroll
+    for (int k = 0; k < kCombineBatch; ++k) {
+      const bool live = use[k] && mv[k].y > 0.f;
+      const float wg = live ? __builtin_amdgcn_exp2f(mv[k].x - M) : 0.0f;
+      L += live ? wg * mv[k].y : 0.0f;
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc[2 * i + (e >> 1)][2 * (e & 1)] += wg * __uint_as_float(v[k][i][e] << 16);
+          acc[2 * i + (e >> 1)][2 * (e & 1) + 1] += wg * __uint_as_float(v[k][i][e] & 0xFFFF0000u);
+        }
+    }
+  }
+  if (redo || M == -INFINITY) {   // as before: nothing summed for a redone head; no token: zeros
+    L = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
   bool fin = __builtin_isfinite(L);
 #pragma unroll
