@@ -1634,9 +1634,9 @@ long long forced_split_tokens() { return env_positive("MLA_SPLIT_TOKENS", 1LL <<
 
 // Small batches: at least this many pages (of the block tables' capacity) per range.  A range
 // costs a fixed ~20K cycles (page table, queries, segment end) and a 128 KiB partial that the
-// combine reads back; at B = 16 x 4096 tokens, 128 ranges of 8 pages took 58 us for split +
-// combine against 67 us for 256 ranges of 4 (64 ranges: 76 us).
-constexpr int kMinRangePages = 8;
+// combine reads back; at B = 16 x 4096 tokens split + combine took 54.6 us with 128 ranges,
+// 51.4 with 160, 50.0 with 192, 50.5 with 224 and 51.5 with 256.
+constexpr int kMinRangePages = 5;
 
 // Most split workgroups (ranges x queries per sequence) a plan may launch; wider plans are refused.
 constexpr long long kMaxSplitGrid = 1LL << 23;

@@ -16,7 +16,7 @@ import pytest
 
 import oracle.mla_oracle as orc
 from mla_latent_kv_40_amd import binding as B, harness, workloads as wl
-from _common import bound, cache_rows, check, dsv2, host, log, oracle_for, run_state
+from _common import STORAGE_SHARE, bound, cache_rows, check, dsv2, host, log, oracle_for, run_state
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -142,7 +142,7 @@ def test_query_rows_without_tokens(fmt):
     o_lat = 0, lse = -inf (and a zero layer output); rows with p >= 0 attend to tokens 0 .. p,
     i.e. equal a one-query decode of length p + 1 (the causal multi-query reduction).  With the
     tile-scaled cache the rows are also checked against the oracle on the rows the cache holds
-    (1x), and the exact oracle at 4x where the storage alone stays within it."""
+    (1x), and the exact oracle at 4x where the storage alone leaves the kernel its 1x share."""
     log(f"case kv_len < Sq: lengths [2, 3, 1, 9], Sq=4, cache {fmt}")
     w, bt, seqs = dsv2(4, [2, 3, 1, 9], sq=4, seed=73, fmt=None if fmt == "bf16" else fmt)
     st = run_state(w, bt, seqs)
@@ -169,7 +169,7 @@ def test_query_rows_without_tokens(fmt):
                             keys_rotated=True)
             for k in ("o", "o_lat", "lse"):
                 check(f"b{b} j{j} {k} vs dequantised cache", got[k][row:row + 1], rd[k])
-                if np.max(np.abs(rd[k] - ref[k])) <= bound(ref[k], 4.0):
+                if np.max(np.abs(rd[k] - ref[k])) <= STORAGE_SHARE * bound(ref[k], 4.0):
                     check(f"b{b} j{j} {k}", got[k][row:row + 1], ref[k], 4.0)
 
 

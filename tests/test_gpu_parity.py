@@ -11,7 +11,7 @@ import pytest
 
 import oracle.mla_oracle as orc
 from mla_latent_kv_40_amd import harness, workloads as wl
-from _common import bound, cache_rows, check, dsv2, host, log, oracle_for, run_state, tiny_sequences
+from _common import STORAGE_SHARE, bound, cache_rows, check, dsv2, host, log, oracle_for, run_state, tiny_sequences
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -32,10 +32,11 @@ def compare_seq(w, bt, seqs, got, b, heads=None, factor=1.0, weights=None, tag="
     an fp8 cache (the oracle then sees the values before quantisation, so the gate covers the
     whole method).  For an fp8 cache a second check runs the oracle on the dequantised cache
     rows (codes x scales from the oracle's own quantiser) at the bf16 rule: what remains there is
-    the kernel's own arithmetic (its e4m3 query and probability terms), not the storage.  Where
-    the storage alone (the oracle on the dequantised rows against the oracle on the exact ones)
-    already exceeds the x4 bound, the format cannot meet it whatever the kernel does: that output
-    is logged and left to the second check."""
+    the kernel's own arithmetic (its e4m3 query and probability terms), not the storage.  The x4
+    bound is the format's share plus the kernel's x1 share (|gpu - exact| <= |gpu - dequantised|
+    + |dequantised - exact|): where the storage alone (the oracle on the dequantised rows against
+    the oracle on the exact ones) takes more than three quarters of it, a kernel within its x1
+    budget can cross x4, so that output is logged and left to the second check."""
     ref = oracle_for(w, bt, seqs, b, heads=heads, weights=weights)
     sl = slice(b * w.sq, (b + 1) * w.sq)
     hs = slice(None) if heads is None else list(heads)
@@ -45,7 +46,7 @@ def compare_seq(w, bt, seqs, got, b, heads=None, factor=1.0, weights=None, tag="
     for k in ("o", "o_lat", "lse"):
         if deq is not None:
             storage = float(np.max(np.abs(deq[k] - ref[k]))) / bound(ref[k], factor)
-            if storage > 1.0:
+            if storage > STORAGE_SHARE:
                 log(f"  {tag}b{b} {k}: storage alone is {storage:.3f} of the x{factor:g} bound (format limit); "
                     f"gpu is {float(np.max(np.abs(g[k] - ref[k]))) / bound(ref[k], factor):.3f} of it")
                 continue
