@@ -78,29 +78,27 @@ __device__ __forceinline__ void absorb_q_block(const AbsorbArgs& aq, const RopeT
     wv[i] = *reinterpret_cast<const u32x4*>(w_uk + (size_t)(128 * qc + (p >> 4)) * (kAbsH * kAbsDH) + h * kAbsDH +
                                             8 * (p & 15));
   }
+  // Rows past T read row T - 1 (T >= 1 here) and are zeroed or skipped where they are used: with
+  // a load or a zero chosen per row, the compiler waits for the loads before the next ones.
   // query rows t0 + p/16 (zeros past T)
   u32x4 qv[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int p = tid + 256 * i, t = t0 + (p >> 4);
-    qv[i] = u32x4{0u, 0u, 0u, 0u};
-    if (t < T) qv[i] = *reinterpret_cast<const u32x4*>(q_nope + ((size_t)t * kAbsH + h) * kAbsDH + 8 * (p & 15));
+    qv[i] = *reinterpret_cast<const u32x4*>(q_nope + ((size_t)(t < T ? t : T - 1) * kAbsH + h) * kAbsDH +
+                                           8 * (p & 15));
   }
   // positional part: rows t0 + 4i + qc (i < 16) x 32 pairs, pair e = tid + 256i' (i' < 2) being
-  // row t0 + 4(e/32) + qc, pair e%32 = tid%32
+  // row t0 + 4(e/32) + qc, pair e%32 = tid%32 (rows past T are not rotated)
   const int jp = tid & 31;
   const double th = theta.v[jp];
   uint32_t rx[2];
   int rpos[2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-    const int t = t0 + 4 * ((tid + 256 * i) >> 5) + qc;
-    rx[i] = 0u;
-    rpos[i] = 0;
-    if (t < T) {
-      rx[i] = *reinterpret_cast<const uint32_t*>(q_rope + ((size_t)t * kAbsH + h) * kAbsDR + 2 * jp);
-      rpos[i] = q_pos[t];
-    }
+    const int t = t0 + 4 * ((tid + 256 * i) >> 5) + qc, tc = t < T ? t : T - 1;
+    rx[i] = *reinterpret_cast<const uint32_t*>(q_rope + ((size_t)tc * kAbsH + h) * kAbsDR + 2 * jp);
+    rpos[i] = q_pos[tc];
   }
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
@@ -110,7 +108,8 @@ __device__ __forceinline__ void absorb_q_block(const AbsorbArgs& aq, const RopeT
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int p = tid + 256 * i;
-    *reinterpret_cast<u32x4*>(qst + (p >> 4) * kRowPitch + 16 * (p & 15)) = qv[i];
+    *reinterpret_cast<u32x4*>(qst + (p >> 4) * kRowPitch + 16 * (p & 15)) =
+        t0 + (p >> 4) < T ? qv[i] : u32x4{0u, 0u, 0u, 0u};
   }
   __syncthreads();
 
@@ -261,13 +260,14 @@ __global__ void __launch_bounds__(256) out_proj_mfma_kernel(
                                            8 * (p & 3));
   }
   // o_lat rows t0 .. t0+63 of head h: piece p = tid + 256i is row p/128 (= 2i + tid/128), floats
-  // 4(p%128) .. +3; rows past T are zeros
+  // 4(p%128) .. +3.  Rows past T read row T - 1 (T >= 1 here) and are staged as zeros: with a load
+  // or a zero chosen per row, the compiler waits for the loads before the next ones.
   f32x4 ov[32];
 #pragma unroll
   for (int i = 0; i < 32; ++i) {
     const int p = tid + 256 * i, t = t0 + (p >> 7);
-    ov[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (t < T) ov[i] = *reinterpret_cast<const f32x4*>(o_lat + ((size_t)t * kAbsH + h) * kAbsDC + 4 * (p & 127));
+    ov[i] = *reinterpret_cast<const f32x4*>(o_lat + ((size_t)(t < T ? t : T - 1) * kAbsH + h) * kAbsDC +
+                                           4 * (p & 127));
   }
 #pragma unroll
   for (int i = 0; i < 8; ++i) *reinterpret_cast<u32x4*>(wl + 16 * (tid + 256 * i)) = r[i];
@@ -284,8 +284,8 @@ __global__ void __launch_bounds__(256) out_proj_mfma_kernel(
     // stage rows 32rt .. 32rt+31 (pieces i = 16rt .. 16rt+15)
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const f32x4 x = ov[16 * rt + i];
       const int p = tid + 256 * i;
+      const f32x4 x = t0 + 32 * rt + (p >> 7) < T ? ov[16 * rt + i] : f32x4{0.f, 0.f, 0.f, 0.f};
       *reinterpret_cast<u32x2*>(ost + (p >> 7) * kOPitch + 8 * (p & 127)) =
           u32x2{cvt_pk_bf16(x[0], x[1]), cvt_pk_bf16(x[2], x[3])};
     }
