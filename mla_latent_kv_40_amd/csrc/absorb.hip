@@ -178,7 +178,10 @@ __global__ void __launch_bounds__(256) append_absorb_kernel(AppendArgs ap, Appen
                                                             RopeTheta theta, int n_append) {
   const int bid = blockIdx.x;
   if (bid < n_append) {
-    append_dsv2_token<CacheFmt>(ap, ath, bid * 4 + (threadIdx.x >> 6));
+    if constexpr (CacheFmt == MLA_FP8_E4M3_B32)
+      append_block_token(ap, ath, bid * 4 + (threadIdx.x >> 6));
+    else
+      append_dsv2_token<CacheFmt>(ap, ath, bid * 4 + (threadIdx.x >> 6));
   } else {
     const int a = bid - n_append;
     absorb_q_block(aq, theta, a % kAbsH, (a / kAbsH) % (kAbsDC / 128), a / (kAbsH * (kAbsDC / 128)));
@@ -406,14 +409,15 @@ hipError_t launch_append(const mla_config_t& cfg, void* cache, float* cache_scal
                          const void* c_kv, const void* k_r, const int32_t* pos, const int32_t* seq_of,
                          const int32_t* block_table, int batch, int max_blocks, int n, hipStream_t stream);
 
-// A step's append and absorption: one launch for the DeepSeek-V2 shape with bf16 activations,
-// else the two launches.
+// A step's append and absorption: one launch for the DeepSeek-V2 shape with bf16 activations
+// (every cache format), else the two launches.
 hipError_t launch_append_absorb(const mla_config_t& cfg, void* cache, float* cache_scale, int num_blocks,
                                 const void* c_kv, const void* k_r, const int32_t* pos, const int32_t* seq_of,
                                 const int32_t* block_table, int batch, int max_blocks, int n, const void* q_nope,
                                 const void* q_rope, const int32_t* q_pos, const void* w_uk, void* q_abs, int T,
                                 hipStream_t stream) {
-  if (n > 0 && T > 0 && append_dsv2_applies(cfg) && is_dsv2_shape(cfg)) {
+  const bool block8 = cfg.cache_dtype == MLA_FP8_E4M3_B32 && cfg.act_dtype == MLA_BF16;
+  if (n > 0 && T > 0 && (append_dsv2_applies(cfg) || block8) && is_dsv2_shape(cfg)) {
     const AppendArgs ap = append_args(cache, cache_scale, num_blocks, c_kv, k_r, pos, seq_of, block_table, batch,
                                       max_blocks, n);
     const AbsorbArgs aq{static_cast<const uint16_t*>(q_nope), static_cast<const uint16_t*>(q_rope), q_pos,
@@ -423,6 +427,9 @@ hipError_t launch_append_absorb(const mla_config_t& cfg, void* cache, float* cac
     if (cfg.cache_dtype == MLA_BF16)
       hipLaunchKernelGGL(append_absorb_kernel<MLA_BF16>, grid, dim3(256), 0, stream, ap, append_theta(cfg), aq,
                          rope_theta(cfg), n_append);
+    else if (block8)
+      hipLaunchKernelGGL(append_absorb_kernel<MLA_FP8_E4M3_B32>, grid, dim3(256), 0, stream, ap, append_theta(cfg),
+                         aq, rope_theta(cfg), n_append);
     else
       hipLaunchKernelGGL(append_absorb_kernel<MLA_FP8_E4M3>, grid, dim3(256), 0, stream, ap, append_theta(cfg), aq,
                          rope_theta(cfg), n_append);

@@ -145,20 +145,24 @@ def test_many_short_sequences():
         compare_seq(w, bt, seqs, got, b, heads=range(b % 5, 128, 11))
 
 
-@pytest.mark.parametrize("fp8", [False, True])
-def test_append_absorb_equals_the_two_calls(fp8):
-    log(f"case mla_append_absorb against mla_cache_append + mla_absorb_q (cache rows, scales, q_abs), fp8={fp8}")
-    w, bt, seqs = dsv2(70, np.arange(1, 71) * 7, seed=67, fp8=fp8)   # 70 query rows: two row blocks
+@pytest.mark.parametrize("fmt", ["bf16", "fp8", "fp8b"])
+def test_append_absorb_equals_the_two_calls(fmt):
+    log(f"case mla_append_absorb against mla_cache_append + mla_absorb_q (cache rows, scales, q_abs), {fmt}")
+    w, bt, seqs = dsv2(70, np.arange(1, 71) * 7, seed=67, fmt=None if fmt == "bf16" else fmt)   # 70 query rows
     fused = run_state(w, bt, seqs, fused=True)
     apart = run_state(w, bt, seqs, fused=False)
     # the written rows (slots past a sequence's length are never written: uninitialised memory)
     for b in range(w.batch):
         L = int(bt.kv_lens[b])
-        pages = torch.as_tensor(bt.block_table[b, (np.arange(L) // 64)], device=fused.cache.device, dtype=torch.long)
-        slots = torch.as_tensor(np.arange(L) % 64, device=fused.cache.device, dtype=torch.long)
+        t = np.arange(L)
+        pages = torch.as_tensor(bt.block_table[b, t // 64], device=fused.cache.device, dtype=torch.long)
+        slots = torch.as_tensor(t % 64, device=fused.cache.device, dtype=torch.long)
         assert torch.equal(fused.cache[pages, slots], apart.cache[pages, slots]), b
-        if fp8:
+        if fmt == "fp8":
             assert torch.equal(fused.cache_scale[pages, slots], apart.cache_scale[pages, slots]), b
+        elif fmt == "fp8b":   # the scales of the tiles (page, token half) the sequence wrote
+            halves = torch.as_tensor((t % 64) // 32, device=fused.cache.device, dtype=torch.long)
+            assert torch.equal(fused.cache_scale[pages, halves], apart.cache_scale[pages, halves]), b
     assert torch.equal(fused.q_abs, apart.q_abs)
     assert torch.equal(fused.out, apart.out)
 
