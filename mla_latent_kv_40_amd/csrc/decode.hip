@@ -815,6 +815,17 @@ __device__ __forceinline__ i32x2 lds_tr8(const uint8_t* __restrict__ base, uint3
   return __builtin_amdgcn_ds_read_tr8_b64_v2i32((MLA_LDS i32x2*)(lb + off));
 }
 
+// e4m3 codes of 16a and 16b packed into half Hi of `old`, the codes v_cvt_pk_fp8_f32 gives for 16a
+// and 16b: v_cvt_scalef32_pk_fp8_f32 with scale 2^-4 (it divides by the power of two of its
+// scale) saves the two multiplications.  The two matched bit for bit on 2^20 pairs of arbitrary
+// and of residual-range inputs on gfx950.
+template <bool Hi>
+__device__ __forceinline__ int cvt_pk_fp8_x16(float a, float b, int old) {
+  typedef short v2i16 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(
+      int, __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(__builtin_bit_cast(v2i16, old), a, b, 0.0625f, Hi));
+}
+
 // O tile += A . B on fp8 operands in the accumulation registers (hazards as for mfma_acc; the
 // 16-pass instruction needs 19 wait states before its results are read, see o_fence<20>).
 __device__ __forceinline__ void mfma8_acc(f32x16& acc, const i32x8& a, const i32x8& b, int sa, int sb) {
@@ -945,8 +956,8 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_fp8_kernel(DecodeArgs a) {
         int h = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, 0, false);
         h = __builtin_amdgcn_cvt_pk_fp8_f32(x2, x3, h, true);
         const auto h01 = __builtin_amdgcn_cvt_pk_f32_fp8(h, false), h23 = __builtin_amdgcn_cvt_pk_f32_fp8(h, true);
-        int l = __builtin_amdgcn_cvt_pk_fp8_f32((x0 - h01[0]) * 16.0f, (x1 - h01[1]) * 16.0f, 0, false);
-        l = __builtin_amdgcn_cvt_pk_fp8_f32((x2 - h23[0]) * 16.0f, (x3 - h23[1]) * 16.0f, l, true);
+        int l = cvt_pk_fp8_x16<false>(x0 - h01[0], x1 - h01[1], 0);
+        l = cvt_pk_fp8_x16<true>(x2 - h23[0], x3 - h23[1], l);
         hw[d] = h;
         lw[d] = l;
       }
@@ -1127,12 +1138,12 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_fp8_kernel(DecodeArgs a) {
       if ((h & 1) == 0) {   // low 16 bits of the block's packed words
         q.w = __builtin_amdgcn_cvt_pk_fp8_f32(t0, t1, 0, false);
         const auto hv = __builtin_amdgcn_cvt_pk_f32_fp8(q.w, false);
-        q.wl = __builtin_amdgcn_cvt_pk_fp8_f32((t0 - hv[0]) * 16.0f, (t1 - hv[1]) * 16.0f, 0, false);
+        q.wl = cvt_pk_fp8_x16<false>(t0 - hv[0], t1 - hv[1], 0);
         asm volatile("" : "+v"(q.lsum), "+v"(q.w), "+v"(q.wl));
       } else {              // high 16 bits
         q.pk[d] = __builtin_amdgcn_cvt_pk_fp8_f32(t0, t1, q.w, true);
         const auto hv = __builtin_amdgcn_cvt_pk_f32_fp8(q.pk[d], true);
-        q.pl[d] = __builtin_amdgcn_cvt_pk_fp8_f32((t0 - hv[0]) * 16.0f, (t1 - hv[1]) * 16.0f, q.wl, true);
+        q.pl[d] = cvt_pk_fp8_x16<true>(t0 - hv[0], t1 - hv[1], q.wl);
         asm volatile("" : "+v"(q.lsum), "+v"(q.pk[d]), "+v"(q.pl[d]));
       }
     } else if (p == 22) {
