@@ -1386,7 +1386,9 @@ __device__ void exact_head(const DecodeArgs& a, int b, int j, int h, int L, int 
 // (i < 2, eight values each), all of head 32w + t%32, so each thread needs one head's
 // weights.  The pieces and (m, l) of KB slots are requested together, so a sequence's slots
 // cost about one memory latency rather than one each; KB = 8 where sequences span many
-// ranges, else 4 (its registers allow more workgroups per CU).  The result goes
+// ranges (G >= 3B), 4 where G >= B, else 2 (the batch's unused slots still load a slot, so a
+// smaller batch reads less where rows have one or two slots, as in a prefill's single range;
+// fewer registers also allow more workgroups per CU).  The result goes
 // through LDS so that each head's 128 columns are written contiguously.  Heads marked by the
 // fast path (or whose sums are not finite) are then recomputed exactly, quarter by quarter.
 constexpr int kCombinePitch = 128 + 4;   // fp32 words per head in the LDS tile (spreads heads over banks)
@@ -1765,8 +1767,10 @@ hipError_t launch_decode(const mla_config_t& cfg, int num_cus, const void* q_abs
       // a sequence spans about G / B + 1 ranges
       if (G >= 3 * B)
         hipLaunchKernelGGL(combine_kernel<8>, dim3(B * Sq, kH / 32, 4), dim3(256), 0, stream, a);
-      else
+      else if (G >= B)
         hipLaunchKernelGGL(combine_kernel<4>, dim3(B * Sq, kH / 32, 4), dim3(256), 0, stream, a);
+      else   // fewer ranges than sequences (prefill: one range): mostly one slot per row
+        hipLaunchKernelGGL(combine_kernel<2>, dim3(B * Sq, kH / 32, 4), dim3(256), 0, stream, a);
     }
     return hipGetLastError();
   }
