@@ -94,6 +94,8 @@ __global__ void __launch_bounds__(256) append_kernel(
   }
 }
 
+// Block-scaled fp8 append (the format and the routine are in append_dsv2.h): one wave per batch
+// entry, four entries per workgroup.
 __global__ void __launch_bounds__(256) append_block_fp8_kernel(AppendArgs ap, AppendTheta theta) {
   append_block_token(ap, theta, blockIdx.x * 4 + (threadIdx.x >> 6));
 }
