@@ -7,9 +7,10 @@
 //
 // One wave per token, four tokens per 256-thread workgroup; rotation in fp64, one rounding
 // to the cache format.  FP8 rows get one fp32 scale amax/448 and e4m3 codes (value/scale).
-// The work is a few KB per step, so the kernel's time is its chain of memory round trips:
-// the DeepSeek-V2-shaped kernel issues the token's row loads together with its sequence
-// and position lookups, so only the page lookup waits on another load.
+// The work is a few KB per step, so the kernel's time is its chain of memory round trips: the
+// sequence and position lookups, the page lookup, then the token's row (the compiler keeps
+// the row loads behind the checks that may return early).  In a step the appends share a
+// launch with the query absorption, whose workgroups take longer.
 #include "append_dsv2.h"
 
 #include <cmath>

@@ -5,9 +5,9 @@
 // Only the latent and the positional key are stored (podcast "What Is Multi-head Latent
 // Attention ...", the paragraph on what the system caches); RoPE is applied to k_R at write
 // time, at the token's position (bembew "Multi-head Latent Attention", "Implementation Logic"
-// step 4).  The work is a few KB per step, so the time is the chain of memory round trips:
-// the token's row loads are issued with its sequence and position lookups, so only the page
-// lookup waits on another load.
+// step 4).  The work is a few KB per step, so the time is the chain of memory round trips
+// (sequence and position lookups, page, then the row: the compiler keeps the row loads
+// behind the checks that may return early).
 #pragma once
 #include "common.h"
 
