@@ -17,6 +17,7 @@ import pytest
 import oracle.mla_oracle as orc
 from mla_latent_kv_40_amd import binding as B, harness, workloads as wl
 from _common import STORAGE_SHARE, bound, cache_rows, check, dsv2, host, log, oracle_for, run_state
+from test_gpu_parity import compare_seq
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -136,6 +137,35 @@ def test_split_tokens_override_equals_range_count(fmt):
         assert np.array_equal(o_t, o_g) and np.array_equal(l_t, l_g), (n, G)
 
 
+@pytest.mark.parametrize("fmt,pages", [("bf16", 1021), ("fp8", 510)])
+def test_page_table_at_capacity(fmt, pages):
+    """One range holding as many pages as the split kernel's LDS page table takes: a single
+    sequence of `pages` full pages with the range count forced to 1.  The planner keeps one range
+    while B (max_blocks + w) fits the table (1,024 entries with w = 3 for bf16, 512 with w = 2
+    for fp8), i.e. up to 1,021 and 510 pages; the workspace size (one partial slot) shows that
+    it did.  Needles (latent x4) at t = 0, in the middle and on the last token make a lost or
+    misplaced page visible."""
+    L = 64 * pages
+    log(f"case page table at capacity, cache {fmt}: one sequence of {pages} pages ({L} tokens), one range")
+    w, bt, seqs = dsv2(1, [L], seed=79, fmt=None if fmt == "bf16" else fmt)
+    seqs[0]["c"] = seqs[0]["c"].copy()
+    for t in (0, L // 2, L - 1):
+        seqs[0]["c"][t] = seqs[0]["c"][t] * 4.0
+    old = os.environ.get("MLA_FORCE_SPLITS")
+    os.environ["MLA_FORCE_SPLITS"] = "1"
+    try:
+        st = run_state(w, bt, seqs)
+        got = host(st)
+    finally:
+        if old is None:
+            os.environ.pop("MLA_FORCE_SPLITS", None)
+        else:
+            os.environ["MLA_FORCE_SPLITS"] = old
+    one_slot = 128 * 512 * 2 + 128 * 2 * 4          # bf16 partial O and (m, l) of one slot
+    assert st.ws_bytes == one_slot, st.ws_bytes     # a single range (both parts 256-byte aligned)
+    compare_seq(w, bt, seqs, got, 0, heads=range(0, 128, 16), factor=4.0 if w.fp8 else 1.0, tag="capacity ")
+
+
 @pytest.mark.parametrize("fmt", ["bf16", "fp8b"])
 def test_query_rows_without_tokens(fmt):
     """kv_len < Sq: query j sits at p = kv_len - Sq + j; rows with p < 0 see no token and give
@@ -232,7 +262,6 @@ def test_chunked_extend_and_prefill(lengths, sq, fmt):
     count falls to CUs / Sq, so each query row's workgroup streams its sequence's pages.  The fp8
     cases append the chunk in the step (for tile scales, runs of up to 32 tokens per tile) and
     take the fp8 gate (the oracle on the rows the cache holds at 1x as well)."""
-    from test_gpu_parity import compare_seq
     log(f"case chunked extend / prefill: lengths {lengths}, Sq={sq}, cache {fmt}")
     w, bt, seqs = dsv2(len(lengths), lengths, sq=sq, seed=97, fmt=None if fmt == "bf16" else fmt)
     st = run_state(w, bt, seqs)
