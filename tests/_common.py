@@ -88,14 +88,15 @@ def host(st):
     return {"o": st.out.float().cpu().numpy(), "o_lat": st.o_lat.cpu().numpy(), "lse": st.lse.cpu().numpy()}
 
 
-def dsv2(batch, lengths, sq=1, seed=7, name="dsv2_b16_l4k", fp8=False, fmt=None):
+def dsv2(batch, lengths, sq=1, seed=7, name="dsv2_b16_l4k", fp8=False, fmt=None, shape=None):
     """A DeepSeek-V2-shaped batch with the given lengths; fp8=True or fmt="fp8" takes the cache
-    with token scales, fmt="fp8b" the one with tile scales."""
+    with token scales, fmt="fp8b" the one with tile scales.  shape (heads, d_h, d_r, d_c, d_v
+    overrides) gives another head shape with the same bf16 draws."""
     if fp8 or fmt == "fp8":
         name = "dsv2_b128_l8k_fp8"
     elif fmt == "fp8b":
         name = "dsv2_b128_l8k_fp8b"
-    w = wl.get(name, batch=batch, sq=sq, seed=seed, ctx_lo=0, ctx_hi=0)
+    w = wl.get(name, batch=batch, sq=sq, seed=seed, ctx_lo=0, ctx_hi=0, **(shape or {}))
     bt = wl.draw_batch(w)
     # replace the lengths with the requested ones (context + sq), rebuilding the page table
     kv = np.asarray(lengths, dtype=np.int32)

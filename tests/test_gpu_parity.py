@@ -93,6 +93,27 @@ def test_tiny_f32_from_hidden_states():
     check("tiny q_abs", st.q_abs.cpu().numpy(), qa, extra_rel=1e-4)
 
 
+# --------------------------------------------------------------------------- other shapes, bf16
+
+@pytest.mark.parametrize("sq", [1, 3])
+@pytest.mark.parametrize("shape", [dict(heads=16, d_h=64, d_r=32, d_c=128, d_v=64),
+                                   dict(heads=32, d_h=128, d_r=64, d_c=256, d_v=96)])
+def test_bf16_generic_shapes(shape, sq):
+    """bf16 cache and activations in head shapes other than DeepSeek-V2's: the generic kernels
+    (append with RoPE, absorption, the decode over whole sequences, the output projection) on
+    lengths around the page size, with causal rows for Sq = 3."""
+    log(f"case bf16 generic shape {shape}, Sq={sq}, lengths [3, 63, 64, 65, 200]")
+    w, bt, seqs = dsv2(5, [3, 63, 64, 65, 200], sq=sq, seed=103, shape=shape)
+    st = run_state(w, bt, seqs)
+    got = host(st)
+    for b in range(w.batch):
+        compare_seq(w, bt, seqs, got, b, tag="generic ")
+    qa = np.concatenate([orc.absorbed_query(s["q_c"], s["q_r"], bt.weights["W_UK"],
+                                            int(bt.kv_lens[b]) - w.sq + np.arange(w.sq), w.rope_base)
+                         for b, s in enumerate(seqs)])
+    check("generic q_abs", st.q_abs.float().cpu().numpy(), qa)
+
+
 # --------------------------------------------------------------------------- DS-V2 shapes, bf16
 
 def test_dsv2_edge_lengths_all_heads():
