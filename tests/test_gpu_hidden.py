@@ -6,7 +6,8 @@
   into W_O, against the oracle's unfolded o W_O.
 
 Cases: the tiny fp32 workload (d_model 512) and DeepSeek-V2 shapes with d_model 5120, the
-model width of DeepSeek-V2 (the pages give none for these workloads), bf16 and fp8 caches.
+model width of DeepSeek-V2 (the pages give none for these workloads), bf16 and fp8 caches, and
+d_model 1040 with a bf16 cache (the generic row products).
 """
 import numpy as np
 import pytest
@@ -135,9 +136,10 @@ def test_tiny_f32_layer_from_hidden_states():
     check("tiny folded weights", got_f, Wf, extra_rel=1e-4)
 
 
-@pytest.mark.parametrize("fmt", ["bf16", "fp8", "fp8b"])
-def test_dsv2_layer_from_hidden_states(fmt):
-    d_model = 5120
+@pytest.mark.parametrize("fmt,d_model", [("bf16", 5120), ("fp8", 5120), ("fp8b", 5120), ("bf16", 1040)])
+def test_dsv2_layer_from_hidden_states(fmt, d_model):
+    """d_model 5120 takes the matrix-core projections; 1040 (a multiple of 16, not of 64) the
+    generic row products for both projections and the folded output."""
     lengths = [300, 65, 1, 130]
     name = {"bf16": "dsv2_b16_l4k", "fp8": "dsv2_b128_l8k_fp8", "fp8b": "dsv2_b128_l8k_fp8b"}[fmt]
     w = wl.get(name, batch=len(lengths), seed=91)
