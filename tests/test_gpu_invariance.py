@@ -166,15 +166,17 @@ def test_page_table_at_capacity(fmt, pages):
     compare_seq(w, bt, seqs, got, 0, heads=range(0, 128, 16), factor=4.0 if w.fp8 else 1.0, tag="capacity ")
 
 
-@pytest.mark.parametrize("fmt", ["bf16", "fp8b"])
+@pytest.mark.parametrize("fmt", ["bf16", "fp8b", "bf16-generic"])
 def test_query_rows_without_tokens(fmt):
     """kv_len < Sq: query j sits at p = kv_len - Sq + j; rows with p < 0 see no token and give
     o_lat = 0, lse = -inf (and a zero layer output); rows with p >= 0 attend to tokens 0 .. p,
-    i.e. equal a one-query decode of length p + 1 (the causal multi-query reduction).  With the
+    i.e. equal a one-query decode of length p + 1 (the causal multi-query reduction); also in a
+    non-DeepSeek-V2 head shape (the generic kernels).  With the
     tile-scaled cache the rows are also checked against the oracle on the rows the cache holds
     (1x), and the exact oracle at 4x where the storage alone leaves the kernel its 1x share."""
     log(f"case kv_len < Sq: lengths [2, 3, 1, 9], Sq=4, cache {fmt}")
-    w, bt, seqs = dsv2(4, [2, 3, 1, 9], sq=4, seed=73, fmt=None if fmt == "bf16" else fmt)
+    shape = dict(heads=16, d_h=64, d_r=32, d_c=128, d_v=64) if fmt == "bf16-generic" else None
+    w, bt, seqs = dsv2(4, [2, 3, 1, 9], sq=4, seed=73, fmt="fp8b" if fmt == "fp8b" else None, shape=shape)
     st = run_state(w, bt, seqs)
     got = host(st)
     for b in range(w.batch):
