@@ -227,14 +227,15 @@ __global__ void __launch_bounds__(256) absorb_q_generic_kernel(
 constexpr int kOutDV = 128;
 
 // out^T[v, t] = W_UV,h^T[v, c] . o_lat^T[c, t] for one head h, output columns
-// v = 32qv .. 32qv+31 and the 64 query rows of block z.  The weight slice W_UV[:, h, 32qv .. +31]
-// (512 rows of 64 bytes) is copied to LDS once; the A operand (rows v, K = c) comes from it
-// through transposing reads, with the 64-byte pitch putting the four rows of one read on four
-// different 64-byte bank groups.  o_lat is read with each load instruction covering 1 KB of
-// one row (a fragment-shaped read, 32 rows of 32 bytes per instruction, costs the memory
-// pipeline about twice as long) and reaches the B operand (K = c, N = t) through an LDS stage
-// in bf16, 32 rows at a time.  The four waves split the contraction (wave w: c = 128w ..
-// 128w+127) and sum their partial tiles through LDS.
+// v = 64qv .. 64qv+63 and the 64 query rows of block z, by eight waves: wave w takes the
+// contraction quarter c = 128(w%4) .. +127 of the 32 columns 64qv + 32(w/4) .. +31, and the four
+// quarters' partial tiles are summed through LDS.  The weight slice W_UV[:, h, 64qv .. +63]
+// (512 rows of 128 bytes, one whole cache line per row) is copied to LDS once, as two planes of
+// 32 columns (64-byte rows); the A operand (rows v, K = c) comes from a plane through transposing
+// reads, with the 64-byte pitch putting the four rows of one read on four different 64-byte bank
+// groups.  o_lat is read with each load instruction covering 1 KB of one row and reaches the B
+// operand (K = c, N = t) through an LDS stage in bf16, 32 rows at a time.  (Against 32 columns
+// per four-wave workgroup: half the o_lat reads through L2, and whole lines of W_UV per row.)
 
 // ds_read_b64_tr_b16 (gfx950): within each group of 16 lanes, output lane i gets element i%4
 // of the four values read by source lane 4j + i/4, as its element j.
@@ -242,54 +243,63 @@ __device__ __forceinline__ bf16x4 op_tr16(const uint8_t* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)(const MLA_LDS uint8_t*)p);
 }
 
-constexpr int kOPitch = kAbsDC * 2 + 16;   // bytes per staged o_lat row (bf16; the pad spreads rows over banks)
+constexpr int kOutCols = 64;                   // output columns per workgroup
+constexpr int kOutThreads = 512;               // 8 waves: 4 contraction quarters x 2 column halves
 
-__global__ void __launch_bounds__(256) out_proj_mfma_kernel(
+__global__ void __launch_bounds__(kOutThreads) out_proj_mfma_kernel(
     const float* __restrict__ o_lat, const uint16_t* __restrict__ w_uv, uint16_t* __restrict__ out,
     int T) {
-  __shared__ __attribute__((aligned(16))) uint8_t wl[kAbsDC * 64];        // [c][32 v] bf16
-  __shared__ __attribute__((aligned(16))) uint8_t ost[32 * kOPitch];      // [32 t][512 c] bf16, then the reduction
-  static_assert(sizeof(f32x4) * 4 * 8 * kPassRows <= sizeof(ost), "reduction tile fits the stage");
-  f32x4 (*red)[8][kPassRows] = reinterpret_cast<f32x4 (*)[8][kPassRows]>(ost);   // [wave][v/4][t]
+  // [column half][c][32 v] bf16, then the reduction [quarter][half][v/4 in the half][t] of f32x4
+  __shared__ __attribute__((aligned(16))) uint8_t wl[2 * kAbsDC * 64];
+  // [32 t][512 c] bf16; the 16-byte chunk k of row t sits at chunk k ^ (t % 16), so that the 16
+  // rows one B-operand read touches fall on different banks
+  __shared__ __attribute__((aligned(16))) uint8_t ost[32 * kAbsDC * 2];
+  f32x4 (*red)[2][8][kPassRows] = reinterpret_cast<f32x4 (*)[2][8][kPassRows]>(wl);
+  static_assert(sizeof(f32x4) * 4 * 2 * 8 * kPassRows <= sizeof(wl), "reduction tile fits the weight stage");
   const int h = blockIdx.x, qv = blockIdx.y, t0 = kPassRows * blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int g = lane >> 5;                // K group of this lane: c = 16ks + 8g .. +7
-  // weight slice: piece p = tid + 256i is row p/4, bytes 16(p%4) .. of that row
+  const int kw = wave & 3, ch = wave >> 2;   // contraction quarter, column half
+  const int g = lane >> 5;                   // K group of this lane: c = 16ks + 8g .. +7
+  // weight slice: piece p = tid + 512i is row p/8, bytes 16(p%8) .. of the row's 128
   u32x4 r[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const int p = tid + 256 * i;
-    r[i] = *reinterpret_cast<const u32x4*>(w_uv + (size_t)(p >> 2) * (kAbsH * kOutDV) + h * kOutDV + 32 * qv +
-                                           8 * (p & 3));
+    const int p = tid + kOutThreads * i;
+    r[i] = *reinterpret_cast<const u32x4*>(w_uv + (size_t)(p >> 3) * (kAbsH * kOutDV) + h * kOutDV +
+                                           kOutCols * qv + 8 * (p & 7));
   }
-  // o_lat rows t0 .. t0+63 of head h: piece p = tid + 256i is row p/128 (= 2i + tid/128), floats
+  // o_lat rows t0 .. t0+63 of head h: piece p = tid + 512i is row p/128 (= 4i + tid/128), floats
   // 4(p%128) .. +3.  Rows past T read row T - 1 (T >= 1 here) and are staged as zeros: with a load
   // or a zero chosen per row, the compiler waits for the loads before the next ones.
-  f32x4 ov[32];
+  f32x4 ov[16];
 #pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    const int p = tid + 256 * i, t = t0 + (p >> 7);
+  for (int i = 0; i < 16; ++i) {
+    const int p = tid + kOutThreads * i, t = t0 + (p >> 7);
     ov[i] = *reinterpret_cast<const f32x4*>(o_lat + ((size_t)(t < T ? t : T - 1) * kAbsH + h) * kAbsDC +
                                            4 * (p & 127));
   }
 #pragma unroll
-  for (int i = 0; i < 8; ++i) *reinterpret_cast<u32x4*>(wl + 16 * (tid + 256 * i)) = r[i];
-  // A operand: source lane s = 16G + 4j + a reads row 128w + 16ks + 8(G/2) + j (+4 for the high
-  // half) at columns 16(G%2) + 4a .. +3, so that output lane l holds column l%32 of the tile
-  // and rows 8(l/32) .. +7 of the K-step, matching B.
+  for (int i = 0; i < 8; ++i) {
+    const int p = tid + kOutThreads * i, pc = p & 7;
+    *reinterpret_cast<u32x4*>(wl + ((pc >> 2) * kAbsDC + (p >> 3)) * 64 + 16 * (pc & 3)) = r[i];
+  }
+  // A operand: source lane s = 16G + 4j + a reads row 128kw + 16ks + 8(G/2) + j (+4 for the high
+  // half) at columns 16(G%2) + 4a .. +3 of its plane, so that output lane l holds column l%32 of
+  // the tile and rows 8(l/32) .. +7 of the K-step, matching B.
   const int G = lane >> 4, jr = (lane >> 2) & 3, ac = lane & 3;
-  const uint8_t* wb = wl + (128 * wave + 8 * (G >> 1) + jr) * 64 + 2 * (16 * (G & 1) + 4 * ac);
-  // B operand: lane l reads staged row l%32, columns 128w + 16ks + 8g .. +7
-  const uint8_t* ob = ost + (lane & 31) * kOPitch + 2 * (128 * wave + 8 * g);
+  const uint8_t* wb = wl + (ch * kAbsDC + 128 * kw + 8 * (G >> 1) + jr) * 64 + 2 * (16 * (G & 1) + 4 * ac);
+  // B operand: lane l reads staged row l%32, chunk 16kw + 2ks + g (columns 128kw + 16ks + 8g .. +7)
+  const int orow = lane & 31;
+  const uint8_t* ob = ost + orow * (kAbsDC * 2);
   f32x16 acc[2] = {};
 #pragma unroll
   for (int rt = 0; rt < 2; ++rt) {
-    // stage rows 32rt .. 32rt+31 (pieces i = 16rt .. 16rt+15)
+    // stage rows 32rt .. 32rt+31 (pieces i = 8rt .. 8rt+7)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int p = tid + 256 * i;
-      const f32x4 x = t0 + 32 * rt + (p >> 7) < T ? ov[16 * rt + i] : f32x4{0.f, 0.f, 0.f, 0.f};
-      *reinterpret_cast<u32x2*>(ost + (p >> 7) * kOPitch + 8 * (p & 127)) =
+    for (int i = 0; i < 8; ++i) {
+      const int p = tid + kOutThreads * i, row = p >> 7, k = (p & 127) >> 1;
+      const f32x4 x = t0 + 32 * rt + row < T ? ov[8 * rt + i] : f32x4{0.f, 0.f, 0.f, 0.f};
+      *reinterpret_cast<u32x2*>(ost + row * (kAbsDC * 2) + 16 * (k ^ (row & 15)) + 8 * (p & 1)) =
           u32x2{cvt_pk_bf16(x[0], x[1]), cvt_pk_bf16(x[2], x[3])};
     }
     __syncthreads();   // weight slice and stage written
@@ -298,31 +308,32 @@ __global__ void __launch_bounds__(256) out_proj_mfma_kernel(
       const bf16x4 lo = op_tr16(wb + 16 * ks * 64);
       const bf16x4 hi = op_tr16(wb + (16 * ks + 4) * 64);
       const bf16x8 a = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      const bf16x8 b = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(ob + 32 * ks));
+      const bf16x8 b =
+          __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(ob + 16 * ((16 * kw + 2 * ks + g) ^ (orow & 15))));
       acc[rt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[rt], 0, 0, 0);
     }
-    __syncthreads();   // stage reads done before it is rewritten (or reused for the reduction)
+    __syncthreads();   // stage and weight reads done before they are rewritten (or reused for the reduction)
   }
-  // acc[rt][4m + i] = partial out^T[v = 8m + 4g + i, t = 32rt + lane%32]
+  // acc[rt][4m + i] = partial out^T[v = 32ch + 8m + 4g + i, t = 32rt + lane%32]
 #pragma unroll
   for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
     for (int m = 0; m < 4; ++m)
-      red[wave][2 * m + g][32 * rt + (lane & 31)] =
+      red[kw][ch][2 * m + g][32 * rt + (lane & 31)] =
           f32x4{acc[rt][4 * m], acc[rt][4 * m + 1], acc[rt][4 * m + 2], acc[rt][4 * m + 3]};
   __syncthreads();
-  // thread tid: row t0 + tid/4, columns 32qv + 8(tid%4) .. +7
+  // thread tid: row t0 + tid/8, columns 64qv + 8(tid%8) .. +7 (half vh = tid%8/4)
   {
-    const int rr = tid >> 2, vc = tid & 3;
-    f32x4 s0 = red[0][2 * vc][rr], s1 = red[0][2 * vc + 1][rr];
+    const int rr = tid >> 3, vq = tid & 7, vh = vq >> 2, vc = vq & 3;
+    f32x4 s0 = red[0][vh][2 * vc][rr], s1 = red[0][vh][2 * vc + 1][rr];
 #pragma unroll
     for (int w = 1; w < 4; ++w) {
-      s0 += red[w][2 * vc][rr];
-      s1 += red[w][2 * vc + 1][rr];
+      s0 += red[w][vh][2 * vc][rr];
+      s1 += red[w][vh][2 * vc + 1][rr];
     }
     const int t = t0 + rr;
     if (t < T)
-      *reinterpret_cast<u32x4*>(out + ((size_t)t * kAbsH + h) * kOutDV + 32 * qv + 8 * vc) =
+      *reinterpret_cast<u32x4*>(out + ((size_t)t * kAbsH + h) * kOutDV + kOutCols * qv + 8 * vq) =
           u32x4{pack_bf16x2(s0[0], s0[1]), pack_bf16x2(s0[2], s0[3]), pack_bf16x2(s1[0], s1[1]),
                 pack_bf16x2(s1[2], s1[3])};
   }
@@ -388,9 +399,9 @@ hipError_t launch_out_proj(const mla_config_t& cfg, const float* o_lat, const vo
                            hipStream_t stream) {
   if (T == 0) return hipSuccess;
   if (cfg.act_dtype == MLA_BF16 && is_dsv2_shape(cfg)) {
-    hipLaunchKernelGGL(out_proj_mfma_kernel, dim3(kAbsH, kOutDV / 32, (T + kPassRows - 1) / kPassRows), dim3(256), 0,
-                       stream, o_lat,
-                       static_cast<const uint16_t*>(w_uv), static_cast<uint16_t*>(out), T);
+    hipLaunchKernelGGL(out_proj_mfma_kernel, dim3(kAbsH, kOutDV / kOutCols, (T + kPassRows - 1) / kPassRows),
+                       dim3(kOutThreads), 0, stream, o_lat, static_cast<const uint16_t*>(w_uv),
+                       static_cast<uint16_t*>(out), T);
     return hipGetLastError();
   }
   const size_t total = (size_t)T * cfg.num_heads * cfg.d_v;
