@@ -27,6 +27,10 @@ configs     the same measurement (shorter) for each DeepSeek-V2-shaped workload 
             fp32 case, with its bound and roofline fraction, and the oracle's max error / tolerance
             on the sequences its CPU sample covers
 cpu_baseline the fp64 oracle on the host cores, on a bounded sample of the same workload
+attainable  what the box reaches on plain work (with the configs): a 1 GiB copy, read streams
+            of ~1 GB (plain vector loads, and the split's buffer->LDS loads and LDS ring without
+            its arithmetic), the vendor bf16 GEMM and a loop of the split's matrix instructions;
+            and the split-K decode's read and matrix rates against the best of them
 """
 from __future__ import annotations
 
@@ -445,6 +449,51 @@ def mfma_loop_rates(log, settle_ms=300.0):
     return r
 
 
+READ_CHUNK = 36864   # one chunk of libmla_attainable's read streams (a bf16 half page)
+
+
+def read_rates(log, settle_ms=200.0):
+    """The HBM read bandwidth the chip sustains: libmla_attainable's read streams over a
+    ~1.06 GB buffer (bytes read / time, median of 20 launches after settle_ms of launches back
+    to back).  `read_vgpr` uses plain vector loads at 1, 4 and 8 workgroups per compute unit;
+    `read_lds` the decode split's buffer->LDS loads and four-stage LDS ring at one workgroup per
+    compute unit, the split's occupancy."""
+    import ctypes
+    import torch
+    L = ctypes.CDLL(ATTAINABLE_LIB)
+    fn = L.mla_attainable_read
+    fn.argtypes = [ctypes.c_int32, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+    fn.restype = ctypes.c_int32
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    nbytes = cus * READ_CHUNK * 112          # a multiple of every workgroup count below
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0").fill_(1)
+    out = torch.empty(8 * cus * 256, dtype=torch.int32, device="cuda:0")
+    stream = torch.cuda.current_stream()
+    r = {}
+    for kind, name, per_cu in ((0, "read_vgpr", 1), (0, "read_vgpr", 4), (0, "read_vgpr", 8), (1, "read_lds", 1)):
+        wgs = cus * per_cu
+
+        def launch():
+            rc = fn(kind, buf.data_ptr(), nbytes, wgs, out.data_ptr(), stream.cuda_stream)
+            if rc != 0:
+                raise RuntimeError(f"mla_attainable_read returned {rc}")
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < settle_ms * 1e-3:
+            for _ in range(10):
+                launch()
+            torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(20)]
+        for e0, e1 in evs:
+            e0.record(stream); launch(); e1.record(stream)
+        torch.cuda.synchronize()
+        ms = float(np.median([e0.elapsed_time(e1) for e0, e1 in evs]))
+        key = f"{name}_GBps" + ("" if kind == 1 else f"_{per_cu}wg_per_cu")
+        r[key] = round(nbytes / (ms * 1e-3) / 1e9, 1)
+    del buf, out
+    log(f"[bench] read streams: {r}")
+    return r
+
+
 def attainable(log):
     """What the box reaches, next to the published peaks: a 1 GiB device-to-device copy (bytes
     read + written / time), an 8192^3 bf16 matrix product (torch.matmul, i.e. the vendor GEMM
@@ -474,6 +523,7 @@ def attainable(log):
     del A, Bm, C
     r = {"copy_GBps": round(2 * (1 << 30) / (copy_ms * 1e-3) / 1e9, 1),
          "bf16_gemm_8192_TFLOPs": round(2 * n ** 3 / (mm_ms * 1e-3) / 1e12, 1)}
+    r.update(read_rates(log))
     r.update(mfma_loop_rates(log))
     log(f"[bench] attainable: {r}")
     return r
@@ -582,6 +632,11 @@ def main() -> int:
         tfl = main_r["flops"] / (main_r["k1_k2_ms"]["mean"] * 1e-3) / 1e12
         reach["k1_k2_TFLOPs"] = round(tfl, 1)
         reach["k1_k2_of_mfma_loop"] = round(tfl / loop, 4)
+        # the split-K decode's latent-cache read rate (K1 + K2) against the best read stream
+        gbps = main_r["bytes"] / (main_r["k1_k2_ms"]["mean"] * 1e-3) / 1e9
+        best = max(v for k, v in reach.items() if k.startswith("read_"))
+        reach["k1_k2_GBps"] = round(gbps, 1)
+        reach["k1_k2_of_best_read_stream"] = round(gbps / best, 4)
         line["attainable"] = reach
     if "cpu_baseline" in main_r:
         line["cpu_baseline"] = main_r["cpu_baseline"]

@@ -5,7 +5,9 @@
  * sustained matrix work the chip holds a lower clock, so a kernel bound by matrix instructions
  * is better read against what the chip sustains.  This library gives that figure: a loop of
  * matrix instructions with no memory traffic, on every compute unit, timed by the caller.
- * Together with a device-to-device copy it gives the attainable rates that a decode kernel's
+ * Two read-only streams of a device buffer give the HBM read bandwidth the chip sustains, one
+ * with plain vector loads and one with the buffer->LDS loads and LDS ring of the decode split.
+ * Together with a device-to-device copy they give the attainable rates that a decode kernel's
  * roofline fraction can be read against.
  */
 #ifndef LIBMLA_ATTAINABLE_H
@@ -40,6 +42,32 @@ typedef enum {
  */
 int32_t mla_attainable_mfma_loop(int32_t kind, int32_t workgroups, int32_t iters, int32_t lds_bytes, float* out,
                                  void* stream);
+
+/* Ways a read stream brings the buffer in. */
+typedef enum {
+  MLA_READ_VGPR = 0, /* 16-byte vector loads into registers (non-temporal), nine per chunk and
+                        lane, issued before they are summed; any number of workgroups per CU */
+  MLA_READ_LDS = 1   /* 16-byte buffer->LDS loads (1 KiB per wave instruction) into a ring of
+                        four 36,864-byte LDS stages, three chunks in flight, one barrier per
+                        chunk: the decode split's loads without its arithmetic; all of a
+                        compute unit's LDS (147,456 B) per workgroup, so one per CU */
+} mla_read_kind_t;
+
+/*
+ * mla_attainable_read -- read `bytes` of `buf` once.  The buffer is cut into chunks of 36,864 B
+ * (a half page of the bf16 decode split); workgroup w (of `workgroups`, 256 threads each) reads
+ * the contiguous chunks w*n .. w*n+n-1, n = bytes / (workgroups * 36864).  Every 32-bit word
+ * is read by exactly one thread, which adds it into a wrapping 32-bit sum.
+ *   buf  device, 256-byte aligned, `bytes` long; bytes must be a multiple of
+ *        workgroups * 36864, and one workgroup's slice below 2^31 bytes.
+ *   out  [workgroups * 256] uint32, device, 16-byte aligned: each thread's sum.  The sum of
+ *        all of them equals the sum of the buffer's 32-bit words mod 2^32.
+ * Bytes read / time is the read bandwidth.  Asynchronous on `stream` (a hipStream_t; NULL is
+ * the default stream).  Returns 0; -1 for an argument out of range (nothing launched; checked
+ * before any HIP call); otherwise the HIP error code of the failed call.
+ */
+int32_t mla_attainable_read(int32_t kind, const void* buf, int64_t bytes, int32_t workgroups, uint32_t* out,
+                            void* stream);
 
 #ifdef __cplusplus
 }

@@ -1,5 +1,6 @@
 // libmla_attainable: a loop of matrix instructions with no memory traffic, for measuring the
-// matrix rate the device sustains (see include/mla_attainable.h).  A measurement aid only.
+// matrix rate the device sustains, and two read-only streams of a device buffer, for the HBM
+// read bandwidth it sustains (see include/mla_attainable.h).  A measurement aid only.
 #include <hip/hip_runtime.h>
 
 #include <atomic>
@@ -90,6 +91,89 @@ __global__ void __launch_bounds__(256) loop_fp8_kernel(int iters, float* out) {
   out[tid] = chain_sum(acc);
 }
 
+// ---- read-only streams.  The buffer is cut into chunks of kChunk bytes (a half page of the
+// bf16 decode split: 32 rows of 1152 B); workgroup w reads chunks w*n .. w*n+n-1.  Every 32-bit
+// word is read exactly once, by one lane, which adds it to its running sum (wrapping), so the
+// sum of all lanes' outputs is the sum of the buffer's words mod 2^32.
+constexpr int kChunk = 36864;
+constexpr int kChunkLoads = kChunk / 4096;   // 16-byte loads per lane and chunk (one workgroup)
+constexpr int kRing = 4;                     // LDS stages of the DMA stream
+constexpr int kRingDepth = kRing - 1;        // chunks in flight ahead of the one being read
+
+// s_waitcnt immediate: at most n vector-memory operations outstanding (gfx9 encoding, the other
+// counters left alone).
+constexpr int waitcnt_vm(int n) { return (n & 15) | (((n >> 4) & 3) << 14) | (7 << 4) | (15 << 8); }
+
+// Plain vector loads into registers: per chunk, each lane loads nine 16-byte pieces 4 KiB apart
+// (256 lanes x 16 B = 4 KiB contiguous per load instruction), all nine issued before the sum.
+__global__ void __launch_bounds__(256) read_vgpr_kernel(const uint8_t* __restrict__ buf, int chunks_per_wg,
+                                                        uint32_t* out) {
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  const uint8_t* base = buf + (size_t)blockIdx.x * chunks_per_wg * kChunk + 16 * threadIdx.x;
+  uint32_t acc = 0;
+  for (int c = 0; c < chunks_per_wg; ++c) {
+    u32x4 v[kChunkLoads];
+#pragma unroll
+    for (int i = 0; i < kChunkLoads; ++i)
+      v[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + (size_t)c * kChunk + 4096 * i));
+#pragma unroll
+    for (int i = 0; i < kChunkLoads; ++i) acc += v[i][0] + v[i][1] + v[i][2] + v[i][3];
+  }
+  out[blockIdx.x * 256 + threadIdx.x] = acc;
+}
+
+// The decode split's way in: 1 KiB buffer->LDS loads (each wave nine per chunk) into a ring of
+// four LDS stages, three chunks in flight, one barrier per chunk; each lane then reads back the
+// nine 16-byte pieces it loaded and sums them.  One workgroup per compute unit (all of its LDS).
+__global__ void __launch_bounds__(256, 1) read_lds_kernel(const uint8_t* __restrict__ buf, int chunks_per_wg,
+                                                          uint32_t* out) {
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  extern __shared__ __attribute__((aligned(256))) uint8_t smem[];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const uint8_t* slice = buf + (size_t)blockIdx.x * chunks_per_wg * kChunk;
+  // the descriptor covers this workgroup's slice exactly; the chunk offset goes in soffset
+  const __amdgpu_buffer_rsrc_t rsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)slice, 0, chunks_per_wg * kChunk, 0x00020000);
+  auto issue = [&](int c) {
+    uint8_t* stage = smem + (c % kRing) * kChunk;
+#pragma unroll
+    for (int i = 0; i < kChunkLoads; ++i) {
+      const int piece = kChunkLoads * wave + i;   // 1 KiB piece of the chunk
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)(stage + 1024 * piece),
+                                               16, 1024 * piece + 16 * lane, c * kChunk, 0, 0);
+    }
+  };
+  uint32_t acc = 0;
+  for (int c = 0; c < kRingDepth && c < chunks_per_wg; ++c) issue(c);
+  for (int c = 0; c < chunks_per_wg; ++c) {
+    // this wave's loads of chunk c have landed (those of up to two younger chunks may not),
+    // then everyone's; the stage refilled below was last read in the previous iteration
+    const int younger = (chunks_per_wg - 1 - c) < (kRingDepth - 1) ? (chunks_per_wg - 1 - c) : (kRingDepth - 1);
+    if (younger >= 2)
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * kChunkLoads));
+    else if (younger == 1)
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(kChunkLoads));
+    else
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (c + kRingDepth < chunks_per_wg) issue(c + kRingDepth);
+    // read through an absolute LDS address with a restrict pointer: through the shared array the
+    // compiler would wait for every load in flight, which it takes to alias the stage
+    const uint32_t stage = (uint32_t)(size_t)(const __attribute__((address_space(3))) uint8_t*)smem +
+                           (uint32_t)((c % kRing) * kChunk);
+#pragma unroll
+    for (int i = 0; i < kChunkLoads; ++i) {
+      const __attribute__((address_space(3))) u32x4* __restrict__ q =
+          (const __attribute__((address_space(3))) u32x4*)(size_t)(stage + 1024 * (kChunkLoads * wave + i) + 16 * lane);
+      const u32x4 v = *q;
+      acc += v[0] + v[1] + v[2] + v[3];
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+  out[blockIdx.x * 256 + threadIdx.x] = acc;
+}
+
 // The kernels reserve dynamic LDS beyond the default limit: raised once per device (idempotent
 // calls; the mark is set only after they succeed).
 constexpr int kMaxDev = 64;
@@ -104,6 +188,8 @@ hipError_t set_lds_limits() {
   e = hipFuncSetAttribute((const void*)loop_bf16_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLds);
   if (e == hipSuccess)
     e = hipFuncSetAttribute((const void*)loop_fp8_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLds);
+  if (e == hipSuccess)
+    e = hipFuncSetAttribute((const void*)read_lds_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLds);
   if (e == hipSuccess && mark) mark->store(1, std::memory_order_release);
   return e;
 }
@@ -123,5 +209,25 @@ extern "C" int32_t mla_attainable_mfma_loop(int32_t kind, int32_t workgroups, in
     hipLaunchKernelGGL(loop_bf16_kernel, dim3(workgroups), dim3(256), lds_bytes, s, iters, out);
   else
     hipLaunchKernelGGL(loop_fp8_kernel, dim3(workgroups), dim3(256), lds_bytes, s, iters, out);
+  return (int32_t)hipGetLastError();
+}
+
+extern "C" int32_t mla_attainable_read(int32_t kind, const void* buf, int64_t bytes, int32_t workgroups, uint32_t* out,
+                                       void* stream) {
+  if (kind != MLA_READ_VGPR && kind != MLA_READ_LDS) return -1;
+  if (workgroups <= 0 || workgroups > (1 << 16) || bytes <= 0) return -1;
+  if (bytes % ((int64_t)workgroups * kChunk) != 0) return -1;
+  const int64_t per = bytes / ((int64_t)workgroups * kChunk);
+  if (per > (int64_t)(0x7fffffff / kChunk)) return -1;   // a slice must fit one buffer descriptor
+  if (buf == nullptr || out == nullptr) return -1;
+  if ((reinterpret_cast<uintptr_t>(buf) & 255u) || (reinterpret_cast<uintptr_t>(out) & 15u)) return -1;
+  hipError_t e = set_lds_limits();
+  if (e != hipSuccess) return (int32_t)e;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const uint8_t* b = static_cast<const uint8_t*>(buf);
+  if (kind == MLA_READ_VGPR)
+    hipLaunchKernelGGL(read_vgpr_kernel, dim3(workgroups), dim3(256), 0, s, b, (int)per, out);
+  else
+    hipLaunchKernelGGL(read_lds_kernel, dim3(workgroups), dim3(256), kRing * kChunk, s, b, (int)per, out);
   return (int32_t)hipGetLastError();
 }

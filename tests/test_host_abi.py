@@ -338,8 +338,20 @@ def test_attainable_library_exports_and_validates():
         pytest.fail("libmla_attainable.so is not built (run __graft_entry__.build())")
     src = open(os.path.join(ROOT, "include", "mla_attainable.h")).read()
     syms = set(re.findall(r"^\s*[A-Za-z_0-9]+\s*\*?\s*(mla_[a-z_0-9]+)\s*\(", src, re.M))
-    assert syms == {"mla_attainable_mfma_loop"}
+    assert syms == {"mla_attainable_mfma_loop", "mla_attainable_read"}
     L = ctypes.CDLL(path)
+    rd = L.mla_attainable_read
+    rd.argtypes = [ctypes.c_int32, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+    rd.restype = ctypes.c_int32
+    chunk = 36864
+    for args in [(2, FAKE, 256 * chunk, 256, FAKE), (-1, FAKE, 256 * chunk, 256, FAKE),
+                 (0, FAKE, 256 * chunk, 0, FAKE), (1, FAKE, 256 * chunk, (1 << 16) + 1, FAKE),
+                 (0, FAKE, 0, 256, FAKE), (1, FAKE, -chunk, 1, FAKE),
+                 (0, FAKE, 256 * chunk + 4, 256, FAKE), (1, FAKE, 255 * chunk, 256, FAKE),
+                 (0, FAKE, (1 << 31) // chunk * chunk + chunk, 1, FAKE),   # one slice above 2^31 - 1 bytes
+                 (0, None, 256 * chunk, 256, FAKE), (1, FAKE, 256 * chunk, 256, None),
+                 (0, FAKE + 16, 256 * chunk, 256, FAKE), (1, FAKE, 256 * chunk, 256, FAKE + 4)]:
+        assert rd(*args, None) == -1, args
     fn = L.mla_attainable_mfma_loop
     fn.argtypes = [ctypes.c_int32] * 4 + [ctypes.c_void_p, ctypes.c_void_p]
     fn.restype = ctypes.c_int32
