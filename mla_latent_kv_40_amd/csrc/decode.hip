@@ -473,7 +473,8 @@ constexpr float kOverflowSum = 0x1p80f;
 //           of token step k is the lane's own probabilities i = 8k .. 8k+7, i.e. tokens
 //           16k + 8(e/4) + 4(l/32) + e%4; the transposing reads deliver V^T in that order.
 // The page loop is software-pipelined by one half page: step y computes the scores of half
-// page y+1 and accumulates the values of half page y, whose probabilities it already holds.
+// page y+1, with the probabilities of half page y (from the raw scores of the step before)
+// worked out between those score MFMAs, then accumulates the values of half page y.
 // Every segment (the part of one sequence inside the range) ends with its unnormalised O and
 // (m, l) per head in workspace slot g + b.
 template <int Aux>
@@ -567,13 +568,16 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_bf16_kernel(DecodeArgs a) 
   // ---- softmax of one half page: raw scores sv -> bf16 probabilities against the segment
   // reference (log2 units).  `fresh` starts a new segment.  The softmax scale rides in the
   // FMA that feeds exp2; l sums the bf16-rounded probabilities (dot2 with ones), the same
-  // values that enter P.V.
+  // values that enter P.V.  soft_begin masks the tail and, when the segment's reference is not
+  // yet set, takes the maximum (a block); the eight probability pairs (soft_pair) then run
+  // between the score MFMAs of the next half page, and soft_end collects them.
   struct Soft {
-    float m_new, l_new;
+    float m_new, l_new, m_use;
     bool over_new, m_set_new;
+    bf16x2 pk[8];
     bf16x8 p0, p1;
   };
-  auto softmax = [&](f32x16& sv, int vis, bool fresh, Soft& st) {
+  auto soft_begin = [&](f32x16& sv, int vis, bool fresh, Soft& st) {
     if (vis < kHalf - 1) {   // partial half page (sequence end, causal limit): mask the tail
 #pragma unroll
       for (int i = 0; i < 16; ++i)
@@ -591,18 +595,20 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_bf16_kernel(DecodeArgs a) 
     } else {
       st.m_new = m_in;
     }
-    const float m_use = (st.m_new == -INFINITY) ? 0.0f : st.m_new;
-    float l = fresh ? 0.0f : l_run;
+    st.m_use = (st.m_new == -INFINITY) ? 0.0f : st.m_new;
+    st.l_new = fresh ? 0.0f : l_run;
+    st.over_new = fresh ? false : over;
+  };
+  auto soft_pair = [&](const f32x16& sv, int u, Soft& st) {
+    const float c = a.scale_log2;
     const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-    bf16x2 pk[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      pk[u] = bf16x2{(__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(sv[2 * u], c, -m_use)),
-                     (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(sv[2 * u + 1], c, -m_use))};
-      l = __builtin_amdgcn_fdot2_f32_bf16(pk[u], ones, l, false);
-    }
-    st.l_new = l;
-    st.over_new = (fresh ? false : over) || !(l < kOverflowSum);   // also catches inf and NaN
+    st.pk[u] = bf16x2{(__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(sv[2 * u], c, -st.m_use)),
+                      (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(sv[2 * u + 1], c, -st.m_use))};
+    st.l_new = __builtin_amdgcn_fdot2_f32_bf16(st.pk[u], ones, st.l_new, false);
+  };
+  auto soft_end = [&](Soft& st) {
+    st.over_new = st.over_new || !(st.l_new < kOverflowSum);   // also catches inf and NaN
+    const bf16x2* pk = st.pk;
     st.p0 = bf16x8{pk[0][0], pk[0][1], pk[1][0], pk[1][1], pk[2][0], pk[2][1], pk[3][0], pk[3][1]};
     st.p1 = bf16x8{pk[4][0], pk[4][1], pk[5][0], pk[5][1], pk[6][0], pk[6][1], pk[7][0], pk[7][1]};
   };
@@ -701,11 +707,9 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_bf16_kernel(DecodeArgs a) 
   issue(load_for(2, e2.x, nvalid(e2, 2), 0));
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(18));
   lds_barrier();
-  {
-    f32x16 s0 = scores(smem, [](int) {});
-    softmax(s0, last_visible(e0, 0), true, sm);
-    soft_commit(sm);
-  }
+  // raw scores of half page 0; its softmax runs under the score MFMAs of half page 1
+  f32x16 s_cur = scores(smem, [](int) {});
+  bool fresh_cur = true;   // half page y starts a segment
 
   // one step; P = y & 1 (a compile-time constant: the loop below runs two steps per page)
   auto step = [&](int y, auto par) {
@@ -722,23 +726,28 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_bf16_kernel(DecodeArgs a) 
     const PageLoad pl = load_for((y + 3) & 3, e3.x, nvalid(e3, y + 3), 1 - P);
     const bool seg_end = (P == 1 && (e0.w & kLast)) || !has_next;
     if (seg_end && has_next) {
-      // the next half page starts another sequence: its queries replace this one's (waiting
-      // here keeps the steady-state loop free of pending query loads)
+      // the next half page starts another sequence: its queries replace this one's before its
+      // scores (waiting here keeps the steady-state loop free of pending query loads)
       load_q(e1.z);
       __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     }
-    // values of half page y first: a segment's stores then go out before this step's page
-    // loads (the wait at the top of the next step covers both) and have the score MFMAs to
-    // drain, and the probabilities of y are dead during the scores of y+1
-    const float m_old = m_ref, l_old = l_run;
-    const bool over_old = over;
+    // scores of half page y+1, with the probabilities of half page y computed between its
+    // matrix instructions (one pair of tokens after every fourth, between the page loads)
+    soft_begin(s_cur, last_visible(e0, y), fresh_cur, sm);
+    f32x16 sv = scores(smem + ((y + 1) & 3) * kStageBytes, [&](int st) {   // stale data if !has_next
+      if ((st & 3) == 0) load_row<Aux>(pl, st >> 2, wave, src[st >> 2]);
+      if ((st & 3) == 2) soft_pair(s_cur, st >> 2, sm);
+    });
+    soft_end(sm);
+    soft_commit(sm);
+    // values of half page y
     values(smem + (y & 3) * kStageBytes, pf);
     if (seg_end) {
       // unnormalised O and (m, l) of this segment into its slot; the combine normalises
-      const float l_tot = pair_sum(l_old);
-      const bool over_seg = pair_sum(over_old ? 1.0f : 0.0f) > 0.0f;   // either half of the head
+      const float l_tot = pair_sum(l_run);
+      const bool over_seg = pair_sum(over ? 1.0f : 0.0f) > 0.0f;   // either half of the head
       const size_t row = ((size_t)(g + e0.z) * a.Sq + j) * kH + head;
-      if (hl == 0) reinterpret_cast<float2*>(a.part_ml)[row] = float2{m_old, over_seg ? -1.0f : l_tot};
+      if (hl == 0) reinterpret_cast<float2*>(a.part_ml)[row] = float2{m_ref, over_seg ? -1.0f : l_tot};
       uint16_t* so = slot_o(e0.z);
       o_fence<20>(oacc);   // results of the last accumulation settled before the stores
       store_partial(so, oacc);
@@ -747,14 +756,8 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_bf16_kernel(DecodeArgs a) 
         for (int t = 0; t < 16; ++t) mfma_zero(oacc[t], zero8);
       }
     }
-    f32x16 sv = scores(smem + ((y + 1) & 3) * kStageBytes, [&](int st) {   // stale data if !has_next
-      if ((st & 3) == 0) load_row<Aux>(pl, st >> 2, wave, src[st >> 2]);
-    });
-    // softmax of half page y+1 (a compact block: on one wave per SIMD, vector instructions
-    // cost the same wherever they sit between the matrix instructions)
-    softmax(sv, last_visible(e1, y + 1), seg_end, sm);
-
-    soft_commit(sm);
+    s_cur = sv;
+    fresh_cur = seg_end;
     // all four words stay live until here (a word the compiler finds unused would otherwise
     // have its register recycled while the read is still in flight, which forces a wait)
     asm volatile("" ::"v"(e4_raw));
